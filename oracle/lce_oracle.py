@@ -1,0 +1,224 @@
+"""CPU oracle for the fused LM-head linear + cross-entropy (linear-LSE).
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously correct reference
+the HIP path is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.  It
+shares no code with the HIP path: it reads nothing from the package
+`linear_cross_entropy_lse_amd` and the package reads nothing from here.
+
+Everything is float64 numpy.  Inputs are the bf16 bits of X and W widened
+exactly to float64, so the oracle sees the same numbers the GPU sees.
+
+Sources (web pages, cited by title and section):
+  [CCE-blog]  "最贵的一层：深入浅出 Liger Kernel 与 Cut Cross-Entropy"
+              (blog.jiaqiguo.xyz), §二 (gradient softmax − onehot), §三 (loss as
+              LSE minus the indexed target logit; running max / sum-exp merge;
+              backward by recomputation).
+  [M011]      AI-infra knowledge base, page M011 (fused Linear + loss), §01 (W[V,D],
+              Z = H·Wᵀ), §03 (stable per-row form and the worked example),
+              §04 (sum per block, divide once by the valid-target count), §05
+              (tile merge, first tile initialises), §06 (backward: p − onehot,
+              scaled by normalisation and upstream gradient, dH += dZ·W,
+              dW += dZᵀ·H), §07 (ignore_index, softcap needs its own definition,
+              all-ignored convention must be stated).
+  [Unsloth]   "03 · 融合交叉熵：让 logits 从不存在" (Unsloth fused cross-entropy
+              chapter), §4 (optional in-kernel softcap scaling; label −100 gives
+              loss 0; backward multiplies the softcap derivative 1 − tanh²;
+              final division by n_items = count of labels ≠ −100).
+
+Readings where the pages leave a step open (each restated where it is used):
+  R1 softcap: z = c·tanh(z_raw / c) is applied to every logit, the target
+     included, before the LSE; its derivative is 1 − tanh²(z_raw / c); c <= 0
+     means no softcap.
+  R2 no intermediate rounding of logits: they are exact float64 products of
+     the bf16 inputs.
+  R3 the LSE of an ignored row is still reported (it depends on X and W only);
+     its loss is 0 and it is excluded from the valid count.
+  R4 the mean divides by the number of valid targets; when that count is 0
+     the mean is 0 and both gradients are 0.
+  R5 `dloss` is the scalar upstream gradient of the mean loss.
+  R6 a label outside [0, V) that is not ignore_index gives a NaN loss for its
+     row (and therefore a NaN mean); its gradient row is NaN.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+IGNORE_INDEX = -100
+
+
+# --------------------------------------------------------------------------- #
+# Building blocks
+# --------------------------------------------------------------------------- #
+def logits(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Z = X · Wᵀ with W stored [V, H] ([M011] §01)."""
+    return X @ W.T
+
+
+def apply_softcap(Z: np.ndarray, softcap: float) -> np.ndarray:
+    """Reading R1: c·tanh(Z/c) when c > 0, else Z unchanged ([Unsloth] §4)."""
+    if softcap > 0:
+        return softcap * np.tanh(Z / softcap)
+    return Z
+
+
+def softcap_derivative(Z: np.ndarray, softcap: float) -> np.ndarray:
+    """d(c·tanh(z/c))/dz = 1 − tanh²(z/c) ([Unsloth] §4 backward); 1 if off."""
+    if softcap > 0:
+        t = np.tanh(Z / softcap)
+        return 1.0 - t * t
+    return np.ones_like(Z)
+
+
+def row_logsumexp(Zc: np.ndarray) -> np.ndarray:
+    """Per-row log Σ_v exp(z_v) in the stable form m + log Σ exp(z − m),
+    m = max_v z ([M011] §03)."""
+    m = Zc.max(axis=1)
+    return m + np.log(np.exp(Zc - m[:, None]).sum(axis=1))
+
+
+def logsumexp_by_vocab_tiles(z: Sequence[float], bounds: Sequence[int]) -> float:
+    """LSE of one logit row visited tile by tile with the running merge.
+
+    `bounds` are the tile edges over the vocabulary (0 = b0 < b1 < ... = V).
+    Each tile yields its own max m_b and its own Σ exp(z − m_b); they are folded
+    into (m, s) with m' = max(m, m_b), s' = s·e^(m − m') + s_b·e^(m_b − m'),
+    and the result is m + log s ([CCE-blog] §三; [M011] §05).  The first tile
+    initialises (m, s) directly so no −inf − (−inf) is ever formed.
+    Plain Python floats: used by the pins on tiny rows.
+    """
+    m = None
+    s = 0.0
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        tile = [float(v) for v in z[a:b]]
+        m_b = max(tile)
+        s_b = math.fsum(math.exp(v - m_b) for v in tile)
+        if m is None:
+            m, s = m_b, s_b
+            continue
+        m_new = max(m, m_b)
+        s = s * math.exp(m - m_new) + s_b * math.exp(m_b - m_new)
+        m = m_new
+    return m + math.log(s)
+
+
+def valid_mask(labels: np.ndarray, ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+    """Rows that carry a target: label ≠ ignore_index ([M011] §07; [Unsloth] §4)."""
+    return labels != ignore_index
+
+
+def bad_mask(labels: np.ndarray, V: int, ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+    """Reading R6: labels neither ignored nor in [0, V)."""
+    return (labels != ignore_index) & ((labels < 0) | (labels >= V))
+
+
+# --------------------------------------------------------------------------- #
+# Forward
+# --------------------------------------------------------------------------- #
+def forward(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
+            ignore_index: int = IGNORE_INDEX, softcap: float = 0.0,
+            n_valid_total: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Per-row LSE and loss, valid count and mean over valid targets.
+
+    loss_i = LSE(z_i) − z_{i, y_i} ([CCE-blog] §三; [M011] §03), 0 for ignored
+    rows ([Unsloth] §4).  mean = Σ_i loss_i / n_valid ([M011] §04; [Unsloth] §4).
+    `n_valid_total` lets a caller evaluate a subset of rows while dividing by
+    the count of the whole batch (the definition is row-separable).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    Z = logits(X, W)
+    Zc = apply_softcap(Z, softcap)
+    lse = row_logsumexp(Zc)
+    valid = valid_mask(labels, ignore_index)
+    bad = bad_mask(labels, V, ignore_index)
+    ok = valid & ~bad
+    target = np.zeros(X.shape[0])
+    rows = np.nonzero(ok)[0]
+    target[rows] = Zc[rows, labels[rows]]
+    loss = np.where(valid, lse - target, 0.0)
+    loss[bad] = np.nan
+    n_valid = int(valid.sum()) if n_valid_total is None else int(n_valid_total)
+    total = loss.sum()
+    mean = total / n_valid if n_valid > 0 else 0.0      # reading R4
+    return {"lse": lse, "loss": loss, "n_valid": n_valid, "mean": mean,
+            "loss_sum": total, "target_logit": target}
+
+
+# --------------------------------------------------------------------------- #
+# Backward
+# --------------------------------------------------------------------------- #
+def logit_gradient(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
+                   lse: np.ndarray, n_valid: int, dloss: float = 1.0,
+                   ignore_index: int = IGNORE_INDEX, softcap: float = 0.0,
+                   vocab_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """dL/dz_raw for the rows of X (all vocabulary columns, or `vocab_rows`).
+
+    The logits are recomputed, p = exp(z − LSE) ([CCE-blog] §三; [M011] §06),
+    dZ = p − onehot(y) ([CCE-blog] §二; [M011] §06), multiplied by the softcap
+    derivative ([Unsloth] §4) and by dloss / n_valid ([M011] §06, §04).
+    Ignored rows have zero gradient.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    Z = logits(X, W[cols])
+    Zc = apply_softcap(Z, softcap)
+    P = np.exp(Zc - lse[:, None])
+    onehot = (labels[:, None] == cols[None, :]).astype(np.float64)
+    dZ = (P - onehot) * softcap_derivative(Z, softcap)
+    valid = valid_mask(labels, ignore_index)
+    scale = (dloss / n_valid) if n_valid > 0 else 0.0      # reading R4
+    dZ = dZ * (scale * valid)[:, None]
+    bad = bad_mask(labels, V, ignore_index)
+    dZ[bad] = np.nan
+    return dZ
+
+
+def backward(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
+             dloss: float = 1.0, ignore_index: int = IGNORE_INDEX,
+             softcap: float = 0.0, lse: Optional[np.ndarray] = None):
+    """(dX, dW) of the mean loss: dX = dZ · W and dW = dZᵀ · X ([M011] §06;
+    the same two contractions appear in [CCE-blog] §二 for the row-chunked
+    variant).  `lse` defaults to the oracle's own forward."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    fwd = forward(X, W, labels, ignore_index, softcap)
+    if lse is None:
+        lse = fwd["lse"]
+    dZ = logit_gradient(X, W, labels, lse, fwd["n_valid"], dloss,
+                        ignore_index, softcap)
+    return dZ @ W, dZ.T @ X
+
+
+def dX_rows(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
+            lse_rows: np.ndarray, n_valid: int, dloss: float = 1.0,
+            ignore_index: int = IGNORE_INDEX, softcap: float = 0.0) -> np.ndarray:
+    """dX for a subset of rows: each row of dX depends on its own row only."""
+    dZ = logit_gradient(X_rows, W, labels_rows, lse_rows, n_valid, dloss,
+                        ignore_index, softcap)
+    return dZ @ np.asarray(W, dtype=np.float64)
+
+
+def dW_vocab_rows(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
+                  lse: np.ndarray, n_valid: int, vocab_rows: np.ndarray,
+                  dloss: float = 1.0, ignore_index: int = IGNORE_INDEX,
+                  softcap: float = 0.0) -> np.ndarray:
+    """dW[v] for selected vocabulary rows v: dW[v] = Σ_i dZ[i, v] · x_i over
+    every token row i (needs the LSE of every row)."""
+    dZ = logit_gradient(X, W, labels, lse, n_valid, dloss, ignore_index,
+                        softcap, vocab_rows=vocab_rows)
+    return dZ.T @ np.asarray(X, dtype=np.float64)
+
+
+def mean_loss_value(X, W, labels, ignore_index=IGNORE_INDEX, softcap=0.0):
+    """Scalar mean loss (used by the finite-difference pins)."""
+    return float(forward(X, W, labels, ignore_index, softcap)["mean"])

@@ -1,0 +1,119 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check the pins notice.
+
+Each mutation replaces one oracle building block by a subtly wrong one; the
+pin suite must then fail at least one of its checks.  This guards the pins
+themselves: a pin set that passes a wrong oracle pins nothing.
+"""
+import numpy as np
+import pytest
+
+from oracle import lce_oracle as O
+from tests import test_oracle_pins as P
+
+PINS = [
+    P.test_worked_example_loss_matches_page,
+    P.test_worked_example_two_tile_merge_and_wrong_value_rejected,
+    P.test_worked_example_gradient_is_softmax_minus_onehot,
+    P.test_textbook_softmax_definition_bruteforce,
+    lambda: P.test_matches_torch_cross_entropy_and_autograd(0.0),
+    lambda: P.test_matches_torch_cross_entropy_and_autograd(2.5),
+    lambda: P.test_finite_differences(0.0),
+    lambda: P.test_finite_differences(0.9),
+    P.test_ignored_rows_contribute_nothing,
+    P.test_zero_weight_closed_form,
+    P.test_bounds_nonnegativity_and_gradient_row_sums,
+]
+
+_orig_forward = O.forward
+_orig_logit_gradient = O.logit_gradient
+
+
+def _forward_mean_over_all_rows(X, W, labels, ignore_index=-100, softcap=0.0, n_valid_total=None):
+    out = _orig_forward(X, W, labels, ignore_index, softcap, n_valid_total)
+    out["n_valid"] = len(labels)
+    out["mean"] = out["loss_sum"] / len(labels)
+    return out
+
+
+def _forward_target_off_by_one(X, W, labels, ignore_index=-100, softcap=0.0, n_valid_total=None):
+    out = _orig_forward(X, W, labels, ignore_index, softcap, n_valid_total)
+    Zc = O.apply_softcap(O.logits(np.asarray(X, float), np.asarray(W, float)), softcap)
+    V = Zc.shape[1]
+    t = np.array([Zc[i, (y + 1) % V] if y != ignore_index else 0.0 for i, y in enumerate(labels)])
+    out["loss"] = np.where(labels != ignore_index, out["lse"] - t, 0.0)
+    out["mean"] = out["loss"].sum() / max(out["n_valid"], 1)
+    return out
+
+
+def _forward_uncapped_target(X, W, labels, ignore_index=-100, softcap=0.0, n_valid_total=None):
+    out = _orig_forward(X, W, labels, ignore_index, softcap, n_valid_total)
+    Z = O.logits(np.asarray(X, float), np.asarray(W, float))
+    t = np.array([Z[i, y] if y != ignore_index else 0.0 for i, y in enumerate(labels)])
+    out["loss"] = np.where(labels != ignore_index, out["lse"] - t, 0.0)
+    out["mean"] = out["loss"].sum() / max(out["n_valid"], 1)
+    return out
+
+
+def _grad_without_onehot(X, W, labels, lse, n_valid, dloss=1.0, ignore_index=-100,
+                         softcap=0.0, vocab_rows=None):
+    g = _orig_logit_gradient(X, W, labels, lse, n_valid, dloss, ignore_index, softcap, vocab_rows)
+    V = np.asarray(W).shape[0]
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    onehot = (np.asarray(labels)[:, None] == cols[None, :])
+    valid = (np.asarray(labels) != ignore_index)[:, None]
+    s = dloss / n_valid if n_valid else 0.0
+    d = O.softcap_derivative(O.logits(np.asarray(X, float), np.asarray(W, float)[cols]), softcap)
+    return g + s * onehot * valid * d
+
+
+def _grad_wrong_sign(X, W, labels, lse, n_valid, dloss=1.0, ignore_index=-100,
+                     softcap=0.0, vocab_rows=None):
+    return -_orig_logit_gradient(X, W, labels, lse, n_valid, dloss, ignore_index, softcap, vocab_rows)
+
+
+def _bad_softcap_derivative(Z, softcap):
+    if softcap > 0:
+        t = np.tanh(Z / softcap)
+        return 1.0 + t * t
+    return np.ones_like(Z)
+
+
+def _no_softcap_derivative(Z, softcap):
+    return np.ones_like(Z)
+
+
+def _transposed_logits(X, W):
+    # uses the weight as if it were stored [H, V] (the orientation conflict
+    # between the pages): only differs for square/compatible shapes, else raises
+    return X @ np.asarray(W).reshape(np.asarray(W).shape[::-1])
+
+
+def _lse_without_log(Zc):
+    m = Zc.max(axis=1)
+    return m + np.exp(Zc - m[:, None]).sum(axis=1) - 1.0
+
+
+MUTATIONS = {
+    "mean_over_all_rows": ("forward", _forward_mean_over_all_rows),
+    "target_off_by_one": ("forward", _forward_target_off_by_one),
+    "uncapped_target": ("forward", _forward_uncapped_target),
+    "gradient_without_onehot": ("logit_gradient", _grad_without_onehot),
+    "gradient_wrong_sign": ("logit_gradient", _grad_wrong_sign),
+    "softcap_derivative_sign": ("softcap_derivative", _bad_softcap_derivative),
+    "softcap_derivative_dropped": ("softcap_derivative", _no_softcap_derivative),
+    "weight_transposed": ("logits", _transposed_logits),
+    "lse_missing_log": ("row_logsumexp", _lse_without_log),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:       # AssertionError or a shape error: both are catches
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
