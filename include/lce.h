@@ -1,0 +1,131 @@
+/*
+ * lce.h — fused LM-head linear + cross-entropy ("linear-LSE") for AMD gfx950.
+ *
+ * C ABI of liblce.so.  Every pointer argument named *_dev is a device pointer
+ * (HIP device memory of the current device); every other pointer is host
+ * memory.  All matrices are dense, row-major and contiguous.  The library never
+ * allocates or frees memory: the caller owns every buffer, including the
+ * workspace, whose size it obtains from the *_workspace_bytes queries.
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *   z_iv    = x_i · w_v                      logits, never stored
+ *             (AI-infra KB page M011, §01: W is [V, D] and Z = H·Wᵀ)
+ *   z_iv   <- c·tanh(z_iv / c)              optional logit softcap, c > 0
+ *             (Unsloth fused cross-entropy chapter, §4: in-kernel softcap)
+ *   LSE_i   = log Σ_v exp(z_iv)             (blog "最贵的一层：深入浅出 Liger
+ *             Kernel 与 Cut Cross-Entropy", §三; M011 §03, §05)
+ *   loss_i  = LSE_i − z_{i,y_i}, or 0 when y_i == ignore_index
+ *             (same blog §三: loss as LSE minus the indexed target logit;
+ *             Unsloth chapter §4: label −100 gives 0)
+ *   mean    = Σ_i loss_i / n_valid, n_valid = #{i : y_i ≠ ignore_index}
+ *             (M011 §04; Unsloth chapter §4, division by n_items)
+ *   dZ_iv   = (dloss / n_valid)·(softmax(z_i)_v − [v == y_i])·(1 − tanh²(z_raw/c))
+ *             (blog §二/§三: softmax − onehot, recomputed from the saved LSE;
+ *             M011 §06; Unsloth chapter §4 for the softcap derivative)
+ *   dX      = dZ · W,   dW = dZᵀ · X        (M011 §06)
+ *
+ * Conventions where the pages leave a choice open:
+ *   - labels are already shifted (position i holds the target of row i);
+ *   - the LSE of an ignored row is still written; its loss is 0;
+ *   - when every row is ignored, mean = 0 and dX = dW = 0;
+ *   - a label that is neither ignore_index nor in [0, V) sets the bad-label
+ *     flag, gives a NaN loss for that row (so a NaN mean) and NaN gradients;
+ *   - results are bitwise reproducible for fixed inputs, shapes and device:
+ *     no floating-point atomics are used anywhere.
+ *
+ * Shapes and alignment (checked on the host before anything is launched):
+ *   N >= 0 tokens, 1 <= H < 2^20 with H % 8 == 0, 1 <= V < 2^31, N < 2^31;
+ *   X_dev, W_dev, dX_dev, dW_dev must be 16-byte aligned, labels_dev 8-byte,
+ *   workspace_dev 256-byte aligned.
+ *
+ * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without waiting.  Calls are re-entrant;
+ * concurrent calls on different streams need separate workspaces.
+ */
+#ifndef LCE_H_
+#define LCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCE_OK = 0,
+  LCE_ERR_INVALID_ARG = 1, /* a required pointer is NULL, or an enum is out of range */
+  LCE_ERR_SHAPE = 2,       /* N, H or V outside the limits above (H % 8 != 0 included) */
+  LCE_ERR_ALIGNMENT = 3,   /* a pointer breaks the alignment rules above */
+  LCE_ERR_WORKSPACE = 4,   /* workspace_bytes is below the size the query returns */
+  LCE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} lce_status;
+
+typedef enum {
+  LCE_F32 = 0,  /* IEEE float32 */
+  LCE_BF16 = 1  /* bfloat16, round-to-nearest-even from the float32 result */
+} lce_dtype;
+
+/* Workspace (device bytes) lce_forward needs for these sizes; 0 if the shape
+ * is invalid.  Pure host computation. */
+size_t lce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V);
+
+/* Workspace lce_backward needs.  With dW_dtype == LCE_BF16 the library keeps
+ * one float32 vocabulary chunk of dW in the workspace before rounding it. */
+size_t lce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V,
+                                    lce_dtype dW_dtype);
+
+/*
+ * Forward.
+ *   X_dev       bf16 [N, H]   hidden states
+ *   W_dev       bf16 [V, H]   LM-head weight (lm_head.weight orientation)
+ *   labels_dev  int64 [N]     targets in [0, V) or ignore_index
+ *   softcap     c > 0 enables z <- c·tanh(z/c); c <= 0 disables it
+ * Outputs (all written, none read):
+ *   loss_dev    float [N]     per-row loss (0 for ignored rows)
+ *   lse_dev     float [N]     per-row log-sum-exp; the only tensor the
+ *                             backward needs besides the inputs
+ *   mean_dev    float [1]     Σ loss / n_valid (0 when n_valid == 0)
+ *   n_valid_dev int32 [1]     number of rows with a target
+ *   bad_label_dev int32 [1]   1 if any label is out of range, else 0; may be NULL
+ * The N×V logits are never stored; the workspace is O(N) bytes.
+ */
+lce_status lce_forward(const void* X_dev, const void* W_dev,
+                       const int64_t* labels_dev, int64_t N, int64_t H,
+                       int64_t V, int64_t ignore_index, float softcap,
+                       float* loss_dev, float* lse_dev, float* mean_dev,
+                       int32_t* n_valid_dev, int32_t* bad_label_dev,
+                       void* workspace_dev, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Backward of the mean loss.
+ *   lse_dev     float [N]     LSE written by lce_forward for the same inputs
+ *   dloss_dev   float [1]     upstream gradient d(objective)/d(mean)
+ *   dX_dev      [N, H] of dX_dtype, overwritten
+ *   dW_dev      [V, H] of dW_dtype, overwritten
+ * The logits are recomputed tile by tile from X, W and the LSE.  The dense
+ * part of dZ is rounded to bf16 for the two gradient contractions, which
+ * accumulate in float32; the one-hot part (−1 at the target, times the
+ * softcap derivative there) is applied exactly in float32.  The workspace
+ * holds one bf16 vocabulary chunk of dZ (never the whole N×V matrix).
+ */
+lce_status lce_backward(const void* X_dev, const void* W_dev,
+                        const int64_t* labels_dev, const float* lse_dev,
+                        const float* dloss_dev, int64_t N, int64_t H,
+                        int64_t V, int64_t ignore_index, float softcap,
+                        void* dX_dev, lce_dtype dX_dtype, void* dW_dev,
+                        lce_dtype dW_dtype, void* workspace_dev,
+                        size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lce_status_string(lce_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H_ */

@@ -1,0 +1,10 @@
+"""Fused LM-head linear + cross-entropy (linear-LSE) for AMD gfx950 (MI355X).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+`include/lce.h` (liblce.so, built in-tree by `linear_cross_entropy_lse_amd.build`).
+This package is a thin binding with the same names, plus an autograd wrapper.
+"""
+from ._lib import (LCE_BF16, LCE_F32, LceError, lce_backward,  # noqa: F401
+                   lce_backward_workspace_bytes, lce_forward, lce_forward_workspace_bytes,
+                   lce_version, load, status_string)
+from .autograd import LinearCrossEntropy, linear_cross_entropy  # noqa: F401

@@ -1,0 +1,184 @@
+"""ctypes binding of liblce.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+include/lce.h; this module only checks tensors, allocates outputs and the
+workspace with torch, and passes raw device pointers and the current HIP
+stream.  There is no fallback: if the library is not built, importing the
+binding's entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblce.so")
+
+LCE_OK = 0
+LCE_ERR_INVALID_ARG = 1
+LCE_ERR_SHAPE = 2
+LCE_ERR_ALIGNMENT = 3
+LCE_ERR_WORKSPACE = 4
+LCE_ERR_HIP = 5
+LCE_F32 = 0
+LCE_BF16 = 1
+
+# Every symbol include/lce.h declares.
+EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_forward",
+            "lce_backward", "lce_status_string", "lce_version")
+
+_lib = None
+
+
+class LceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load liblce.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"liblce.so is not built ({p}); run "
+                           "`python -m linear_cross_entropy_lse_amd.build`")
+    lib = ctypes.CDLL(p)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.lce_forward_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.lce_forward_workspace_bytes.restype = sz
+    lib.lce_backward_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.lce_backward_workspace_bytes.restype = sz
+    lib.lce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lce_forward.restype = ctypes.c_int
+    lib.lce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                 vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
+    lib.lce_backward.restype = ctypes.c_int
+    lib.lce_status_string.argtypes = [ctypes.c_int]
+    lib.lce_status_string.restype = ctypes.c_char_p
+    lib.lce_version.argtypes = []
+    lib.lce_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().lce_status_string(int(status)).decode()
+
+
+def lce_version() -> int:
+    return int(load().lce_version())
+
+
+def lce_forward_workspace_bytes(N: int, H: int, V: int) -> int:
+    return int(load().lce_forward_workspace_bytes(N, H, V))
+
+
+def lce_backward_workspace_bytes(N: int, H: int, V: int, dW_dtype=None) -> int:
+    return int(load().lce_backward_workspace_bytes(N, H, V, _dtype_code(dW_dtype)))
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype is None or dtype == torch.float32:
+        return LCE_F32
+    if dtype == torch.bfloat16:
+        return LCE_BF16
+    raise ValueError(f"gradient dtype must be float32 or bfloat16, got {dtype}")
+
+
+def _check(status: int, where: str):
+    if status != LCE_OK:
+        raise LceError(status, where)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None and t.numel() > 0 else 0
+
+
+def _prep(X, W, labels):
+    import torch
+    if not (X.is_cuda and W.is_cuda and labels.is_cuda):
+        raise ValueError("X, W and labels must be device (HIP) tensors")
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("X and W must be bfloat16")
+    if labels.dtype != torch.int64:
+        raise ValueError("labels must be int64")
+    if X.dim() != 2 or W.dim() != 2 or labels.dim() != 1:
+        raise ValueError("expected X [N, H], W [V, H], labels [N]")
+    if X.shape[1] != W.shape[1] or labels.shape[0] != X.shape[0]:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, "
+                         f"labels {tuple(labels.shape)}")
+    # Kernels address memory directly: non-contiguous views would be read wrong.
+    return X.contiguous(), W.contiguous(), labels.contiguous()
+
+
+def _stream(dev) -> int:
+    import torch
+    return int(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def lce_forward(X, W, labels, ignore_index: int = -100, softcap: float = 0.0,
+                workspace=None):
+    """Forward of the fused linear cross-entropy on the current HIP stream.
+
+    Returns a dict of device tensors: loss [N] f32, lse [N] f32, mean [] f32,
+    n_valid [] i32, bad_label [] i32.
+    """
+    import torch
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    mean = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int32, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    need = lce_forward_workspace_bytes(N, H, V)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_forward")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_forward(_ptr(X), _ptr(W), _ptr(labels), N, H, V, int(ignore_index),
+                            float(softcap), _ptr(loss), _ptr(lse), mean.data_ptr(),
+                            n_valid.data_ptr(), bad.data_ptr(), _ptr(workspace),
+                            workspace.numel(), _stream(dev))
+    _check(st, "lce_forward")
+    return {"loss": loss, "lse": lse, "mean": mean, "n_valid": n_valid, "bad_label": bad}
+
+
+def lce_backward(X, W, labels, lse, dloss, ignore_index: int = -100, softcap: float = 0.0,
+                 dX_dtype=None, dW_dtype=None, workspace=None):
+    """Backward of the mean loss; `dloss` is a device scalar (or a float).
+    Returns (dX [N, H], dW [V, H]) in the requested dtypes (float32 default)."""
+    import torch
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    if not torch.is_tensor(dloss):
+        dloss = torch.tensor(float(dloss), dtype=torch.float32, device=dev)
+    dloss = dloss.to(device=dev, dtype=torch.float32).reshape(1).contiguous()
+    lse = lse.to(device=dev, dtype=torch.float32).contiguous()
+    if lse.shape != (N,):
+        raise ValueError("lse must have shape [N]")
+    dXc, dWc = _dtype_code(dX_dtype), _dtype_code(dW_dtype)
+    dX = torch.empty(N, H, dtype=dX_dtype or torch.float32, device=dev)
+    dW = torch.empty(V, H, dtype=dW_dtype or torch.float32, device=dev)
+    need = lce_backward_workspace_bytes(N, H, V, dW_dtype)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_backward")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_backward(_ptr(X), _ptr(W), _ptr(labels), _ptr(lse), dloss.data_ptr(),
+                             N, H, V, int(ignore_index), float(softcap), _ptr(dX), dXc,
+                             dW.data_ptr(), dWc, _ptr(workspace), workspace.numel(),
+                             _stream(dev))
+    _check(st, "lce_backward")
+    return dX, dW

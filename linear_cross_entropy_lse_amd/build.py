@@ -1,0 +1,68 @@
+"""Build liblce.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+    python -m linear_cross_entropy_lse_amd.build [--verbose]
+
+hipcc cross-compiles for gfx950 without a GPU.  Packed fp32 instructions are
+disabled for the device code (-packed-fp32-ops); hipcc's host pass warns that
+it does not know the feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB_PATH = os.path.join(HERE, "liblce.so")
+SOURCES = ["lce_api.hip", "lce_gemm.hip", "lce_rows.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build liblce)")
+
+
+def compile_flags(extra=()):
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-result", f"-I{os.path.join(ROOT, 'include')}", *extra]
+
+
+def build(verbose: bool = False, out: str = LIB_PATH, extra=()) -> str:
+    """Compile every HIP source and link liblce.so.  Always rebuilds."""
+    cc = hipcc()
+    objs = []
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        cmd = [cc, *compile_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                         if "packed-fp32-ops" not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+        if verbose and msgs.strip():
+            print(msgs)
+        objs.append(obj)
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

@@ -1,0 +1,274 @@
+// C-ABI entry points of liblce (declared in include/lce.h): argument checks,
+// workspace layout and the launch sequence of the forward and backward passes.
+// No device memory is ever allocated here; everything lives in the caller's
+// workspace.
+#include <algorithm>
+#include <climits>
+
+#include "../../include/lce.h"
+#include "lce_device.h"
+#include "lce_internal.h"
+
+namespace lce {
+namespace {
+
+// Plans are computed for the 256 compute units of the gfx950 MI355X, so the
+// workspace size depends on the shape only.
+constexpr int kTargetCUs = 256;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool shape_ok(int64_t N, int64_t H, int64_t V) {
+  return N >= 0 && N < INT_MAX && H >= 8 && H < (1 << 20) && H % 8 == 0 && V >= 1 && V < INT_MAX;
+}
+
+// Vocabulary splits of the persistent (token tile, split) grids.
+int pick_splits(int T, int n_vtiles) {
+  int S = (int)ceil_div(kTargetCUs, T);
+  S = std::max(1, std::min(S, n_vtiles));
+  return S;
+}
+
+struct FwdPlan {
+  int T, S, n_vtiles, nb_fin;
+  size_t off_state, off_target, off_pm, off_ps, off_blocks, total;
+};
+
+FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
+  (void)H;
+  FwdPlan p{};
+  p.T = (int)std::max<int64_t>(1, ceil_div(N, kTile));
+  p.n_vtiles = (int)ceil_div(V, kTile);
+  p.S = pick_splits(p.T, p.n_vtiles);
+  p.nb_fin = lse_finalize_blocks(std::max<int64_t>(N, 1));
+  size_t o = 0;
+  p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_target = o;  o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_pm = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
+  p.off_ps = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
+  p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_fin);
+  p.total = std::max<size_t>(o, kAlign);
+  return p;
+}
+
+struct BwdPlan {
+  int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, KS, nb_prep;
+  int64_t Vc, ldg;
+  size_t off_state, off_key, off_deriv, off_sorted, off_blocks, off_scalars, off_G, off_dXp,
+      off_dWs, total;
+};
+
+// Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
+// (N·Vc ≤ V·H), with a floor of 4096 columns; chunks are multiples of 256 so
+// tiles never straddle two chunks.
+BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+  BwdPlan p{};
+  const int64_t Nc = std::max<int64_t>(N, 1);
+  p.T = (int)ceil_div(Nc, kTile);
+  int64_t vc = std::max<int64_t>(4096, (V * H) / Nc);
+  vc = std::max<int64_t>(kTile, vc / kTile * kTile);
+  p.nchunks = (int)ceil_div(V, vc);
+  p.Vc = ceil_div(ceil_div(V, p.nchunks), kTile) * kTile;
+  p.nchunks = (int)ceil_div(V, p.Vc);
+  p.ldg = p.Vc;
+  p.n_vtiles_chunk = (int)(p.Vc / kTile);
+  p.S_chunk = pick_splits(p.T, p.n_vtiles_chunk);
+  p.nt_h = (int)ceil_div(H, kTile);
+  // Split the dX contraction of a chunk over KS partial buffers when the
+  // output alone has too few tiles to fill the chip (tile-quantisation ≥ 90 %).
+  const int64_t tiles = (int64_t)p.T * p.nt_h;
+  const int64_t steps = ceil_div(p.Vc, kBK);
+  p.KS = 1;
+  for (int ks = 1; ks <= 8; ks *= 2) {
+    if (steps / ks < 8) break;
+    const int64_t t = tiles * ks;
+    const double eff = (double)t / (double)(ceil_div(t, kTargetCUs) * kTargetCUs);
+    p.KS = ks;
+    if (eff >= 0.9) break;
+  }
+  p.nb_prep = row_prep_blocks(Nc);
+  size_t o = 0;
+  p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_key = o;     o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_deriv = o;   o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_sorted = o;  o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
+  p.off_scalars = o; o = align_up(o + 16);
+  p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)N * (size_t)p.ldg);
+  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.KS * (size_t)N * (size_t)H);
+  p.off_dWs = o;
+  if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
+  p.total = std::max<size_t>(o, kAlign);
+  return p;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+#define LCE_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return LCE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+}  // namespace lce
+
+using namespace lce;
+
+extern "C" {
+
+int lce_version(void) { return 100; }
+
+const char* lce_status_string(lce_status status) {
+  switch (status) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_INVALID_ARG: return "invalid argument (NULL pointer or enum out of range)";
+    case LCE_ERR_SHAPE: return "shape out of range (need N >= 0, 8 <= H < 2^20, H % 8 == 0, 1 <= V < 2^31)";
+    case LCE_ERR_ALIGNMENT: return "misaligned pointer (X/W/dX/dW 16 B, labels 8 B, workspace 256 B)";
+    case LCE_ERR_WORKSPACE: return "workspace smaller than the size query returns";
+    case LCE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t lce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V) {
+  if (!shape_ok(N, H, V)) return 0;
+  return plan_forward(N, H, V).total;
+}
+
+size_t lce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+  if (!shape_ok(N, H, V) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16)) return 0;
+  return plan_backward(N, H, V, dW_dtype).total;
+}
+
+lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                       int64_t N, int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                       float* loss_dev, float* lse_dev, float* mean_dev, int32_t* n_valid_dev,
+                       int32_t* bad_label_dev, void* workspace_dev, size_t workspace_bytes,
+                       void* stream_ptr) {
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if (!mean_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !loss_dev || !lse_dev || !workspace_dev))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(workspace_dev, kAlign) || !aligned(loss_dev, 4) || !aligned(lse_dev, 4) ||
+      !aligned(mean_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
+    return LCE_ERR_ALIGNMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (N == 0) {
+    LCE_TRY(launch_empty_forward(mean_dev, n_valid_dev, bad_label_dev, stream));
+    return LCE_OK;
+  }
+  const FwdPlan pl = plan_forward(N, H, V);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+
+  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
+  float* target = at<float>(workspace_dev, pl.off_target);
+  float* pm = at<float>(workspace_dev, pl.off_pm);
+  float* ps = at<float>(workspace_dev, pl.off_ps);
+  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
+  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+
+  LCE_TRY(launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, nullptr,
+                          target, nullptr, nullptr, stream));
+  LseParams lp{};
+  lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
+  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles; lp.softcap = softcap;
+  lp.part_m = pm; lp.part_s = ps;
+  LCE_TRY(launch_lse_partials(lp, stream));
+  LCE_TRY(launch_lse_finalize(pm, ps, pl.S, N, state, target, lse_dev, loss_dev, blocks, stream));
+  LCE_TRY(launch_mean_finalize(blocks, pl.nb_fin, mean_dev, n_valid_dev, bad_label_dev, stream));
+  return LCE_OK;
+}
+
+lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                        const float* lse_dev, const float* dloss_dev, int64_t N, int64_t H,
+                        int64_t V, int64_t ignore_index, float softcap, void* dX_dev,
+                        lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                        void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
+    return LCE_ERR_INVALID_ARG;
+  if (!dW_dev) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !lse_dev || !dloss_dev || !dX_dev ||
+                !workspace_dev))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(lse_dev, 4) || !aligned(dloss_dev, 4) || !aligned(dX_dev, 16) ||
+      !aligned(dW_dev, 16) || !aligned(workspace_dev, kAlign))
+    return LCE_ERR_ALIGNMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int64_t dw_bytes = V * H * (dW_dtype == LCE_BF16 ? 2 : 4);
+  if (N == 0) {
+    LCE_TRY(launch_fill_zero(dW_dev, dw_bytes, stream));
+    return LCE_OK;
+  }
+  const BwdPlan pl = plan_backward(N, H, V, dW_dtype);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+
+  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
+  int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
+  float* deriv = at<float>(workspace_dev, pl.off_deriv);
+  int32_t* sorted = at<int32_t>(workspace_dev, pl.off_sorted);
+  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
+  float* scale = at<float>(workspace_dev, pl.off_scalars);
+  int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
+  uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
+  float* dXp = at<float>(workspace_dev, pl.off_dXp);
+  float* dWs = at<float>(workspace_dev, pl.off_dWs);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
+  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+
+  LCE_TRY(launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, key, nullptr,
+                          deriv, blocks, stream));
+  LCE_TRY(launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, scale, counts, stream));
+  LCE_TRY(launch_sort_by_label(key, N, sorted, stream));
+
+  for (int c = 0; c < pl.nchunks; ++c) {
+    const int64_t v_begin = (int64_t)c * pl.Vc;
+    const int64_t chunk_len = std::min<int64_t>(pl.Vc, V - v_begin);
+    const int n_vt = (int)ceil_div(chunk_len, kTile);
+
+    GradParams gp{};
+    gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
+    gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt; gp.softcap = softcap;
+    gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
+    LCE_TRY(launch_grad_logits(gp, stream));
+
+    DxParams xp{};
+    xp.G = G; xp.ldg = pl.ldg; xp.Wc = W + v_begin * H; xp.wc_rows = V - v_begin;
+    xp.N = N; xp.H = H; xp.k_len = chunk_len;
+    xp.nt_tok = pl.T; xp.nt_h = pl.nt_h; xp.KS = pl.KS; xp.accumulate = c > 0; xp.dXp = dXp;
+    LCE_TRY(launch_dx_gemm(xp, stream));
+
+    DwParams wp{};
+    wp.G = G; wp.ldg = pl.ldg; wp.X = X; wp.N = N; wp.H = H; wp.chunk_len = chunk_len;
+    wp.nt_v = n_vt; wp.nt_h = pl.nt_h; wp.scale = scale;
+    if (dW_dtype == LCE_F32) {
+      wp.dst = static_cast<float*>(dW_dev) + v_begin * H;
+      LCE_TRY(launch_dw_gemm(wp, stream));
+    } else {
+      wp.dst = dWs;
+      LCE_TRY(launch_dw_gemm(wp, stream));
+      LCE_TRY(launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale, dWs, v_begin,
+                                v_begin + chunk_len, stream));
+      LCE_TRY(launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
+                               chunk_len * H, stream));
+    }
+  }
+  if (dW_dtype == LCE_F32)
+    LCE_TRY(launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale,
+                              static_cast<float*>(dW_dev), 0, V, stream));
+  LCE_TRY(launch_dx_finalize(dXp, pl.KS, N, H, state, key, deriv, W, scale, dX_dev,
+                             dX_dtype == LCE_BF16, stream));
+  return LCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// Device-side building blocks shared by the gfx950 kernels of liblce.
+//
+// Tiles: one workgroup of 256 threads (4 waves of 64) computes a 256 x 256
+// fp32 tile C = A · Bᵀ over a K range, 64 K-values per pipeline step.  Each
+// wave owns a 128 x 128 quarter as 4 x 4 blocks of the 32x32x16 bf16 MFMA.
+// Operands are staged through LDS in a K-major layout (each tile row holds 64
+// consecutive K values = 128 bytes), so that one 16-byte LDS read gives a lane
+// its 8-element MFMA fragment.  The 16-byte chunks of a row are XOR-swizzled
+// by the row index to keep the fragment reads and the tile writes free of
+// bank conflicts.
+//
+// MFMA lane layout (v_mfma_f32_32x32x16_bf16, checked on gfx950):
+//   A fragment: lane l holds A[l % 32][8*(l/32) .. 8*(l/32)+7]
+//   B fragment: lane l holds B[8*(l/32) .. +7][l % 32]   (i.e. Bᵀ row l % 32)
+//   C/D:        lane l, element r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kTile = 256;      // output tile edge (both M and N)
+constexpr int kBK = 64;         // K values per pipeline step
+constexpr int kWaveTile = 128;  // each wave: 128 x 128
+constexpr int kMI = 4;          // 32x32 MFMA blocks per wave along M
+constexpr int kNI = 4;          // ... along N
+constexpr int kStageElems = kTile * kBK;      // bf16 elements per operand per stage
+constexpr int kLoadsPerThread = kStageElems / 8 / kThreads;  // 16-byte loads: 8
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh(x) = 1 - 2 / (exp(2x) + 1); saturates correctly at +-inf.
+// `two_log2e_over_c` folds x = z / c and the base change into one multiply.
+__device__ __forceinline__ float tanh_of_scaled(float z, float two_log2e_over_c) {
+  float e = exp2_fast(z * two_log2e_over_c);
+  return 1.0f - 2.0f * rcp_fast(e + 1.0f);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows r
+// and r+8 differ in the low bit so that 16 consecutive rows reading the same
+// logical chunk land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kBK + ((chunk ^ swz(row)) << 3);
+}
+
+// ----------------------------------------------------------------------------
+// Global -> register loaders for one 256 x 64 operand tile, via buffer loads.
+//
+// A buffer descriptor covers exactly the valid bytes of the operand from the
+// tile's first row on; every byte offset is carried in the VGPR operand so the
+// hardware range check sees all of it, and any access at or beyond the
+// descriptor's size returns zeros.  Descriptor sizes are capped at 2^31 − 1
+// bytes, far above the largest in-tile offset (256 rows · 2^21 bytes).
+// ----------------------------------------------------------------------------
+constexpr uint32_t kBufferConfig = 0x00020000u;  // raw 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;    // offset that always reads 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes,
+                                           (int)kBufferConfig);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// K-major operand: element (row, k) at base[row * ld + k].  Rows at or beyond
+// `rows_total` read as zero, and so do K chunks at or beyond `k_total`
+// (k_total % 8 == 0).
+struct KMajorTile {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;      // byte offset of this thread's first 16-byte chunk
+  uint32_t row_step;  // bytes between the rows of consecutive loads (32 rows)
+  int32_t kchunk;     // this thread's K offset inside a 64-wide step
+  int64_t k_total;
+  u32x4 r[kLoadsPerThread];
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0,
+                                       int64_t rows_total, int64_t k_total_, int tid) {
+    rsrc = make_rsrc(base + row0 * ld, (rows_total - row0) * ld * 2);
+    const int row = tid >> 3, chunk = tid & 7;
+    voff = (uint32_t)(row * ld * 2 + chunk * 16);
+    row_step = (uint32_t)(kThreads / 8 * ld * 2);
+    kchunk = chunk * 8;
+    k_total = k_total_;
+  }
+  __device__ __forceinline__ void load(int64_t k0) {
+    const bool kv = k0 + kchunk < k_total;
+    const uint32_t base = voff + (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int it = 0; it < kLoadsPerThread; ++it)
+      r[it] = buffer_load16(rsrc, kv ? base + it * row_step : kOutOfRange);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < kLoadsPerThread; ++it) {
+      const int idx = it * kThreads + tid;
+      const int row = idx >> 3, chunk = idx & 7;
+      *reinterpret_cast<u32x4*>(lds + lds_off(row, chunk)) = r[it];
+    }
+  }
+};
+
+// MN-major operand: element (row, k) at base[k * ld + row], i.e. the tile's
+// rows are contiguous in memory.  Each thread loads an 8 (k) x 8 (row) block
+// with 8 16-byte loads and transposes it in registers, so LDS receives the same
+// K-major layout as above.  K rows at or beyond `k_total` read as zero; rows
+// (the contiguous dimension) are clamped in blocks of 8 (rows_total % 8 == 0).
+struct MNMajorTile {
+  const uint16_t* base;
+  int64_t ld, k_total;
+  uint32_t voff;  // byte offset of (k = 8·kb, row block) from the step's first K row
+  uint32_t ld_bytes;
+  u32x4 r[8];
+
+  __device__ __forceinline__ void init(const uint16_t* base_, int64_t ld_, int64_t row0,
+                                       int64_t rows_total, int64_t k_total_, int tid) {
+    base = base_;
+    ld = ld_;
+    k_total = k_total_;
+    const int rb = tid >> 3, kb = tid & 7;
+    int64_t gr = row0 + rb * 8;
+    gr = gr < rows_total ? gr : rows_total - 8;
+    ld_bytes = (uint32_t)(ld * 2);
+    voff = (uint32_t)(kb * 8 * ld * 2 + gr * 2);
+  }
+  __device__ __forceinline__ void load(int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld, (k_total - k0) * ld * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = buffer_load16(rs, voff + j * ld_bytes);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    const int rb = tid >> 3;
+    const int kb = tid & 7;
+    // out[i] = column i of the 8x8 block = (r[0][i], r[1][i], ..., r[7][i]).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+      o[0] = __builtin_amdgcn_perm(r[1][i >> 1], r[0][i >> 1], sel);
+      o[1] = __builtin_amdgcn_perm(r[3][i >> 1], r[2][i >> 1], sel);
+      o[2] = __builtin_amdgcn_perm(r[5][i >> 1], r[4][i >> 1], sel);
+      o[3] = __builtin_amdgcn_perm(r[7][i >> 1], r[6][i >> 1], sel);
+      *reinterpret_cast<u32x4*>(lds + lds_off(rb * 8 + i, kb)) = o;
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// LDS -> MFMA for one 64-deep pipeline step of a wave's 128 x 128 quarter.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_step(const uint16_t* __restrict__ sA,
+                                          const uint16_t* __restrict__ sB, int wm, int wn,
+                                          int lane, f32x16 (&acc)[kMI][kNI]) {
+  const int lrow = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < kBK / 16; ++t) {
+    const int chunk = t * 2 + half;
+    bf16x8 a[kMI], b[kNI];
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int row = wm * kWaveTile + mi * 32 + lrow;
+      a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + lds_off(row, chunk)));
+    }
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int row = wn * kWaveTile + ni * 32 + lrow;
+      b[ni] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sB + lds_off(row, chunk)));
+    }
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMI][kNI]) {
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+}
+
+// Row (within the 256-row tile) of accumulator element r of block mi for `lane`.
+__device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
+  return wm * kWaveTile + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+// Compile-time part of acc_row: acc_row = acc_row_lane(wm, lane) + acc_row_const(mi, r).
+__device__ __forceinline__ int acc_row_lane(int wm, int lane) { return wm * kWaveTile + 4 * (lane >> 5); }
+__device__ __forceinline__ constexpr int acc_row_const(int mi, int r) { return mi * 32 + 8 * (r >> 2) + (r & 3); }
+// Column (within the 256-column tile) of block ni for `lane`.
+__device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
+  return wn * kWaveTile + ni * 32 + (lane & 31);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map the
+// hardware id to a logical id so that each XCD receives a contiguous range of
+// logical ids; neighbouring logical tiles then share operands in one L2.
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+  const int per = nwg >> 3;
+  if (b >= per * 8) return b;
+  return (b & 7) * per + (b >> 3);
+}
+
+// Row classes written by the row-preparation kernels.
+enum RowState : int32_t { kRowIgnored = 0, kRowValid = 1, kRowBad = 2 };
+
+}  // namespace lce

@@ -1,0 +1,107 @@
+// Internal interfaces between the liblce entry points and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+// Forward partials: grid T x S, T token tiles of 256, S vocabulary splits.
+struct LseParams {
+  const uint16_t* X;  // bf16 [N, H]
+  const uint16_t* W;  // bf16 [V, H]
+  int64_t N, H, V;
+  int T, S, n_vtiles;
+  float softcap;
+  float* part_m;      // [S, N] base-2 running max
+  float* part_s;      // [S, N] Σ 2^(u − m)
+};
+
+// Recomputed logit gradient of one vocabulary chunk [v_begin, v_begin + 256·n_vtiles).
+struct GradParams {
+  const uint16_t* X;
+  const uint16_t* W;
+  int64_t N, H, V;
+  int64_t v_begin;
+  int T, S, n_vtiles;
+  float softcap;
+  const float* lse;          // [N]
+  const int32_t* row_state;  // [N]
+  uint16_t* G;               // bf16 [N, ldg]
+  int64_t ldg;
+};
+
+struct DxParams {
+  const uint16_t* G;   // bf16 [N, ldg], chunk-local vocabulary columns
+  int64_t ldg;
+  const uint16_t* Wc;  // W + v_begin * H
+  int64_t wc_rows;     // V − v_begin (rows of W readable from Wc)
+  int64_t N, H;
+  int64_t k_len;       // chunk length (vocabulary rows in this chunk)
+  int nt_tok, nt_h, KS;
+  int accumulate;      // 0: first chunk writes, 1: later chunks add
+  float* dXp;          // fp32 [KS, N, H]
+};
+
+struct DwParams {
+  const uint16_t* G;
+  int64_t ldg;
+  const uint16_t* X;
+  int64_t N, H;
+  int64_t chunk_len;
+  int nt_v, nt_h;
+  const float* scale;  // device scalar dloss / n_valid
+  float* dst;          // fp32 [chunk_len, H] (row v_local)
+};
+
+hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream);
+hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream);
+hipError_t launch_dx_gemm(const DxParams& p, hipStream_t stream);
+hipError_t launch_dw_gemm(const DwParams& p, hipStream_t stream);
+
+// Row-wise kernels (lce_rows.hip).
+struct BlockStats {  // per-block partial of the row scan, combined in a fixed order
+  double loss_sum;
+  int32_t n_valid;
+  int32_t n_bad;
+};
+
+hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* labels,
+                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           float softcap, int32_t* row_state, int32_t* row_key,
+                           float* target, float* target_deriv, BlockStats* blocks,
+                           hipStream_t stream);
+int row_prep_blocks(int64_t N);
+
+hipError_t launch_lse_finalize(const float* part_m, const float* part_s, int S, int64_t N,
+                               const int32_t* row_state, const float* target, float* lse,
+                               float* loss, BlockStats* blocks, hipStream_t stream);
+int lse_finalize_blocks(int64_t N);
+
+hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, float* mean,
+                                int32_t* n_valid, int32_t* bad_flag, hipStream_t stream);
+
+hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const float* dloss,
+                                 float* scale, int32_t* n_valid, hipStream_t stream);
+
+hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, int32_t* sorted,
+                                hipStream_t stream);
+
+hipError_t launch_dx_finalize(const float* dXp, int KS, int64_t N, int64_t H,
+                              const int32_t* row_state, const int32_t* row_key,
+                              const float* target_deriv, const uint16_t* W,
+                              const float* scale, void* dX, int dX_bf16, hipStream_t stream);
+
+hipError_t launch_dw_correct(const int32_t* sorted, const int32_t* row_key,
+                             const int32_t* n_valid, const float* target_deriv,
+                             const uint16_t* X, int64_t N, int64_t H, const float* scale,
+                             float* dst, int64_t v_lo, int64_t v_hi, hipStream_t stream);
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t count, hipStream_t stream);
+
+hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
+
+hipError_t launch_empty_forward(float* mean, int32_t* n_valid, int32_t* bad_flag,
+                                hipStream_t stream);
+
+}  // namespace lce

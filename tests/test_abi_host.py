@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status before
+touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_lse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("liblce.so not built")
+    return _lib.load()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "lce.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lce_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_binding_symbols():
+    assert declared_symbols() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lce_version() >= 100
+    for st in range(6):
+        assert len(lib.lce_status_string(st)) > 0
+
+
+def test_workspace_queries(lib):
+    assert lib.lce_forward_workspace_bytes(256, 64, 1000) > 0
+    assert lib.lce_forward_workspace_bytes(256, 63, 1000) == 0        # H % 8
+    assert lib.lce_forward_workspace_bytes(-1, 64, 1000) == 0
+    assert lib.lce_backward_workspace_bytes(256, 64, 0, 0) == 0
+    assert lib.lce_backward_workspace_bytes(256, 64, 1000, 7) == 0    # bad dtype enum
+    # The backward workspace never holds the whole N x V logit matrix.
+    for (N, H, V) in [(8192, 2304, 256128), (32768, 3584, 152064), (16384, 4096, 32000),
+                      (8192, 4096, 128256)]:
+        ws = lib.lce_backward_workspace_bytes(N, H, V, 0)
+        assert 0 < ws < N * V * 2
+        assert lib.lce_backward_workspace_bytes(N, H, V, 1) > ws      # + fp32 dW chunk
+        assert lib.lce_forward_workspace_bytes(N, H, V) < 64 * N * 8 + (1 << 20)
+
+
+FAKE = 1 << 20  # a 256-byte-aligned non-NULL address: never dereferenced on these paths
+
+
+def fwd(lib, X=FAKE, W=FAKE, y=FAKE, N=4, H=8, V=5, loss=FAKE, lse=FAKE, mean=FAKE,
+        nv=FAKE, bad=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.lce_forward_workspace_bytes(max(N, 0), H, V)
+    return lib.lce_forward(X, W, y, N, H, V, -100, 0.0, loss, lse, mean, nv, bad, ws, wsb, None)
+
+
+def bwd(lib, X=FAKE, W=FAKE, y=FAKE, lse=FAKE, dl=FAKE, N=4, H=8, V=5, dX=FAKE, dXt=0,
+        dW=FAKE, dWt=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.lce_backward_workspace_bytes(max(N, 0), H, V, dWt if dWt in (0, 1) else 0)
+    return lib.lce_backward(X, W, y, lse, dl, N, H, V, -100, 0.0, dX, dXt, dW, dWt, ws, wsb,
+                            None)
+
+
+def test_forward_error_paths(lib):
+    assert fwd(lib, H=12) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, H=0) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, V=0) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, N=-1) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, X=0) == _lib.LCE_ERR_INVALID_ARG
+    assert fwd(lib, mean=0) == _lib.LCE_ERR_INVALID_ARG
+    assert fwd(lib, ws=0) == _lib.LCE_ERR_INVALID_ARG
+    assert fwd(lib, X=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
+    assert fwd(lib, y=FAKE + 4) == _lib.LCE_ERR_ALIGNMENT
+    assert fwd(lib, ws=FAKE + 16) == _lib.LCE_ERR_ALIGNMENT
+    assert fwd(lib, wsb=16) == _lib.LCE_ERR_WORKSPACE
+
+
+def test_backward_error_paths(lib):
+    assert bwd(lib, H=20) == _lib.LCE_ERR_SHAPE
+    assert bwd(lib, dXt=3) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd(lib, dWt=-1) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd(lib, dW=0) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd(lib, lse=0) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd(lib, dl=0) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd(lib, dX=FAKE + 4) == _lib.LCE_ERR_ALIGNMENT
+    assert bwd(lib, dW=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
+    assert bwd(lib, wsb=255) == _lib.LCE_ERR_WORKSPACE
