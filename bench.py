@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head linear + cross-entropy on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gemma2_2b]
+
+One step = lce_forward + lce_backward (fp32 dX and dW) over one batch of the
+chosen synthetic workload, inputs resident in HBM.  Prints ONE JSON line:
+fwd+bwd tokens/s, the dense-MFMA roofline of the dominant kernel (per-kernel
+durations from hipEvents recorded on the launch stream inside the timed
+region), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_DENSE_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0
+METRIC = "fwd+bwd tokens/s and % bf16 MFMA peak, Gemma-2 2B LM-head shape, 1 GPU"
+GEMM_KERNELS = ("lse_partials", "grad_logits", "dx_gemm", "dw_gemm")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gemma2_2b")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="token rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype-grad", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_cross_entropy_lse_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload, src_hash):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != src_hash:
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(w, X, W, y, rows):
+    """The oracle, as it stands, on `rows` seeded token rows: their forward,
+    their dX rows and their share of dW."""
+    import numpy as np
+    import lce_inputs as L
+    from oracle import lce_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    idx = L.row_sample(w.N, rows, seed=w.seed + 77)
+    W64 = L.to_f64(W)
+    X64 = L.to_f64(X[idx])
+    y64 = y[idx].numpy()
+    n_valid = int((y != L.IGNORE_INDEX).sum())
+    t0 = time.perf_counter()
+    f = O.forward(X64, W64, y64, L.IGNORE_INDEX, w.softcap, n_valid_total=n_valid)
+    O.backward_rows(X64, W64, y64, f["lse"], n_valid, 1.0, L.IGNORE_INDEX, w.softcap)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(idx) / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(idx)} seeded token rows of {w.name} (N={w.N}, H={w.H}, V={w.V}): "
+                      f"float64 forward, dX rows and their dW share, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import lce_inputs as L
+    import linear_cross_entropy_lse_amd as P
+    from linear_cross_entropy_lse_amd import _lib
+
+    w = L.WORKLOADS[args.workload]
+    lib = P.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name}: N={w.N} H={w.H} V={w.V} softcap={w.softcap}")
+    Xc, Wc, yc = L.make_inputs(w)
+    X, W, y = Xc.to(dev), Wc.to(dev), yc.to(dev)
+    N, H, V = w.N, w.H, w.V
+    gdt = torch.float32 if args.dtype_grad == "f32" else torch.bfloat16
+    gcode = _lib.LCE_F32 if args.dtype_grad == "f32" else _lib.LCE_BF16
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    nval = torch.empty(1, dtype=torch.int32, device=dev)
+    bad = torch.empty(1, dtype=torch.int32, device=dev)
+    dloss = torch.ones(1, dtype=torch.float32, device=dev)
+    dX = torch.empty(N, H, dtype=gdt, device=dev)
+    dW = torch.empty(V, H, dtype=gdt, device=dev)
+    fws_n = lib.lce_forward_workspace_bytes(N, H, V)
+    bws_n = lib.lce_backward_workspace_bytes(N, H, V, gcode)
+    fws = torch.empty(fws_n, dtype=torch.uint8, device=dev)
+    bws = torch.empty(bws_n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step():
+        st = lib.lce_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
+                             float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
+                             nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        st = lib.lce_backward(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                              dloss.data_ptr(), N, H, V, L.IGNORE_INDEX, float(w.softcap),
+                              dX.data_ptr(), gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n,
+                              sptr)
+        if st:
+            raise RuntimeError(f"lce_backward: {_lib.status_string(st)}")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1073741824 bytes read, 1073741824 bytes written")
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    log(f"[bench] timing {args.steps} steps")
+    P.lce_timing_reset()
+    P.lce_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    P.lce_timing_enable(False)
+    kernels = P.lce_timing_read()
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = N / (ms_per_step / 1e3)
+    flops = 8 * N * H * V
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+
+    # Dominant kernel and its roofline (algorithmic work: 2·N·H·V per step for
+    # each of the four contractions, spread over that kernel's launches).
+    dom = max(GEMM_KERNELS, key=lambda k: kernels.get(k, (0, 0.0))[1])
+    launches, total_ms = kernels[dom]
+    avg_ms = total_ms / launches
+    dom_flops_per_launch = 2 * N * H * V * args.steps / launches
+    achieved = dom_flops_per_launch / (avg_ms / 1e3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(dom, w.name, src_hash)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1),
+                "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom,
+                "avg_launch_ms": round(avg_ms, 4),
+                "algorithmic_flops_per_launch": dom_flops_per_launch}
+    per_kernel = {k: {"launches_per_step": v[0] / args.steps,
+                      "ms_per_step": round(v[1] / args.steps, 4)}
+                  for k, v in kernels.items()}
+    for k in GEMM_KERNELS:
+        if k in kernels:
+            per_kernel[k]["tflops"] = round(2 * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(w, Xc, Wc, yc, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {"workload": w.name, "N": N, "H": H, "V": V, "softcap": w.softcap,
+                   "labels": w.labels, "grad_dtype": args.dtype_grad},
+        "tflops": round(tflops, 1),
+        "frac_of_bf16_dense_peak": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": per_kernel,
+        "memory_bytes": {"peak_allocated": int(peak_mem),
+                         "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),
+                         "grad_outputs": int(dX.numel() * dX.element_size() +
+                                             dW.numel() * dW.element_size()),
+                         "workspace_forward": int(fws_n), "workspace_backward": int(bws_n),
+                         "bf16_logits_never_allocated": int(N * V * 2)},
+        "kernel_source_hash": src_hash,
+        "mean_loss": float(mean.item()),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

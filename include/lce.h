@@ -124,6 +124,28 @@ const char* lce_status_string(lce_status status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int lce_version(void);
 
+/*
+ * Kernel timing instrumentation (for benchmarks; off by default).
+ * While enabled, every kernel the two calls above enqueue is bracketed by a
+ * pair of hipEvents recorded on the same stream.  lce_timing_read waits for the
+ * recorded events, then fills up to `max_entries` records (one per kernel
+ * name, in first-launch order) with the number of launches and their summed
+ * duration in milliseconds since the last reset, and returns the number of
+ * distinct kernels (which may exceed max_entries).  `out` may be NULL to
+ * query the count.  Returns a negative value if a HIP event call failed.
+ * Not thread-safe with respect to concurrent lce_forward/lce_backward calls
+ * that toggle or read it.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} lce_kernel_timing;
+
+void lce_timing_enable(int enable);
+void lce_timing_reset(void);
+int lce_timing_read(lce_kernel_timing* out, int max_entries);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,13 @@ LCE_BF16 = 1
 
 # Every symbol include/lce.h declares.
 EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_forward",
-            "lce_backward", "lce_status_string", "lce_version")
+            "lce_backward", "lce_status_string", "lce_version", "lce_timing_enable",
+            "lce_timing_reset", "lce_timing_read")
+
+
+class KernelTiming(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 _lib = None
 
@@ -62,6 +68,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
     lib.lce_version.restype = ctypes.c_int
+    lib.lce_timing_enable.argtypes = [ctypes.c_int]
+    lib.lce_timing_enable.restype = None
+    lib.lce_timing_reset.argtypes = []
+    lib.lce_timing_reset.restype = None
+    lib.lce_timing_read.argtypes = [ctypes.POINTER(KernelTiming), ctypes.c_int]
+    lib.lce_timing_read.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -73,6 +85,29 @@ def status_string(status: int) -> str:
 
 def lce_version() -> int:
     return int(load().lce_version())
+
+
+def lce_timing_enable(enable: bool = True) -> None:
+    load().lce_timing_enable(1 if enable else 0)
+
+
+def lce_timing_reset() -> None:
+    load().lce_timing_reset()
+
+
+def lce_timing_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last reset (waits for the
+    recorded events)."""
+    lib = load()
+    n = lib.lce_timing_read(None, 0)
+    if n < 0:
+        raise RuntimeError("lce_timing_read: HIP event error")
+    buf = (KernelTiming * max(n, 1))()
+    n = lib.lce_timing_read(buf, n)
+    if n < 0:
+        raise RuntimeError("lce_timing_read: HIP event error")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(n)}
 
 
 def lce_forward_workspace_bytes(N: int, H: int, V: int) -> int:

@@ -4,6 +4,10 @@
 // workspace.
 #include <algorithm>
 #include <climits>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "../../include/lce.h"
 #include "lce_device.h"
@@ -111,10 +115,78 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// ---------------------------------------------------------------------------
+// Optional kernel timing: hipEvent pairs around each launch on its stream.
+// ---------------------------------------------------------------------------
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::string> names;
+  std::vector<int64_t> launches;
+  std::vector<double> total_ms;
+  struct Pending { int id; hipEvent_t a, b; };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+
+  int id_of(const char* name) {
+    for (size_t i = 0; i < names.size(); ++i)
+      if (names[i] == name) return (int)i;
+    names.emplace_back(name);
+    launches.push_back(0);
+    total_ms.push_back(0.0);
+    return (int)names.size() - 1;
+  }
+  hipError_t take(hipEvent_t* e) {
+    if (!pool.empty()) {
+      *e = pool.back();
+      pool.pop_back();
+      return hipSuccess;
+    }
+    return hipEventCreate(e);
+  }
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Runs `launch` (which enqueues one kernel on `stream`), bracketed by events
+// when timing is enabled.
+template <class F>
+hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+  Timing& t = timing();
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    on = t.on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    hipError_t e = t.take(&a);
+    if (e != hipSuccess) return e;
+    e = t.take(&b);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(t.mu);
+  t.pending.push_back({t.id_of(name), a, b});
+  return hipSuccess;
+}
+
 #define LCE_TRY(expr)                         \
   do {                                        \
     if ((expr) != hipSuccess) return LCE_ERR_HIP; \
   } while (0)
+
+#define LCE_LAUNCH(name, stream, call) LCE_TRY(timed(name, stream, [&]() { return call; }))
 
 }  // namespace
 }  // namespace lce
@@ -124,6 +196,54 @@ using namespace lce;
 extern "C" {
 
 int lce_version(void) { return 100; }
+
+void lce_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.on = enable != 0;
+}
+
+void lce_timing_reset(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (auto& p : t.pending) {
+    (void)hipEventSynchronize(p.b);
+    t.pool.push_back(p.a);
+    t.pool.push_back(p.b);
+  }
+  t.pending.clear();
+  for (size_t i = 0; i < t.names.size(); ++i) {
+    t.launches[i] = 0;
+    t.total_ms[i] = 0.0;
+  }
+}
+
+int lce_timing_read(lce_kernel_timing* out, int max_entries) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  int rc = 0;
+  for (auto& p : t.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
+      rc = -1;
+    t.launches[p.id] += 1;
+    t.total_ms[p.id] += ms;
+    t.pool.push_back(p.a);
+    t.pool.push_back(p.b);
+  }
+  t.pending.clear();
+  if (rc < 0) return rc;
+  const int n = (int)t.names.size();
+  if (out) {
+    for (int i = 0; i < n && i < max_entries; ++i) {
+      std::memset(out[i].name, 0, sizeof(out[i].name));
+      std::strncpy(out[i].name, t.names[i].c_str(), sizeof(out[i].name) - 1);
+      out[i].launches = t.launches[i];
+      out[i].total_ms = t.total_ms[i];
+    }
+  }
+  return n;
+}
 
 const char* lce_status_string(lce_status status) {
   switch (status) {
@@ -162,7 +282,7 @@ lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labe
     return LCE_ERR_ALIGNMENT;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   if (N == 0) {
-    LCE_TRY(launch_empty_forward(mean_dev, n_valid_dev, bad_label_dev, stream));
+    LCE_LAUNCH("empty_forward", stream, launch_empty_forward(mean_dev, n_valid_dev, bad_label_dev, stream));
     return LCE_OK;
   }
   const FwdPlan pl = plan_forward(N, H, V);
@@ -176,15 +296,15 @@ lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labe
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
 
-  LCE_TRY(launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, nullptr,
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, nullptr,
                           target, nullptr, nullptr, stream));
   LseParams lp{};
   lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
   lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles; lp.softcap = softcap;
   lp.part_m = pm; lp.part_s = ps;
-  LCE_TRY(launch_lse_partials(lp, stream));
-  LCE_TRY(launch_lse_finalize(pm, ps, pl.S, N, state, target, lse_dev, loss_dev, blocks, stream));
-  LCE_TRY(launch_mean_finalize(blocks, pl.nb_fin, mean_dev, n_valid_dev, bad_label_dev, stream));
+  LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
+  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, lse_dev, loss_dev, blocks, stream));
+  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, mean_dev, n_valid_dev, bad_label_dev, stream));
   return LCE_OK;
 }
 
@@ -207,7 +327,7 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int64_t dw_bytes = V * H * (dW_dtype == LCE_BF16 ? 2 : 4);
   if (N == 0) {
-    LCE_TRY(launch_fill_zero(dW_dev, dw_bytes, stream));
+    LCE_LAUNCH("fill_zero", stream, launch_fill_zero(dW_dev, dw_bytes, stream));
     return LCE_OK;
   }
   const BwdPlan pl = plan_backward(N, H, V, dW_dtype);
@@ -226,10 +346,10 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
 
-  LCE_TRY(launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, key, nullptr,
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, key, nullptr,
                           deriv, blocks, stream));
-  LCE_TRY(launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, scale, counts, stream));
-  LCE_TRY(launch_sort_by_label(key, N, sorted, stream));
+  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, scale, counts, stream));
+  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, sorted, stream));
 
   for (int c = 0; c < pl.nchunks; ++c) {
     const int64_t v_begin = (int64_t)c * pl.Vc;
@@ -240,33 +360,33 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
     gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
     gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt; gp.softcap = softcap;
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
-    LCE_TRY(launch_grad_logits(gp, stream));
+    LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 
     DxParams xp{};
     xp.G = G; xp.ldg = pl.ldg; xp.Wc = W + v_begin * H; xp.wc_rows = V - v_begin;
     xp.N = N; xp.H = H; xp.k_len = chunk_len;
     xp.nt_tok = pl.T; xp.nt_h = pl.nt_h; xp.KS = pl.KS; xp.accumulate = c > 0; xp.dXp = dXp;
-    LCE_TRY(launch_dx_gemm(xp, stream));
+    LCE_LAUNCH("dx_gemm", stream, launch_dx_gemm(xp, stream));
 
     DwParams wp{};
     wp.G = G; wp.ldg = pl.ldg; wp.X = X; wp.N = N; wp.H = H; wp.chunk_len = chunk_len;
     wp.nt_v = n_vt; wp.nt_h = pl.nt_h; wp.scale = scale;
     if (dW_dtype == LCE_F32) {
       wp.dst = static_cast<float*>(dW_dev) + v_begin * H;
-      LCE_TRY(launch_dw_gemm(wp, stream));
+      LCE_LAUNCH("dw_gemm", stream, launch_dw_gemm(wp, stream));
     } else {
       wp.dst = dWs;
-      LCE_TRY(launch_dw_gemm(wp, stream));
-      LCE_TRY(launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale, dWs, v_begin,
+      LCE_LAUNCH("dw_gemm", stream, launch_dw_gemm(wp, stream));
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale, dWs, v_begin,
                                 v_begin + chunk_len, stream));
-      LCE_TRY(launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
+      LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
                                chunk_len * H, stream));
     }
   }
   if (dW_dtype == LCE_F32)
-    LCE_TRY(launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale,
+    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale,
                               static_cast<float*>(dW_dev), 0, V, stream));
-  LCE_TRY(launch_dx_finalize(dXp, pl.KS, N, H, state, key, deriv, W, scale, dX_dev,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.KS, N, H, state, key, deriv, W, scale, dX_dev,
                              dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }

@@ -222,3 +222,16 @@ def dW_vocab_rows(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
 def mean_loss_value(X, W, labels, ignore_index=IGNORE_INDEX, softcap=0.0):
     """Scalar mean loss (used by the finite-difference pins)."""
     return float(forward(X, W, labels, ignore_index, softcap)["mean"])
+
+
+def backward_rows(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
+                  lse_rows: np.ndarray, n_valid: int, dloss: float = 1.0,
+                  ignore_index: int = IGNORE_INDEX, softcap: float = 0.0):
+    """Contribution of a subset of token rows to the backward: their dX rows
+    and their share Σ_{i in subset} dZ[i, :]ᵀ x_i of dW ([M011] §06: dH += dZ·W,
+    dW accumulates dZᵀ·H over the token rows).  Summing the dW shares of a
+    partition of the rows gives the full dW."""
+    X_rows = np.asarray(X_rows, dtype=np.float64)
+    dZ = logit_gradient(X_rows, W, labels_rows, lse_rows, n_valid, dloss,
+                        ignore_index, softcap)
+    return dZ @ np.asarray(W, dtype=np.float64), dZ.T @ X_rows

@@ -319,6 +319,14 @@ def test_subset_evaluations_agree(softcap):
     dXr = O.dX_rows(X[rows], W, y[rows], full["lse"][rows], full["n_valid"], 1.5,
                     softcap=softcap)
     np.testing.assert_allclose(dXr, dX[rows], atol=1e-14)
+    # dW shares of a row partition add up to the full dW
+    parts = [np.arange(0, 9), np.arange(9, 23)]
+    dW_sum = sum(O.backward_rows(X[r], W, y[r], full["lse"][r], full["n_valid"], 1.5,
+                                 softcap=softcap)[1] for r in parts)
+    np.testing.assert_allclose(dW_sum, dW, atol=1e-14)
+    dXb, _ = O.backward_rows(X[rows], W, y[rows], full["lse"][rows], full["n_valid"], 1.5,
+                             softcap=softcap)
+    np.testing.assert_allclose(dXb, dX[rows], atol=1e-14)
     vrows = np.array([1, 7, 30])
     dWr = O.dW_vocab_rows(X, W, y, full["lse"], full["n_valid"], vrows, 1.5,
                           softcap=softcap)
