@@ -3,6 +3,7 @@
 // No device memory is ever allocated here; everything lives in the caller's
 // workspace.
 #include <algorithm>
+#include <cstdlib>
 #include <climits>
 #include <cstring>
 #include <mutex>
@@ -33,6 +34,29 @@ int pick_splits(int T, int n_vtiles) {
   int S = (int)ceil_div(kTargetCUs, T);
   S = std::max(1, std::min(S, n_vtiles));
   return S;
+}
+
+// XCD sub-grid of a T x S (token tile, split) persistent grid: each of the 8
+// XCDs takes a tt x ss block (tt | T, ss | S, (T/tt)·(S/ss) = 8), as square as
+// possible, fewer token tiles on ties.  tt = 0 keeps the plain order.
+void pick_xcd_grid(int T, int S, int& tt, int& ss) {
+  tt = 0;
+  ss = 0;
+  const int nwg = T * S;
+  if (nwg % 8 != 0) return;
+  const int per = nwg / 8;
+  int best = INT_MAX;
+  for (int s = 1; s <= per; ++s) {
+    if (per % s != 0 || S % s != 0) continue;
+    const int t = per / s;
+    if (T % t != 0 || (T / t) * (S / s) != 8) continue;
+    const int score = 2 * std::abs(t - s) + (t > s ? 1 : 0);
+    if (score < best) {
+      best = score;
+      tt = t;
+      ss = s;
+    }
+  }
 }
 
 struct FwdPlan {
@@ -301,6 +325,7 @@ lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labe
   LseParams lp{};
   lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
   lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles; lp.softcap = softcap;
+  pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
   lp.part_m = pm; lp.part_s = ps;
   LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
   LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, lse_dev, loss_dev, blocks, stream));
@@ -359,6 +384,7 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
     GradParams gp{};
     gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
     gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt; gp.softcap = softcap;
+    pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 

@@ -56,6 +56,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two floats -> packed bf16 pair (lo, hi), round to nearest even; gfx950 does
+// this in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows r
 // and r+8 differ in the low bit so that 16 consecutive rows reading the same
 // logical chunk land in 16 distinct 16-byte bank groups.
@@ -169,6 +177,174 @@ struct MNMajorTile {
     }
   }
 };
+
+// ----------------------------------------------------------------------------
+// Direct-to-LDS K-major loader (buffer_load_dwordx4 ... lds).  One wave
+// instruction fills a 1 KiB block of LDS, lane l writing bytes [16·l, 16·l+16)
+// of it (checked on gfx950: out-of-range lanes write zeros).  Block b holds
+// tile rows 8b .. 8b+7; lane l therefore fetches row 8b + l/8 at physical
+// chunk l % 8, i.e. logical K chunk (l % 8) ^ swz(row), so the LDS image is the
+// same swizzled K-major layout the fragment reads expect.  Each of the 4 waves
+// issues 8 instructions per operand per 64-deep step (blocks 4i + wave).
+// ----------------------------------------------------------------------------
+#define LCE_LDS __attribute__((address_space(3)))
+
+template <bool kTail>
+struct DtlKMajorTile {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;      // byte offset of this lane's chunk in block `wave`
+  uint32_t row_step;  // bytes between blocks 4i + wave and 4(i+1) + wave (32 rows)
+  int32_t kchunk;     // this lane's logical K offset inside a 64-deep block
+  int32_t wave;       // wave index, wave-uniform (kept in an SGPR)
+  int64_t k_total;
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0,
+                                       int64_t rows_total, int64_t k_total_, int tid) {
+    rsrc = make_rsrc(base + row0 * ld, (rows_total - row0) * ld * 2);
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Rows 8(4i + w) + lane/8 all share swz(row) = (lane/8) ^ (w & 1), so the
+    // lane's logical chunk is the same in every block it fills.
+    const int row = wave * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    kchunk = c * 8;
+    k_total = k_total_;
+    voff = (uint32_t)(row * ld * 2 + c * 16);
+    row_step = (uint32_t)(32 * ld * 2);
+  }
+  // Enqueue the 64-deep K block starting at k0 into `stage` (asynchronous:
+  // complete once this wave's vmcnt has drained past these 8 loads).  Without
+  // kTail, k_total must be a multiple of 64 and every chunk is in range.
+  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+    uint32_t base = voff + (uint32_t)(k0 * 2);
+    if (kTail) base = (k0 + kchunk < k_total) ? base : kOutOfRange;
+    LCE_LDS uint16_t* dst = stage + wave * 512;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t vo = (kTail && base == kOutOfRange) ? kOutOfRange : base + i * row_step;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LCE_LDS void*)(dst + i * 2048), 16, (int)vo,
+                                               0, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);
+
+// Workgroup barrier without the memory fence __syncthreads() carries (that
+// fence would drain every outstanding direct-to-LDS load).  Callers wait for
+// the loads that must be visible with an explicit vmcnt first; the empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMA operand fragments of one 16-deep K slice for a wave's 128 x 128 quarter.
+struct Frag {
+  bf16x8 a[kMI], b[kNI];
+};
+
+__device__ __forceinline__ void read_frag(Frag& f, const LCE_LDS uint16_t* sA,
+                                          const LCE_LDS uint16_t* sB, int wm, int wn, int lane,
+                                          int t) {
+  const int lrow = lane & 31, chunk = t * 2 + (lane >> 5);
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+    f.a[mi] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(sA + lds_off(wm * kWaveTile + mi * 32 + lrow, chunk)));
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni)
+    f.b[ni] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(sB + lds_off(wn * kWaveTile + ni * 32 + lrow, chunk)));
+}
+
+__device__ __forceinline__ void mfma_group(const Frag& f, f32x16 (&acc)[kMI][kNI]) {
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+}
+
+#define LCE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One 256 x 256 tile, both operands K-major, K range [0, k_total) with
+// k_total >= 1 (so the loop runs at least once), through a
+// two-stage direct-to-LDS pipeline.  Per 64-deep step: enqueue the next
+// block, read the next K-slice fragments while the current slice's 16 MFMAs
+// run, and issue the step's last slice only after the barrier so that it
+// overlaps the first fragment reads of the next stage.  LDS: 128 KiB
+// (stage s of A at smem + s·kStageElems, of B at smem + (2 + s)·kStageElems).
+template <bool kTail>
+__device__ __forceinline__ void gemm_tile_kk(const uint16_t* A, int64_t lda, int64_t a_row0,
+                                             int64_t a_rows, const uint16_t* B, int64_t ldb,
+                                             int64_t b_row0, int64_t b_rows, int64_t k_total,
+                                             LCE_LDS uint16_t* smem, f32x16 (&acc)[kMI][kNI]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nsteps = (int)((k_total + kBK - 1) / kBK);
+  DtlKMajorTile<kTail> la, lb;
+  la.init(A, lda, a_row0, a_rows, k_total, tid);
+  lb.init(B, ldb, b_row0, b_rows, k_total, tid);
+  lds_barrier();  // every wave is done with the LDS of the previous tile
+  la.load(smem, 0);
+  lb.load(smem + 2 * kStageElems, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  lds_barrier();
+  Frag f0, f1, f2, f3;
+  read_frag(f0, smem, smem + 2 * kStageElems, wm, wn, lane, 0);
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    const LCE_LDS uint16_t* sa = smem + cur * kStageElems;
+    const LCE_LDS uint16_t* sb = smem + (2 + cur) * kStageElems;
+    if (step + 1 < nsteps) {
+      la.load(smem + (cur ^ 1) * kStageElems, (int64_t)(step + 1) * kBK);
+      lb.load(smem + (2 + (cur ^ 1)) * kStageElems, (int64_t)(step + 1) * kBK);
+    }
+    read_frag(f1, sa, sb, wm, wn, lane, 1);
+    LCE_SCHED_FENCE();
+    if (step > 0) mfma_group(f3, acc);
+    LCE_SCHED_FENCE();
+    mfma_group(f0, acc);
+    LCE_SCHED_FENCE();
+    read_frag(f2, sa, sb, wm, wn, lane, 2);
+    LCE_SCHED_FENCE();
+    mfma_group(f1, acc);
+    LCE_SCHED_FENCE();
+    read_frag(f3, sa, sb, wm, wn, lane, 3);
+    LCE_SCHED_FENCE();
+    mfma_group(f2, acc);
+    LCE_SCHED_FENCE();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of the next stage landed
+    lds_barrier();                          // ... and every other wave's
+    if (step + 1 < nsteps)
+      read_frag(f0, smem + (cur ^ 1) * kStageElems, smem + (2 + (cur ^ 1)) * kStageElems, wm, wn,
+                lane, 0);
+    LCE_SCHED_FENCE();
+  }
+  mfma_group(f3, acc);
+}
+
+// Map a logical workgroup id of a (token tile, split) grid so that each XCD
+// (a contiguous range of nwg/8 logical ids after xcd_remap) covers a tt x ss
+// block of token tiles x vocabulary splits: per pipeline step the XCD then
+// touches tt distinct X blocks and ss distinct W blocks.  tt == 0 keeps the
+// plain order (token tile fastest).
+__device__ __forceinline__ void grid_tile(int g, int T, int tt, int ss, int& ti, int& split) {
+  if (tt == 0) {
+    ti = g % T;
+    split = g / T;
+    return;
+  }
+  const int per = tt * ss, x = g / per, local = g % per, ngt = T / tt;
+  ti = (x % ngt) * tt + local % tt;
+  split = (x / ngt) * ss + local / tt;
+}
 
 // ----------------------------------------------------------------------------
 // LDS -> MFMA for one 64-deep pipeline step of a wave's 128 x 128 quarter.

@@ -38,8 +38,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int64_
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t nsteps = (k_end - k_begin + kBK - 1) / kBK;
   if (nsteps <= 0) return;
-  uint16_t* sA[2] = {smem, smem + kStageElems};
-  uint16_t* sB[2] = {smem + 2 * kStageElems, smem + 3 * kStageElems};
+  // Stage s of A at smem + s·kStageElems, of B at smem + (2 + s)·kStageElems.
+  // (Plain offset arithmetic keeps the LDS address space visible to the
+  // compiler, so fragment reads are ds_read and not flat loads.)
   LA la;
   LB lb;
   la.init(A, lda, a_row0, a_rows, a_ktotal, tid);
@@ -47,8 +48,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int64_
   la.load(k_begin);
   lb.load(k_begin);
   __syncthreads();  // the previous tile's last readers of stage 0 are done
-  la.store(sA[0], tid);
-  lb.store(sB[0], tid);
+  la.store(smem, tid);
+  lb.store(smem + 2 * kStageElems, tid);
   __syncthreads();
   for (int64_t step = 0; step < nsteps; ++step) {
     const int cur = (int)(step & 1);
@@ -58,10 +59,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int64_
       la.load(k);
       lb.load(k);
     }
-    mfma_step(sA[cur], sB[cur], wm, wn, lane, acc);
+    mfma_step(smem + cur * kStageElems, smem + (2 + cur) * kStageElems, wm, wn, lane, acc);
     if (more) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
+      la.store(smem + (cur ^ 1) * kStageElems, tid);
+      lb.store(smem + (2 + (cur ^ 1)) * kStageElems, tid);
     }
     __syncthreads();
   }
@@ -70,56 +71,90 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int64_
 // ---------------------------------------------------------------------------
 // Forward: per (token tile, vocabulary split) partial (max, sum-exp).
 // Values are kept in base 2: u = z·log2(e), s = Σ 2^(u − m).
+//
+// Epilogue modes (kMode):
+//   kPlain     no softcap: a max pass over the tile's raw logits, then the
+//              sum pass against the merged running max.
+//   kCapFixed  softcap c with 2c·log2(e) < 120: u = c·log2(e)·tanh(z/c) is
+//              bounded by c2 = c·log2(e), so the fixed reference m = c2 needs
+//              no max pass; every term 2^(u − c2) lies in [2^(−2·c2), 1],
+//              above the smallest normal float.  With r = 1/(2^(z·k2) + 1),
+//              u − c2 = −2·c2·r.
+//   kCapGeneral softcap too large for the fixed reference: max pass on raw z
+//              (tanh is increasing), then the sum pass.
 // ---------------------------------------------------------------------------
+enum EpiMode { kPlain = 0, kCapFixed = 1, kCapGeneral = 2 };
+
+template <bool kTail, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 lse_partials_kernel(LseParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
+  LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int g = xcd_remap(blockIdx.x, gridDim.x);
-  const int ti = g % p.T, split = g / p.T;
+  int ti, split;
+  grid_tile(g, p.T, p.tt, p.ss, ti, split);
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;
-  const bool capped = p.softcap > 0.0f;
-  const float k2 = capped ? 2.0f * kLog2e / p.softcap : 0.0f;
-  const float c2 = capped ? p.softcap * kLog2e : kLog2e;
+  const float k2 = kMode != kPlain ? 2.0f * kLog2e / p.softcap : 0.0f;
+  const float c2 = kMode != kPlain ? p.softcap * kLog2e : 0.0f;
   const float NEG_INF = -__builtin_inff();
 
   float m[kNI], s[kNI];
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) { m[ni] = NEG_INF; s[ni] = 0.0f; }
+  for (int ni = 0; ni < kNI; ++ni) {
+    m[ni] = kMode == kCapFixed ? c2 : NEG_INF;
+    s[ni] = 0.0f;
+  }
 
   f32x16 acc[kMI][kNI];
   for (int j = j0; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
     zero_acc(acc);
-    gemm_tile<KMajorTile, KMajorTile>(p.W, p.H, v0, p.V, p.H, p.X, p.H, tok0, p.N, p.H, 0, p.H,
-                                      smem, acc);
-    // Vocabulary rows of this tile at or beyond V are masked: row_const >= lim.
+    gemm_tile_kk<kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, p.H, smem, acc);
+    // Vocabulary rows of this tile at or beyond V are masked (only in the last
+    // tile, so the test is a uniform branch): masked iff row_const >= lim.
+    const bool full = v0 + kTile <= p.V;
     const int lim = (int)(p.V - v0 < kTile ? p.V - v0 : kTile) - acc_row_lane(wm, lane);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      float tmax = NEG_INF;
+      float mref = m[ni];
+      if (kMode != kCapFixed) {
+        float zmax = NEG_INF;
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = acc[mi][ni][r];
+            zmax = fmaxf(zmax, (full || acc_row_const(mi, r) < lim) ? z : NEG_INF);
+          }
+        const float umax = kMode == kPlain ? zmax * kLog2e
+                                           : (zmax == NEG_INF ? NEG_INF : c2 * tanh_of_scaled(zmax, k2));
+        const float mn = fmaxf(m[ni], umax);
+        mref = mn == NEG_INF ? 0.0f : mn;   // nothing valid yet: every term is an exact 0
+        s[ni] *= exp2_fast(m[ni] - mref);
+        m[ni] = mn;
+      }
+      float sum = 0.0f;
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float z = acc[mi][ni][r];
-          float u = capped ? c2 * tanh_of_scaled(z, k2) : z * kLog2e;
-          if (acc_row_const(mi, r) >= lim) u = NEG_INF;
-          acc[mi][ni][r] = u;
-          tmax = fmaxf(tmax, u);
+          float e;
+          if (kMode == kPlain) {
+            e = exp2_fast(fmaf(z, kLog2e, -mref));
+          } else if (kMode == kCapFixed) {
+            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+            e = exp2_fast(-2.0f * c2 * rr);
+          } else {
+            e = exp2_fast(c2 * tanh_of_scaled(z, k2) - mref);
+          }
+          sum += (full || acc_row_const(mi, r) < lim) ? e : 0.0f;
         }
-      const float mn = fmaxf(m[ni], tmax);
-      if (mn == NEG_INF) continue;  // no valid vocabulary row seen yet
-      float sum = 0.0f;
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += exp2_fast(acc[mi][ni][r] - mn);
-      s[ni] = s[ni] * exp2_fast(m[ni] - mn) + sum;
-      m[ni] = mn;
+      s[ni] += sum;
     }
   }
 
@@ -129,14 +164,13 @@ lse_partials_kernel(LseParams p) {
     const float m2 = __shfl_xor(m[ni], 32);
     const float s2 = __shfl_xor(s[ni], 32);
     const float mn = fmaxf(m[ni], m2);
-    if (mn != NEG_INF) {
-      s[ni] = s[ni] * exp2_fast(m[ni] - mn) + s2 * exp2_fast(m2 - mn);
-      m[ni] = mn;
-    }
+    const float mref = mn == NEG_INF ? 0.0f : mn;
+    s[ni] = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
+    m[ni] = mn;
   }
   // Waves wm = 0 and wm = 1 cover the two vocabulary halves of the same tokens.
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
+  float* red = reinterpret_cast<float*>(smem_raw);
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
@@ -151,15 +185,12 @@ lse_partials_kernel(LseParams p) {
     for (int ni = 0; ni < kNI; ++ni) {
       const int col = acc_col(wn, ni, lane);
       const float m2 = red[col], s2 = red[kTile + col];
-      float mm = m[ni], ss = s[ni];
-      const float mn = fmaxf(mm, m2);
-      if (mn != NEG_INF) {
-        ss = ss * exp2_fast(mm - mn) + s2 * exp2_fast(m2 - mn);
-        mm = mn;
-      }
+      const float mn = fmaxf(m[ni], m2);
+      const float mref = mn == NEG_INF ? 0.0f : mn;
+      const float ss = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
       const int64_t tok = tok0 + col;
       if (tok < p.N) {
-        p.part_m[(int64_t)split * p.N + tok] = mm;
+        p.part_m[(int64_t)split * p.N + tok] = mn;
         p.part_s[(int64_t)split * p.N + tok] = ss;
       }
     }
@@ -170,32 +201,35 @@ lse_partials_kernel(LseParams p) {
 // Backward, step 1: recompute the logits of one vocabulary chunk and write
 // G = p · (1 − tanh²) (the dense part of dZ before the 1/n_valid scale) as
 // bf16 into G[token][v − v_begin].  Ignored rows give 0, bad rows NaN,
-// vocabulary rows beyond V give 0.
+// vocabulary rows beyond V give 0.  With softcap, r = 1/(2^(z·k2) + 1) gives
+// tanh = 1 − 2r, p = 2^((c2 − lse2) − 2·c2·r) and 1 − tanh² = 4r(1 − r).
 // ---------------------------------------------------------------------------
+template <bool kTail, bool kCapped>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
+  LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int g = xcd_remap(blockIdx.x, gridDim.x);
-  const int ti = g % p.T, split = g / p.T;
+  int ti, split;
+  grid_tile(g, p.T, p.tt, p.ss, ti, split);
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;
-  const bool capped = p.softcap > 0.0f;
-  const float k2 = capped ? 2.0f * kLog2e / p.softcap : 0.0f;
-  const float c2 = capped ? p.softcap * kLog2e : kLog2e;
+  const float k2 = kCapped ? 2.0f * kLog2e / p.softcap : 0.0f;
+  const float c2 = kCapped ? p.softcap * kLog2e : 0.0f;
   const float qnan = __builtin_nanf("");
 
-  // Per token column: base-2 LSE and the row class (fixed for all tiles).
-  float lse2[kNI], rscale[kNI];
-  bool tok_ok[kNI];
+  // Per token column: exponent offset and the row class (fixed for all tiles).
+  float off[kNI], rscale[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     const int64_t tok = tok0 + acc_col(wn, ni, lane);
-    tok_ok[ni] = tok < p.N;
-    const int st = tok_ok[ni] ? p.row_state[tok] : (int)kRowIgnored;
-    lse2[ni] = tok_ok[ni] ? p.lse[tok] * kLog2e : 0.0f;
+    const bool ok = tok < p.N;
+    const int st = ok ? p.row_state[tok] : (int)kRowIgnored;
+    const float lse2 = ok ? p.lse[tok] * kLog2e : 0.0f;
+    off[ni] = kCapped ? c2 - lse2 : -lse2;
     rscale[ni] = st == kRowValid ? 1.0f : (st == kRowBad ? qnan : 0.0f);
   }
 
@@ -204,13 +238,14 @@ grad_logits_kernel(GradParams p) {
     const int64_t vloc0 = (int64_t)j * kTile;      // chunk-local vocabulary row
     const int64_t v0 = p.v_begin + vloc0;          // global vocabulary row
     zero_acc(acc);
-    gemm_tile<KMajorTile, KMajorTile>(p.W, p.H, v0, p.V, p.H, p.X, p.H, tok0, p.N, p.H, 0, p.H,
-                                      smem, acc);
+    gemm_tile_kk<kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, p.H, smem, acc);
+    const bool full = v0 + kTile <= p.V;
     const int lim = (int)(p.V - v0 < kTile ? p.V - v0 : kTile) - acc_row_lane(wm, lane);
     const int64_t vl_lane = vloc0 + acc_row_lane(wm, lane);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      uint16_t* grow = p.G + (tok0 + acc_col(wn, ni, lane)) * p.ldg + vl_lane;
+      const int64_t tok = tok0 + acc_col(wn, ni, lane);
+      uint16_t* grow = p.G + tok * p.ldg + vl_lane;
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
@@ -220,23 +255,21 @@ grad_logits_kernel(GradParams p) {
           for (int q = 0; q < 4; ++q) {
             const int r = gq * 4 + q;
             const float z = acc[mi][ni][r];
-            float u, d;
-            if (capped) {
-              const float t = tanh_of_scaled(z, k2);
-              u = c2 * t;
-              d = 1.0f - t * t;
+            float val;
+            if (kCapped) {
+              const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+              const float d = 4.0f * rr * (1.0f - rr);
+              val = exp2_fast(fmaf(-2.0f * c2, rr, off[ni])) * d;
             } else {
-              u = z * kLog2e;
-              d = 1.0f;
+              val = exp2_fast(fmaf(z, kLog2e, off[ni]));
             }
-            float val = exp2_fast(u - lse2[ni]) * d * rscale[ni];
-            if (acc_row_const(mi, r) >= lim) val = 0.0f;
-            gv[q] = val;
+            val *= rscale[ni];
+            gv[q] = (full || acc_row_const(mi, r) < lim) ? val : 0.0f;
           }
-          if (tok_ok[ni]) {
+          if (tok < p.N) {
             u32x2 packed;
-            packed[0] = f32_to_bf16_bits(gv[0]) | (f32_to_bf16_bits(gv[1]) << 16);
-            packed[1] = f32_to_bf16_bits(gv[2]) | (f32_to_bf16_bits(gv[3]) << 16);
+            packed[0] = pack_bf16x2(gv[0], gv[1]);
+            packed[1] = pack_bf16x2(gv[2], gv[3]);
             *reinterpret_cast<u32x2*>(grow + acc_row_const(mi, gq * 4)) = packed;
           }
         }
@@ -324,13 +357,36 @@ dw_gemm_kernel(DwParams p) {
 // ---------------------------------------------------------------------------
 hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
-  hipLaunchKernelGGL(lse_partials_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  const bool tail = p.H % kBK != 0;
+  // Fixed reference 2^(u - c2) >= 2^(-2·c2) stays a normal float for c2 < 60.
+  const int mode = p.softcap <= 0.0f ? kPlain
+                   : (p.softcap * kLog2e < 60.0f ? kCapFixed : kCapGeneral);
+#define LCE_LSE_LAUNCH(T_, M_) \
+  hipLaunchKernelGGL((lse_partials_kernel<T_, M_>), dim3(grid), dim3(kThreads), 0, stream, p)
+  if (tail) {
+    if (mode == kPlain) LCE_LSE_LAUNCH(true, kPlain);
+    else if (mode == kCapFixed) LCE_LSE_LAUNCH(true, kCapFixed);
+    else LCE_LSE_LAUNCH(true, kCapGeneral);
+  } else {
+    if (mode == kPlain) LCE_LSE_LAUNCH(false, kPlain);
+    else if (mode == kCapFixed) LCE_LSE_LAUNCH(false, kCapFixed);
+    else LCE_LSE_LAUNCH(false, kCapGeneral);
+  }
+#undef LCE_LSE_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
-  hipLaunchKernelGGL(grad_logits_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f;
+  if (tail && capped)
+    hipLaunchKernelGGL((grad_logits_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (tail)
+    hipLaunchKernelGGL((grad_logits_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (capped)
+    hipLaunchKernelGGL((grad_logits_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((grad_logits_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ struct LseParams {
   const uint16_t* W;  // bf16 [V, H]
   int64_t N, H, V;
   int T, S, n_vtiles;
+  int tt, ss;         // XCD sub-grid (see grid_tile); 0 = plain order
   float softcap;
   float* part_m;      // [S, N] base-2 running max
   float* part_s;      // [S, N] Σ 2^(u − m)
@@ -24,6 +25,7 @@ struct GradParams {
   int64_t N, H, V;
   int64_t v_begin;
   int T, S, n_vtiles;
+  int tt, ss;
   float softcap;
   const float* lse;          // [N]
   const int32_t* row_state;  // [N]
