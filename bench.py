@@ -24,7 +24,10 @@ sys.path.insert(0, ROOT)
 BF16_DENSE_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0
 METRIC = "fwd+bwd tokens/s and % bf16 MFMA peak, Gemma-2 2B LM-head shape, 1 GPU"
-GEMM_KERNELS = ("lse_partials", "grad_logits", "dx_gemm", "dw_gemm")
+# MFMA kernels and their algorithmic work per fwd+bwd step, in units of
+# N·H·V multiply-adds x 2 flops: the forward logits, the recomputed logits,
+# and the two gradient contractions (done together per vocabulary chunk).
+GEMM_KERNELS = {"lse_partials": 2, "grad_logits": 2, "chunk_gemm": 4}
 
 
 def log(*a):
@@ -175,12 +178,12 @@ def main():
     flops = 8 * N * H * V
     tflops = flops / (ms_per_step / 1e3) / 1e12
 
-    # Dominant kernel and its roofline (algorithmic work: 2·N·H·V per step for
-    # each of the four contractions, spread over that kernel's launches).
+    # Dominant kernel and its roofline (algorithmic work per step from
+    # GEMM_KERNELS, spread over that kernel's launches).
     dom = max(GEMM_KERNELS, key=lambda k: kernels.get(k, (0, 0.0))[1])
     launches, total_ms = kernels[dom]
     avg_ms = total_ms / launches
-    dom_flops_per_launch = 2 * N * H * V * args.steps / launches
+    dom_flops_per_launch = GEMM_KERNELS[dom] * N * H * V * args.steps / launches
     achieved = dom_flops_per_launch / (avg_ms / 1e3) / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles(dom, w.name, src_hash)
@@ -193,9 +196,9 @@ def main():
     per_kernel = {k: {"launches_per_step": v[0] / args.steps,
                       "ms_per_step": round(v[1] / args.steps, 4)}
                   for k, v in kernels.items()}
-    for k in GEMM_KERNELS:
+    for k, units in GEMM_KERNELS.items():
         if k in kernels:
-            per_kernel[k]["tflops"] = round(2 * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
+            per_kernel[k]["tflops"] = round(units * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
 
     cpu = None
     if not args.no_cpu_baseline:

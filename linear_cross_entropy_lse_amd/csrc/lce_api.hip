@@ -82,7 +82,7 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 }
 
 struct BwdPlan {
-  int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, KS, nb_prep;
+  int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
   int64_t Vc, ldg;
   size_t off_state, off_key, off_deriv, off_sorted, off_blocks, off_scalars, off_G, off_dXp,
       off_dWs, total;
@@ -104,18 +104,6 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.n_vtiles_chunk = (int)(p.Vc / kTile);
   p.S_chunk = pick_splits(p.T, p.n_vtiles_chunk);
   p.nt_h = (int)ceil_div(H, kTile);
-  // Split the dX contraction of a chunk over KS partial buffers when the
-  // output alone has too few tiles to fill the chip (tile-quantisation ≥ 90 %).
-  const int64_t tiles = (int64_t)p.T * p.nt_h;
-  const int64_t steps = ceil_div(p.Vc, kBK);
-  p.KS = 1;
-  for (int ks = 1; ks <= 8; ks *= 2) {
-    if (steps / ks < 8) break;
-    const int64_t t = tiles * ks;
-    const double eff = (double)t / (double)(ceil_div(t, kTargetCUs) * kTargetCUs);
-    p.KS = ks;
-    if (eff >= 0.9) break;
-  }
   p.nb_prep = row_prep_blocks(Nc);
   size_t o = 0;
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
@@ -125,7 +113,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
   p.off_scalars = o; o = align_up(o + 16);
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)N * (size_t)p.ldg);
-  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.KS * (size_t)N * (size_t)H);
+  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
   p.off_dWs = o;
   if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
   p.total = std::max<size_t>(o, kAlign);
@@ -388,21 +376,15 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 
-    DxParams xp{};
-    xp.G = G; xp.ldg = pl.ldg; xp.Wc = W + v_begin * H; xp.wc_rows = V - v_begin;
-    xp.N = N; xp.H = H; xp.k_len = chunk_len;
-    xp.nt_tok = pl.T; xp.nt_h = pl.nt_h; xp.KS = pl.KS; xp.accumulate = c > 0; xp.dXp = dXp;
-    LCE_LAUNCH("dx_gemm", stream, launch_dx_gemm(xp, stream));
-
-    DwParams wp{};
-    wp.G = G; wp.ldg = pl.ldg; wp.X = X; wp.N = N; wp.H = H; wp.chunk_len = chunk_len;
-    wp.nt_v = n_vt; wp.nt_h = pl.nt_h; wp.scale = scale;
-    if (dW_dtype == LCE_F32) {
-      wp.dst = static_cast<float*>(dW_dev) + v_begin * H;
-      LCE_LAUNCH("dw_gemm", stream, launch_dw_gemm(wp, stream));
-    } else {
-      wp.dst = dWs;
-      LCE_LAUNCH("dw_gemm", stream, launch_dw_gemm(wp, stream));
+    ChunkGemmParams cp{};
+    cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
+    cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
+    cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
+    cp.dx_first = ceil_div(chunk_len, kBK) >= ceil_div(N, kBK);  // longer tiles first
+    cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = scale;
+    cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
+    LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
+    if (dW_dtype == LCE_BF16) {
       LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale, dWs, v_begin,
                                 v_begin + chunk_len, stream));
       LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
@@ -412,7 +394,7 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   if (dW_dtype == LCE_F32)
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale,
                               static_cast<float*>(dW_dev), 0, V, stream));
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.KS, N, H, state, key, deriv, W, scale, dX_dev,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, deriv, W, scale, dX_dev,
                              dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -32,7 +34,6 @@ constexpr int kWaveTile = 128;  // each wave: 128 x 128
 constexpr int kMI = 4;          // 32x32 MFMA blocks per wave along M
 constexpr int kNI = 4;          // ... along N
 constexpr int kStageElems = kTile * kBK;      // bf16 elements per operand per stage
-constexpr int kLoadsPerThread = kStageElems / 8 / kThreads;  // 16-byte loads: 8
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -96,88 +97,6 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
-// K-major operand: element (row, k) at base[row * ld + k].  Rows at or beyond
-// `rows_total` read as zero, and so do K chunks at or beyond `k_total`
-// (k_total % 8 == 0).
-struct KMajorTile {
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff;      // byte offset of this thread's first 16-byte chunk
-  uint32_t row_step;  // bytes between the rows of consecutive loads (32 rows)
-  int32_t kchunk;     // this thread's K offset inside a 64-wide step
-  int64_t k_total;
-  u32x4 r[kLoadsPerThread];
-
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0,
-                                       int64_t rows_total, int64_t k_total_, int tid) {
-    rsrc = make_rsrc(base + row0 * ld, (rows_total - row0) * ld * 2);
-    const int row = tid >> 3, chunk = tid & 7;
-    voff = (uint32_t)(row * ld * 2 + chunk * 16);
-    row_step = (uint32_t)(kThreads / 8 * ld * 2);
-    kchunk = chunk * 8;
-    k_total = k_total_;
-  }
-  __device__ __forceinline__ void load(int64_t k0) {
-    const bool kv = k0 + kchunk < k_total;
-    const uint32_t base = voff + (uint32_t)(k0 * 2);
-#pragma unroll
-    for (int it = 0; it < kLoadsPerThread; ++it)
-      r[it] = buffer_load16(rsrc, kv ? base + it * row_step : kOutOfRange);
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int it = 0; it < kLoadsPerThread; ++it) {
-      const int idx = it * kThreads + tid;
-      const int row = idx >> 3, chunk = idx & 7;
-      *reinterpret_cast<u32x4*>(lds + lds_off(row, chunk)) = r[it];
-    }
-  }
-};
-
-// MN-major operand: element (row, k) at base[k * ld + row], i.e. the tile's
-// rows are contiguous in memory.  Each thread loads an 8 (k) x 8 (row) block
-// with 8 16-byte loads and transposes it in registers, so LDS receives the same
-// K-major layout as above.  K rows at or beyond `k_total` read as zero; rows
-// (the contiguous dimension) are clamped in blocks of 8 (rows_total % 8 == 0).
-struct MNMajorTile {
-  const uint16_t* base;
-  int64_t ld, k_total;
-  uint32_t voff;  // byte offset of (k = 8·kb, row block) from the step's first K row
-  uint32_t ld_bytes;
-  u32x4 r[8];
-
-  __device__ __forceinline__ void init(const uint16_t* base_, int64_t ld_, int64_t row0,
-                                       int64_t rows_total, int64_t k_total_, int tid) {
-    base = base_;
-    ld = ld_;
-    k_total = k_total_;
-    const int rb = tid >> 3, kb = tid & 7;
-    int64_t gr = row0 + rb * 8;
-    gr = gr < rows_total ? gr : rows_total - 8;
-    ld_bytes = (uint32_t)(ld * 2);
-    voff = (uint32_t)(kb * 8 * ld * 2 + gr * 2);
-  }
-  __device__ __forceinline__ void load(int64_t k0) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld, (k_total - k0) * ld * 2);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = buffer_load16(rs, voff + j * ld_bytes);
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int rb = tid >> 3;
-    const int kb = tid & 7;
-    // out[i] = column i of the 8x8 block = (r[0][i], r[1][i], ..., r[7][i]).
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 o;
-      o[0] = __builtin_amdgcn_perm(r[1][i >> 1], r[0][i >> 1], sel);
-      o[1] = __builtin_amdgcn_perm(r[3][i >> 1], r[2][i >> 1], sel);
-      o[2] = __builtin_amdgcn_perm(r[5][i >> 1], r[4][i >> 1], sel);
-      o[3] = __builtin_amdgcn_perm(r[7][i >> 1], r[6][i >> 1], sel);
-      *reinterpret_cast<u32x4*>(lds + lds_off(rb * 8 + i, kb)) = o;
-    }
-  }
-};
-
 // ----------------------------------------------------------------------------
 // Direct-to-LDS K-major loader (buffer_load_dwordx4 ... lds).  One wave
 // instruction fills a 1 KiB block of LDS, lane l writing bytes [16·l, 16·l+16)
@@ -228,6 +147,72 @@ struct DtlKMajorTile {
   }
 };
 
+// Direct-to-LDS MN-major loader: the tile's contiguous dimension m runs along
+// memory rows of length ld (element (m, k) at base[k·ld + m]).  LDS holds the
+// tile as 64 rows (one per k) of 256 m values = 512 B, its 16-byte chunks
+// XOR-swizzled by 4·(k % 4) so that the transposing fragment reads below hit
+// 16 distinct 16-byte bank groups.  One wave instruction fills two LDS rows
+// (1 KiB, lane l -> row l/32, physical chunk l % 32); blocks 4i + wave.
+// K rows at or beyond k_total read as zero (the descriptor ends there);
+// columns past the end of a memory row only reach output columns that are
+// never stored.
+__device__ __forceinline__ int mn_off(int k, int m) {
+  return k * 256 + ((((m >> 3) ^ ((k & 3) << 2))) << 3) + (m & 7);
+}
+
+struct DtlMNMajorTile {
+  const uint16_t* base;
+  int64_t ld, k_total;
+  uint32_t voff, row_step;
+  int32_t wave;
+
+  __device__ __forceinline__ void init(const uint16_t* base_, int64_t ld_, int64_t col0,
+                                       int64_t /*cols_total*/, int64_t k_total_, int tid) {
+    base = base_;
+    ld = ld_;
+    k_total = k_total_;
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = 2 * wave + (lane >> 5);  // + 8i for block 4i + wave; row % 4 fixed
+    const int c = (lane & 31) ^ ((row & 3) << 2);
+    voff = (uint32_t)(row * ld * 2 + (col0 + c * 8) * 2);
+    row_step = (uint32_t)(8 * ld * 2);
+  }
+  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * ld, (k_total - k0) * ld * 2);
+    LCE_LDS uint16_t* dst = stage + wave * 512;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LCE_LDS void*)(dst + i * 2048), 16,
+                                               (int)(voff + i * row_step), 0, 0, 0);
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA fragment of tile rows mbase .. mbase+31, K slice t (16 deep).
+// K-major LDS: one 16-byte read.  MN-major LDS: two ds_read_b64_tr_b16.  That
+// instruction works on groups of 16 lanes: lane k supplies 4 consecutive
+// elements P_k and lane i receives P_{4j + i/4}[i % 4], j = 0..3 (checked on
+// gfx950).  Pointing lane k' at k-row (k0 + k'/4), columns m0 + 4(k' % 4)
+// therefore hands lane i the 4 consecutive k of column m0 + i.
+template <bool kMN>
+__device__ __forceinline__ bf16x8 frag_read(const LCE_LDS uint16_t* s, int mbase, int t, int lane) {
+  if (!kMN) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(s + lds_off(mbase + (lane & 31), t * 2 + (lane >> 5))));
+  } else {
+    const int g = lane >> 4, kk = lane & 15;
+    const int m = mbase + 16 * (g & 1) + 4 * (kk & 3);
+    const int k0 = t * 16 + 8 * (g >> 1) + (kk >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCE_LDS s16x4*)(s + mn_off(k0, m)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCE_LDS s16x4*)(s + mn_off(k0 + 4, m)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
@@ -249,18 +234,14 @@ struct Frag {
   bf16x8 a[kMI], b[kNI];
 };
 
+template <bool kAmn, bool kBmn>
 __device__ __forceinline__ void read_frag(Frag& f, const LCE_LDS uint16_t* sA,
                                           const LCE_LDS uint16_t* sB, int wm, int wn, int lane,
                                           int t) {
-  const int lrow = lane & 31, chunk = t * 2 + (lane >> 5);
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
-    f.a[mi] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(sA + lds_off(wm * kWaveTile + mi * 32 + lrow, chunk)));
+  for (int mi = 0; mi < kMI; ++mi) f.a[mi] = frag_read<kAmn>(sA, wm * kWaveTile + mi * 32, t, lane);
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni)
-    f.b[ni] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(sB + lds_off(wn * kWaveTile + ni * 32 + lrow, chunk)));
+  for (int ni = 0; ni < kNI; ++ni) f.b[ni] = frag_read<kBmn>(sB, wn * kWaveTile + ni * 32, t, lane);
 }
 
 __device__ __forceinline__ void mfma_group(const Frag& f, f32x16 (&acc)[kMI][kNI]) {
@@ -273,58 +254,64 @@ __device__ __forceinline__ void mfma_group(const Frag& f, f32x16 (&acc)[kMI][kNI
 
 #define LCE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// One 256 x 256 tile, both operands K-major, K range [0, k_total) with
-// k_total >= 1 (so the loop runs at least once), through a
-// two-stage direct-to-LDS pipeline.  Per 64-deep step: enqueue the next
-// block, read the next K-slice fragments while the current slice's 16 MFMAs
-// run, and issue the step's last slice only after the barrier so that it
-// overlaps the first fragment reads of the next stage.  LDS: 128 KiB
-// (stage s of A at smem + s·kStageElems, of B at smem + (2 + s)·kStageElems).
-template <bool kTail>
-__device__ __forceinline__ void gemm_tile_kk(const uint16_t* A, int64_t lda, int64_t a_row0,
-                                             int64_t a_rows, const uint16_t* B, int64_t ldb,
-                                             int64_t b_row0, int64_t b_rows, int64_t k_total,
-                                             LCE_LDS uint16_t* smem, f32x16 (&acc)[kMI][kNI]) {
+// One 256 x 256 tile C += A·Bᵀ over the K range [k_begin, k_end) (at least
+// one 64-deep step), each operand K-major (kAmn/kBmn false: DtlKMajorTile) or
+// MN-major (true: DtlMNMajorTile), through a two-stage direct-to-LDS
+// pipeline.  Per step: enqueue the next block, read the next K-slice
+// fragments while the current slice's 16 MFMAs run, and issue the step's last
+// slice only after the barrier so it overlaps the first fragment reads of the
+// next stage.  LDS: 128 KiB (stage s of A at smem + s·kStageElems, of B at
+// smem + (2 + s)·kStageElems).  For a K-major operand `row0/rows` are its
+// tile rows; for an MN-major one they are its column offset / column count.
+template <bool kAmn, bool kBmn, bool kTail>
+__device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_t a_row0,
+                                          int64_t a_rows, const uint16_t* B, int64_t ldb,
+                                          int64_t b_row0, int64_t b_rows, int64_t k_begin,
+                                          int64_t k_end, int64_t k_total, LCE_LDS uint16_t* smem,
+                                          f32x16 (&acc)[kMI][kNI]) {
+  typedef typename std::conditional<kAmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LA;
+  typedef typename std::conditional<kBmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nsteps = (int)((k_total + kBK - 1) / kBK);
-  DtlKMajorTile<kTail> la, lb;
+  const int nsteps = (int)((k_end - k_begin + kBK - 1) / kBK);
+  LA la;
+  LB lb;
   la.init(A, lda, a_row0, a_rows, k_total, tid);
   lb.init(B, ldb, b_row0, b_rows, k_total, tid);
   lds_barrier();  // every wave is done with the LDS of the previous tile
-  la.load(smem, 0);
-  lb.load(smem + 2 * kStageElems, 0);
+  la.load(smem, k_begin);
+  lb.load(smem + 2 * kStageElems, k_begin);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   lds_barrier();
   Frag f0, f1, f2, f3;
-  read_frag(f0, smem, smem + 2 * kStageElems, wm, wn, lane, 0);
+  read_frag<kAmn, kBmn>(f0, smem, smem + 2 * kStageElems, wm, wn, lane, 0);
   for (int step = 0; step < nsteps; ++step) {
     const int cur = step & 1;
     const LCE_LDS uint16_t* sa = smem + cur * kStageElems;
     const LCE_LDS uint16_t* sb = smem + (2 + cur) * kStageElems;
     if (step + 1 < nsteps) {
-      la.load(smem + (cur ^ 1) * kStageElems, (int64_t)(step + 1) * kBK);
-      lb.load(smem + (2 + (cur ^ 1)) * kStageElems, (int64_t)(step + 1) * kBK);
+      la.load(smem + (cur ^ 1) * kStageElems, k_begin + (int64_t)(step + 1) * kBK);
+      lb.load(smem + (2 + (cur ^ 1)) * kStageElems, k_begin + (int64_t)(step + 1) * kBK);
     }
-    read_frag(f1, sa, sb, wm, wn, lane, 1);
+    read_frag<kAmn, kBmn>(f1, sa, sb, wm, wn, lane, 1);
     LCE_SCHED_FENCE();
     if (step > 0) mfma_group(f3, acc);
     LCE_SCHED_FENCE();
     mfma_group(f0, acc);
     LCE_SCHED_FENCE();
-    read_frag(f2, sa, sb, wm, wn, lane, 2);
+    read_frag<kAmn, kBmn>(f2, sa, sb, wm, wn, lane, 2);
     LCE_SCHED_FENCE();
     mfma_group(f1, acc);
     LCE_SCHED_FENCE();
-    read_frag(f3, sa, sb, wm, wn, lane, 3);
+    read_frag<kAmn, kBmn>(f3, sa, sb, wm, wn, lane, 3);
     LCE_SCHED_FENCE();
     mfma_group(f2, acc);
     LCE_SCHED_FENCE();
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of the next stage landed
     lds_barrier();                          // ... and every other wave's
     if (step + 1 < nsteps)
-      read_frag(f0, smem + (cur ^ 1) * kStageElems, smem + (2 + (cur ^ 1)) * kStageElems, wm, wn,
-                lane, 0);
+      read_frag<kAmn, kBmn>(f0, smem + (cur ^ 1) * kStageElems, smem + (2 + (cur ^ 1)) * kStageElems,
+                            wm, wn, lane, 0);
     LCE_SCHED_FENCE();
   }
   mfma_group(f3, acc);
@@ -344,35 +331,6 @@ __device__ __forceinline__ void grid_tile(int g, int T, int tt, int ss, int& ti,
   const int per = tt * ss, x = g / per, local = g % per, ngt = T / tt;
   ti = (x % ngt) * tt + local % tt;
   split = (x / ngt) * ss + local / tt;
-}
-
-// ----------------------------------------------------------------------------
-// LDS -> MFMA for one 64-deep pipeline step of a wave's 128 x 128 quarter.
-// ----------------------------------------------------------------------------
-__device__ __forceinline__ void mfma_step(const uint16_t* __restrict__ sA,
-                                          const uint16_t* __restrict__ sB, int wm, int wn,
-                                          int lane, f32x16 (&acc)[kMI][kNI]) {
-  const int lrow = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int t = 0; t < kBK / 16; ++t) {
-    const int chunk = t * 2 + half;
-    bf16x8 a[kMI], b[kNI];
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      const int row = wm * kWaveTile + mi * 32 + lrow;
-      a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + lds_off(row, chunk)));
-    }
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int row = wn * kWaveTile + ni * 32 + lrow;
-      b[ni] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sB + lds_off(row, chunk)));
-    }
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-  }
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMI][kNI]) {

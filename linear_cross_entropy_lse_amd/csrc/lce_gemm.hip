@@ -14,8 +14,9 @@
 //                         fused-CE chapter §4), written as bf16 into a chunk of
 //                         the vocabulary (M011 §06: recompute the tile from the
 //                         saved LSE)
-//   dx_gemm_kernel        dX partial += G_chunk · W_chunk  (M011 §06: dH += dZ·W)
-//   dw_gemm_kernel        dW_chunk = s · G_chunkᵀ · X      (M011 §06: dW += dZᵀ·H)
+//   chunk_gemm_kernel     per vocabulary chunk, one launch holding both
+//                         dX_acc += G_chunk · W_chunk       (M011 §06: dH += dZ·W)
+//                         dW_chunk = s · G_chunkᵀ · X       (M011 §06: dW += dZᵀ·H)
 //
 // The pages merge per-tile LSEs with spin-locked atomics; here every
 // (token tile, split) writes its own partial and a second pass merges them in
@@ -24,49 +25,6 @@
 #include "lce_internal.h"
 
 namespace lce {
-
-// One 256x256 tile over K range [k_begin, k_end).  The shared buffer holds two
-// pipeline stages of both operands (128 KiB).
-template <class LA, class LB>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int64_t lda,
-                                          int64_t a_row0, int64_t a_rows, int64_t a_ktotal,
-                                          const uint16_t* __restrict__ B, int64_t ldb,
-                                          int64_t b_row0, int64_t b_rows, int64_t b_ktotal,
-                                          int64_t k_begin, int64_t k_end, uint16_t* smem,
-                                          f32x16 (&acc)[kMI][kNI]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t nsteps = (k_end - k_begin + kBK - 1) / kBK;
-  if (nsteps <= 0) return;
-  // Stage s of A at smem + s·kStageElems, of B at smem + (2 + s)·kStageElems.
-  // (Plain offset arithmetic keeps the LDS address space visible to the
-  // compiler, so fragment reads are ds_read and not flat loads.)
-  LA la;
-  LB lb;
-  la.init(A, lda, a_row0, a_rows, a_ktotal, tid);
-  lb.init(B, ldb, b_row0, b_rows, b_ktotal, tid);
-  la.load(k_begin);
-  lb.load(k_begin);
-  __syncthreads();  // the previous tile's last readers of stage 0 are done
-  la.store(smem, tid);
-  lb.store(smem + 2 * kStageElems, tid);
-  __syncthreads();
-  for (int64_t step = 0; step < nsteps; ++step) {
-    const int cur = (int)(step & 1);
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      const int64_t k = k_begin + (step + 1) * kBK;
-      la.load(k);
-      lb.load(k);
-    }
-    mfma_step(smem + cur * kStageElems, smem + (2 + cur) * kStageElems, wm, wn, lane, acc);
-    if (more) {
-      la.store(smem + (cur ^ 1) * kStageElems, tid);
-      lb.store(smem + (2 + (cur ^ 1)) * kStageElems, tid);
-    }
-    __syncthreads();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Forward: per (token tile, vocabulary split) partial (max, sum-exp).
@@ -113,7 +71,7 @@ lse_partials_kernel(LseParams p) {
   for (int j = j0; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
     zero_acc(acc);
-    gemm_tile_kk<kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, p.H, smem, acc);
+    gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
     // Vocabulary rows of this tile at or beyond V are masked (only in the last
     // tile, so the test is a uniform branch): masked iff row_const >= lim.
     const bool full = v0 + kTile <= p.V;
@@ -238,7 +196,7 @@ grad_logits_kernel(GradParams p) {
     const int64_t vloc0 = (int64_t)j * kTile;      // chunk-local vocabulary row
     const int64_t v0 = p.v_begin + vloc0;          // global vocabulary row
     zero_acc(acc);
-    gemm_tile_kk<kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, p.H, smem, acc);
+    gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
     const bool full = v0 + kTile <= p.V;
     const int lim = (int)(p.V - v0 < kTile ? p.V - v0 : kTile) - acc_row_lane(wm, lane);
     const int64_t vl_lane = vloc0 + acc_row_lane(wm, lane);
@@ -278,78 +236,80 @@ grad_logits_kernel(GradParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward, step 2: dXp[split] (+)= G[:, k-range] · W[v_begin + k-range, :].
-// M = tokens (A = G, K-major), N = hidden (B = W chunk, stored [K, N]).
+// Backward, steps 2 and 3 for one vocabulary chunk, in one launch.
+//
+//   dX tile (256 tokens x 256 hidden): dX_acc (+)= G[:, chunk] · W[chunk, :]
+//     M = tokens (A = G, K-major), N = hidden (B = W chunk, MN-major: its rows
+//     are vocabulary entries, i.e. K); G is zero past V and W reads past V
+//     return 0.  (AI-infra KB M011 §06: dH accumulates dZ · W over the
+//     vocabulary tiles.)
+//   dW tile (256 vocabulary x 256 hidden): dW[v] = s · Σ_tok G[tok][v]·x_tok
+//     M = chunk vocabulary (A = G, MN-major), N = hidden (B = X, MN-major),
+//     K = tokens, rows past N read as zero.  (M011 §06: dW += dZᵀ · H.)
+//
+// The two tile kinds read the same G chunk and write disjoint outputs.  The
+// kind with more K steps per tile takes the first workgroup ids so the short
+// tiles fill the tail of the launch; within each kind, ids are XCD-remapped.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads, 1)
-dx_gemm_kernel(DxParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStageElems];
+chunk_gemm_kernel(ChunkGemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
+  LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_split = p.nt_tok * p.nt_h;
-  const int split = g / per_split;
-  const int g2 = g % per_split;
-  const int64_t tok0 = (int64_t)(g2 / p.nt_h) * kTile;
-  const int64_t h0 = (int64_t)(g2 % p.nt_h) * kTile;
-  const int64_t steps = (p.k_len + kBK - 1) / kBK;
-  const int64_t k_begin = (steps * split / p.KS) * kBK;
-  const int64_t k_end = (steps * (split + 1) / p.KS) * kBK;
-
+  const int n_dx = p.nt_tok * p.nt_h, n_dw = p.nt_v * p.nt_h;
+  const int b = blockIdx.x;
+  bool is_dx;
+  int g;
+  if (p.dx_first) {
+    is_dx = b < n_dx;
+    g = is_dx ? xcd_remap(b, n_dx) : xcd_remap(b - n_dx, n_dw);
+  } else {
+    is_dx = b >= n_dw;
+    g = is_dx ? xcd_remap(b - n_dw, n_dx) : xcd_remap(b, n_dw);
+  }
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
-  gemm_tile<KMajorTile, MNMajorTile>(p.G, p.ldg, tok0, p.N, p.ldg,
-                                     p.Wc, p.H, h0, p.H, p.wc_rows,
-                                     k_begin, k_end, smem, acc);
-  float* dst = p.dXp + (int64_t)split * p.N * p.H;
+  if (is_dx) {
+    const int64_t tok0 = (int64_t)(g / p.nt_h) * kTile;
+    const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
+    const int64_t k_end = (p.chunk_len + kBK - 1) / kBK * kBK;
+    gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, 0, k_end,
+                                  p.wc_rows, smem, acc);
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int64_t h = h0 + acc_col(wn, ni, lane);
-      if (h >= p.H) continue;
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t h = h0 + acc_col(wn, ni, lane);
+        if (h >= p.H) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t tok = tok0 + acc_row(wm, mi, r, lane);
-        if (tok < p.N) {
-          float* q = dst + tok * p.H + h;
-          *q = p.accumulate ? *q + acc[mi][ni][r] : acc[mi][ni][r];
+        for (int r = 0; r < 16; ++r) {
+          const int64_t tok = tok0 + acc_row(wm, mi, r, lane);
+          if (tok < p.N) {
+            float* q = p.dX_acc + tok * p.H + h;
+            *q = p.accumulate ? *q + acc[mi][ni][r] : acc[mi][ni][r];
+          }
         }
       }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Backward, step 3: dst[v_local][h] = s · Σ_tok G[tok][v_local] · X[tok][h].
-// M = chunk vocabulary (A = G, stored [K, M]), N = hidden (B = X, [K, N]).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads, 1)
-dw_gemm_kernel(DwParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStageElems];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
-  const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
-
-  f32x16 acc[kMI][kNI];
-  zero_acc(acc);
-  gemm_tile<MNMajorTile, MNMajorTile>(p.G, p.ldg, vt0, p.ldg, p.N,
-                                      p.X, p.H, h0, p.H, p.N,
-                                      0, p.N, smem, acc);
-  const float sc = *p.scale;
+  } else {
+    const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
+    const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
+    gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem,
+                                 acc);
+    const float sc = *p.scale;
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int64_t h = h0 + acc_col(wn, ni, lane);
-      if (h >= p.H) continue;
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t h = h0 + acc_col(wn, ni, lane);
+        if (h >= p.H) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t vl = vt0 + acc_row(wm, mi, r, lane);
-        if (vl < p.chunk_len) p.dst[vl * p.H + h] = sc * acc[mi][ni][r];
+        for (int r = 0; r < 16; ++r) {
+          const int64_t vl = vt0 + acc_row(wm, mi, r, lane);
+          if (vl < p.chunk_len) p.dW_dst[vl * p.H + h] = sc * acc[mi][ni][r];
+        }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -390,15 +350,9 @@ hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_dx_gemm(const DxParams& p, hipStream_t stream) {
-  const int grid = p.nt_tok * p.nt_h * p.KS;
-  hipLaunchKernelGGL(dx_gemm_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_dw_gemm(const DwParams& p, hipStream_t stream) {
-  const int grid = p.nt_v * p.nt_h;
-  hipLaunchKernelGGL(dw_gemm_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
+  const int grid = p.nt_tok * p.nt_h + p.nt_v * p.nt_h;
+  hipLaunchKernelGGL(chunk_gemm_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -33,33 +33,27 @@ struct GradParams {
   int64_t ldg;
 };
 
-struct DxParams {
-  const uint16_t* G;   // bf16 [N, ldg], chunk-local vocabulary columns
+// dX and dW contractions of one vocabulary chunk, scheduled in one launch:
+// n_dx tiles of dX_acc (+)= G · W_chunk and n_dw tiles of dW_chunk = s·Gᵀ·X.
+struct ChunkGemmParams {
+  const uint16_t* G;   // bf16 [N, ldg], chunk-local vocabulary columns (0 past V)
   int64_t ldg;
-  const uint16_t* Wc;  // W + v_begin * H
+  const uint16_t* Wc;  // W + v_begin · H
   int64_t wc_rows;     // V − v_begin (rows of W readable from Wc)
+  const uint16_t* X;   // bf16 [N, H]
   int64_t N, H;
-  int64_t k_len;       // chunk length (vocabulary rows in this chunk)
-  int nt_tok, nt_h, KS;
-  int accumulate;      // 0: first chunk writes, 1: later chunks add
-  float* dXp;          // fp32 [KS, N, H]
-};
-
-struct DwParams {
-  const uint16_t* G;
-  int64_t ldg;
-  const uint16_t* X;
-  int64_t N, H;
-  int64_t chunk_len;
-  int nt_v, nt_h;
+  int64_t chunk_len;   // vocabulary rows in this chunk
+  int nt_tok, nt_h, nt_v;
+  int dx_first;        // 1: dX tiles take the first workgroup ids (longer per tile)
+  int accumulate;      // 0: first chunk writes dX_acc, 1: later chunks add
+  float* dX_acc;       // fp32 [N, H]
   const float* scale;  // device scalar dloss / n_valid
-  float* dst;          // fp32 [chunk_len, H] (row v_local)
+  float* dW_dst;       // fp32 [chunk_len, H] (row v_local)
 };
 
 hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream);
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream);
-hipError_t launch_dx_gemm(const DxParams& p, hipStream_t stream);
-hipError_t launch_dw_gemm(const DwParams& p, hipStream_t stream);
+hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream);
 
 // Row-wise kernels (lce_rows.hip).
 struct BlockStats {  // per-block partial of the row scan, combined in a fixed order
@@ -89,7 +83,7 @@ hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const fl
 hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, int32_t* sorted,
                                 hipStream_t stream);
 
-hipError_t launch_dx_finalize(const float* dXp, int KS, int64_t N, int64_t H,
+hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
                               const float* target_deriv, const uint16_t* W,
                               const float* scale, void* dX, int dX_bf16, hipStream_t stream);

@@ -271,12 +271,12 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, int32_t* sort
 }
 
 // ---------------------------------------------------------------------------
-// dX_i = s · (Σ_k dXp[k][i] − e_i · w_{y_i})   (valid rows)
+// dX_i = s · (dX_acc[i] − e_i · w_{y_i})   (valid rows)
 //      = 0 (ignored rows), NaN (bad rows)
 // The one-hot part −1 · e_i at the target is applied here exactly in fp32.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-dx_finalize_kernel(const float* __restrict__ dXp, int KS, int64_t N, int64_t H,
+dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
                    const int32_t* __restrict__ row_state, const int32_t* __restrict__ row_key,
                    const float* __restrict__ target_deriv, const uint16_t* __restrict__ W,
                    const float* __restrict__ scale, void* __restrict__ dX, int dX_bf16) {
@@ -288,11 +288,8 @@ dx_finalize_kernel(const float* __restrict__ dXp, int KS, int64_t N, int64_t H,
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (st == kRowValid) {
-      float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int k = 0; k < KS; ++k) {
-        const float4 v = *reinterpret_cast<const float4*>(dXp + ((int64_t)k * N + row) * H + h);
-        a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
-      }
+      const float4 v = *reinterpret_cast<const float4*>(dX_acc + row * H + h);
+      const float a[4] = {v.x, v.y, v.z, v.w};
       const u32x2 wv = *reinterpret_cast<const u32x2*>(W + y * H + h);
       const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
                            __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
@@ -314,11 +311,11 @@ dx_finalize_kernel(const float* __restrict__ dXp, int KS, int64_t N, int64_t H,
   }
 }
 
-hipError_t launch_dx_finalize(const float* dXp, int KS, int64_t N, int64_t H,
+hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
                               const float* target_deriv, const uint16_t* W,
                               const float* scale, void* dX, int dX_bf16, hipStream_t stream) {
-  hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dXp, KS, N, H,
+  hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, N, H,
                      row_state, row_key, target_deriv, W, scale, dX, dX_bf16);
   return hipGetLastError();
 }
