@@ -98,6 +98,45 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 // ----------------------------------------------------------------------------
+// Direct-to-LDS loads, issued through inline asm.
+//
+// buffer_load_dwordx4 ... lds writes each lane's 16 bytes to LDS at
+// M0 + 16·lane instead of to registers.  Issued through the compiler's builtin,
+// the compiler tracks these writes and, for LDS reads it cannot prove
+// disjoint (the transposing reads below), inserts a full vmcnt(0) wait after
+// every load, which serialises the pipeline.  Issued as asm, the compiler
+// tracks none of them; the pipeline itself guarantees visibility: every
+// stage is read only after an explicit vmcnt(0) and a workgroup barrier.
+// (Compiler-inserted vmcnt waits for its own loads stay correct: loads
+// complete in order, so extra outstanding loads only make them stricter.)
+// M0 is written here and nowhere else in these kernels.
+// ----------------------------------------------------------------------------
+typedef u32x4 rsrc_t;
+
+// Raw buffer descriptor: base, stride 0, size in bytes (capped at 2^31 − 1),
+// raw 32-bit data format.
+__device__ __forceinline__ rsrc_t make_rsrc_raw(const uint16_t* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r[3] = kBufferConfig;
+  return r;
+}
+
+__device__ __forceinline__ void dtl16(const rsrc_t& rsrc, const void __attribute__((address_space(3)))* lds,
+                                      uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// ----------------------------------------------------------------------------
 // Direct-to-LDS K-major loader (buffer_load_dwordx4 ... lds).  One wave
 // instruction fills a 1 KiB block of LDS, lane l writing bytes [16·l, 16·l+16)
 // of it (checked on gfx950: out-of-range lanes write zeros).  Block b holds
@@ -110,7 +149,7 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 
 template <bool kTail>
 struct DtlKMajorTile {
-  __amdgpu_buffer_rsrc_t rsrc;
+  rsrc_t rsrc;
   uint32_t voff;      // byte offset of this lane's chunk in block `wave`
   uint32_t row_step;  // bytes between blocks 4i + wave and 4(i+1) + wave (32 rows)
   int32_t kchunk;     // this lane's logical K offset inside a 64-deep block
@@ -119,7 +158,7 @@ struct DtlKMajorTile {
 
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0,
                                        int64_t rows_total, int64_t k_total_, int tid) {
-    rsrc = make_rsrc(base + row0 * ld, (rows_total - row0) * ld * 2);
+    rsrc = make_rsrc_raw(base + row0 * ld, (rows_total - row0) * ld * 2);
     const int lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Rows 8(4i + w) + lane/8 all share swz(row) = (lane/8) ^ (w & 1), so the
@@ -131,19 +170,27 @@ struct DtlKMajorTile {
     voff = (uint32_t)(row * ld * 2 + c * 16);
     row_step = (uint32_t)(32 * ld * 2);
   }
-  // Enqueue the 64-deep K block starting at k0 into `stage` (asynchronous:
-  // complete once this wave's vmcnt has drained past these 8 loads).  Without
-  // kTail, k_total must be a multiple of 64 and every chunk is in range.
-  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+  // Per-step state: the lane's byte offset of the 64-deep K block at k0
+  // (an always-out-of-range offset for chunks past k_total when kTail).
+  struct Step {
+    uint32_t base;
+  };
+  __device__ __forceinline__ Step prepare(int64_t k0) const {
     uint32_t base = voff + (uint32_t)(k0 * 2);
     if (kTail) base = (k0 + kchunk < k_total) ? base : kOutOfRange;
-    LCE_LDS uint16_t* dst = stage + wave * 512;
+    return Step{base};
+  }
+  // Enqueue load i (0..7) of the step into `stage`: asynchronous, complete
+  // once this wave's vmcnt has drained past it.  Without kTail, k_total must
+  // be a multiple of 64 so every chunk is in range.
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
+    const uint32_t vo = (kTail && st.base == kOutOfRange) ? kOutOfRange : st.base + i * row_step;
+    dtl16(rsrc, stage + wave * 512 + i * 2048, vo);
+  }
+  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+    const Step st = prepare(k0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t vo = (kTail && base == kOutOfRange) ? kOutOfRange : base + i * row_step;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LCE_LDS void*)(dst + i * 2048), 16, (int)vo,
-                                               0, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i) issue(st, stage, i);
   }
 };
 
@@ -178,13 +225,20 @@ struct DtlMNMajorTile {
     voff = (uint32_t)(row * ld * 2 + (col0 + c * 8) * 2);
     row_step = (uint32_t)(8 * ld * 2);
   }
+  // Per-step state: a descriptor starting at K row k0 and ending at k_total.
+  struct Step {
+    rsrc_t rsrc;
+  };
+  __device__ __forceinline__ Step prepare(int64_t k0) const {
+    return Step{make_rsrc_raw(base + k0 * ld, (k_total - k0) * ld * 2)};
+  }
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
+    dtl16(st.rsrc, stage + wave * 512 + i * 2048, voff + i * row_step);
+  }
   __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * ld, (k_total - k0) * ld * 2);
-    LCE_LDS uint16_t* dst = stage + wave * 512;
+    const Step st = prepare(k0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LCE_LDS void*)(dst + i * 2048), 16,
-                                               (int)(voff + i * row_step), 0, 0, 0);
+    for (int i = 0; i < 8; ++i) issue(st, stage, i);
   }
 };
 
@@ -254,15 +308,51 @@ __device__ __forceinline__ void mfma_group(const Frag& f, f32x16 (&acc)[kMI][kNI
 
 #define LCE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Fragment piece p (0..7) of K slice t: A rows for p < 4, B rows otherwise.
+template <bool kAmn, bool kBmn>
+__device__ __forceinline__ void read_piece(Frag& f, const LCE_LDS uint16_t* sA,
+                                           const LCE_LDS uint16_t* sB, int wm, int wn, int lane,
+                                           int t, int p) {
+  if (p < kMI)
+    f.a[p] = frag_read<kAmn>(sA, wm * kWaveTile + p * 32, t, lane);
+  else
+    f.b[p - kMI] = frag_read<kBmn>(sB, wn * kWaveTile + (p - kMI) * 32, t, lane);
+}
+
+#define LCE_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// MFMA group of fragment set `fm` with the 8 fragment reads of K slice t into
+// `fr` interleaved one per MFMA (ds reads 0x100, MFMA 0x008).
+template <bool kAmn, bool kBmn>
+__device__ __forceinline__ void mfma_with_reads(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* sA,
+                                                const LCE_LDS uint16_t* sB, int wm, int wn,
+                                                int lane, int t, f32x16 (&acc)[kMI][kNI]) {
+  read_frag<kAmn, kBmn>(fr, sA, sB, wm, wn, lane, t);
+  mfma_group(fm, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    LCE_SCHED_GROUP(0x008, 1);
+    LCE_SCHED_GROUP(0x100, kAmn || kBmn ? 2 : 1);
+  }
+  LCE_SCHED_GROUP(0x008, 8);
+  LCE_SCHED_FENCE();
+}
+
 // One 256 x 256 tile C += A·Bᵀ over the K range [k_begin, k_end) (at least
 // one 64-deep step), each operand K-major (kAmn/kBmn false: DtlKMajorTile) or
 // MN-major (true: DtlMNMajorTile), through a two-stage direct-to-LDS
-// pipeline.  Per step: enqueue the next block, read the next K-slice
-// fragments while the current slice's 16 MFMAs run, and issue the step's last
-// slice only after the barrier so it overlaps the first fragment reads of the
-// next stage.  LDS: 128 KiB (stage s of A at smem + s·kStageElems, of B at
+// pipeline.  LDS: 128 KiB (stage s of A at smem + s·kStageElems, of B at
 // smem + (2 + s)·kStageElems).  For a K-major operand `row0/rows` are its
 // tile rows; for an MN-major one they are its column offset / column count.
+//
+// Step k (K slices 0..3 of stage k % 2, fragments f0..f3):
+//   MFMA f0 while reading f2; MFMA f1 while reading f3; MFMA f2;
+//   wait for this wave's loads of stage (k+1) % 2, workgroup barrier;
+//   then 16 (MFMA, load, fragment read) triples, issued in that order and
+//   fenced one by one: the deferred MFMA group f3, the 16 loads of step k + 2
+//   into the stage just consumed, and slices 0 and 1 of the next stage.
+// The MFMA pipe therefore always has independent work while the loads and
+// the LDS reads of the next stage are in flight.
 template <bool kAmn, bool kBmn, bool kTail>
 __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_t a_row0,
                                           int64_t a_rows, const uint16_t* B, int64_t ldb,
@@ -278,43 +368,80 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
   LB lb;
   la.init(A, lda, a_row0, a_rows, k_total, tid);
   lb.init(B, ldb, b_row0, b_rows, k_total, tid);
+  LCE_LDS uint16_t* sA0 = smem;
+  LCE_LDS uint16_t* sA1 = smem + kStageElems;
+  LCE_LDS uint16_t* sB0 = smem + 2 * kStageElems;
+  LCE_LDS uint16_t* sB1 = smem + 3 * kStageElems;
   lds_barrier();  // every wave is done with the LDS of the previous tile
-  la.load(smem, k_begin);
-  lb.load(smem + 2 * kStageElems, k_begin);
+  la.load(sA0, k_begin);
+  lb.load(sB0, k_begin);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   lds_barrier();
+  if (nsteps > 1) {
+    la.load(sA1, k_begin + kBK);
+    lb.load(sB1, k_begin + kBK);
+  }
   Frag f0, f1, f2, f3;
-  read_frag<kAmn, kBmn>(f0, smem, smem + 2 * kStageElems, wm, wn, lane, 0);
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const LCE_LDS uint16_t* sa = smem + cur * kStageElems;
-    const LCE_LDS uint16_t* sb = smem + (2 + cur) * kStageElems;
-    if (step + 1 < nsteps) {
-      la.load(smem + (cur ^ 1) * kStageElems, k_begin + (int64_t)(step + 1) * kBK);
-      lb.load(smem + (2 + (cur ^ 1)) * kStageElems, k_begin + (int64_t)(step + 1) * kBK);
-    }
-    read_frag<kAmn, kBmn>(f1, sa, sb, wm, wn, lane, 1);
-    LCE_SCHED_FENCE();
-    if (step > 0) mfma_group(f3, acc);
-    LCE_SCHED_FENCE();
-    mfma_group(f0, acc);
-    LCE_SCHED_FENCE();
-    read_frag<kAmn, kBmn>(f2, sa, sb, wm, wn, lane, 2);
-    LCE_SCHED_FENCE();
-    mfma_group(f1, acc);
-    LCE_SCHED_FENCE();
-    read_frag<kAmn, kBmn>(f3, sa, sb, wm, wn, lane, 3);
-    LCE_SCHED_FENCE();
+  read_frag<kAmn, kBmn>(f0, sA0, sB0, wm, wn, lane, 0);
+  read_frag<kAmn, kBmn>(f1, sA0, sB0, wm, wn, lane, 1);
+  LCE_SCHED_FENCE();
+  int k = 0;
+  for (; k + 2 < nsteps; ++k) {
+    const bool odd = k & 1;
+    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
+    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
+    const LCE_LDS uint16_t* na = odd ? sA0 : sA1;
+    const LCE_LDS uint16_t* nb = odd ? sB0 : sB1;
+    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
+    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
     mfma_group(f2, acc);
     LCE_SCHED_FENCE();
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of the next stage landed
     lds_barrier();                          // ... and every other wave's
-    if (step + 1 < nsteps)
-      read_frag<kAmn, kBmn>(f0, smem + (cur ^ 1) * kStageElems, smem + (2 + (cur ^ 1)) * kStageElems,
-                            wm, wn, lane, 0);
-    LCE_SCHED_FENCE();
+    const typename LA::Step sta = la.prepare(k_begin + (int64_t)(k + 2) * kBK);
+    const typename LB::Step stb = lb.prepare(k_begin + (int64_t)(k + 2) * kBK);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mi = i >> 2, ni = i & 3;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
+      if (i < 8)
+        la.issue(sta, ca, i);
+      else
+        lb.issue(stb, cb, i - 8);
+      read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
+      LCE_SCHED_FENCE();
+    }
   }
-  mfma_group(f3, acc);
+  if (k + 1 < nsteps) {  // second-to-last step: nothing left to load
+    const bool odd = k & 1;
+    const LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
+    const LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
+    const LCE_LDS uint16_t* na = odd ? sA0 : sA1;
+    const LCE_LDS uint16_t* nb = odd ? sB0 : sB1;
+    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
+    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
+    mfma_group(f2, acc);
+    LCE_SCHED_FENCE();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mi = i >> 2, ni = i & 3;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
+      read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
+      LCE_SCHED_FENCE();
+    }
+    ++k;
+  }
+  {  // last step
+    const bool odd = k & 1;
+    const LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
+    const LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
+    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
+    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
+    mfma_group(f2, acc);
+    mfma_group(f3, acc);
+  }
 }
 
 // Map a logical workgroup id of a (token tile, split) grid so that each XCD
