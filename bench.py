@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma2_2b")
-    ap.add_argument("--cpu-rows", type=int, default=512,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype-grad", default="f32", choices=["f32", "bf16"])
@@ -73,6 +73,16 @@ def traffic_from_profiles(kernel, workload, src_hash):
     return float(b.group(1))
 
 
+def quantiles(v):
+    """Median, 20th and 80th percentile of a sorted list (linear interpolation)."""
+    def q(f):
+        x = f * (len(v) - 1)
+        i = int(x)
+        j = min(i + 1, len(v) - 1)
+        return v[i] + (v[j] - v[i]) * (x - i)
+    return [q(0.5), q(0.2), q(0.8)]
+
+
 def cpu_baseline(w, X, W, y, rows):
     """The oracle, as it stands, on `rows` seeded token rows: their forward,
     their dX rows and their share of dW."""
@@ -96,7 +106,8 @@ def cpu_baseline(w, X, W, y, rows):
     return {"value": round(len(idx) / dt, 3), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{len(idx)} seeded token rows of {w.name} (N={w.N}, H={w.H}, V={w.V}): "
-                      f"float64 forward, dX rows and their dW share, {dt:.1f} s"}
+                      f"float64 forward, dX rows and their dW share in {dt:.1f} s; the "
+                      f"full-batch rate is extrapolated from these rows"}
 
 
 def main():
@@ -149,11 +160,16 @@ def main():
             raise RuntimeError(f"lce_backward: {_lib.status_string(st)}")
 
     if args.copy_calibration:
-        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        # A 1 GiB fill (writes only), then a 1 GiB device copy of the filled
+        # buffer (reads 1 GiB, writes 1 GiB): the counters of these two
+        # dispatches give the scale from counter units to bytes.
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        a.fill_(1)
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 1073741824 bytes read, 1073741824 bytes written")
+        log("[bench] copy calibration: fill 1073741824 bytes written; "
+            "copy 1073741824 bytes read, 1073741824 bytes written")
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -165,11 +181,15 @@ def main():
     P.lce_timing_reset()
     P.lce_timing_enable(True)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     P.lce_timing_enable(False)
     kernels = P.lce_timing_read()
     peak_mem = torch.cuda.max_memory_allocated(dev)
@@ -213,6 +233,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median_q20_q80": [round(q, 3) for q in quantiles(step_ms)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
