@@ -75,26 +75,27 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 }
 
 // ----------------------------------------------------------------------------
-// Global -> register loaders for one 256 x 64 operand tile, via buffer loads.
-//
-// A buffer descriptor covers exactly the valid bytes of the operand from the
-// tile's first row on; every byte offset is carried in the VGPR operand so the
-// hardware range check sees all of it, and any access at or beyond the
-// descriptor's size returns zeros.  Descriptor sizes are capped at 2^31 − 1
-// bytes, far above the largest in-tile offset (256 rows · 2^21 bytes).
+// Buffer descriptors.  A descriptor covers `bytes` bytes from `base` (capped
+// at 2^31 − 1); the hardware range check turns every access at an offset at
+// or beyond that size into a zero read or a dropped write.  All of an
+// access's offset is carried in the VGPR operand so the check sees it.
+// kOutOfRange plus any in-tile offset (< 2^30) stays out of range.
 // ----------------------------------------------------------------------------
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw 32-bit data format
 constexpr uint32_t kOutOfRange = 0x80000000u;    // offset that always reads 0
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
+// Compiler-visible form, for the epilogue loads and stores of fp32 tiles.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   if (bytes < 0) bytes = 0;
   if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes,
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            (int)kBufferConfig);
 }
-
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, 0, 0);
 }
 
 // ----------------------------------------------------------------------------

@@ -276,39 +276,59 @@ chunk_gemm_kernel(ChunkGemmParams p) {
     const int64_t k_end = (p.chunk_len + kBK - 1) / kBK * kBK;
     gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, 0, k_end,
                                   p.wc_rows, smem, acc);
+    // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
+    // past H are pushed out of range.  The 64 previous values of one mi row
+    // block are loaded together, so a tile costs 4 round trips, not 256.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dX_acc + tok0 * p.H, (p.N - tok0) * p.H * 4);
+    const uint32_t rowb = (uint32_t)(p.H * 4);
+    uint32_t cbase[kNI];
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int64_t h = h0 + acc_col(wn, ni, lane);
+      cbase[ni] = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
+    }
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const int64_t h = h0 + acc_col(wn, ni, lane);
-        if (h >= p.H) continue;
+    for (int mi = 0; mi < kMI; ++mi) {
+      float prev[kNI][16];
+      if (p.accumulate) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t tok = tok0 + acc_row(wm, mi, r, lane);
-          if (tok < p.N) {
-            float* q = p.dX_acc + tok * p.H + h;
-            *q = p.accumulate ? *q + acc[mi][ni][r] : acc[mi][ni][r];
-          }
-        }
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            prev[ni][r] = buffer_load_f32(rs, cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) prev[ni][r] = 0.0f;
       }
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          buffer_store_f32(prev[ni][r] + acc[mi][ni][r], rs,
+                           cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+    }
   } else {
     const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
     const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
     gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem,
                                  acc);
+    // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
+    // columns at or past H are pushed out of range.
     const float sc = *p.scale;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW_dst + vt0 * p.H, (p.chunk_len - vt0) * p.H * 4);
+    const uint32_t rowb = (uint32_t)(p.H * 4);
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int64_t h = h0 + acc_col(wn, ni, lane);
+      const uint32_t cb = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const int64_t h = h0 + acc_col(wn, ni, lane);
-        if (h >= p.H) continue;
+      for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t vl = vt0 + acc_row(wm, mi, r, lane);
-          if (vl < p.chunk_len) p.dW_dst[vl * p.H + h] = sc * acc[mi][ni][r];
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          buffer_store_f32(sc * acc[mi][ni][r], rs, cb + (uint32_t)acc_row_const(mi, r) * rowb);
+    }
   }
 }
 
