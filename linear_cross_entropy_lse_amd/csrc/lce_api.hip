@@ -96,6 +96,9 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   const int64_t Nc = std::max<int64_t>(N, 1);
   p.T = (int)ceil_div(Nc, kTile);
   int64_t vc = std::max<int64_t>(4096, (V * H) / Nc);
+  // At most 2^21 columns, so a 256-row block of a chunk spans < 2^31 bytes
+  // (the 32-bit buffer offsets of the gradient kernels).
+  vc = std::min<int64_t>(vc, (int64_t)1 << 21);
   vc = std::max<int64_t>(kTile, vc / kTile * kTile);
   p.nchunks = (int)ceil_div(V, vc);
   p.Vc = ceil_div(ceil_div(V, p.nchunks), kTile) * kTile;

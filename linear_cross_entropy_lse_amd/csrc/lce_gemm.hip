@@ -43,6 +43,54 @@ namespace lce {
 // ---------------------------------------------------------------------------
 enum EpiMode { kPlain = 0, kCapFixed = 1, kCapGeneral = 2 };
 
+// Fold one finished 256 x 256 logit tile into the per-column running (m, s).
+// kMasked: vocabulary rows at or beyond V are present in this tile (only the
+// last one); row_const >= lim marks them.  Split out so that every other tile
+// runs without per-element tests.
+template <int kMode, bool kMasked>
+__device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], float (&m)[kNI],
+                                              float (&s)[kNI], int lim, float k2, float c2) {
+  const float NEG_INF = -__builtin_inff();
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    float mref = m[ni];
+    if (kMode != kCapFixed) {
+      float zmax = NEG_INF;
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = acc[mi][ni][r];
+          zmax = fmaxf(zmax, (!kMasked || acc_row_const(mi, r) < lim) ? z : NEG_INF);
+        }
+      const float umax = kMode == kPlain ? zmax * kLog2e
+                                         : (zmax == NEG_INF ? NEG_INF : c2 * tanh_of_scaled(zmax, k2));
+      const float mn = fmaxf(m[ni], umax);
+      mref = mn == NEG_INF ? 0.0f : mn;   // nothing valid yet: every term is an exact 0
+      s[ni] *= exp2_fast(m[ni] - mref);
+      m[ni] = mn;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float z = acc[mi][ni][r];
+        float e;
+        if (kMode == kPlain) {
+          e = exp2_fast(fmaf(z, kLog2e, -mref));
+        } else if (kMode == kCapFixed) {
+          const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+          e = exp2_fast(-2.0f * c2 * rr);
+        } else {
+          e = exp2_fast(c2 * tanh_of_scaled(z, k2) - mref);
+        }
+        sum += (!kMasked || acc_row_const(mi, r) < lim) ? e : 0.0f;
+      }
+    s[ni] += sum;
+  }
+}
+
 template <bool kTail, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 lse_partials_kernel(LseParams p) {
@@ -67,53 +115,23 @@ lse_partials_kernel(LseParams p) {
     s[ni] = 0.0f;
   }
 
+  // Tiles j < j_mid have every vocabulary row below V; the one tile that
+  // reaches past V (if this split holds it) runs in a loop of its own with the
+  // masked fold, so the common path carries no per-element tests.
+  const int j_mid = (int)(j1 < p.V / kTile ? j1 : (j0 > p.V / kTile ? j0 : p.V / kTile));
   f32x16 acc[kMI][kNI];
-  for (int j = j0; j < j1; ++j) {
+  for (int j = j0; j < j_mid; ++j) {
+    zero_acc(acc);
+    gemm_tile<false, false, kTail>(p.W, p.H, (int64_t)j * kTile, p.V, p.X, p.H, tok0, p.N, 0, p.H,
+                                   p.H, smem, acc);
+    lse_fold_tile<kMode, false>(acc, m, s, 0, k2, c2);
+  }
+  for (int j = j_mid; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
     zero_acc(acc);
     gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
-    // Vocabulary rows of this tile at or beyond V are masked (only in the last
-    // tile, so the test is a uniform branch): masked iff row_const >= lim.
-    const bool full = v0 + kTile <= p.V;
-    const int lim = (int)(p.V - v0 < kTile ? p.V - v0 : kTile) - acc_row_lane(wm, lane);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      float mref = m[ni];
-      if (kMode != kCapFixed) {
-        float zmax = NEG_INF;
-#pragma unroll
-        for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float z = acc[mi][ni][r];
-            zmax = fmaxf(zmax, (full || acc_row_const(mi, r) < lim) ? z : NEG_INF);
-          }
-        const float umax = kMode == kPlain ? zmax * kLog2e
-                                           : (zmax == NEG_INF ? NEG_INF : c2 * tanh_of_scaled(zmax, k2));
-        const float mn = fmaxf(m[ni], umax);
-        mref = mn == NEG_INF ? 0.0f : mn;   // nothing valid yet: every term is an exact 0
-        s[ni] *= exp2_fast(m[ni] - mref);
-        m[ni] = mn;
-      }
-      float sum = 0.0f;
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float z = acc[mi][ni][r];
-          float e;
-          if (kMode == kPlain) {
-            e = exp2_fast(fmaf(z, kLog2e, -mref));
-          } else if (kMode == kCapFixed) {
-            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-            e = exp2_fast(-2.0f * c2 * rr);
-          } else {
-            e = exp2_fast(c2 * tanh_of_scaled(z, k2) - mref);
-          }
-          sum += (full || acc_row_const(mi, r) < lim) ? e : 0.0f;
-        }
-      s[ni] += sum;
-    }
+    const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
+    lse_fold_tile<kMode, true>(acc, m, s, lim, k2, c2);
   }
 
   // Lanes l and l^32 hold the same token column (different vocabulary rows).
@@ -162,6 +180,42 @@ lse_partials_kernel(LseParams p) {
 // vocabulary rows beyond V give 0.  With softcap, r = 1/(2^(z·k2) + 1) gives
 // tanh = 1 − 2r, p = 2^((c2 − lse2) − 2·c2·r) and 1 − tanh² = 4r(1 − r).
 // ---------------------------------------------------------------------------
+// G of one finished tile, as bf16, through the G descriptor (rows past N are
+// out of range).  off[ni] folds the row class in: −inf for ignored rows (G = 0)
+// and NaN for rows with a bad label.  kMasked: the tile reaches past V and
+// rows with row_const >= lim are written as 0.
+template <bool kCapped, bool kMasked>
+__device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
+                                                __amdgpu_buffer_rsrc_t rs, const uint32_t (&cb)[kNI],
+                                                int lim, float k2, float c2) {
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float gv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = gq * 4 + q;
+          const float z = acc[mi][ni][r];
+          float val;
+          if (kCapped) {
+            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+            const float d4 = 4.0f * rr;
+            val = exp2_fast(fmaf(-2.0f * c2, rr, off[ni])) * fmaf(-d4, rr, d4);
+          } else {
+            val = exp2_fast(fmaf(z, kLog2e, off[ni]));
+          }
+          gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
+        }
+        u32x2 packed;
+        packed[0] = pack_bf16x2(gv[0], gv[1]);
+        packed[1] = pack_bf16x2(gv[2], gv[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * acc_row_const(mi, gq * 4)), 0, 0);
+      }
+}
+
 template <bool kTail, bool kCapped>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
@@ -177,61 +231,49 @@ grad_logits_kernel(GradParams p) {
   const int64_t tok0 = (int64_t)ti * kTile;
   const float k2 = kCapped ? 2.0f * kLog2e / p.softcap : 0.0f;
   const float c2 = kCapped ? p.softcap * kLog2e : 0.0f;
-  const float qnan = __builtin_nanf("");
 
-  // Per token column: exponent offset and the row class (fixed for all tiles).
-  float off[kNI], rscale[kNI];
+  // Per token column: exponent offset with the row class folded in.
+  float off[kNI];
+  uint32_t col_base[kNI];   // byte offset of (token column, lane's first row) in the G rows
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = tok0 + acc_col(wn, ni, lane);
+    const int col = acc_col(wn, ni, lane);
+    const int64_t tok = tok0 + col;
     const bool ok = tok < p.N;
     const int st = ok ? p.row_state[tok] : (int)kRowIgnored;
     const float lse2 = ok ? p.lse[tok] * kLog2e : 0.0f;
-    off[ni] = kCapped ? c2 - lse2 : -lse2;
-    rscale[ni] = st == kRowValid ? 1.0f : (st == kRowBad ? qnan : 0.0f);
+    const float o = kCapped ? c2 - lse2 : -lse2;
+    off[ni] = st == kRowValid ? o : (st == kRowBad ? __builtin_nanf("") : -__builtin_inff());
+    col_base[ni] = (uint32_t)(col * p.ldg * 2 + acc_row_lane(wm, lane) * 2);
   }
+  // G rows tok0 .. N − 1; a tile's offsets stay below 256 · ldg · 2 bytes.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + tok0 * p.ldg, (p.N - tok0) * p.ldg * 2);
 
+  // Chunk-local tiles j < j_mid lie below V; the tile that reaches past V (at
+  // most one) runs in a loop of its own with the masked store.
+  const int64_t full_local = (p.V - p.v_begin) / kTile;
+  const int j_mid = (int)(j1 < full_local ? j1 : (j0 > full_local ? j0 : full_local));
   f32x16 acc[kMI][kNI];
-  for (int j = j0; j < j1; ++j) {
+  for (int j = j0; j < j_mid; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;      // chunk-local vocabulary row
-    const int64_t v0 = p.v_begin + vloc0;          // global vocabulary row
+    zero_acc(acc);
+    gemm_tile<false, false, kTail>(p.W, p.H, p.v_begin + vloc0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
+                                   p.H, smem, acc);
+    uint32_t cb[kNI];
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
+    grad_store_tile<kCapped, false>(acc, off, rs, cb, 0, k2, c2);
+  }
+  for (int j = j_mid; j < j1; ++j) {
+    const int64_t vloc0 = (int64_t)j * kTile;
+    const int64_t v0 = p.v_begin + vloc0;
     zero_acc(acc);
     gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
-    const bool full = v0 + kTile <= p.V;
-    const int lim = (int)(p.V - v0 < kTile ? p.V - v0 : kTile) - acc_row_lane(wm, lane);
-    const int64_t vl_lane = vloc0 + acc_row_lane(wm, lane);
+    uint32_t cb[kNI];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int64_t tok = tok0 + acc_col(wn, ni, lane);
-      uint16_t* grow = p.G + tok * p.ldg + vl_lane;
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float gv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = gq * 4 + q;
-            const float z = acc[mi][ni][r];
-            float val;
-            if (kCapped) {
-              const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-              const float d = 4.0f * rr * (1.0f - rr);
-              val = exp2_fast(fmaf(-2.0f * c2, rr, off[ni])) * d;
-            } else {
-              val = exp2_fast(fmaf(z, kLog2e, off[ni]));
-            }
-            val *= rscale[ni];
-            gv[q] = (full || acc_row_const(mi, r) < lim) ? val : 0.0f;
-          }
-          if (tok < p.N) {
-            u32x2 packed;
-            packed[0] = pack_bf16x2(gv[0], gv[1]);
-            packed[1] = pack_bf16x2(gv[2], gv[3]);
-            *reinterpret_cast<u32x2*>(grow + acc_row_const(mi, gq * 4)) = packed;
-          }
-        }
-    }
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
+    const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
+    grad_store_tile<kCapped, true>(acc, off, rs, cb, lim, k2, c2);
   }
 }
 
