@@ -84,8 +84,8 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 struct BwdPlan {
   int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
   int64_t Vc, ldg;
-  size_t off_state, off_key, off_deriv, off_sorted, off_blocks, off_scalars, off_G, off_dXp,
-      off_dWs, total;
+  size_t off_state, off_key, off_deriv, off_keys_a, off_keys_b, off_head, off_tail, off_blocks,
+      off_scalars, off_G, off_dXp, off_dWs, total;
 };
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
@@ -112,7 +112,10 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_key = o;     o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_deriv = o;   o = align_up(o + sizeof(float) * (size_t)N);
-  p.off_sorted = o;  o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_keys_a = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_keys_b = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_head = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
+  p.off_tail = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
   p.off_scalars = o; o = align_up(o + 16);
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)N * (size_t)p.ldg);
@@ -352,7 +355,11 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
   int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
   float* deriv = at<float>(workspace_dev, pl.off_deriv);
-  int32_t* sorted = at<int32_t>(workspace_dev, pl.off_sorted);
+  uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
+  uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
+  const uint64_t* keys = sort_passes(N) % 2 == 0 ? keys_a : keys_b;   // where the sort ends
+  float* part_head = at<float>(workspace_dev, pl.off_head);
+  float* part_tail = at<float>(workspace_dev, pl.off_tail);
   BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
   float* scale = at<float>(workspace_dev, pl.off_scalars);
   int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
@@ -365,7 +372,7 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, key, nullptr,
                           deriv, blocks, stream));
   LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, scale, counts, stream));
-  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, sorted, stream));
+  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
 
   for (int c = 0; c < pl.nchunks; ++c) {
     const int64_t v_begin = (int64_t)c * pl.Vc;
@@ -388,15 +395,15 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (dW_dtype == LCE_BF16) {
-      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale, dWs, v_begin,
-                                v_begin + chunk_len, stream));
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, deriv, X, N, H, scale, dWs, v_begin,
+                                v_begin + chunk_len, part_head, part_tail, stream));
       LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
                                chunk_len * H, stream));
     }
   }
   if (dW_dtype == LCE_F32)
-    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(sorted, key, counts, deriv, X, N, H, scale,
-                              static_cast<float*>(dW_dev), 0, V, stream));
+    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, deriv, X, N, H, scale,
+                              static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
   LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, deriv, W, scale, dX_dev,
                              dX_dtype == LCE_BF16, stream));
   return LCE_OK;

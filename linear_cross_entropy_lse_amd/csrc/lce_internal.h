@@ -80,18 +80,28 @@ hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, float* me
 hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const float* dloss,
                                  float* scale, int32_t* n_valid, hipStream_t stream);
 
-hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, int32_t* sorted,
-                                hipStream_t stream);
+// Label sort of the valid rows (keys: label << 32 | row, ascending).
+constexpr int kSortBlock = 2048;   // keys sorted per block in LDS
+int sort_padded(int64_t N);        // N rounded up to kSortBlock
+int sort_passes(int64_t N);        // merge passes after the block sort
+// Sorted keys end up in keys_a after an even number of passes, else keys_b;
+// each buffer holds sort_padded(N) keys.
+hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* keys_a,
+                                uint64_t* keys_b, hipStream_t stream);
 
 hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
                               const float* target_deriv, const uint16_t* W,
                               const float* scale, void* dX, int dX_bf16, hipStream_t stream);
 
-hipError_t launch_dw_correct(const int32_t* sorted, const int32_t* row_key,
-                             const int32_t* n_valid, const float* target_deriv,
+// One-hot part of dW from the sorted keys, in chunks of kSegRows sorted rows;
+// part_head / part_tail hold seg_chunks(N) x H floats each.
+constexpr int kSegRows = 32;
+inline int64_t seg_chunks(int64_t N) { return (N + kSegRows - 1) / kSegRows; }
+hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* target_deriv,
                              const uint16_t* X, int64_t N, int64_t H, const float* scale,
-                             float* dst, int64_t v_lo, int64_t v_hi, hipStream_t stream);
+                             float* dst, int64_t v_lo, int64_t v_hi, float* part_head,
+                             float* part_tail, hipStream_t stream);
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t count, hipStream_t stream);
 

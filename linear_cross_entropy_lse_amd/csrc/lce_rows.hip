@@ -243,30 +243,82 @@ hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const fl
 // of valid rows j with (y_j, j) < (y_i, i).  Quadratic in N but trivially
 // parallel and exact; 64 rows per block, each wave scans a quarter of the keys.
 // ---------------------------------------------------------------------------
+// Order of the valid rows by label, ties in row order: a sort of the unique
+// 64-bit keys (label << 32 | row).  Rows without an in-range label carry the
+// label INT_MAX and padding carries ~0, so both end up behind every valid row.
+// Step 1 sorts blocks of kSortBlock keys in LDS (bitonic network); step 2
+// merges sorted runs pairwise (each output element finds its source by a
+// binary search along the merge path), doubling the run length per pass.
+// ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-sort_by_label_kernel(const int32_t* __restrict__ row_key, int64_t N, int32_t* __restrict__ sorted) {
-  __shared__ int32_t part[4][64];
-  const int r = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 64 + r;
-  const int32_t ki = row < N ? row_key[row] : INT_MAX;
-  const int64_t jb = N * q / 4, je = N * (q + 1) / 4;
-  int32_t cnt = 0;
-  for (int64_t j = jb; j < je; ++j) {
-    const int32_t kj = row_key[j];
-    cnt += (kj < ki) | ((kj == ki) & (j < row));
+sort_block_kernel(const int32_t* __restrict__ row_key, int64_t N, uint64_t* __restrict__ out) {
+  __shared__ uint64_t sk[kSortBlock];
+  const int64_t base = (int64_t)blockIdx.x * kSortBlock;
+  for (int i = threadIdx.x; i < kSortBlock; i += 256) {
+    const int64_t row = base + i;
+    sk[i] = row < N ? ((uint64_t)(uint32_t)row_key[row] << 32) | (uint64_t)row : ~0ull;
   }
-  part[q][r] = cnt;
   __syncthreads();
-  if (q == 0 && row < N && ki != INT_MAX) {
-    const int32_t pos = part[0][r] + part[1][r] + part[2][r] + part[3][r];
-    sorted[pos] = (int32_t)row;
-  }
+  for (int k = 2; k <= kSortBlock; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < kSortBlock / 2; t += 256) {
+        const int i = 2 * t - (t & (j - 1));   // lower element of compare pair t
+        const uint64_t a = sk[i], b = sk[i + j];
+        if ((a > b) == ((i & k) == 0)) {
+          sk[i] = b;
+          sk[i + j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < kSortBlock; i += 256) out[base + i] = sk[i];
 }
 
-hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, int32_t* sorted,
-                                hipStream_t stream) {
-  const int grid = (int)((N + 63) / 64);
-  hipLaunchKernelGGL(sort_by_label_kernel, dim3(grid), dim3(256), 0, stream, row_key, N, sorted);
+__global__ void __launch_bounds__(256)
+merge_pass_kernel(const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n,
+                  int64_t run) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n) return;
+  const int64_t q0 = g / (2 * run) * (2 * run);
+  const int64_t lenA = run < n - q0 ? run : n - q0;
+  const int64_t b0 = q0 + lenA;
+  const int64_t lenB = b0 >= n ? 0 : (run < n - b0 ? run : n - b0);
+  const int64_t o = g - q0;
+  int64_t lo = o - lenB > 0 ? o - lenB : 0, hi = o < lenA ? o : lenA;
+  while (lo < hi) {   // smallest a with A[a] not before B[o − a − 1]
+    const int64_t mid = (lo + hi) >> 1;
+    if (in[q0 + mid] < in[b0 + o - mid - 1]) lo = mid + 1;
+    else hi = mid;
+  }
+  const int64_t a = lo, b = o - lo;
+  const uint64_t v = (b >= lenB || (a < lenA && in[q0 + a] < in[b0 + b])) ? in[q0 + a] : in[b0 + b];
+  out[g] = v;
+}
+
+int sort_padded(int64_t N) { return (int)((N + kSortBlock - 1) / kSortBlock * kSortBlock); }
+
+int sort_passes(int64_t N) {
+  int passes = 0;
+  for (int64_t run = kSortBlock; run < sort_padded(N); run *= 2) ++passes;
+  return passes;
+}
+
+hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* keys_a,
+                                uint64_t* keys_b, hipStream_t stream) {
+  const int64_t n = sort_padded(N);
+  const int passes = sort_passes(N);
+  hipLaunchKernelGGL(sort_block_kernel, dim3((unsigned)(n / kSortBlock)), dim3(256), 0, stream, row_key,
+                     N, keys_a);
+  uint64_t* src = keys_a;
+  uint64_t* dst = keys_b;
+  int64_t run = kSortBlock;
+  for (int ps = 0; ps < passes; ++ps, run *= 2) {
+    hipLaunchKernelGGL(merge_pass_kernel, dim3((unsigned)(n / 256)), dim3(256), 0, stream, src, dst, n,
+                       run);
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
+  }
   return hipGetLastError();
 }
 
@@ -321,62 +373,127 @@ hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
 }
 
 // ---------------------------------------------------------------------------
-// dW_v −= s · Σ_{i : y_i = v} e_i · x_i for every label v in [v_lo, v_hi),
-// summed over the label's rows in row order (waves take every 4th row, the
-// four wave sums are added in wave order).  dst row v − v_lo.
+// dW_v −= s · Σ_{i : y_i = v} e_i · x_i for every label v in [v_lo, v_hi)
+// (dst row v − v_lo), from the label-sorted keys.
+//
+// dw_seg_kernel: block (c, slice) walks sorted positions [32c, 32c + 32) in
+// order, 8 columns per lane, accumulating one run of equal labels at a time.
+// A run that starts and ends inside the chunk is applied at once; the run at
+// the chunk start that continues from the previous chunk goes to
+// part_head[c]; a run that starts in the chunk and continues into the next
+// goes to part_tail[c].  dw_seg_fix_kernel then adds, for each such run,
+// part_tail of its first chunk and part_head of every later chunk it covers,
+// in chunk order, and applies the total.  Every sum is taken in a fixed
+// order, so the result is reproducible bit for bit.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-dw_correct_kernel(const int32_t* __restrict__ sorted, const int32_t* __restrict__ row_key,
-                  const int32_t* __restrict__ counts, const float* __restrict__ target_deriv,
-                  const uint16_t* __restrict__ X, int64_t H, const float* __restrict__ scale,
-                  float* __restrict__ dst, int64_t v_lo, int64_t v_hi) {
-  __shared__ float part[4][512];
-  const int64_t p = blockIdx.x;
-  const int n_ok = counts[1];
-  if (p >= n_ok) return;
-  const int32_t v = row_key[sorted[p]];
-  if (v < v_lo || v >= v_hi) return;
-  if (p > 0 && row_key[sorted[p - 1]] == v) return;  // not the start of v's rows
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int32_t key_label(uint64_t k) { return (int32_t)(k >> 32); }
+
+__global__ void __launch_bounds__(64)
+dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts,
+              const float* __restrict__ target_deriv, const uint16_t* __restrict__ X, int64_t H,
+              const float* __restrict__ scale, float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
+              float* __restrict__ part_head, float* __restrict__ part_tail) {
+  __shared__ int32_t s_row[kSegRows], s_lab[kSegRows];
+  __shared__ float s_e[kSegRows];
+  const int64_t n_ok = counts[1];
+  const int64_t c = blockIdx.x;
+  const int64_t p0 = c * kSegRows;
+  if (p0 >= n_ok) return;
+  const int cnt = (int)(n_ok - p0 < kSegRows ? n_ok - p0 : kSegRows);
+  const int lane = threadIdx.x;
+  if (lane < cnt) {
+    const uint64_t k = keys[p0 + lane];
+    s_row[lane] = (int32_t)(uint32_t)k;
+    s_lab[lane] = key_label(k);
+    s_e[lane] = target_deriv[(uint32_t)k];
+  }
+  const int32_t lab_prev = p0 > 0 ? key_label(keys[p0 - 1]) : -1;
+  const int32_t lab_next = p0 + cnt < n_ok ? key_label(keys[p0 + cnt]) : -1;
+  __syncthreads();
+  const int64_t h = (int64_t)blockIdx.y * 512 + lane * 8;
+  const bool col_ok = h < H;
   const float s = *scale;
-  for (int64_t hc = 0; hc < H; hc += 512) {
-    const int64_t h = hc + lane * 8;
-    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int64_t q = p + wave; q < n_ok; q += 4) {
-      const int32_t r = sorted[q];
-      if (row_key[r] != v) break;
-      if (h < H) {
-        const float e = target_deriv[r];
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(X + (int64_t)r * H + h);
+  // All rows of the chunk are loaded up front so the loads overlap.
+  u32x4 xv[kSegRows];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          a[2 * k] = fmaf(e, __uint_as_float(xv[k] << 16), a[2 * k]);
-          a[2 * k + 1] = fmaf(e, __uint_as_float(xv[k] & 0xffff0000u), a[2 * k + 1]);
+  for (int i = 0; i < kSegRows; ++i)
+    xv[i] = (col_ok && i < cnt) ? *reinterpret_cast<const u32x4*>(X + (int64_t)s_row[i] * H + h)
+                                : u32x4{0u, 0u, 0u, 0u};
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int run_start = 0;
+#pragma unroll
+  for (int i = 0; i < kSegRows; ++i) {
+    if (i < cnt) {
+      const float e = s_e[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(e, __uint_as_float(xv[i][k] << 16), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(e, __uint_as_float(xv[i][k] & 0xffff0000u), acc[2 * k + 1]);
+      }
+      const int32_t v = s_lab[i];
+      if (i + 1 == cnt || s_lab[i + 1] != v) {      // last row of this run
+        const bool open_left = run_start == 0 && lab_prev == v;
+        const bool open_right = i + 1 == cnt && lab_next == v;
+        if (col_ok) {
+          if (open_left || open_right) {
+            float* d = (open_left ? part_head : part_tail) + c * H + h;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) d[k] = acc[k];
+          } else if (v >= v_lo && v < v_hi) {
+            float* d = dst + (int64_t)(v - v_lo) * H + h;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) d[k] = fmaf(-s, acc[k], d[k]);
+          }
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+        run_start = i + 1;
       }
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) part[wave][lane * 8 + k] = a[k];
-    __syncthreads();
-    if (wave == 0 && h < H) {
-      float* d = dst + (int64_t)(v - v_lo) * H + h;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float tot = ((part[0][lane * 8 + k] + part[1][lane * 8 + k]) + part[2][lane * 8 + k]) +
-                          part[3][lane * 8 + k];
-        d[k] -= s * tot;
-      }
-    }
-    __syncthreads();
   }
 }
 
-hipError_t launch_dw_correct(const int32_t* sorted, const int32_t* row_key,
-                             const int32_t* counts, const float* target_deriv,
+__global__ void __launch_bounds__(64)
+dw_seg_fix_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts, int64_t H,
+                  const float* __restrict__ scale, float* __restrict__ dst, int64_t v_lo,
+                  int64_t v_hi, const float* __restrict__ part_head,
+                  const float* __restrict__ part_tail) {
+  const int64_t n_ok = counts[1];
+  const int64_t c = blockIdx.x;
+  const int64_t p0 = c * kSegRows;
+  if (p0 >= n_ok) return;
+  const int64_t p1 = p0 + kSegRows < n_ok ? p0 + kSegRows : n_ok;
+  const int32_t v = key_label(keys[p1 - 1]);
+  if (p1 >= n_ok || key_label(keys[p1]) != v) return;           // last run ends in this chunk
+  if (key_label(keys[p0]) == v && p0 > 0 && key_label(keys[p0 - 1]) == v) return;  // not its first chunk
+  if (v < v_lo || v >= v_hi) return;
+  const int64_t h = (int64_t)blockIdx.y * 512 + threadIdx.x * 8;
+  if (h >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = part_tail[c * H + h + k];
+  for (int64_t c2 = c + 1;; ++c2) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += part_head[c2 * H + h + k];
+    const int64_t q0 = c2 * kSegRows;
+    const int64_t q1 = q0 + kSegRows < n_ok ? q0 + kSegRows : n_ok;
+    if (!(q1 < n_ok && key_label(keys[q1 - 1]) == v && key_label(keys[q1]) == v)) break;
+  }
+  const float s = *scale;
+  float* d = dst + (int64_t)(v - v_lo) * H + h;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k] = fmaf(-s, acc[k], d[k]);
+}
+
+hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* target_deriv,
                              const uint16_t* X, int64_t N, int64_t H, const float* scale,
-                             float* dst, int64_t v_lo, int64_t v_hi, hipStream_t stream) {
-  hipLaunchKernelGGL(dw_correct_kernel, dim3((unsigned)N), dim3(256), 0, stream, sorted, row_key,
-                     counts, target_deriv, X, H, scale, dst, v_lo, v_hi);
+                             float* dst, int64_t v_lo, int64_t v_hi, float* part_head,
+                             float* part_tail, hipStream_t stream) {
+  const dim3 grid((unsigned)seg_chunks(N), (unsigned)((H + 511) / 512));
+  hipLaunchKernelGGL(dw_seg_kernel, grid, dim3(64), 0, stream, keys, counts, target_deriv, X, H, scale,
+                     dst, v_lo, v_hi, part_head, part_tail);
+  hipLaunchKernelGGL(dw_seg_fix_kernel, grid, dim3(64), 0, stream, keys, counts, H, scale, dst, v_lo,
+                     v_hi, part_head, part_tail);
   return hipGetLastError();
 }
 
