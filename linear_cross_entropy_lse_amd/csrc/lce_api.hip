@@ -390,7 +390,6 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
     cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
-    cp.dx_first = ceil_div(chunk_len, kBK) >= ceil_div(N, kBK);  // longer tiles first
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = scale;
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));

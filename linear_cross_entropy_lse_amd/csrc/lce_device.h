@@ -34,6 +34,8 @@ constexpr int kWaveTile = 128;  // each wave: 128 x 128
 constexpr int kMI = 4;          // 32x32 MFMA blocks per wave along M
 constexpr int kNI = 4;          // ... along N
 constexpr int kStageElems = kTile * kBK;      // bf16 elements per operand per stage
+constexpr int kXcds = 8;                      // MI355X: 8 XCDs ...
+constexpr int kCusPerXcd = 32;                // ... of 32 compute units
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -271,6 +273,7 @@ __device__ __forceinline__ bf16x8 frag_read(const LCE_LDS uint16_t* s, int mbase
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);   // vmcnt <= 16
 constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);
 
 // Workgroup barrier without the memory fence __syncthreads() carries (that
@@ -339,6 +342,17 @@ __device__ __forceinline__ void mfma_with_reads(const Frag& fm, Frag& fr, const 
   LCE_SCHED_FENCE();
 }
 
+// Cross-tile prefetch state of a persistent sweep over A tiles that share one
+// B tile (the forward and the logit-gradient kernels walk the vocabulary
+// tiles of one token tile).  While a tile finishes, its last two pipeline
+// steps issue the first two steps of the next A tile into the stages they
+// free, so those loads are in flight during the caller's epilogue and the
+// next tile starts without a pipeline fill.
+struct Sweep {
+  int par = 0;             // stage index holding step 0 of the current tile
+  bool preloaded = false;  // steps 0 and 1 of the current tile are in flight
+};
+
 // One 256 x 256 tile C += A·Bᵀ over the K range [k_begin, k_end) (at least
 // one 64-deep step), each operand K-major (kAmn/kBmn false: DtlKMajorTile) or
 // MN-major (true: DtlMNMajorTile), through a two-stage direct-to-LDS
@@ -354,34 +368,58 @@ __device__ __forceinline__ void mfma_with_reads(const Frag& fm, Frag& fr, const 
 //   into the stage just consumed, and slices 0 and 1 of the next stage.
 // The MFMA pipe therefore always has independent work while the loads and
 // the LDS reads of the next stage are in flight.
-template <bool kAmn, bool kBmn, bool kTail>
+//
+// kSweep (K-major operands only, k_begin = 0): `sw` carries the prefetch
+// state; when next_a_row0 >= 0 and the tile has at least two steps, step 0 of
+// the next A tile (rows next_a_row0.., same B) is loaded during the
+// second-to-last step and step 1 after the last step's reads.  kWaitAll: the
+// caller issues other memory operations between two tiles, so a preloaded
+// tile waits for all of them (vmcnt 0) instead of only for its step 0.  The
+// caller waits for vmcnt 0 after the sweep before reusing the LDS.
+template <bool kAmn, bool kBmn, bool kTail, bool kSweep = false, bool kWaitAll = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_t a_row0,
                                           int64_t a_rows, const uint16_t* B, int64_t ldb,
                                           int64_t b_row0, int64_t b_rows, int64_t k_begin,
                                           int64_t k_end, int64_t k_total, LCE_LDS uint16_t* smem,
-                                          f32x16 (&acc)[kMI][kNI]) {
+                                          f32x16 (&acc)[kMI][kNI], Sweep* sw = nullptr,
+                                          int64_t next_a_row0 = -1) {
   typedef typename std::conditional<kAmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LA;
   typedef typename std::conditional<kBmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LB;
+  static_assert(!kSweep || (!kAmn && !kBmn), "the sweep prefetch handles K-major operands");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int nsteps = (int)((k_end - k_begin + kBK - 1) / kBK);
+  const int par = kSweep ? sw->par : 0;
+  // In sweep mode the prefetch loads are always issued (a fixed code path);
+  // without a next tile they carry an always-out-of-range offset and only
+  // zero-fill stages this tile no longer reads.
+  const bool prefetch = kSweep && next_a_row0 >= 0 && nsteps >= 2;
   LA la;
   LB lb;
   la.init(A, lda, a_row0, a_rows, k_total, tid);
   lb.init(B, ldb, b_row0, b_rows, k_total, tid);
-  LCE_LDS uint16_t* sA0 = smem;
-  LCE_LDS uint16_t* sA1 = smem + kStageElems;
-  LCE_LDS uint16_t* sB0 = smem + 2 * kStageElems;
-  LCE_LDS uint16_t* sB1 = smem + 3 * kStageElems;
-  lds_barrier();  // every wave is done with the LDS of the previous tile
-  la.load(sA0, k_begin);
-  lb.load(sB0, k_begin);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  lds_barrier();
-  if (nsteps > 1) {
-    la.load(sA1, k_begin + kBK);
-    lb.load(sB1, k_begin + kBK);
+  LCE_LDS uint16_t* sA0 = smem + par * kStageElems;
+  LCE_LDS uint16_t* sA1 = smem + (par ^ 1) * kStageElems;
+  LCE_LDS uint16_t* sB0 = smem + (2 + par) * kStageElems;
+  LCE_LDS uint16_t* sB1 = smem + (2 + (par ^ 1)) * kStageElems;
+  if (kSweep && sw->preloaded) {
+    // Steps 0 and 1 (16 loads each per wave) were issued by the previous tile.
+    if (kWaitAll || nsteps < 2) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm16);
+    lds_barrier();
+  } else {
+    lds_barrier();  // every wave is done with the LDS of the previous tile
+    la.load(sA0, k_begin);
+    lb.load(sB0, k_begin);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    if (nsteps > 1) {
+      la.load(sA1, k_begin + kBK);
+      lb.load(sB1, k_begin + kBK);
+    }
   }
+  LA ln;  // loader of the next A tile (sweep mode)
+  if (kSweep) ln.init(A, lda, prefetch ? next_a_row0 : a_row0, a_rows, k_total, tid);
   Frag f0, f1, f2, f3;
   read_frag<kAmn, kBmn>(f0, sA0, sB0, wm, wn, lane, 0);
   read_frag<kAmn, kBmn>(f1, sA0, sB0, wm, wn, lane, 1);
@@ -413,10 +451,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
       LCE_SCHED_FENCE();
     }
   }
-  if (k + 1 < nsteps) {  // second-to-last step: nothing left to load
+  if (k + 1 < nsteps) {  // second-to-last step: nothing of this tile left to load
     const bool odd = k & 1;
-    const LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
-    const LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
+    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
+    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
     const LCE_LDS uint16_t* na = odd ? sA0 : sA1;
     const LCE_LDS uint16_t* nb = odd ? sB0 : sB1;
     mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
@@ -425,23 +463,61 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
     LCE_SCHED_FENCE();
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     lds_barrier();
+    if constexpr (kSweep) {  // step 0 of the next tile into the stage just consumed
+      typename LA::Step sta = ln.prepare(0);
+      typename LB::Step stb = lb.prepare(0);
+      if (!prefetch) sta.base = stb.base = kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mi = i >> 2, ni = i & 3;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
-      read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
-      LCE_SCHED_FENCE();
+      for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
+        if (i < 8)
+          ln.issue(sta, ca, i);
+        else
+          lb.issue(stb, cb, i - 8);
+        read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
+        LCE_SCHED_FENCE();
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
+        read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
+        LCE_SCHED_FENCE();
+      }
     }
     ++k;
   }
   {  // last step
     const bool odd = k & 1;
-    const LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
-    const LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
+    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
+    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
     mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
     mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
-    mfma_group(f2, acc);
+    if constexpr (kSweep) {  // every wave has read this stage: step 1 of the next tile goes here
+      lds_barrier();
+      typename LA::Step sta = ln.prepare(kBK);
+      typename LB::Step stb = lb.prepare(kBK);
+      if (!prefetch) sta.base = stb.base = kOutOfRange;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2.a[mi], f2.b[ni], acc[mi][ni], 0, 0, 0);
+        if (i < 8)
+          ln.issue(sta, ca, i);
+        else
+          lb.issue(stb, cb, i - 8);
+        LCE_SCHED_FENCE();
+      }
+    } else {
+      mfma_group(f2, acc);
+    }
     mfma_group(f3, acc);
+  }
+  if (kSweep) {
+    sw->par = (par + nsteps) & 1;  // stage of the next tile's step 0
+    sw->preloaded = prefetch;
   }
 }
 

@@ -119,20 +119,26 @@ lse_partials_kernel(LseParams p) {
   // reaches past V (if this split holds it) runs in a loop of its own with the
   // masked fold, so the common path carries no per-element tests.
   const int j_mid = (int)(j1 < p.V / kTile ? j1 : (j0 > p.V / kTile ? j0 : p.V / kTile));
+  // Every tile prefetches the first two steps of the next one (same token
+  // tile, next vocabulary rows) while its fold runs.
+  Sweep sw;
   f32x16 acc[kMI][kNI];
   for (int j = j0; j < j_mid; ++j) {
     zero_acc(acc);
-    gemm_tile<false, false, kTail>(p.W, p.H, (int64_t)j * kTile, p.V, p.X, p.H, tok0, p.N, 0, p.H,
-                                   p.H, smem, acc);
+    gemm_tile<false, false, kTail, true>(p.W, p.H, (int64_t)j * kTile, p.V, p.X, p.H, tok0, p.N, 0,
+                                         p.H, p.H, smem, acc, &sw,
+                                         j + 1 < j1 ? (int64_t)(j + 1) * kTile : -1);
     lse_fold_tile<kMode, false>(acc, m, s, 0, k2, c2);
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
     zero_acc(acc);
-    gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
+    gemm_tile<false, false, kTail, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem,
+                                         acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
     lse_fold_tile<kMode, true>(acc, m, s, lim, k2, c2);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) prefetch has landed
 
   // Lanes l and l^32 hold the same token column (different vocabulary rows).
 #pragma unroll
@@ -253,12 +259,16 @@ grad_logits_kernel(GradParams p) {
   // most one) runs in a loop of its own with the masked store.
   const int64_t full_local = (p.V - p.v_begin) / kTile;
   const int j_mid = (int)(j1 < full_local ? j1 : (j0 > full_local ? j0 : full_local));
+  // Cross-tile prefetch as in the forward; the G stores between two tiles
+  // make a preloaded tile wait for all outstanding memory operations.
+  Sweep sw;
   f32x16 acc[kMI][kNI];
   for (int j = j0; j < j_mid; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;      // chunk-local vocabulary row
     zero_acc(acc);
-    gemm_tile<false, false, kTail>(p.W, p.H, p.v_begin + vloc0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
-                                   p.H, smem, acc);
+    gemm_tile<false, false, kTail, true, true>(p.W, p.H, p.v_begin + vloc0, p.V, p.X, p.H, tok0, p.N,
+                                               0, p.H, p.H, smem, acc, &sw,
+                                               j + 1 < j1 ? p.v_begin + vloc0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
@@ -268,17 +278,19 @@ grad_logits_kernel(GradParams p) {
     const int64_t vloc0 = (int64_t)j * kTile;
     const int64_t v0 = p.v_begin + vloc0;
     zero_acc(acc);
-    gemm_tile<false, false, kTail>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem, acc);
+    gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H,
+                                               smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
     grad_store_tile<kCapped, true>(acc, off, rs, cb, lim, k2, c2);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 // ---------------------------------------------------------------------------
-// Backward, steps 2 and 3 for one vocabulary chunk, in one launch.
+// Backward, steps 2 and 3 for one vocabulary chunk, in one persistent launch.
 //
 //   dX tile (256 tokens x 256 hidden): dX_acc (+)= G[:, chunk] · W[chunk, :]
 //     M = tokens (A = G, K-major), N = hidden (B = W chunk, MN-major: its rows
@@ -289,88 +301,111 @@ grad_logits_kernel(GradParams p) {
 //     M = chunk vocabulary (A = G, MN-major), N = hidden (B = X, MN-major),
 //     K = tokens, rows past N read as zero.  (M011 §06: dW += dZᵀ · H.)
 //
-// The two tile kinds read the same G chunk and write disjoint outputs.  The
-// kind with more K steps per tile takes the first workgroup ids so the short
-// tiles fill the tail of the launch; within each kind, ids are XCD-remapped.
+// Schedule: kXcds x kCusPerXcd workgroups, one per compute unit; workgroup b
+// runs on XCD b % kXcds.  Each XCD owns a contiguous range of dX tile ids and
+// of dW tile ids (neighbouring ids share G, W and X slices in its L2).  Inside
+// an XCD the dX tiles (K = chunk length, long) are dealt round-robin, so the
+// first rx workgroups hold one more of them; the dW tiles (K = N) are dealt
+// round-robin as well, the rx heavier workgroups taking only what balances
+// the cost (K steps) of the two groups.  Concurrent workgroups therefore work
+// on consecutive tile ids, and every tile has exactly one owner, so the dX
+// read-modify-write needs no synchronisation.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, LCE_LDS uint16_t* smem,
+                                              int wm, int wn, int lane) {
+  f32x16 acc[kMI][kNI];
+  zero_acc(acc);
+  const int64_t tok0 = (int64_t)(g / p.nt_h) * kTile;
+  const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
+  const int64_t k_end = (p.chunk_len + kBK - 1) / kBK * kBK;
+  gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, 0, k_end, p.wc_rows,
+                                smem, acc);
+  // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
+  // past H are pushed out of range.  The 64 previous values of one mi row
+  // block are loaded together, so a tile costs 4 round trips, not 256.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dX_acc + tok0 * p.H, (p.N - tok0) * p.H * 4);
+  const uint32_t rowb = (uint32_t)(p.H * 4);
+  uint32_t cbase[kNI];
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t h = h0 + acc_col(wn, ni, lane);
+    cbase[ni] = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
+  }
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi) {
+    float prev[kNI][16];
+    if (p.accumulate) {
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          prev[ni][r] = buffer_load_f32(rs, cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) prev[ni][r] = 0.0f;
+    }
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        buffer_store_f32(prev[ni][r] + acc[mi][ni][r], rs,
+                         cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+  }
+}
+
+__device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, float sc,
+                                              LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
+  f32x16 acc[kMI][kNI];
+  zero_acc(acc);
+  const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
+  const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
+  gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem, acc);
+  // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
+  // columns at or past H are pushed out of range.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW_dst + vt0 * p.H, (p.chunk_len - vt0) * p.H * 4);
+  const uint32_t rowb = (uint32_t)(p.H * 4);
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t h = h0 + acc_col(wn, ni, lane);
+    const uint32_t cb = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        buffer_store_f32(sc * acc[mi][ni][r], rs, cb + (uint32_t)acc_row_const(mi, r) * rowb);
+  }
+}
+
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_gemm_kernel(ChunkGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
   LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int n_dx = p.nt_tok * p.nt_h, n_dw = p.nt_v * p.nt_h;
-  const int b = blockIdx.x;
-  bool is_dx;
-  int g;
-  if (p.dx_first) {
-    is_dx = b < n_dx;
-    g = is_dx ? xcd_remap(b, n_dx) : xcd_remap(b - n_dx, n_dw);
+  const int dx_lo = (int)((int64_t)xcd * n_dx / kXcds);
+  const int nx = (int)((int64_t)(xcd + 1) * n_dx / kXcds) - dx_lo;
+  const int dw_lo = (int)((int64_t)xcd * n_dw / kXcds);
+  const int nw = (int)((int64_t)(xcd + 1) * n_dw / kXcds) - dw_lo;
+  // Cost of a tile in K steps: D for dX tiles, E for dW tiles.
+  const int64_t D = (p.chunk_len + kBK - 1) / kBK, E = (p.N + kBK - 1) / kBK;
+  const int rx = nx % kCusPerXcd;                 // workgroups holding one extra dX tile
+  const int64_t per_wg = ((int64_t)nx * D + (int64_t)nw * E) / kCusPerXcd;
+  const int64_t heavy_budget = per_wg - (int64_t)(nx / kCusPerXcd + 1) * D;
+  const int h_k = (rx == 0 || heavy_budget <= 0) ? 0 : (int)((heavy_budget + E / 2) / E);
+  const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
+  const int nw_light = nw - nw_heavy;
+
+  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile(p, dx_lo + t, smem, wm, wn, lane);
+  const float sc = *p.scale;
+  if (li >= rx) {
+    const int nl = kCusPerXcd - rx;
+    for (int t = li - rx; t < nw_light; t += nl) chunk_dw_tile(p, dw_lo + t, sc, smem, wm, wn, lane);
   } else {
-    is_dx = b >= n_dw;
-    g = is_dx ? xcd_remap(b - n_dw, n_dx) : xcd_remap(b, n_dw);
-  }
-  f32x16 acc[kMI][kNI];
-  zero_acc(acc);
-  if (is_dx) {
-    const int64_t tok0 = (int64_t)(g / p.nt_h) * kTile;
-    const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
-    const int64_t k_end = (p.chunk_len + kBK - 1) / kBK * kBK;
-    gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, 0, k_end,
-                                  p.wc_rows, smem, acc);
-    // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
-    // past H are pushed out of range.  The 64 previous values of one mi row
-    // block are loaded together, so a tile costs 4 round trips, not 256.
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dX_acc + tok0 * p.H, (p.N - tok0) * p.H * 4);
-    const uint32_t rowb = (uint32_t)(p.H * 4);
-    uint32_t cbase[kNI];
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int64_t h = h0 + acc_col(wn, ni, lane);
-      cbase[ni] = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
-    }
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      float prev[kNI][16];
-      if (p.accumulate) {
-#pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            prev[ni][r] = buffer_load_f32(rs, cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) prev[ni][r] = 0.0f;
-      }
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          buffer_store_f32(prev[ni][r] + acc[mi][ni][r], rs,
-                           cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
-    }
-  } else {
-    const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
-    const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
-    gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem,
-                                 acc);
-    // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
-    // columns at or past H are pushed out of range.
-    const float sc = *p.scale;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW_dst + vt0 * p.H, (p.chunk_len - vt0) * p.H * 4);
-    const uint32_t rowb = (uint32_t)(p.H * 4);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int64_t h = h0 + acc_col(wn, ni, lane);
-      const uint32_t cb = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          buffer_store_f32(sc * acc[mi][ni][r], rs, cb + (uint32_t)acc_row_const(mi, r) * rowb);
-    }
+    for (int t = li; t < nw_heavy; t += rx) chunk_dw_tile(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
   }
 }
 
@@ -413,7 +448,7 @@ hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
-  const int grid = p.nt_tok * p.nt_h + p.nt_v * p.nt_h;
+  const int grid = kXcds * kCusPerXcd;
   hipLaunchKernelGGL(chunk_gemm_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

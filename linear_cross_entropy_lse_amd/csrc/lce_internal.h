@@ -33,8 +33,9 @@ struct GradParams {
   int64_t ldg;
 };
 
-// dX and dW contractions of one vocabulary chunk, scheduled in one launch:
-// n_dx tiles of dX_acc (+)= G · W_chunk and n_dw tiles of dW_chunk = s·Gᵀ·X.
+// dX and dW contractions of one vocabulary chunk, in one persistent launch of
+// kXcds x kCusPerXcd workgroups: nt_tok·nt_h tiles of dX_acc (+)= G · W_chunk
+// and nt_v·nt_h tiles of dW_chunk = s·Gᵀ·X.
 struct ChunkGemmParams {
   const uint16_t* G;   // bf16 [N, ldg], chunk-local vocabulary columns (0 past V)
   int64_t ldg;
@@ -44,7 +45,6 @@ struct ChunkGemmParams {
   int64_t N, H;
   int64_t chunk_len;   // vocabulary rows in this chunk
   int nt_tok, nt_h, nt_v;
-  int dx_first;        // 1: dX tiles take the first workgroup ids (longer per tile)
   int accumulate;      // 0: first chunk writes dX_acc, 1: later chunks add
   float* dX_acc;       // fp32 [N, H]
   const float* scale;  // device scalar dloss / n_valid
