@@ -39,6 +39,23 @@ Readings where the pages leave a step open (each restated where it is used):
   R5 `dloss` is the scalar upstream gradient of the mean loss.
   R6 a label outside [0, V) that is not ignore_index gives a NaN loss for its
      row (and therefore a NaN mean); its gradient row is NaN.
+
+Loss variants (forward_ex / backward_ex).  [M011] §07 lists label smoothing,
+Z-loss and the reduction mode as terms that need their own definition, and
+[Unsloth] §4 an optional logit scaling (Cohere's logit_scale) next to the
+softcap; the pages give no formulas, so the plainest standard readings are
+taken:
+  R7 logit_scale a: z = a·(x·w), applied before the softcap.
+  R8 label smoothing e: the target distribution is (1 − e)·onehot(y) + e/V,
+     so loss_i = LSE_i − (1 − e)·z_{i,y} − (e/V)·Σ_v z_{i,v} (the definition
+     of PyTorch's CrossEntropyLoss, which [M011] §07 cites for its semantics).
+  R9 Z-loss l: each valid row adds l·LSE_i².
+  R10 reduction: "mean" divides the sum of the row losses by n_valid (R4),
+     "sum" does not divide, "none" keeps the row losses; the backward of
+     "none" takes one upstream gradient per row.
+  Gradient of a valid row: dL_i/dz_v = (1 + 2l·LSE_i)·p_v − (1 − e)·[v = y_i]
+  − e/V, times the softcap derivative, times a, times the row's upstream
+  scale (dloss / n_valid, dloss, or dloss_i).
 """
 from __future__ import annotations
 
@@ -235,3 +252,102 @@ def backward_rows(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
     dZ = logit_gradient(X_rows, W, labels_rows, lse_rows, n_valid, dloss,
                         ignore_index, softcap)
     return dZ @ np.asarray(W, dtype=np.float64), dZ.T @ X_rows
+
+
+# --------------------------------------------------------------------------- #
+# Loss variants (readings R7 - R10)
+# --------------------------------------------------------------------------- #
+DEFAULT_OPTIONS = {"softcap": 0.0, "logit_scale": 1.0, "label_smoothing": 0.0,
+                   "z_loss": 0.0, "reduction": "mean", "ignore_index": IGNORE_INDEX}
+
+
+def options(**kw) -> Dict[str, object]:
+    o = dict(DEFAULT_OPTIONS)
+    o.update(kw)
+    return o
+
+
+def forward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, opts: Dict[str, object],
+               n_valid_total: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Per-row LSE and loss with logit scale (R7), label smoothing (R8) and
+    Z-loss (R9); `reduced` is the mean, the sum, or (for "none") the sum of
+    the row losses (R10)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    a, e, lam = float(opts["logit_scale"]), float(opts["label_smoothing"]), float(opts["z_loss"])
+    ignore_index = int(opts["ignore_index"])
+    Z = a * logits(X, W)
+    Zc = apply_softcap(Z, float(opts["softcap"]))
+    lse = row_logsumexp(Zc)
+    valid = valid_mask(labels, ignore_index)
+    bad = bad_mask(labels, V, ignore_index)
+    ok = valid & ~bad
+    target = np.zeros(X.shape[0])
+    rows = np.nonzero(ok)[0]
+    target[rows] = Zc[rows, labels[rows]]
+    zsum = Zc.sum(axis=1)
+    row_loss = lse - (1.0 - e) * target - (e / V) * zsum + lam * lse * lse
+    loss = np.where(valid, row_loss, 0.0)
+    loss[bad] = np.nan
+    n_valid = int(valid.sum()) if n_valid_total is None else int(n_valid_total)
+    total = loss.sum()
+    if opts["reduction"] == "mean":
+        reduced = total / n_valid if n_valid > 0 else 0.0
+    else:
+        reduced = total
+    return {"lse": lse, "loss": loss, "n_valid": n_valid, "reduced": reduced,
+            "loss_sum": total, "target_logit": target, "logit_sum": zsum}
+
+
+def row_scale(labels: np.ndarray, dloss, n_valid: int, opts: Dict[str, object]) -> np.ndarray:
+    """Upstream scale of each row's gradient (R10): dloss / n_valid ("mean",
+    0 when n_valid = 0), dloss ("sum"), or the row's own dloss_i ("none");
+    zero for ignored rows."""
+    labels = np.asarray(labels, dtype=np.int64)
+    valid = valid_mask(labels, int(opts["ignore_index"]))
+    if opts["reduction"] == "none":
+        s = np.asarray(dloss, dtype=np.float64).reshape(-1)
+    elif opts["reduction"] == "sum":
+        s = np.full(labels.shape[0], float(dloss))
+    else:
+        s = np.full(labels.shape[0], float(dloss) / n_valid if n_valid > 0 else 0.0)
+    return s * valid
+
+
+def logit_gradient_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.ndarray,
+                      scale: np.ndarray, opts: Dict[str, object],
+                      vocab_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """dL/d(x·w) for the rows of X: ((1 + 2l·LSE)·p − (1 − e)·onehot − e/V)
+    · softcap derivative · a · scale_i (gradient of R7 - R9)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    a, e, lam = float(opts["logit_scale"]), float(opts["label_smoothing"]), float(opts["z_loss"])
+    c = float(opts["softcap"])
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    Z = a * logits(X, W[cols])
+    Zc = apply_softcap(Z, c)
+    P = np.exp(Zc - lse[:, None])
+    onehot = (labels[:, None] == cols[None, :]).astype(np.float64)
+    dZ = (1.0 + 2.0 * lam * lse)[:, None] * P - (1.0 - e) * onehot - e / V
+    dZ = dZ * softcap_derivative(Z, c) * a * np.asarray(scale, dtype=np.float64)[:, None]
+    bad = bad_mask(labels, V, int(opts["ignore_index"]))
+    dZ[bad] = np.nan
+    return dZ
+
+
+def backward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
+                opts: Dict[str, object], lse: Optional[np.ndarray] = None):
+    """(dX, dW) of the reduced loss with the variant options."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    fwd = forward_ex(X, W, labels, opts)
+    if lse is None:
+        lse = fwd["lse"]
+    scale = row_scale(labels, dloss, fwd["n_valid"], opts)
+    dZ = logit_gradient_ex(X, W, labels, lse, scale, opts)
+    return dZ @ W, dZ.T @ X
+

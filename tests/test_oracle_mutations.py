@@ -117,3 +117,103 @@ def test_pins_catch_mutation(name, monkeypatch):
         except Exception:       # AssertionError or a shape error: both are catches
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# --------------------------------------------------------------------------- #
+# Loss variants: mistakes planted in forward_ex / logit_gradient_ex must be
+# caught by the variant pins.
+# --------------------------------------------------------------------------- #
+from tests import test_oracle_variants as PV  # noqa: E402
+
+VARIANT_PINS = [
+    lambda: PV.test_label_smoothing_and_reduction_match_torch("mean", 0.0, 1.0, 0.1),
+    lambda: PV.test_label_smoothing_and_reduction_match_torch("none", 2.0, 0.5, 0.3),
+    lambda: PV.test_label_smoothing_and_reduction_match_torch("sum", 0.0, 1.7, 0.0),
+    PV.test_zero_weight_closed_forms,
+    lambda: PV.test_finite_differences_all_options("mean"),
+    lambda: PV.test_finite_differences_all_options("none"),
+    PV.test_logit_scale_is_a_scale_of_W,
+    PV.test_reduction_relations,
+]
+
+_orig_forward_ex = O.forward_ex
+_orig_grad_ex = O.logit_gradient_ex
+_orig_row_scale = O.row_scale
+
+
+def _fx_smoothing_over_v_minus_1(X, W, labels, opts, n_valid_total=None):
+    out = _orig_forward_ex(X, W, labels, opts, n_valid_total)
+    V = np.asarray(W).shape[0]
+    e = float(opts["label_smoothing"])
+    valid = np.asarray(labels) != int(opts["ignore_index"])
+    out["loss"] = out["loss"] + valid * (e / V - e / (V - 1)) * out["logit_sum"]
+    out["reduced"] = out["loss"].sum() / (out["n_valid"] if opts["reduction"] == "mean" else 1)
+    return out
+
+
+def _fx_zloss_not_squared(X, W, labels, opts, n_valid_total=None):
+    out = _orig_forward_ex(X, W, labels, opts, n_valid_total)
+    lam = float(opts["z_loss"])
+    valid = np.asarray(labels) != int(opts["ignore_index"])
+    out["loss"] = out["loss"] + valid * lam * (out["lse"] - out["lse"] ** 2)
+    out["reduced"] = out["loss"].sum() / (out["n_valid"] if opts["reduction"] == "mean" else 1)
+    return out
+
+
+def _fx_scale_after_softcap(X, W, labels, opts, n_valid_total=None):
+    # a · c·tanh(z / c) (scale applied after the cap) equals a softcap of a·c
+    # applied to a·z; without a softcap the order does not matter, so the
+    # mutant then drops the scale instead.
+    o = dict(opts)
+    if float(o["softcap"]) > 0:
+        o["softcap"] = float(o["softcap"]) * float(o["logit_scale"])
+    else:
+        o["logit_scale"] = 1.0
+    return _orig_forward_ex(X, W, labels, o, n_valid_total)
+
+
+def _gx_onehot_not_smoothed(X, W, labels, lse, scale, opts, vocab_rows=None):
+    g = _orig_grad_ex(X, W, labels, lse, scale, opts, vocab_rows)
+    V = np.asarray(W).shape[0]
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    e, a = float(opts["label_smoothing"]), float(opts["logit_scale"])
+    onehot = (np.asarray(labels)[:, None] == cols[None, :])
+    Z = a * O.logits(np.asarray(X, float), np.asarray(W, float)[cols])
+    d = O.softcap_derivative(Z, float(opts["softcap"]))
+    return g - e * onehot * d * a * np.asarray(scale)[:, None]
+
+
+def _gx_zloss_factor_one(X, W, labels, lse, scale, opts, vocab_rows=None):
+    o = dict(opts)
+    o["z_loss"] = float(opts["z_loss"]) / 2.0      # (1 + l·LSE) instead of (1 + 2l·LSE)
+    return _orig_grad_ex(X, W, labels, lse, scale, o, vocab_rows)
+
+
+def _rs_none_uses_mean(labels, dloss, n_valid, opts):
+    if opts["reduction"] == "none":
+        s = np.asarray(dloss, dtype=np.float64).reshape(-1) / max(n_valid, 1)
+        return s * (np.asarray(labels) != int(opts["ignore_index"]))
+    return _orig_row_scale(labels, dloss, n_valid, opts)
+
+
+VARIANT_MUTATIONS = {
+    "smoothing_over_V_minus_1": ("forward_ex", _fx_smoothing_over_v_minus_1),
+    "zloss_not_squared": ("forward_ex", _fx_zloss_not_squared),
+    "scale_after_softcap": ("forward_ex", _fx_scale_after_softcap),
+    "onehot_not_smoothed": ("logit_gradient_ex", _gx_onehot_not_smoothed),
+    "zloss_gradient_factor": ("logit_gradient_ex", _gx_zloss_factor_one),
+    "none_reduction_divides": ("row_scale", _rs_none_uses_mean),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANT_MUTATIONS))
+def test_variant_pins_catch_mutation(name, monkeypatch):
+    attr, fn = VARIANT_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in VARIANT_PINS:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
