@@ -118,6 +118,69 @@ lce_status lce_backward(const void* X_dev, const void* W_dev,
                         lce_dtype dW_dtype, void* workspace_dev,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * Loss variants.  The AI-infra KB page M011 (§07) lists label smoothing,
+ * Z-loss and the reduction mode as terms that need their own definition, and
+ * the Unsloth fused cross-entropy chapter (§4) an optional logit scaling next
+ * to the softcap.  The definitions taken:
+ *   z_iv     = a · (x_i · w_v), then the optional softcap c
+ *   loss_i   = LSE_i − (1 − e)·z_{i,y_i} − (e / V)·Σ_v z_iv + l·LSE_i²
+ *              (label smoothing e as in PyTorch's CrossEntropyLoss: target
+ *              distribution (1 − e)·onehot + e/V; Z-loss l on the row's LSE)
+ *   reduced  = Σ_i loss_i / n_valid (MEAN), Σ_i loss_i (SUM, NONE)
+ *   dZ_iv    = s_i · a · ((1 + 2l·LSE_i)·softmax_v − (1 − e)·[v == y_i] − e/V)
+ *              · (1 − tanh²) with s_i = dloss / n_valid (MEAN), dloss (SUM) or
+ *              dloss_i (NONE: one upstream gradient per row).
+ * With every option at its default the results are those of lce_forward /
+ * lce_backward.
+ */
+typedef enum {
+  LCE_REDUCE_MEAN = 0,
+  LCE_REDUCE_SUM = 1,
+  LCE_REDUCE_NONE = 2
+} lce_reduction;
+
+typedef struct {
+  int64_t ignore_index;   /* label value of rows without a target (default −100) */
+  float softcap;          /* c > 0 enables z <- c·tanh(z/c) (default 0: off) */
+  float logit_scale;      /* a, finite and > 0 (default 1) */
+  float label_smoothing;  /* e in [0, 1] (default 0) */
+  float z_loss;           /* l, finite and >= 0 (default 0) */
+  int32_t reduction;      /* an lce_reduction (default LCE_REDUCE_MEAN) */
+} lce_options;
+
+/* Fill *opt with the defaults listed above (host call). */
+void lce_options_default(lce_options* opt);
+
+/*
+ * Forward with options.  Arguments as lce_forward, plus
+ *   opt          host pointer to the options (out-of-range values give
+ *                LCE_ERR_INVALID_ARG before anything is launched)
+ *   reduced_dev  float [1]  mean (MEAN) or sum (SUM, NONE) of the row losses
+ * The workspace size is the one lce_forward_workspace_bytes returns.
+ */
+lce_status lce_forward_ex(const void* X_dev, const void* W_dev,
+                          const int64_t* labels_dev, int64_t N, int64_t H,
+                          int64_t V, const lce_options* opt, float* loss_dev,
+                          float* lse_dev, float* reduced_dev,
+                          int32_t* n_valid_dev, int32_t* bad_label_dev,
+                          void* workspace_dev, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * Backward with options.  Arguments as lce_backward, plus `opt`; dloss_dev
+ * holds one float (MEAN, SUM) or N floats (NONE: the upstream gradient of
+ * each row's loss; ignored rows' entries are not used).  The workspace size
+ * is the one lce_backward_workspace_bytes returns.
+ */
+lce_status lce_backward_ex(const void* X_dev, const void* W_dev,
+                           const int64_t* labels_dev, const float* lse_dev,
+                           const float* dloss_dev, int64_t N, int64_t H,
+                           int64_t V, const lce_options* opt, void* dX_dev,
+                           lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                           void* workspace_dev, size_t workspace_bytes,
+                           void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);
 

@@ -23,11 +23,32 @@ LCE_ERR_WORKSPACE = 4
 LCE_ERR_HIP = 5
 LCE_F32 = 0
 LCE_BF16 = 1
+LCE_REDUCE_MEAN = 0
+LCE_REDUCE_SUM = 1
+LCE_REDUCE_NONE = 2
+REDUCTIONS = {"mean": LCE_REDUCE_MEAN, "sum": LCE_REDUCE_SUM, "none": LCE_REDUCE_NONE}
 
 # Every symbol include/lce.h declares.
 EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_forward",
-            "lce_backward", "lce_status_string", "lce_version", "lce_timing_enable",
-            "lce_timing_reset", "lce_timing_read")
+            "lce_backward", "lce_options_default", "lce_forward_ex", "lce_backward_ex",
+            "lce_status_string", "lce_version", "lce_timing_enable", "lce_timing_reset",
+            "lce_timing_read")
+
+
+class Options(ctypes.Structure):
+    """lce_options (include/lce.h)."""
+    _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
+                ("logit_scale", ctypes.c_float), ("label_smoothing", ctypes.c_float),
+                ("z_loss", ctypes.c_float), ("reduction", ctypes.c_int32)]
+
+
+def make_options(ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
+                 label_smoothing: float = 0.0, z_loss: float = 0.0,
+                 reduction: str = "mean") -> Options:
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}, got {reduction!r}")
+    return Options(int(ignore_index), float(softcap), float(logit_scale),
+                   float(label_smoothing), float(z_loss), REDUCTIONS[reduction])
 
 
 class KernelTiming(ctypes.Structure):
@@ -64,6 +85,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                  vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
     lib.lce_backward.restype = ctypes.c_int
+    opt_p = ctypes.POINTER(Options)
+    lib.lce_options_default.argtypes = [opt_p]
+    lib.lce_options_default.restype = None
+    lib.lce_forward_ex.argtypes = [vp, vp, vp, i64, i64, i64, opt_p, vp, vp, vp, vp, vp, vp,
+                                   sz, vp]
+    lib.lce_forward_ex.restype = ctypes.c_int
+    lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, opt_p, vp, ctypes.c_int,
+                                    vp, ctypes.c_int, vp, sz, vp]
+    lib.lce_backward_ex.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -217,3 +247,70 @@ def lce_backward(X, W, labels, lse, dloss, ignore_index: int = -100, softcap: fl
                              _stream(dev))
     _check(st, "lce_backward")
     return dX, dW
+
+
+def lce_forward_ex(X, W, labels, ignore_index: int = -100, softcap: float = 0.0,
+                   logit_scale: float = 1.0, label_smoothing: float = 0.0, z_loss: float = 0.0,
+                   reduction: str = "mean", workspace=None):
+    """Forward with the loss variants of include/lce.h (logit scale, label
+    smoothing, Z-loss, reduction).  Returns a dict of device tensors: loss [N],
+    lse [N], reduced [] (mean or sum of the row losses), n_valid [], bad_label []."""
+    import torch
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    reduced = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int32, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    need = lce_forward_workspace_bytes(N, H, V)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_forward_ex")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_forward_ex(_ptr(X), _ptr(W), _ptr(labels), N, H, V, ctypes.byref(opt),
+                               _ptr(loss), _ptr(lse), reduced.data_ptr(), n_valid.data_ptr(),
+                               bad.data_ptr(), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "lce_forward_ex")
+    return {"loss": loss, "lse": lse, "reduced": reduced, "n_valid": n_valid, "bad_label": bad}
+
+
+def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap: float = 0.0,
+                    logit_scale: float = 1.0, label_smoothing: float = 0.0, z_loss: float = 0.0,
+                    reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None):
+    """Backward with the loss variants.  `dloss`: a scalar (mean, sum) or an
+    [N] tensor of per-row upstream gradients (none).  Returns (dX, dW)."""
+    import torch
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    n_d = N if reduction == "none" else 1
+    if not torch.is_tensor(dloss):
+        dloss = torch.full((n_d,), float(dloss), dtype=torch.float32, device=dev)
+    dloss = dloss.to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+    if dloss.numel() != n_d:
+        raise ValueError(f"dloss must hold {n_d} value(s) for reduction {reduction!r}")
+    if n_d == 0:
+        dloss = torch.zeros(1, dtype=torch.float32, device=dev)
+    lse = lse.to(device=dev, dtype=torch.float32).contiguous()
+    if lse.shape != (N,):
+        raise ValueError("lse must have shape [N]")
+    dXc, dWc = _dtype_code(dX_dtype), _dtype_code(dW_dtype)
+    dX = torch.empty(N, H, dtype=dX_dtype or torch.float32, device=dev)
+    dW = torch.empty(V, H, dtype=dW_dtype or torch.float32, device=dev)
+    need = lce_backward_workspace_bytes(N, H, V, dW_dtype)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_backward_ex")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_backward_ex(_ptr(X), _ptr(W), _ptr(labels), _ptr(lse), dloss.data_ptr(),
+                                N, H, V, ctypes.byref(opt), _ptr(dX), dXc, dW.data_ptr(), dWc,
+                                _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "lce_backward_ex")
+    return dX, dW
+

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <climits>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -24,6 +25,15 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool options_ok(const lce_options* o) {
+  if (!o) return false;
+  const bool finite = std::isfinite(o->softcap) && std::isfinite(o->logit_scale) &&
+                      std::isfinite(o->label_smoothing) && std::isfinite(o->z_loss);
+  return finite && o->logit_scale > 0.0f && o->label_smoothing >= 0.0f &&
+         o->label_smoothing <= 1.0f && o->z_loss >= 0.0f && o->reduction >= LCE_REDUCE_MEAN &&
+         o->reduction <= LCE_REDUCE_NONE;
+}
 
 bool shape_ok(int64_t N, int64_t H, int64_t V) {
   return N >= 0 && N < INT_MAX && H >= 8 && H < (1 << 20) && H % 8 == 0 && V >= 1 && V < INT_MAX;
@@ -61,7 +71,7 @@ void pick_xcd_grid(int T, int S, int& tt, int& ss) {
 
 struct FwdPlan {
   int T, S, n_vtiles, nb_fin;
-  size_t off_state, off_target, off_pm, off_ps, off_blocks, total;
+  size_t off_state, off_target, off_pm, off_ps, off_pz, off_blocks, total;
 };
 
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
@@ -76,6 +86,7 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
   p.off_target = o;  o = align_up(o + sizeof(float) * (size_t)N);
   p.off_pm = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
   p.off_ps = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
+  p.off_pz = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_fin);
   p.total = std::max<size_t>(o, kAlign);
   return p;
@@ -84,8 +95,8 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 struct BwdPlan {
   int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
   int64_t Vc, ldg;
-  size_t off_state, off_key, off_deriv, off_keys_a, off_keys_b, off_head, off_tail, off_blocks,
-      off_scalars, off_G, off_dXp, off_dWs, total;
+  size_t off_state, off_key, off_deriv, off_gs, off_c1, off_oh, off_keys_a, off_keys_b, off_head,
+      off_tail, off_blocks, off_scalars, off_G, off_dXp, off_dWs, total;
 };
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
@@ -112,6 +123,9 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_key = o;     o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_deriv = o;   o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_gs = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_c1 = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_oh = o;      o = align_up(o + sizeof(float) * (size_t)N);
   p.off_keys_a = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
   p.off_keys_b = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
   p.off_head = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
@@ -285,22 +299,45 @@ size_t lce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype d
   return plan_backward(N, H, V, dW_dtype).total;
 }
 
+void lce_options_default(lce_options* opt) {
+  if (!opt) return;
+  opt->ignore_index = -100;
+  opt->softcap = 0.0f;
+  opt->logit_scale = 1.0f;
+  opt->label_smoothing = 0.0f;
+  opt->z_loss = 0.0f;
+  opt->reduction = LCE_REDUCE_MEAN;
+}
+
 lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
                        int64_t N, int64_t H, int64_t V, int64_t ignore_index, float softcap,
                        float* loss_dev, float* lse_dev, float* mean_dev, int32_t* n_valid_dev,
                        int32_t* bad_label_dev, void* workspace_dev, size_t workspace_bytes,
                        void* stream_ptr) {
+  lce_options opt;
+  lce_options_default(&opt);
+  opt.ignore_index = ignore_index;
+  opt.softcap = softcap;
+  return lce_forward_ex(X_dev, W_dev, labels_dev, N, H, V, &opt, loss_dev, lse_dev, mean_dev,
+                        n_valid_dev, bad_label_dev, workspace_dev, workspace_bytes, stream_ptr);
+}
+
+lce_status lce_forward_ex(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                          int64_t N, int64_t H, int64_t V, const lce_options* opt,
+                          float* loss_dev, float* lse_dev, float* reduced_dev,
+                          int32_t* n_valid_dev, int32_t* bad_label_dev, void* workspace_dev,
+                          size_t workspace_bytes, void* stream_ptr) {
   if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
-  if (!mean_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
+  if (!options_ok(opt) || !reduced_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
   if (N > 0 && (!X_dev || !W_dev || !labels_dev || !loss_dev || !lse_dev || !workspace_dev))
     return LCE_ERR_INVALID_ARG;
   if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
       !aligned(workspace_dev, kAlign) || !aligned(loss_dev, 4) || !aligned(lse_dev, 4) ||
-      !aligned(mean_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
+      !aligned(reduced_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
     return LCE_ERR_ALIGNMENT;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   if (N == 0) {
-    LCE_LAUNCH("empty_forward", stream, launch_empty_forward(mean_dev, n_valid_dev, bad_label_dev, stream));
+    LCE_LAUNCH("empty_forward", stream, launch_empty_forward(reduced_dev, n_valid_dev, bad_label_dev, stream));
     return LCE_OK;
   }
   const FwdPlan pl = plan_forward(N, H, V);
@@ -310,20 +347,28 @@ lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labe
   float* target = at<float>(workspace_dev, pl.off_target);
   float* pm = at<float>(workspace_dev, pl.off_pm);
   float* ps = at<float>(workspace_dev, pl.off_ps);
+  float* pz = at<float>(workspace_dev, pl.off_pz);
   BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+  const bool smoothing = opt->label_smoothing > 0.0f;
 
-  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, nullptr,
-                          target, nullptr, nullptr, stream));
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, opt->ignore_index, opt->softcap,
+                          opt->logit_scale, state, nullptr, target, nullptr, nullptr, stream));
   LseParams lp{};
   lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
-  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles; lp.softcap = softcap;
+  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
+  lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
   pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
-  lp.part_m = pm; lp.part_s = ps;
+  lp.part_m = pm; lp.part_s = ps; lp.part_z = smoothing ? pz : nullptr;
   LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
-  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, lse_dev, loss_dev, blocks, stream));
-  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, mean_dev, n_valid_dev, bad_label_dev, stream));
+  LossTerms terms{};
+  terms.one_minus_eps = 1.0f - opt->label_smoothing;
+  terms.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
+  terms.z_loss = opt->z_loss;
+  terms.part_z = smoothing ? pz : nullptr;
+  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, terms, lse_dev, loss_dev, blocks, stream));
+  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, opt->reduction == LCE_REDUCE_MEAN, reduced_dev, n_valid_dev, bad_label_dev, stream));
   return LCE_OK;
 }
 
@@ -332,7 +377,21 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
                         int64_t V, int64_t ignore_index, float softcap, void* dX_dev,
                         lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
                         void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  lce_options opt;
+  lce_options_default(&opt);
+  opt.ignore_index = ignore_index;
+  opt.softcap = softcap;
+  return lce_backward_ex(X_dev, W_dev, labels_dev, lse_dev, dloss_dev, N, H, V, &opt, dX_dev,
+                         dX_dtype, dW_dev, dW_dtype, workspace_dev, workspace_bytes, stream_ptr);
+}
+
+lce_status lce_backward_ex(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                           const float* lse_dev, const float* dloss_dev, int64_t N, int64_t H,
+                           int64_t V, const lce_options* opt, void* dX_dev, lce_dtype dX_dtype,
+                           void* dW_dev, lce_dtype dW_dtype, void* workspace_dev,
+                           size_t workspace_bytes, void* stream_ptr) {
   if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
   if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
     return LCE_ERR_INVALID_ARG;
   if (!dW_dev) return LCE_ERR_INVALID_ARG;
@@ -355,23 +414,35 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
   int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
   int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
   float* deriv = at<float>(workspace_dev, pl.off_deriv);
+  float* gs = at<float>(workspace_dev, pl.off_gs);
+  float* c1 = at<float>(workspace_dev, pl.off_c1);
+  float* oh = at<float>(workspace_dev, pl.off_oh);
   uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
   uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
   const uint64_t* keys = sort_passes(N) % 2 == 0 ? keys_a : keys_b;   // where the sort ends
   float* part_head = at<float>(workspace_dev, pl.off_head);
   float* part_tail = at<float>(workspace_dev, pl.off_tail);
   BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
-  float* scale = at<float>(workspace_dev, pl.off_scalars);
+  float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] plain scale, [1] = 1
   int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
   uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
   float* dXp = at<float>(workspace_dev, pl.off_dXp);
   float* dWs = at<float>(workspace_dev, pl.off_dWs);
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+  // The plain path stores G = p·d and applies one scalar scale afterwards; label
+  // smoothing, Z-loss or a per-row upstream gradient need G scaled row by row.
+  const bool general = opt->label_smoothing > 0.0f || opt->z_loss > 0.0f ||
+                       opt->reduction == LCE_REDUCE_NONE;
+  const float* gemm_scale = general ? scalars + 1 : scalars;
 
-  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, ignore_index, softcap, state, key, nullptr,
-                          deriv, blocks, stream));
-  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, scale, counts, stream));
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, opt->ignore_index, opt->softcap,
+                          opt->logit_scale, state, key, nullptr, deriv, blocks, stream));
+  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, opt->reduction == LCE_REDUCE_MEAN,
+                                opt->logit_scale, scalars, counts, stream));
+  LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
+                          scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
+                          general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
   LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
 
   for (int c = 0; c < pl.nchunks; ++c) {
@@ -381,29 +452,32 @@ lce_status lce_backward(const void* X_dev, const void* W_dev, const int64_t* lab
 
     GradParams gp{};
     gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
-    gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt; gp.softcap = softcap;
+    gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
+    gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
     pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
+    gp.gs = general ? gs : nullptr; gp.c1 = c1;
+    gp.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 
     ChunkGemmParams cp{};
     cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
-    cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = scale;
+    cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (dW_dtype == LCE_BF16) {
-      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, deriv, X, N, H, scale, dWs, v_begin,
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
                                 v_begin + chunk_len, part_head, part_tail, stream));
       LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
                                chunk_len * H, stream));
     }
   }
   if (dW_dtype == LCE_F32)
-    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, deriv, X, N, H, scale,
+    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, deriv, W, scale, dX_dev,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, oh, W, gemm_scale, dX_dev,
                              dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }

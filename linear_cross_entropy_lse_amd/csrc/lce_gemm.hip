@@ -46,10 +46,14 @@ enum EpiMode { kPlain = 0, kCapFixed = 1, kCapGeneral = 2 };
 // Fold one finished 256 x 256 logit tile into the per-column running (m, s).
 // kMasked: vocabulary rows at or beyond V are present in this tile (only the
 // last one); row_const >= lim marks them.  Split out so that every other tile
-// runs without per-element tests.
-template <int kMode, bool kMasked>
+// runs without per-element tests.  The logit scale a is folded into k2 and
+// l2a = a·log2(e).  kZSum (label smoothing): zs gathers the per-column sum of
+// the final logits in units of the softcap (capped modes: Σ tanh) or of the
+// raw product (plain mode: Σ z); the caller rescales it.
+template <int kMode, bool kMasked, bool kZSum>
 __device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], float (&m)[kNI],
-                                              float (&s)[kNI], int lim, float k2, float c2) {
+                                              float (&s)[kNI], float (&zs)[kNI], int lim, float k2,
+                                              float c2, float l2a) {
   const float NEG_INF = -__builtin_inff();
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
@@ -63,35 +67,42 @@ __device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], flo
           const float z = acc[mi][ni][r];
           zmax = fmaxf(zmax, (!kMasked || acc_row_const(mi, r) < lim) ? z : NEG_INF);
         }
-      const float umax = kMode == kPlain ? zmax * kLog2e
+      const float umax = kMode == kPlain ? zmax * l2a
                                          : (zmax == NEG_INF ? NEG_INF : c2 * tanh_of_scaled(zmax, k2));
       const float mn = fmaxf(m[ni], umax);
       mref = mn == NEG_INF ? 0.0f : mn;   // nothing valid yet: every term is an exact 0
       s[ni] *= exp2_fast(m[ni] - mref);
       m[ni] = mn;
     }
-    float sum = 0.0f;
+    float sum = 0.0f, zsum = 0.0f;
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float z = acc[mi][ni][r];
-        float e;
+        const bool ok = !kMasked || acc_row_const(mi, r) < lim;
+        float e, zt = 0.0f;
         if (kMode == kPlain) {
-          e = exp2_fast(fmaf(z, kLog2e, -mref));
+          e = exp2_fast(fmaf(z, l2a, -mref));
+          zt = z;
         } else if (kMode == kCapFixed) {
           const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
           e = exp2_fast(-2.0f * c2 * rr);
+          zt = fmaf(-2.0f, rr, 1.0f);           // tanh = 1 − 2r
         } else {
-          e = exp2_fast(c2 * tanh_of_scaled(z, k2) - mref);
+          const float t = tanh_of_scaled(z, k2);
+          e = exp2_fast(c2 * t - mref);
+          zt = t;
         }
-        sum += (!kMasked || acc_row_const(mi, r) < lim) ? e : 0.0f;
+        sum += ok ? e : 0.0f;
+        if (kZSum) zsum += ok ? zt : 0.0f;
       }
     s[ni] += sum;
+    if (kZSum) zs[ni] += zsum;
   }
 }
 
-template <bool kTail, int kMode>
+template <bool kTail, int kMode, bool kZSum>
 __global__ void __launch_bounds__(kThreads, 1)
 lse_partials_kernel(LseParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -104,15 +115,17 @@ lse_partials_kernel(LseParams p) {
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;
-  const float k2 = kMode != kPlain ? 2.0f * kLog2e / p.softcap : 0.0f;
+  const float k2 = kMode != kPlain ? 2.0f * kLog2e * p.logit_scale / p.softcap : 0.0f;
   const float c2 = kMode != kPlain ? p.softcap * kLog2e : 0.0f;
+  const float l2a = kLog2e * p.logit_scale;
   const float NEG_INF = -__builtin_inff();
 
-  float m[kNI], s[kNI];
+  float m[kNI], s[kNI], zs[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     m[ni] = kMode == kCapFixed ? c2 : NEG_INF;
     s[ni] = 0.0f;
+    zs[ni] = 0.0f;
   }
 
   // Tiles j < j_mid have every vocabulary row below V; the one tile that
@@ -128,7 +141,7 @@ lse_partials_kernel(LseParams p) {
     gemm_tile<false, false, kTail, true>(p.W, p.H, (int64_t)j * kTile, p.V, p.X, p.H, tok0, p.N, 0,
                                          p.H, p.H, smem, acc, &sw,
                                          j + 1 < j1 ? (int64_t)(j + 1) * kTile : -1);
-    lse_fold_tile<kMode, false>(acc, m, s, 0, k2, c2);
+    lse_fold_tile<kMode, false, kZSum>(acc, m, s, zs, 0, k2, c2, l2a);
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
@@ -136,7 +149,7 @@ lse_partials_kernel(LseParams p) {
     gemm_tile<false, false, kTail, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem,
                                          acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    lse_fold_tile<kMode, true>(acc, m, s, lim, k2, c2);
+    lse_fold_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) prefetch has landed
 
@@ -149,6 +162,7 @@ lse_partials_kernel(LseParams p) {
     const float mref = mn == NEG_INF ? 0.0f : mn;
     s[ni] = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
     m[ni] = mn;
+    if (kZSum) zs[ni] += __shfl_xor(zs[ni], 32);
   }
   // Waves wm = 0 and wm = 1 cover the two vocabulary halves of the same tokens.
   __syncthreads();
@@ -159,10 +173,13 @@ lse_partials_kernel(LseParams p) {
       const int col = acc_col(wn, ni, lane);
       red[col] = m[ni];
       red[kTile + col] = s[ni];
+      if (kZSum) red[2 * kTile + col] = zs[ni];
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
+    // Σ z in natural units: c·Σ tanh (capped) or a·Σ (x·w) (plain).
+    const float zunit = kMode == kPlain ? p.logit_scale : p.softcap;
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
       const int col = acc_col(wn, ni, lane);
@@ -174,6 +191,7 @@ lse_partials_kernel(LseParams p) {
       if (tok < p.N) {
         p.part_m[(int64_t)split * p.N + tok] = mn;
         p.part_s[(int64_t)split * p.N + tok] = ss;
+        if (kZSum) p.part_z[(int64_t)split * p.N + tok] = zunit * (zs[ni] + red[2 * kTile + col]);
       }
     }
   }
@@ -187,13 +205,17 @@ lse_partials_kernel(LseParams p) {
 // tanh = 1 − 2r, p = 2^((c2 − lse2) − 2·c2·r) and 1 − tanh² = 4r(1 − r).
 // ---------------------------------------------------------------------------
 // G of one finished tile, as bf16, through the G descriptor (rows past N are
-// out of range).  off[ni] folds the row class in: −inf for ignored rows (G = 0)
-// and NaN for rows with a bad label.  kMasked: the tile reaches past V and
-// rows with row_const >= lim are written as 0.
-template <bool kCapped, bool kMasked>
+// out of range).  Plain form (kGen false): G = p·d, off[ni] folding the row
+// class in (−inf for ignored rows, so G = 0; NaN for rows with a bad label).
+// General form: G = gsc[ni]·(c1[ni]·p − eps_v)·d with the row's scale gsc (0
+// ignored, NaN bad) and Z-loss factor c1.  kMasked: the tile reaches past V
+// and rows with row_const >= lim are written as 0.
+template <bool kCapped, bool kMasked, bool kGen>
 __device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
-                                                __amdgpu_buffer_rsrc_t rs, const uint32_t (&cb)[kNI],
-                                                int lim, float k2, float c2) {
+                                                const float (&gsc)[kNI], const float (&c1)[kNI],
+                                                float eps_v, __amdgpu_buffer_rsrc_t rs,
+                                                const uint32_t (&cb)[kNI], int lim, float k2,
+                                                float c2, float l2a) {
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
@@ -209,9 +231,12 @@ __device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
           if (kCapped) {
             const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
             const float d4 = 4.0f * rr;
-            val = exp2_fast(fmaf(-2.0f * c2, rr, off[ni])) * fmaf(-d4, rr, d4);
+            const float pr = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
+            const float d = fmaf(-d4, rr, d4);
+            val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) * d : pr * d;
           } else {
-            val = exp2_fast(fmaf(z, kLog2e, off[ni]));
+            const float pr = exp2_fast(fmaf(z, l2a, off[ni]));
+            val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
           }
           gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
         }
@@ -222,7 +247,7 @@ __device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
       }
 }
 
-template <bool kTail, bool kCapped>
+template <bool kTail, bool kCapped, bool kGen>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -235,11 +260,13 @@ grad_logits_kernel(GradParams p) {
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;
-  const float k2 = kCapped ? 2.0f * kLog2e / p.softcap : 0.0f;
+  const float k2 = kCapped ? 2.0f * kLog2e * p.logit_scale / p.softcap : 0.0f;
   const float c2 = kCapped ? p.softcap * kLog2e : 0.0f;
+  const float l2a = kLog2e * p.logit_scale;
 
-  // Per token column: exponent offset with the row class folded in.
-  float off[kNI];
+  // Per token column: exponent offset (plain form: with the row class folded
+  // in), and in the general form the row scale and Z-loss factor.
+  float off[kNI], gsc[kNI], c1[kNI];
   uint32_t col_base[kNI];   // byte offset of (token column, lane's first row) in the G rows
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
@@ -249,7 +276,15 @@ grad_logits_kernel(GradParams p) {
     const int st = ok ? p.row_state[tok] : (int)kRowIgnored;
     const float lse2 = ok ? p.lse[tok] * kLog2e : 0.0f;
     const float o = kCapped ? c2 - lse2 : -lse2;
-    off[ni] = st == kRowValid ? o : (st == kRowBad ? __builtin_nanf("") : -__builtin_inff());
+    if (kGen) {
+      off[ni] = o;
+      gsc[ni] = ok ? p.gs[tok] : 0.0f;
+      c1[ni] = ok ? p.c1[tok] : 1.0f;
+    } else {
+      off[ni] = st == kRowValid ? o : (st == kRowBad ? __builtin_nanf("") : -__builtin_inff());
+      gsc[ni] = 1.0f;
+      c1[ni] = 1.0f;
+    }
     col_base[ni] = (uint32_t)(col * p.ldg * 2 + acc_row_lane(wm, lane) * 2);
   }
   // G rows tok0 .. N − 1; a tile's offsets stay below 256 · ldg · 2 bytes.
@@ -272,7 +307,7 @@ grad_logits_kernel(GradParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
-    grad_store_tile<kCapped, false>(acc, off, rs, cb, 0, k2, c2);
+    grad_store_tile<kCapped, false, kGen>(acc, off, gsc, c1, p.eps_over_v, rs, cb, 0, k2, c2, l2a);
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;
@@ -284,7 +319,7 @@ grad_logits_kernel(GradParams p) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    grad_store_tile<kCapped, true>(acc, off, rs, cb, lim, k2, c2);
+    grad_store_tile<kCapped, true, kGen>(acc, off, gsc, c1, p.eps_over_v, rs, cb, lim, k2, c2, l2a);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
@@ -414,36 +449,46 @@ chunk_gemm_kernel(ChunkGemmParams p) {
 // ---------------------------------------------------------------------------
 hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
-  const bool tail = p.H % kBK != 0;
+  const bool tail = p.H % kBK != 0, zsum = p.part_z != nullptr;
   // Fixed reference 2^(u - c2) >= 2^(-2·c2) stays a normal float for c2 < 60.
   const int mode = p.softcap <= 0.0f ? kPlain
                    : (p.softcap * kLog2e < 60.0f ? kCapFixed : kCapGeneral);
-#define LCE_LSE_LAUNCH(T_, M_) \
-  hipLaunchKernelGGL((lse_partials_kernel<T_, M_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_LSE_LAUNCH(T_, M_, Z_) \
+  hipLaunchKernelGGL((lse_partials_kernel<T_, M_, Z_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_LSE_MODES(T_, Z_)                          \
+  do {                                                 \
+    if (mode == kPlain) LCE_LSE_LAUNCH(T_, kPlain, Z_);     \
+    else if (mode == kCapFixed) LCE_LSE_LAUNCH(T_, kCapFixed, Z_); \
+    else LCE_LSE_LAUNCH(T_, kCapGeneral, Z_);          \
+  } while (0)
   if (tail) {
-    if (mode == kPlain) LCE_LSE_LAUNCH(true, kPlain);
-    else if (mode == kCapFixed) LCE_LSE_LAUNCH(true, kCapFixed);
-    else LCE_LSE_LAUNCH(true, kCapGeneral);
+    if (zsum) LCE_LSE_MODES(true, true);
+    else LCE_LSE_MODES(true, false);
   } else {
-    if (mode == kPlain) LCE_LSE_LAUNCH(false, kPlain);
-    else if (mode == kCapFixed) LCE_LSE_LAUNCH(false, kCapFixed);
-    else LCE_LSE_LAUNCH(false, kCapGeneral);
+    if (zsum) LCE_LSE_MODES(false, true);
+    else LCE_LSE_MODES(false, false);
   }
+#undef LCE_LSE_MODES
 #undef LCE_LSE_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
-  const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f;
-  if (tail && capped)
-    hipLaunchKernelGGL((grad_logits_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (tail)
-    hipLaunchKernelGGL((grad_logits_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (capped)
-    hipLaunchKernelGGL((grad_logits_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((grad_logits_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+  const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f, gen = p.gs != nullptr;
+#define LCE_GRAD_LAUNCH(T_, C_, G_) \
+  hipLaunchKernelGGL((grad_logits_kernel<T_, C_, G_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_GRAD_TC(G_)                                   \
+  do {                                                    \
+    if (tail && capped) LCE_GRAD_LAUNCH(true, true, G_);  \
+    else if (tail) LCE_GRAD_LAUNCH(true, false, G_);      \
+    else if (capped) LCE_GRAD_LAUNCH(false, true, G_);    \
+    else LCE_GRAD_LAUNCH(false, false, G_);               \
+  } while (0)
+  if (gen) LCE_GRAD_TC(true);
+  else LCE_GRAD_TC(false);
+#undef LCE_GRAD_TC
+#undef LCE_GRAD_LAUNCH
   return hipGetLastError();
 }
 

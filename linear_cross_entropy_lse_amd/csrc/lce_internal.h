@@ -14,8 +14,10 @@ struct LseParams {
   int T, S, n_vtiles;
   int tt, ss;         // XCD sub-grid (see grid_tile); 0 = plain order
   float softcap;
+  float logit_scale;  // a > 0: z = a·(x·w) before the softcap
   float* part_m;      // [S, N] base-2 running max
   float* part_s;      // [S, N] Σ 2^(u − m)
+  float* part_z;      // [S, N] Σ_v z_v (label smoothing), or null
 };
 
 // Recomputed logit gradient of one vocabulary chunk [v_begin, v_begin + 256·n_vtiles).
@@ -27,10 +29,16 @@ struct GradParams {
   int T, S, n_vtiles;
   int tt, ss;
   float softcap;
+  float logit_scale;
   const float* lse;          // [N]
   const int32_t* row_state;  // [N]
   uint16_t* G;               // bf16 [N, ldg]
   int64_t ldg;
+  // General form (label smoothing, Z-loss, per-row upstream gradient):
+  // G = gs_i·(c1_i·p − eps_over_v)·d; null gs selects the plain G = p·d.
+  const float* gs;           // [N] per-row scale s_i·a (0 ignored, NaN bad)
+  const float* c1;           // [N] 1 + 2l·LSE_i
+  float eps_over_v;          // e / V
 };
 
 // dX and dW contractions of one vocabulary chunk, in one persistent launch of
@@ -64,21 +72,43 @@ struct BlockStats {  // per-block partial of the row scan, combined in a fixed o
 
 hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* labels,
                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
-                           float softcap, int32_t* row_state, int32_t* row_key,
-                           float* target, float* target_deriv, BlockStats* blocks,
-                           hipStream_t stream);
+                           float softcap, float logit_scale, int32_t* row_state,
+                           int32_t* row_key, float* target, float* target_deriv,
+                           BlockStats* blocks, hipStream_t stream);
 int row_prep_blocks(int64_t N);
 
+// Loss-variant terms applied when the row loss is formed.
+struct LossTerms {
+  float one_minus_eps;   // 1 − e (target weight)
+  float eps_over_v;      // e / V (weight of Σ_v z_v)
+  float z_loss;          // l
+  const float* part_z;   // [S, N] or null (e = 0)
+};
+
 hipError_t launch_lse_finalize(const float* part_m, const float* part_s, int S, int64_t N,
-                               const int32_t* row_state, const float* target, float* lse,
-                               float* loss, BlockStats* blocks, hipStream_t stream);
+                               const int32_t* row_state, const float* target,
+                               const LossTerms& terms, float* lse, float* loss,
+                               BlockStats* blocks, hipStream_t stream);
 int lse_finalize_blocks(int64_t N);
 
-hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, float* mean,
+// reduced = Σ loss / n_valid (divide = 1) or Σ loss (divide = 0).
+hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, int divide, float* reduced,
                                 int32_t* n_valid, int32_t* bad_flag, hipStream_t stream);
 
+// scalars[0] = a·dloss / n_valid (divide = 1) or a·dloss (divide = 0), the
+// upstream scale of the plain path; scalars[1] = 1.  counts as below.
 hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const float* dloss,
-                                 float* scale, int32_t* n_valid, hipStream_t stream);
+                                 int divide, float logit_scale, float* scalars, int32_t* counts,
+                                 hipStream_t stream);
+
+// Per-row gradient coefficients: gs_i (row scale, times a), c1_i = 1 + 2l·LSE_i
+// and oh_i = gs_i·(1 − e)·d_i (the one-hot coefficient, d_i the softcap
+// derivative at the target).  Row scale: dloss_rows[i] when dloss_rows is not
+// null, else the scalar scalars[0] / a.
+hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
+                           const float* dloss_rows, const float* scalars, int64_t N,
+                           float logit_scale, float one_minus_eps, float z_loss, float* gs,
+                           float* c1, float* oh, hipStream_t stream);
 
 // Label sort of the valid rows (keys: label << 32 | row, ascending).
 constexpr int kSortBlock = 2048;   // keys sorted per block in LDS
@@ -89,19 +119,21 @@ int sort_passes(int64_t N);        // merge passes after the block sort
 hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* keys_a,
                                 uint64_t* keys_b, hipStream_t stream);
 
+// dX_i = sx·dX_acc_i − oh_i·w_{y_i} (valid rows), 0 (ignored), NaN (bad).
 hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
-                              const float* target_deriv, const uint16_t* W,
-                              const float* scale, void* dX, int dX_bf16, hipStream_t stream);
+                              const float* oh, const uint16_t* W, const float* sx,
+                              void* dX, int dX_bf16, hipStream_t stream);
 
 // One-hot part of dW from the sorted keys, in chunks of kSegRows sorted rows;
 // part_head / part_tail hold seg_chunks(N) x H floats each.
 constexpr int kSegRows = 32;
 inline int64_t seg_chunks(int64_t N) { return (N + kSegRows - 1) / kSegRows; }
-hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* target_deriv,
-                             const uint16_t* X, int64_t N, int64_t H, const float* scale,
-                             float* dst, int64_t v_lo, int64_t v_hi, float* part_head,
-                             float* part_tail, hipStream_t stream);
+// dst[v − v_lo] −= Σ_{i : y_i = v} oh_i · x_i for v in [v_lo, v_hi).
+hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* oh,
+                             const uint16_t* X, int64_t N, int64_t H, float* dst, int64_t v_lo,
+                             int64_t v_hi, float* part_head, float* part_tail,
+                             hipStream_t stream);
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t count, hipStream_t stream);
 

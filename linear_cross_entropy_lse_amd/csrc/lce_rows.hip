@@ -30,8 +30,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Row classification and the target logit.  One wave per row.
 //   row_state:    0 ignored, 1 valid, 2 label out of range
 //   row_key:      label for valid rows, INT_MAX otherwise (sort key)
-//   target:       softcapped target logit (valid rows), else 0
-//   target_deriv: 1 − tanh²(t_raw / c) at the target (1 without softcap)
+//   target:       scaled, softcapped target logit (valid rows), else 0
+//   target_deriv: 1 − tanh²(t_raw / c) at the target (1 without softcap),
+//                 t_raw = a·(x_i · w_{y_i})
 //   blocks:       per-block counts of non-ignored and bad rows
 // ---------------------------------------------------------------------------
 constexpr int kRowsPerPrepBlock = 4;
@@ -39,9 +40,10 @@ constexpr int kRowsPerPrepBlock = 4;
 __global__ void __launch_bounds__(256)
 row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                 const int64_t* __restrict__ labels, int64_t N, int64_t H, int64_t V,
-                int64_t ignore_index, float softcap, int32_t* __restrict__ row_state,
-                int32_t* __restrict__ row_key, float* __restrict__ target,
-                float* __restrict__ target_deriv, BlockStats* __restrict__ blocks) {
+                int64_t ignore_index, float softcap, float logit_scale,
+                int32_t* __restrict__ row_state, int32_t* __restrict__ row_key,
+                float* __restrict__ target, float* __restrict__ target_deriv,
+                BlockStats* __restrict__ blocks) {
   __shared__ int counts[kRowsPerPrepBlock][2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerPrepBlock + wave;
@@ -63,7 +65,7 @@ row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
           dot = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[q] & 0xffff0000u), dot);
         }
       }
-      dot = wave_sum(dot);
+      dot = wave_sum(dot) * logit_scale;
       if (softcap > 0.0f) {
         const float th = tanhf(dot / softcap);
         t = softcap * th;
@@ -95,26 +97,29 @@ int row_prep_blocks(int64_t N) { return (int)((N + kRowsPerPrepBlock - 1) / kRow
 
 hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* labels,
                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
-                           float softcap, int32_t* row_state, int32_t* row_key,
-                           float* target, float* target_deriv, BlockStats* blocks,
-                           hipStream_t stream) {
+                           float softcap, float logit_scale, int32_t* row_state,
+                           int32_t* row_key, float* target, float* target_deriv,
+                           BlockStats* blocks, hipStream_t stream) {
   hipLaunchKernelGGL(row_prep_kernel, dim3(row_prep_blocks(N)), dim3(256), 0, stream, X, W,
-                     labels, N, H, V, ignore_index, softcap, row_state, row_key, target,
-                     target_deriv, blocks);
+                     labels, N, H, V, ignore_index, softcap, logit_scale, row_state, row_key,
+                     target, target_deriv, blocks);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Merge the S forward partials of each row in split order, then loss and the
-// per-block loss sums (fixed-shape tree in double precision).
+// per-block loss sums (fixed-shape tree in double precision).  With the loss
+// variants the row loss is LSE − (1 − e)·t − (e/V)·Σ_v z_v + l·LSE², the
+// logit sum merged from its per-split partials in split order.
 // ---------------------------------------------------------------------------
 constexpr int kFinThreads = 256;
 
 __global__ void __launch_bounds__(kFinThreads)
 lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ part_s, int S,
                     int64_t N, const int32_t* __restrict__ row_state,
-                    const float* __restrict__ target, float* __restrict__ lse_out,
-                    float* __restrict__ loss_out, BlockStats* __restrict__ blocks) {
+                    const float* __restrict__ target, LossTerms terms,
+                    float* __restrict__ lse_out, float* __restrict__ loss_out,
+                    BlockStats* __restrict__ blocks) {
   __shared__ double ssum[kFinThreads];
   __shared__ int scnt[kFinThreads][2];
   const int tid = threadIdx.x;
@@ -133,8 +138,17 @@ lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ 
     const float lse = (m + log2f(sum)) * kLn2;
     const int st = row_state[row];
     float l = 0.0f;
-    if (st == kRowValid) l = lse - target[row];
-    else if (st == kRowBad) l = __builtin_nanf("");
+    if (st == kRowValid) {
+      l = fmaf(-terms.one_minus_eps, target[row], lse);
+      if (terms.part_z) {
+        float zs = 0.0f;
+        for (int s = 0; s < S; ++s) zs += terms.part_z[(int64_t)s * N + row];
+        l = fmaf(-terms.eps_over_v, zs, l);
+      }
+      l = fmaf(terms.z_loss * lse, lse, l);
+    } else if (st == kRowBad) {
+      l = __builtin_nanf("");
+    }
     lse_out[row] = lse;
     loss_out[row] = l;
     lossv = (double)l;
@@ -159,10 +173,11 @@ lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ 
 int lse_finalize_blocks(int64_t N) { return (int)((N + kFinThreads - 1) / kFinThreads); }
 
 hipError_t launch_lse_finalize(const float* part_m, const float* part_s, int S, int64_t N,
-                               const int32_t* row_state, const float* target, float* lse,
-                               float* loss, BlockStats* blocks, hipStream_t stream) {
+                               const int32_t* row_state, const float* target,
+                               const LossTerms& terms, float* lse, float* loss,
+                               BlockStats* blocks, hipStream_t stream) {
   hipLaunchKernelGGL(lse_finalize_kernel, dim3(lse_finalize_blocks(N)), dim3(kFinThreads), 0,
-                     stream, part_m, part_s, S, N, row_state, target, lse, loss, blocks);
+                     stream, part_m, part_s, S, N, row_state, target, terms, lse, loss, blocks);
   return hipGetLastError();
 }
 
@@ -197,51 +212,82 @@ __device__ void reduce_blocks(const BlockStats* __restrict__ blocks, int nblocks
 }
 
 __global__ void __launch_bounds__(256)
-mean_finalize_kernel(const BlockStats* __restrict__ blocks, int nblocks, float* mean,
-                     int32_t* n_valid, int32_t* bad_flag) {
+mean_finalize_kernel(const BlockStats* __restrict__ blocks, int nblocks, int divide,
+                     float* reduced, int32_t* n_valid, int32_t* bad_flag) {
   double sum;
   int nv, nb;
   reduce_blocks(blocks, nblocks, sum, nv, nb);
   if (threadIdx.x == 0) {
-    *mean = nv > 0 ? (float)(sum / (double)nv) : 0.0f;
+    if (divide) *reduced = nv > 0 ? (float)(sum / (double)nv) : 0.0f;
+    else *reduced = (float)sum;
     *n_valid = nv;
     if (bad_flag) *bad_flag = nb > 0 ? 1 : 0;
   }
 }
 
-hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, float* mean,
+hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, int divide, float* reduced,
                                 int32_t* n_valid, int32_t* bad_flag, hipStream_t stream) {
-  hipLaunchKernelGGL(mean_finalize_kernel, dim3(1), dim3(256), 0, stream, blocks, nblocks, mean,
-                     n_valid, bad_flag);
+  hipLaunchKernelGGL(mean_finalize_kernel, dim3(1), dim3(256), 0, stream, blocks, nblocks, divide,
+                     reduced, n_valid, bad_flag);
   return hipGetLastError();
 }
 
-// scale = dloss / n_valid (0 when no row has a target); counts[0] = n_valid,
-// counts[1] = valid rows with an in-range label (the rows that get sorted).
+// scalars[0] = a·dloss / n_valid (divide; 0 when no row has a target) or
+// a·dloss, the upstream scale of the plain gradient path; scalars[1] = 1.
+// counts[0] = n_valid, counts[1] = valid rows with an in-range label (the rows
+// that get sorted).
 __global__ void __launch_bounds__(256)
 scale_finalize_kernel(const BlockStats* __restrict__ blocks, int nblocks,
-                      const float* __restrict__ dloss, float* scale, int32_t* counts) {
+                      const float* __restrict__ dloss, int divide, float logit_scale,
+                      float* scalars, int32_t* counts) {
   double sum;
   int nv, nb;
   reduce_blocks(blocks, nblocks, sum, nv, nb);
   if (threadIdx.x == 0) {
-    *scale = nv > 0 ? __fdiv_rn(*dloss, (float)nv) : 0.0f;
+    const float base = divide ? (nv > 0 ? __fdiv_rn(*dloss, (float)nv) : 0.0f) : *dloss;
+    scalars[0] = base * logit_scale;
+    scalars[1] = 1.0f;
     counts[0] = nv;
     counts[1] = nv - nb;
   }
 }
 
 hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const float* dloss,
-                                 float* scale, int32_t* n_valid, hipStream_t stream) {
+                                 int divide, float logit_scale, float* scalars, int32_t* counts,
+                                 hipStream_t stream) {
   hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(256), 0, stream, blocks, nblocks,
-                     dloss, scale, n_valid);
+                     dloss, divide, logit_scale, scalars, counts);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Stable order of the valid rows by label: the position of row i is the number
-// of valid rows j with (y_j, j) < (y_i, i).  Quadratic in N but trivially
-// parallel and exact; 64 rows per block, each wave scans a quarter of the keys.
+// Per-row coefficients of the gradient (see launch_row_coef).
+__global__ void __launch_bounds__(256)
+row_coef_kernel(const int32_t* __restrict__ row_state, const float* __restrict__ lse,
+                const float* __restrict__ target_deriv, const float* __restrict__ dloss_rows,
+                const float* __restrict__ scalars, int64_t N, float logit_scale,
+                float one_minus_eps, float z_loss, float* __restrict__ gs, float* __restrict__ c1,
+                float* __restrict__ oh) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const int st = row_state[i];
+  float g = 0.0f;
+  if (st == kRowValid) g = dloss_rows ? dloss_rows[i] * logit_scale : scalars[0];
+  else if (st == kRowBad) g = __builtin_nanf("");
+  if (gs) gs[i] = g;
+  if (c1) c1[i] = fmaf(2.0f * z_loss, lse[i], 1.0f);
+  oh[i] = st == kRowValid ? g * one_minus_eps * target_deriv[i] : 0.0f;
+}
+
+hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
+                           const float* dloss_rows, const float* scalars, int64_t N,
+                           float logit_scale, float one_minus_eps, float z_loss, float* gs,
+                           float* c1, float* oh, hipStream_t stream) {
+  hipLaunchKernelGGL(row_coef_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     row_state, lse, target_deriv, dloss_rows, scalars, N, logit_scale,
+                     one_minus_eps, z_loss, gs, c1, oh);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Order of the valid rows by label, ties in row order: a sort of the unique
 // 64-bit keys (label << 32 | row).  Rows without an in-range label carry the
@@ -323,19 +369,21 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
 }
 
 // ---------------------------------------------------------------------------
-// dX_i = s · (dX_acc[i] − e_i · w_{y_i})   (valid rows)
+// dX_i = sx · dX_acc[i] − oh_i · w_{y_i}   (valid rows)
 //      = 0 (ignored rows), NaN (bad rows)
-// The one-hot part −1 · e_i at the target is applied here exactly in fp32.
+// The one-hot part of dZ (coefficient oh_i at the target) is applied here
+// exactly in fp32; sx is the upstream scale when G was stored unscaled, 1
+// when G already carries each row's scale.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
                    const int32_t* __restrict__ row_state, const int32_t* __restrict__ row_key,
-                   const float* __restrict__ target_deriv, const uint16_t* __restrict__ W,
-                   const float* __restrict__ scale, void* __restrict__ dX, int dX_bf16) {
+                   const float* __restrict__ oh, const uint16_t* __restrict__ W,
+                   const float* __restrict__ sx, void* __restrict__ dX, int dX_bf16) {
   const int64_t row = blockIdx.x;
   const int st = row_state[row];
-  const float s = *scale;
-  const float e = target_deriv[row];
+  const float s = *sx;
+  const float e = oh[row];
   const int64_t y = (st == kRowValid) ? row_key[row] : 0;
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -346,7 +394,7 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
       const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
                            __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = s * (a[q] - e * w4[q]);
+      for (int q = 0; q < 4; ++q) o[q] = fmaf(s, a[q], -e * w4[q]);
     } else if (st == kRowBad) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __builtin_nanf("");
@@ -365,16 +413,17 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
 
 hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
-                              const float* target_deriv, const uint16_t* W,
-                              const float* scale, void* dX, int dX_bf16, hipStream_t stream) {
+                              const float* oh, const uint16_t* W, const float* sx,
+                              void* dX, int dX_bf16, hipStream_t stream) {
   hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, N, H,
-                     row_state, row_key, target_deriv, W, scale, dX, dX_bf16);
+                     row_state, row_key, oh, W, sx, dX, dX_bf16);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// dW_v −= s · Σ_{i : y_i = v} e_i · x_i for every label v in [v_lo, v_hi)
-// (dst row v − v_lo), from the label-sorted keys.
+// dW_v −= Σ_{i : y_i = v} oh_i · x_i for every label v in [v_lo, v_hi)
+// (dst row v − v_lo), from the label-sorted keys; oh_i is the one-hot
+// coefficient of row i (upstream scale included).
 //
 // dw_seg_kernel: block (c, slice) walks sorted positions [32c, 32c + 32) in
 // order, 8 columns per lane, accumulating one run of equal labels at a time.
@@ -390,8 +439,8 @@ __device__ __forceinline__ int32_t key_label(uint64_t k) { return (int32_t)(k >>
 
 __global__ void __launch_bounds__(64)
 dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts,
-              const float* __restrict__ target_deriv, const uint16_t* __restrict__ X, int64_t H,
-              const float* __restrict__ scale, float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
+              const float* __restrict__ oh, const uint16_t* __restrict__ X, int64_t H,
+              float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
               float* __restrict__ part_head, float* __restrict__ part_tail) {
   __shared__ int32_t s_row[kSegRows], s_lab[kSegRows];
   __shared__ float s_e[kSegRows];
@@ -405,14 +454,13 @@ dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ cou
     const uint64_t k = keys[p0 + lane];
     s_row[lane] = (int32_t)(uint32_t)k;
     s_lab[lane] = key_label(k);
-    s_e[lane] = target_deriv[(uint32_t)k];
+    s_e[lane] = oh[(uint32_t)k];
   }
   const int32_t lab_prev = p0 > 0 ? key_label(keys[p0 - 1]) : -1;
   const int32_t lab_next = p0 + cnt < n_ok ? key_label(keys[p0 + cnt]) : -1;
   __syncthreads();
   const int64_t h = (int64_t)blockIdx.y * 512 + lane * 8;
   const bool col_ok = h < H;
-  const float s = *scale;
   // All rows of the chunk are loaded up front so the loads overlap.
   u32x4 xv[kSegRows];
 #pragma unroll
@@ -442,7 +490,7 @@ dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ cou
           } else if (v >= v_lo && v < v_hi) {
             float* d = dst + (int64_t)(v - v_lo) * H + h;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) d[k] = fmaf(-s, acc[k], d[k]);
+            for (int k = 0; k < 8; ++k) d[k] -= acc[k];
           }
         }
 #pragma unroll
@@ -455,9 +503,8 @@ dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ cou
 
 __global__ void __launch_bounds__(64)
 dw_seg_fix_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts, int64_t H,
-                  const float* __restrict__ scale, float* __restrict__ dst, int64_t v_lo,
-                  int64_t v_hi, const float* __restrict__ part_head,
-                  const float* __restrict__ part_tail) {
+                  float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
+                  const float* __restrict__ part_head, const float* __restrict__ part_tail) {
   const int64_t n_ok = counts[1];
   const int64_t c = blockIdx.x;
   const int64_t p0 = c * kSegRows;
@@ -479,20 +526,19 @@ dw_seg_fix_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__
     const int64_t q1 = q0 + kSegRows < n_ok ? q0 + kSegRows : n_ok;
     if (!(q1 < n_ok && key_label(keys[q1 - 1]) == v && key_label(keys[q1]) == v)) break;
   }
-  const float s = *scale;
   float* d = dst + (int64_t)(v - v_lo) * H + h;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) d[k] = fmaf(-s, acc[k], d[k]);
+  for (int k = 0; k < 8; ++k) d[k] -= acc[k];
 }
 
-hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* target_deriv,
-                             const uint16_t* X, int64_t N, int64_t H, const float* scale,
-                             float* dst, int64_t v_lo, int64_t v_hi, float* part_head,
-                             float* part_tail, hipStream_t stream) {
+hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const float* oh,
+                             const uint16_t* X, int64_t N, int64_t H, float* dst, int64_t v_lo,
+                             int64_t v_hi, float* part_head, float* part_tail,
+                             hipStream_t stream) {
   const dim3 grid((unsigned)seg_chunks(N), (unsigned)((H + 511) / 512));
-  hipLaunchKernelGGL(dw_seg_kernel, grid, dim3(64), 0, stream, keys, counts, target_deriv, X, H, scale,
-                     dst, v_lo, v_hi, part_head, part_tail);
-  hipLaunchKernelGGL(dw_seg_fix_kernel, grid, dim3(64), 0, stream, keys, counts, H, scale, dst, v_lo,
+  hipLaunchKernelGGL(dw_seg_kernel, grid, dim3(64), 0, stream, keys, counts, oh, X, H, dst, v_lo,
+                     v_hi, part_head, part_tail);
+  hipLaunchKernelGGL(dw_seg_fix_kernel, grid, dim3(64), 0, stream, keys, counts, H, dst, v_lo,
                      v_hi, part_head, part_tail);
   return hipGetLastError();
 }

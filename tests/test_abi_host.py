@@ -97,3 +97,48 @@ def test_backward_error_paths(lib):
     assert bwd(lib, dX=FAKE + 4) == _lib.LCE_ERR_ALIGNMENT
     assert bwd(lib, dW=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
     assert bwd(lib, wsb=255) == _lib.LCE_ERR_WORKSPACE
+
+
+def opts(**kw):
+    o = _lib.Options()
+    _lib.load().lce_options_default(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def test_options_default(lib):
+    o = opts()
+    assert (o.ignore_index, o.softcap, o.logit_scale, o.label_smoothing, o.z_loss,
+            o.reduction) == (-100, 0.0, 1.0, 0.0, 0.0, _lib.LCE_REDUCE_MEAN)
+
+
+def fwd_ex(lib, o, N=4, H=8, V=5):
+    wsb = lib.lce_forward_workspace_bytes(N, H, V)
+    return lib.lce_forward_ex(FAKE, FAKE, FAKE, N, H, V, o, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                              wsb, None)
+
+
+def bwd_ex(lib, o, N=4, H=8, V=5):
+    wsb = lib.lce_backward_workspace_bytes(N, H, V, 0)
+    return lib.lce_backward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, N, H, V, o, FAKE, 0, FAKE, 0, FAKE,
+                               wsb, None)
+
+
+@pytest.mark.parametrize("bad", [dict(logit_scale=0.0), dict(logit_scale=-1.0),
+                                 dict(logit_scale=float("inf")), dict(label_smoothing=1.01),
+                                 dict(label_smoothing=-0.5), dict(z_loss=-1e-3),
+                                 dict(z_loss=float("nan")), dict(softcap=float("nan")),
+                                 dict(reduction=3), dict(reduction=-1)])
+def test_ex_rejects_bad_options(lib, bad):
+    o = opts(**bad)
+    assert fwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+
+
+def test_ex_null_options_and_shapes(lib):
+    assert fwd_ex(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    assert bwd_ex(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    o = opts()
+    assert fwd_ex(lib, ctypes.byref(o), H=12) == _lib.LCE_ERR_SHAPE
+    assert bwd_ex(lib, ctypes.byref(o), V=0) == _lib.LCE_ERR_SHAPE
