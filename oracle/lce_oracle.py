@@ -26,7 +26,8 @@ Sources (web pages, cited by title and section):
               loss 0; backward multiplies the softcap derivative 1 − tanh²;
               final division by n_items = count of labels ≠ −100).
 
-Readings where the pages leave a step open (each restated where it is used):
+Readings where the pages leave a step open (each restated where it is used;
+R7 - R12 concern the GPU path's interface and are listed with its design):
   R1 softcap: z = c·tanh(z_raw / c) is applied to every logit, the target
      included, before the LSE; its derivative is 1 − tanh²(z_raw / c); c <= 0
      means no softcap.
@@ -45,12 +46,12 @@ Z-loss and the reduction mode as terms that need their own definition, and
 [Unsloth] §4 an optional logit scaling (Cohere's logit_scale) next to the
 softcap; the pages give no formulas, so the plainest standard readings are
 taken:
-  R7 logit_scale a: z = a·(x·w), applied before the softcap.
-  R8 label smoothing e: the target distribution is (1 − e)·onehot(y) + e/V,
+  R13 logit_scale a: z = a·(x·w), applied before the softcap.
+  R14 label smoothing e: the target distribution is (1 − e)·onehot(y) + e/V,
      so loss_i = LSE_i − (1 − e)·z_{i,y} − (e/V)·Σ_v z_{i,v} (the definition
      of PyTorch's CrossEntropyLoss, which [M011] §07 cites for its semantics).
-  R9 Z-loss l: each valid row adds l·LSE_i².
-  R10 reduction: "mean" divides the sum of the row losses by n_valid (R4),
+  R15 Z-loss l: each valid row adds l·LSE_i².
+  R16 reduction: "mean" divides the sum of the row losses by n_valid (R4),
      "sum" does not divide, "none" keeps the row losses; the backward of
      "none" takes one upstream gradient per row.
   Gradient of a valid row: dL_i/dz_v = (1 + 2l·LSE_i)·p_v − (1 − e)·[v = y_i]
@@ -255,7 +256,7 @@ def backward_rows(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
 
 
 # --------------------------------------------------------------------------- #
-# Loss variants (readings R7 - R10)
+# Loss variants (readings R13 - R16)
 # --------------------------------------------------------------------------- #
 DEFAULT_OPTIONS = {"softcap": 0.0, "logit_scale": 1.0, "label_smoothing": 0.0,
                    "z_loss": 0.0, "reduction": "mean", "ignore_index": IGNORE_INDEX}
@@ -269,9 +270,9 @@ def options(**kw) -> Dict[str, object]:
 
 def forward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, opts: Dict[str, object],
                n_valid_total: Optional[int] = None) -> Dict[str, np.ndarray]:
-    """Per-row LSE and loss with logit scale (R7), label smoothing (R8) and
-    Z-loss (R9); `reduced` is the mean, the sum, or (for "none") the sum of
-    the row losses (R10)."""
+    """Per-row LSE and loss with logit scale (R13), label smoothing (R14) and
+    Z-loss (R15); `reduced` is the mean, the sum, or (for "none") the sum of
+    the row losses (R16)."""
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
     labels = np.asarray(labels, dtype=np.int64)
@@ -302,7 +303,7 @@ def forward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, opts: Dict[str,
 
 
 def row_scale(labels: np.ndarray, dloss, n_valid: int, opts: Dict[str, object]) -> np.ndarray:
-    """Upstream scale of each row's gradient (R10): dloss / n_valid ("mean",
+    """Upstream scale of each row's gradient (R16): dloss / n_valid ("mean",
     0 when n_valid = 0), dloss ("sum"), or the row's own dloss_i ("none");
     zero for ignored rows."""
     labels = np.asarray(labels, dtype=np.int64)
@@ -320,7 +321,7 @@ def logit_gradient_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.
                       scale: np.ndarray, opts: Dict[str, object],
                       vocab_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """dL/d(x·w) for the rows of X: ((1 + 2l·LSE)·p − (1 − e)·onehot − e/V)
-    · softcap derivative · a · scale_i (gradient of R7 - R9)."""
+    · softcap derivative · a · scale_i (gradient of R13 - R15)."""
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
     labels = np.asarray(labels, dtype=np.int64)
