@@ -352,3 +352,87 @@ def backward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
     dZ = logit_gradient_ex(X, W, labels, lse, scale, opts)
     return dZ @ W, dZ.T @ X
 
+
+
+# --------------------------------------------------------------------------- #
+# Vocabulary shards (reading R17)
+# --------------------------------------------------------------------------- #
+# [M011] §07 places the vocabulary columns on several ranks: the per-row max,
+# exp-sum and target score have to be made global before the loss is formed,
+# the hidden-state gradient is a sum of per-shard contributions, and averaging
+# a per-shard cross-entropy gives a wrong loss.  The news-site article on GPU
+# acceleration of the loss function (§4.3, sharded softmax) describes the same
+# split of the class dimension with an all-reduce of the global denominator.
+#   R17 a shard owns the contiguous vocabulary rows [v_lo, v_lo + V_shard) of
+#       W.  Per shard and row it reports log Σ_{v in shard} exp(z_v), the
+#       target logit when the label lies in the shard (else 0) and Σ_{v in
+#       shard} z_v.  The merge takes the log-sum-exp of the shard values in
+#       shard order (the §05 merge with one block per shard), sums the target
+#       and logit-sum parts, and forms the loss of R14 - R16 with the full
+#       vocabulary size.  The backward of a shard uses the merged LSE, applies
+#       the one-hot term only on the shard that owns the label, and returns
+#       its share of dX (the shares add up to dX) and its rows of dW.
+def forward_shard(X: np.ndarray, W_shard: np.ndarray, labels: np.ndarray, v_lo: int,
+                  V_total: int, opts: Dict[str, object]) -> Dict[str, np.ndarray]:
+    """Per-row partials of one vocabulary shard (R17)."""
+    X = np.asarray(X, dtype=np.float64)
+    W_shard = np.asarray(W_shard, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    a, c = float(opts["logit_scale"]), float(opts["softcap"])
+    Zc = apply_softcap(a * logits(X, W_shard), c)
+    ok = valid_mask(labels, int(opts["ignore_index"])) & \
+        ~bad_mask(labels, V_total, int(opts["ignore_index"]))
+    owned = ok & (labels >= v_lo) & (labels < v_lo + W_shard.shape[0])
+    target = np.zeros(X.shape[0])
+    rows = np.nonzero(owned)[0]
+    target[rows] = Zc[rows, labels[rows] - v_lo]
+    return {"lse_part": row_logsumexp(Zc), "target_part": target,
+            "zsum_part": Zc.sum(axis=1)}
+
+
+def merge_shards(parts: Sequence[Dict[str, np.ndarray]], labels: np.ndarray, V_total: int,
+                 opts: Dict[str, object]) -> Dict[str, np.ndarray]:
+    """Global LSE, row losses and the reduced loss from the shard partials,
+    taken in shard order (R17)."""
+    labels = np.asarray(labels, dtype=np.int64)
+    L = np.stack([p["lse_part"] for p in parts])
+    m = L.max(axis=0)
+    lse = m + np.log(np.exp(L - m[None, :]).sum(axis=0))
+    target = np.sum([p["target_part"] for p in parts], axis=0)
+    zsum = np.sum([p["zsum_part"] for p in parts], axis=0)
+    e, lam = float(opts["label_smoothing"]), float(opts["z_loss"])
+    ignore_index = int(opts["ignore_index"])
+    valid = valid_mask(labels, ignore_index)
+    bad = bad_mask(labels, V_total, ignore_index)
+    row_loss = lse - (1.0 - e) * target - (e / V_total) * zsum + lam * lse * lse
+    loss = np.where(valid, row_loss, 0.0)
+    loss[bad] = np.nan
+    n_valid = int(valid.sum())
+    total = loss.sum()
+    if opts["reduction"] == "mean":
+        reduced = total / n_valid if n_valid > 0 else 0.0
+    else:
+        reduced = total
+    return {"lse": lse, "loss": loss, "n_valid": n_valid, "reduced": reduced}
+
+
+def backward_shard(X: np.ndarray, W_shard: np.ndarray, labels: np.ndarray, lse: np.ndarray,
+                   dloss, v_lo: int, V_total: int, opts: Dict[str, object]):
+    """(dX share, dW rows) of one vocabulary shard given the merged LSE (R17)."""
+    X = np.asarray(X, dtype=np.float64)
+    W_shard = np.asarray(W_shard, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    ignore_index = int(opts["ignore_index"])
+    n_valid = int(valid_mask(labels, ignore_index).sum())
+    scale = row_scale(labels, dloss, n_valid, opts)
+    a, c = float(opts["logit_scale"]), float(opts["softcap"])
+    e, lam = float(opts["label_smoothing"]), float(opts["z_loss"])
+    Z = a * logits(X, W_shard)
+    Zc = apply_softcap(Z, c)
+    P = np.exp(Zc - lse[:, None])
+    cols = v_lo + np.arange(W_shard.shape[0])
+    onehot = (labels[:, None] == cols[None, :]).astype(np.float64)
+    dZ = (1.0 + 2.0 * lam * lse)[:, None] * P - (1.0 - e) * onehot - e / V_total
+    dZ = dZ * softcap_derivative(Z, c) * a * scale[:, None]
+    dZ[bad_mask(labels, V_total, ignore_index)] = np.nan
+    return dZ @ W_shard, dZ.T @ X

@@ -217,3 +217,71 @@ def test_variant_pins_catch_mutation(name, monkeypatch):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# --------------------------------------------------------------------------- #
+# Vocabulary shards: mistakes planted in forward_shard / merge_shards /
+# backward_shard must be caught by the shard pins.
+# --------------------------------------------------------------------------- #
+from tests import test_oracle_shards as PS  # noqa: E402
+
+SHARD_PINS = [
+    PS.test_worked_example_split_in_two_shards,
+    lambda: PS.test_partition_independence(PS.OPTION_SETS[2], [0, 4, 5, 13]),
+    lambda: PS.test_partition_independence(PS.OPTION_SETS[0], [0, 6, 12, 13]),
+    lambda: PS.test_finite_differences_through_the_merge("mean"),
+]
+
+_orig_forward_shard = O.forward_shard
+_orig_merge_shards = O.merge_shards
+_orig_backward_shard = O.backward_shard
+
+
+def _ms_max_of_shards(parts, labels, V_total, opts):
+    # Keeps only the largest shard's mass instead of adding all of them.
+    out = _orig_merge_shards(parts, labels, V_total, opts)
+    L = np.stack([p["lse_part"] for p in parts]).max(axis=0)
+    delta = L - out["lse"]
+    valid = np.asarray(labels) != int(opts["ignore_index"])
+    out["lse"] = L
+    out["loss"] = out["loss"] + valid * delta
+    return out
+
+
+def _fs_target_on_every_shard(X, W_shard, labels, v_lo, V_total, opts):
+    out = _orig_forward_shard(X, W_shard, labels, v_lo, V_total, opts)
+    Vs = np.asarray(W_shard).shape[0]
+    Zc = O.apply_softcap(float(opts["logit_scale"]) * O.logits(np.asarray(X, float),
+                                                               np.asarray(W_shard, float)),
+                         float(opts["softcap"]))
+    lab = np.asarray(labels)
+    ok = (lab != int(opts["ignore_index"])) & (lab >= 0) & (lab < V_total)
+    rows = np.nonzero(ok)[0]
+    out["target_part"] = np.zeros(len(lab))
+    out["target_part"][rows] = Zc[rows, (lab[rows] - v_lo) % Vs]
+    return out
+
+
+def _bs_local_lse(X, W_shard, labels, lse, dloss, v_lo, V_total, opts):
+    local = _orig_forward_shard(X, W_shard, labels, v_lo, V_total, opts)["lse_part"]
+    return _orig_backward_shard(X, W_shard, labels, local, dloss, v_lo, V_total, opts)
+
+
+SHARD_MUTATIONS = {
+    "merge_keeps_max_shard": ("merge_shards", _ms_max_of_shards),
+    "target_on_every_shard": ("forward_shard", _fs_target_on_every_shard),
+    "backward_with_shard_lse": ("backward_shard", _bs_local_lse),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHARD_MUTATIONS))
+def test_shard_pins_catch_mutation(name, monkeypatch):
+    attr, fn = SHARD_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in SHARD_PINS:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
