@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--dtype-grad", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--shards", type=int, default=8,
+                    help="also time one vocabulary shard of V/shards rows (0: skip)")
     return ap.parse_args()
 
 
@@ -108,6 +110,53 @@ def cpu_baseline(w, X, W, y, rows):
             "sample": f"{len(idx)} seeded token rows of {w.name} (N={w.N}, H={w.H}, V={w.V}): "
                       f"float64 forward, dX rows and their dW share in {dt:.1f} s; the "
                       f"full-batch rate is extrapolated from these rows"}
+
+
+def time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, sptr, stream):
+    """One rank's share at vocabulary-parallel degree args.shards: the shard
+    forward and the shard backward of the first V/shards rows of W, timed
+    apart from the whole-vocabulary step (the exchange between ranks is not
+    part of it).  The backward uses the whole-vocabulary LSE of the last step,
+    which the merge of all shards would reproduce."""
+    import ctypes
+    import torch
+    import lce_inputs as L
+    N, H = w.N, w.H
+    Vs = w.V // args.shards
+    opt = _lib.make_options(L.IGNORE_INDEX, float(w.softcap))
+    lse_part = torch.empty(N, dtype=torch.float32, device=X.device)
+    tgt_part = torch.empty(N, dtype=torch.float32, device=X.device)
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+
+    def sstep():
+        st = lib.lce_shard_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, Vs, 0, w.V,
+                                   ctypes.byref(opt), lse_part.data_ptr(), tgt_part.data_ptr(),
+                                   None, fws.data_ptr(), fws.numel(), sptr)
+        if st:
+            raise RuntimeError(f"lce_shard_forward: {_lib.status_string(st)}")
+        st = lib.lce_shard_backward(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                                    dloss.data_ptr(), N, H, Vs, 0, w.V, ctypes.byref(opt),
+                                    dX.data_ptr(), gcode, dW.data_ptr(), gcode, bws.data_ptr(),
+                                    bws.numel(), sptr)
+        if st:
+            raise RuntimeError(f"lce_shard_backward: {_lib.status_string(st)}")
+
+    log(f"[bench] vocabulary shard: V/{args.shards} = {Vs} rows")
+    for _ in range(args.warmup):
+        sstep()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        sstep()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    tf = 8 * N * H * Vs / (ms / 1e3) / 1e12
+    return {"degree": args.shards, "V_shard": Vs, "ms_per_step": round(ms, 3),
+            "tokens_per_s": round(N / (ms / 1e3), 1), "tflops": round(tf, 1),
+            "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4),
+            "note": "one rank's shard forward + shard backward, collectives excluded"}
 
 
 def main():
@@ -220,6 +269,11 @@ def main():
         if k in kernels:
             per_kernel[k]["tflops"] = round(units * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
 
+    shard = None
+    if args.shards > 1:
+        shard = time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, sptr,
+                                 stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} rows")
@@ -245,6 +299,7 @@ def main():
         "frac_of_bf16_dense_peak": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "vocab_shard": shard,
         "kernels": per_kernel,
         "memory_bytes": {"peak_allocated": int(peak_mem),
                          "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),

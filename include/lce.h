@@ -181,6 +181,82 @@ lce_status lce_backward_ex(const void* X_dev, const void* W_dev,
                            void* workspace_dev, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * Vocabulary shards.  The AI-infra KB page M011 (§07) splits the vocabulary
+ * columns over ranks: each row's max, exp-sum and target score must be made
+ * global before its loss is formed, the hidden-state gradient is the sum of
+ * the shards' contributions, and averaging per-shard cross-entropies is
+ * wrong.  The news-site article on GPU acceleration of the loss function
+ * (§4.3) describes the same sharded softmax with an all-reduce of the global
+ * denominator.  These three calls are the per-rank pieces of that scheme; the
+ * exchange between ranks (an all-gather of the [N] partials, an all-reduce of
+ * the dX shares) belongs to the caller's collective library.
+ *
+ * A shard owns the contiguous vocabulary rows [vocab_offset, vocab_offset +
+ * V_shard) of a vocabulary of vocab_total rows; W_shard_dev points to those
+ * rows (bf16 [V_shard, H]).  Labels are global ids, checked against
+ * [0, vocab_total).  Shapes as above, with 0 <= vocab_offset and
+ * vocab_offset + V_shard <= vocab_total < 2^31 (else LCE_ERR_SHAPE).
+ */
+
+/*
+ * Per-row partials of one shard (workspace: lce_forward_workspace_bytes(N, H,
+ * V_shard)).  Only opt's ignore_index, softcap and logit_scale matter here.
+ *   lse_part_dev    float [N]  log Σ_{v in shard} exp(z_v)
+ *   target_part_dev float [N]  z_{y_i} when the label lies in the shard and the
+ *                              row is valid, else 0
+ *   zsum_part_dev   float [N]  Σ_{v in shard} z_v; may be NULL (needed by the
+ *                              merge only with label smoothing)
+ */
+lce_status lce_shard_forward(const void* X_dev, const void* W_shard_dev,
+                             const int64_t* labels_dev, int64_t N, int64_t H,
+                             int64_t V_shard, int64_t vocab_offset,
+                             int64_t vocab_total, const lce_options* opt,
+                             float* lse_part_dev, float* target_part_dev,
+                             float* zsum_part_dev, void* workspace_dev,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace lce_shard_merge needs (O(N / 256) bytes); 0 if N is invalid. */
+size_t lce_shard_merge_workspace_bytes(int64_t N);
+
+/*
+ * Merge of n_shards shards' partials, laid out [n_shards, N] in shard order
+ * (row k·N + i holds shard k's value for row i; zsum_parts_dev may be NULL
+ * unless opt->label_smoothing > 0).  LSE_i = m + log Σ_k exp(L_ki − m) with
+ * m = max_k L_ki, the target logit and the logit sum are the sums over the
+ * shards, each taken in shard order, and the loss, reduction, n_valid and
+ * bad-label flag follow lce_forward_ex with vocab_total as V.  Outputs as
+ * lce_forward_ex.
+ */
+lce_status lce_shard_merge(const float* lse_parts_dev, const float* target_parts_dev,
+                           const float* zsum_parts_dev, int32_t n_shards,
+                           const int64_t* labels_dev, int64_t N, int64_t vocab_total,
+                           const lce_options* opt, float* loss_dev, float* lse_dev,
+                           float* reduced_dev, int32_t* n_valid_dev,
+                           int32_t* bad_label_dev, void* workspace_dev,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of one shard given the merged LSE (workspace:
+ * lce_backward_workspace_bytes(N, H, V_shard, dW_dtype)).  dloss_dev as in
+ * lce_backward_ex.  The gradient of the shard's logit columns uses the merged
+ * LSE; the one-hot term (−(1 − e) at the target) appears only on the shard
+ * that owns the label; label smoothing divides by vocab_total.
+ *   dX_part_dev  [N, H] of dX_dtype, overwritten: this shard's share of dX
+ *                (the shares of all shards add up to dX)
+ *   dW_shard_dev [V_shard, H] of dW_dtype, overwritten: rows vocab_offset ...
+ *                of dW
+ */
+lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
+                              const int64_t* labels_dev, const float* lse_dev,
+                              const float* dloss_dev, int64_t N, int64_t H,
+                              int64_t V_shard, int64_t vocab_offset,
+                              int64_t vocab_total, const lce_options* opt,
+                              void* dX_part_dev, lce_dtype dX_dtype,
+                              void* dW_shard_dev, lce_dtype dW_dtype,
+                              void* workspace_dev, size_t workspace_bytes,
+                              void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);
 

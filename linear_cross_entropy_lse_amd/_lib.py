@@ -31,8 +31,9 @@ REDUCTIONS = {"mean": LCE_REDUCE_MEAN, "sum": LCE_REDUCE_SUM, "none": LCE_REDUCE
 # Every symbol include/lce.h declares.
 EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_forward",
             "lce_backward", "lce_options_default", "lce_forward_ex", "lce_backward_ex",
-            "lce_status_string", "lce_version", "lce_timing_enable", "lce_timing_reset",
-            "lce_timing_read")
+            "lce_shard_forward", "lce_shard_merge_workspace_bytes", "lce_shard_merge",
+            "lce_shard_backward", "lce_status_string", "lce_version", "lce_timing_enable",
+            "lce_timing_reset", "lce_timing_read")
 
 
 class Options(ctypes.Structure):
@@ -94,6 +95,17 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, opt_p, vp, ctypes.c_int,
                                     vp, ctypes.c_int, vp, sz, vp]
     lib.lce_backward_ex.restype = ctypes.c_int
+    lib.lce_shard_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, opt_p, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.lce_shard_forward.restype = ctypes.c_int
+    lib.lce_shard_merge_workspace_bytes.argtypes = [i64]
+    lib.lce_shard_merge_workspace_bytes.restype = sz
+    lib.lce_shard_merge.argtypes = [vp, vp, vp, ctypes.c_int32, vp, i64, i64, opt_p, vp, vp, vp,
+                                    vp, vp, vp, sz, vp]
+    lib.lce_shard_merge.restype = ctypes.c_int
+    lib.lce_shard_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, opt_p, vp,
+                                       ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
+    lib.lce_shard_backward.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -314,3 +326,113 @@ def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap:
     _check(st, "lce_backward_ex")
     return dX, dW
 
+
+
+# --------------------------------------------------------------------------- #
+# Vocabulary shards
+# --------------------------------------------------------------------------- #
+def lce_shard_forward(X, W_shard, labels, vocab_offset: int, vocab_total: int,
+                      ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
+                      with_zsum: bool = False, workspace=None):
+    """Per-row partials of the vocabulary shard W_shard = rows [vocab_offset,
+    vocab_offset + V_shard) of a vocabulary of vocab_total rows.  Returns a
+    dict of [N] device tensors: lse_part, target_part and (with_zsum) zsum_part."""
+    import torch
+    opt = make_options(ignore_index, softcap, logit_scale)
+    X, W_shard, labels = _prep(X, W_shard, labels)
+    N, H = X.shape
+    Vs = W_shard.shape[0]
+    dev = X.device
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    tgt = torch.empty(N, dtype=torch.float32, device=dev)
+    zs = torch.empty(N, dtype=torch.float32, device=dev) if with_zsum else None
+    need = lce_forward_workspace_bytes(N, H, Vs)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_shard_forward")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_shard_forward(_ptr(X), _ptr(W_shard), _ptr(labels), N, H, Vs,
+                                  int(vocab_offset), int(vocab_total), ctypes.byref(opt),
+                                  _ptr(lse), _ptr(tgt), _ptr(zs) if zs is not None else None,
+                                  _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "lce_shard_forward")
+    out = {"lse_part": lse, "target_part": tgt}
+    if zs is not None:
+        out["zsum_part"] = zs
+    return out
+
+
+def lce_shard_merge(lse_parts, target_parts, labels, vocab_total: int, zsum_parts=None,
+                    ignore_index: int = -100, label_smoothing: float = 0.0, z_loss: float = 0.0,
+                    reduction: str = "mean"):
+    """Merge [n_shards, N] shard partials (shard order along dim 0) into the
+    loss.  Returns the dict of lce_forward_ex (loss, lse, reduced, n_valid,
+    bad_label)."""
+    import torch
+    opt = make_options(ignore_index, 0.0, 1.0, label_smoothing, z_loss, reduction)
+    dev = lse_parts.device
+    lse_parts = lse_parts.to(torch.float32).contiguous()
+    target_parts = target_parts.to(torch.float32).contiguous()
+    if zsum_parts is not None:
+        zsum_parts = zsum_parts.to(torch.float32).contiguous()
+    labels = labels.to(device=dev, dtype=torch.int64).contiguous()
+    g, N = lse_parts.shape
+    if target_parts.shape != (g, N) or labels.shape != (N,) or \
+            (zsum_parts is not None and zsum_parts.shape != (g, N)):
+        raise ValueError("shard partials must be [n_shards, N] and labels [N]")
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    reduced = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int32, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    need = load().lce_shard_merge_workspace_bytes(N)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_shard_merge")
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_shard_merge(_ptr(lse_parts), _ptr(target_parts),
+                                _ptr(zsum_parts) if zsum_parts is not None else None, g,
+                                _ptr(labels), N, int(vocab_total), ctypes.byref(opt), _ptr(loss),
+                                _ptr(lse), reduced.data_ptr(), n_valid.data_ptr(), bad.data_ptr(),
+                                _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "lce_shard_merge")
+    return {"loss": loss, "lse": lse, "reduced": reduced, "n_valid": n_valid, "bad_label": bad}
+
+
+def lce_shard_backward(X, W_shard, labels, lse, dloss, vocab_offset: int, vocab_total: int,
+                       ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
+                       label_smoothing: float = 0.0, z_loss: float = 0.0,
+                       reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None):
+    """Backward of one vocabulary shard given the merged LSE.  Returns
+    (dX share [N, H], dW rows of the shard [V_shard, H])."""
+    import torch
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    X, W_shard, labels = _prep(X, W_shard, labels)
+    N, H = X.shape
+    Vs = W_shard.shape[0]
+    dev = X.device
+    n_d = N if reduction == "none" else 1
+    if not torch.is_tensor(dloss):
+        dloss = torch.full((n_d,), float(dloss), dtype=torch.float32, device=dev)
+    dloss = dloss.to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+    if dloss.numel() != n_d:
+        raise ValueError(f"dloss must hold {n_d} value(s) for reduction {reduction!r}")
+    if n_d == 0:
+        dloss = torch.zeros(1, dtype=torch.float32, device=dev)
+    lse = lse.to(device=dev, dtype=torch.float32).contiguous()
+    if lse.shape != (N,):
+        raise ValueError("lse must have shape [N]")
+    dXc, dWc = _dtype_code(dX_dtype), _dtype_code(dW_dtype)
+    dX = torch.empty(N, H, dtype=dX_dtype or torch.float32, device=dev)
+    dW = torch.empty(Vs, H, dtype=dW_dtype or torch.float32, device=dev)
+    need = lce_backward_workspace_bytes(N, H, Vs, dW_dtype)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_shard_backward")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_shard_backward(_ptr(X), _ptr(W_shard), _ptr(labels), _ptr(lse),
+                                   dloss.data_ptr(), N, H, Vs, int(vocab_offset),
+                                   int(vocab_total), ctypes.byref(opt), _ptr(dX), dXc,
+                                   dW.data_ptr(), dWc, _ptr(workspace), workspace.numel(),
+                                   _stream(dev))
+    _check(st, "lce_shard_backward")
+    return dX, dW

@@ -220,6 +220,178 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
 
 #define LCE_LAUNCH(name, stream, call) LCE_TRY(timed(name, stream, [&]() { return call; }))
 
+bool range_ok(int64_t V, int64_t v_lo, int64_t V_total) {
+  return v_lo >= 0 && V_total < INT_MAX && v_lo <= V_total - V;
+}
+
+LossTerms loss_terms(const lce_options* opt, int64_t V_total, const float* part_z) {
+  LossTerms t{};
+  t.one_minus_eps = 1.0f - opt->label_smoothing;
+  t.eps_over_v = (float)((double)opt->label_smoothing / (double)V_total);
+  t.z_loss = opt->z_loss;
+  t.part_z = part_z;
+  return t;
+}
+
+// Outputs of a forward pass.  The full forward sets loss, reduced and
+// n_valid; a vocabulary shard's forward sets target (and optionally zsum)
+// instead and leaves reduced null.
+struct FwdOut {
+  float* loss = nullptr;
+  float* lse = nullptr;
+  float* reduced = nullptr;
+  int32_t* n_valid = nullptr;
+  int32_t* bad_label = nullptr;
+  float* target = nullptr;
+  float* zsum = nullptr;
+};
+
+lce_status forward_impl(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                        int64_t N, int64_t H, int64_t V, VocabRange vr, const lce_options* opt,
+                        const FwdOut& out, void* workspace_dev, size_t workspace_bytes,
+                        void* stream_ptr) {
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !workspace_dev)) return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(workspace_dev, kAlign))
+    return LCE_ERR_ALIGNMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const bool shard = out.reduced == nullptr;
+  if (N == 0) {
+    if (!shard)
+      LCE_LAUNCH("empty_forward", stream, launch_empty_forward(out.reduced, out.n_valid, out.bad_label, stream));
+    return LCE_OK;
+  }
+  const FwdPlan pl = plan_forward(N, H, V);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+
+  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
+  float* target = out.target ? out.target : at<float>(workspace_dev, pl.off_target);
+  float* pm = at<float>(workspace_dev, pl.off_pm);
+  float* ps = at<float>(workspace_dev, pl.off_ps);
+  float* pz = at<float>(workspace_dev, pl.off_pz);
+  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
+  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+  // Per-row logit sums: for label smoothing, or when a shard reports them.
+  const bool zsum = shard ? out.zsum != nullptr : opt->label_smoothing > 0.0f;
+
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
+                          opt->logit_scale, state, nullptr, target, nullptr, nullptr, stream));
+  LseParams lp{};
+  lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
+  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
+  lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
+  pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
+  lp.part_m = pm; lp.part_s = ps; lp.part_z = zsum ? pz : nullptr;
+  LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
+  const LossTerms terms = loss_terms(opt, vr.V_total, zsum ? pz : nullptr);
+  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, terms, out.lse, out.loss,
+                              shard ? nullptr : blocks, out.zsum, stream));
+  if (!shard)
+    LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, opt->reduction == LCE_REDUCE_MEAN,
+                                  out.reduced, out.n_valid, out.bad_label, stream));
+  return LCE_OK;
+}
+
+// Backward over the vocabulary rows W holds ([vr.v_lo, vr.v_lo + V) of
+// vr.V_total): their rows of dW and their share of dX.
+lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                         const float* lse_dev, const float* dloss_dev, int64_t N, int64_t H,
+                         int64_t V, VocabRange vr, const lce_options* opt, void* dX_dev,
+                         lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                         void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
+  if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
+    return LCE_ERR_INVALID_ARG;
+  if (!dW_dev) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !lse_dev || !dloss_dev || !dX_dev ||
+                !workspace_dev))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(lse_dev, 4) || !aligned(dloss_dev, 4) || !aligned(dX_dev, 16) ||
+      !aligned(dW_dev, 16) || !aligned(workspace_dev, kAlign))
+    return LCE_ERR_ALIGNMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int64_t dw_bytes = V * H * (dW_dtype == LCE_BF16 ? 2 : 4);
+  if (N == 0) {
+    LCE_LAUNCH("fill_zero", stream, launch_fill_zero(dW_dev, dw_bytes, stream));
+    return LCE_OK;
+  }
+  const BwdPlan pl = plan_backward(N, H, V, dW_dtype);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+
+  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
+  int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
+  float* deriv = at<float>(workspace_dev, pl.off_deriv);
+  float* gs = at<float>(workspace_dev, pl.off_gs);
+  float* c1 = at<float>(workspace_dev, pl.off_c1);
+  float* oh = at<float>(workspace_dev, pl.off_oh);
+  uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
+  uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
+  const uint64_t* keys = sort_passes(N) % 2 == 0 ? keys_a : keys_b;   // where the sort ends
+  float* part_head = at<float>(workspace_dev, pl.off_head);
+  float* part_tail = at<float>(workspace_dev, pl.off_tail);
+  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
+  float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] plain scale, [1] = 1
+  int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
+  uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
+  float* dXp = at<float>(workspace_dev, pl.off_dXp);
+  float* dWs = at<float>(workspace_dev, pl.off_dWs);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
+  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+  // The plain path stores G = p·d and applies one scalar scale afterwards; label
+  // smoothing, Z-loss or a per-row upstream gradient need G scaled row by row.
+  const bool general = opt->label_smoothing > 0.0f || opt->z_loss > 0.0f ||
+                       opt->reduction == LCE_REDUCE_NONE;
+  const float* gemm_scale = general ? scalars + 1 : scalars;
+
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
+                          opt->logit_scale, state, key, nullptr, deriv, blocks, stream));
+  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, opt->reduction == LCE_REDUCE_MEAN,
+                                opt->logit_scale, scalars, counts, stream));
+  LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
+                          scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
+                          general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
+  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
+
+  for (int c = 0; c < pl.nchunks; ++c) {
+    const int64_t v_begin = (int64_t)c * pl.Vc;
+    const int64_t chunk_len = std::min<int64_t>(pl.Vc, V - v_begin);
+    const int n_vt = (int)ceil_div(chunk_len, kTile);
+
+    GradParams gp{};
+    gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
+    gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
+    gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
+    pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
+    gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
+    gp.gs = general ? gs : nullptr; gp.c1 = c1;
+    gp.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);
+    LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
+
+    ChunkGemmParams cp{};
+    cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
+    cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
+    cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
+    cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
+    cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
+    LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
+    if (dW_dtype == LCE_BF16) {
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
+                                v_begin + chunk_len, part_head, part_tail, stream));
+      LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
+                               chunk_len * H, stream));
+    }
+  }
+  if (dW_dtype == LCE_F32)
+    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
+                              static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, oh, W, gemm_scale, dX_dev,
+                             dX_dtype == LCE_BF16, stream));
+  return LCE_OK;
+}
+
+
 }  // namespace
 }  // namespace lce
 
@@ -329,46 +501,72 @@ lce_status lce_forward_ex(const void* X_dev, const void* W_dev, const int64_t* l
                           size_t workspace_bytes, void* stream_ptr) {
   if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
   if (!options_ok(opt) || !reduced_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
-  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !loss_dev || !lse_dev || !workspace_dev))
+  if (N > 0 && (!loss_dev || !lse_dev)) return LCE_ERR_INVALID_ARG;
+  if (!aligned(loss_dev, 4) || !aligned(lse_dev, 4) || !aligned(reduced_dev, 4) ||
+      !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
+    return LCE_ERR_ALIGNMENT;
+  FwdOut out{};
+  out.loss = loss_dev; out.lse = lse_dev; out.reduced = reduced_dev;
+  out.n_valid = n_valid_dev; out.bad_label = bad_label_dev;
+  return forward_impl(X_dev, W_dev, labels_dev, N, H, V, VocabRange{0, V}, opt, out,
+                      workspace_dev, workspace_bytes, stream_ptr);
+}
+
+lce_status lce_shard_forward(const void* X_dev, const void* W_shard_dev,
+                             const int64_t* labels_dev, int64_t N, int64_t H, int64_t V_shard,
+                             int64_t vocab_offset, int64_t vocab_total, const lce_options* opt,
+                             float* lse_part_dev, float* target_part_dev, float* zsum_part_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  if (!shape_ok(N, H, V_shard) || !range_ok(V_shard, vocab_offset, vocab_total))
+    return LCE_ERR_SHAPE;
+  if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!lse_part_dev || !target_part_dev)) return LCE_ERR_INVALID_ARG;
+  if (!aligned(lse_part_dev, 4) || !aligned(target_part_dev, 4) || !aligned(zsum_part_dev, 4))
+    return LCE_ERR_ALIGNMENT;
+  if (N == 0) return LCE_OK;
+  FwdOut out{};
+  out.lse = lse_part_dev; out.target = target_part_dev; out.zsum = zsum_part_dev;
+  return forward_impl(X_dev, W_shard_dev, labels_dev, N, H, V_shard,
+                      VocabRange{vocab_offset, vocab_total}, opt, out, workspace_dev,
+                      workspace_bytes, stream_ptr);
+}
+
+size_t lce_shard_merge_workspace_bytes(int64_t N) {
+  if (N < 0 || N >= INT_MAX) return 0;
+  return std::max<size_t>(align_up(sizeof(BlockStats) * (size_t)lse_finalize_blocks(std::max<int64_t>(N, 1))), kAlign);
+}
+
+lce_status lce_shard_merge(const float* lse_parts_dev, const float* target_parts_dev,
+                           const float* zsum_parts_dev, int32_t n_shards,
+                           const int64_t* labels_dev, int64_t N, int64_t vocab_total,
+                           const lce_options* opt, float* loss_dev, float* lse_dev,
+                           float* reduced_dev, int32_t* n_valid_dev, int32_t* bad_label_dev,
+                           void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  if (N < 0 || N >= INT_MAX || vocab_total < 1 || vocab_total >= INT_MAX) return LCE_ERR_SHAPE;
+  if (!options_ok(opt) || n_shards < 1 || !reduced_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!lse_parts_dev || !target_parts_dev || !labels_dev || !loss_dev || !lse_dev ||
+                !workspace_dev))
     return LCE_ERR_INVALID_ARG;
-  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
-      !aligned(workspace_dev, kAlign) || !aligned(loss_dev, 4) || !aligned(lse_dev, 4) ||
-      !aligned(reduced_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
+  const bool smoothing = opt->label_smoothing > 0.0f;
+  if (N > 0 && smoothing && !zsum_parts_dev) return LCE_ERR_INVALID_ARG;
+  if (!aligned(lse_parts_dev, 4) || !aligned(target_parts_dev, 4) || !aligned(zsum_parts_dev, 4) ||
+      !aligned(labels_dev, 8) || !aligned(loss_dev, 4) || !aligned(lse_dev, 4) ||
+      !aligned(reduced_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4) ||
+      !aligned(workspace_dev, kAlign))
     return LCE_ERR_ALIGNMENT;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   if (N == 0) {
     LCE_LAUNCH("empty_forward", stream, launch_empty_forward(reduced_dev, n_valid_dev, bad_label_dev, stream));
     return LCE_OK;
   }
-  const FwdPlan pl = plan_forward(N, H, V);
-  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
-
-  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
-  float* target = at<float>(workspace_dev, pl.off_target);
-  float* pm = at<float>(workspace_dev, pl.off_pm);
-  float* ps = at<float>(workspace_dev, pl.off_ps);
-  float* pz = at<float>(workspace_dev, pl.off_pz);
-  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
-  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
-  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
-  const bool smoothing = opt->label_smoothing > 0.0f;
-
-  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, opt->ignore_index, opt->softcap,
-                          opt->logit_scale, state, nullptr, target, nullptr, nullptr, stream));
-  LseParams lp{};
-  lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
-  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
-  lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
-  pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
-  lp.part_m = pm; lp.part_s = ps; lp.part_z = smoothing ? pz : nullptr;
-  LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
-  LossTerms terms{};
-  terms.one_minus_eps = 1.0f - opt->label_smoothing;
-  terms.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
-  terms.z_loss = opt->z_loss;
-  terms.part_z = smoothing ? pz : nullptr;
-  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, terms, lse_dev, loss_dev, blocks, stream));
-  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, opt->reduction == LCE_REDUCE_MEAN, reduced_dev, n_valid_dev, bad_label_dev, stream));
+  if (workspace_bytes < lce_shard_merge_workspace_bytes(N)) return LCE_ERR_WORKSPACE;
+  BlockStats* blocks = static_cast<BlockStats*>(workspace_dev);
+  const LossTerms terms = loss_terms(opt, vocab_total, nullptr);
+  LCE_LAUNCH("shard_merge", stream, launch_shard_merge(lse_parts_dev, target_parts_dev, smoothing ? zsum_parts_dev : nullptr,
+                               n_shards, labels_dev, N, vocab_total, opt->ignore_index, terms,
+                               lse_dev, loss_dev, blocks, stream));
+  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, lse_finalize_blocks(N), opt->reduction == LCE_REDUCE_MEAN,
+                                reduced_dev, n_valid_dev, bad_label_dev, stream));
   return LCE_OK;
 }
 
@@ -391,95 +589,23 @@ lce_status lce_backward_ex(const void* X_dev, const void* W_dev, const int64_t* 
                            void* dW_dev, lce_dtype dW_dtype, void* workspace_dev,
                            size_t workspace_bytes, void* stream_ptr) {
   if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
-  if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
-  if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
-    return LCE_ERR_INVALID_ARG;
-  if (!dW_dev) return LCE_ERR_INVALID_ARG;
-  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !lse_dev || !dloss_dev || !dX_dev ||
-                !workspace_dev))
-    return LCE_ERR_INVALID_ARG;
-  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
-      !aligned(lse_dev, 4) || !aligned(dloss_dev, 4) || !aligned(dX_dev, 16) ||
-      !aligned(dW_dev, 16) || !aligned(workspace_dev, kAlign))
-    return LCE_ERR_ALIGNMENT;
-  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const int64_t dw_bytes = V * H * (dW_dtype == LCE_BF16 ? 2 : 4);
-  if (N == 0) {
-    LCE_LAUNCH("fill_zero", stream, launch_fill_zero(dW_dev, dw_bytes, stream));
-    return LCE_OK;
-  }
-  const BwdPlan pl = plan_backward(N, H, V, dW_dtype);
-  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+  return backward_impl(X_dev, W_dev, labels_dev, lse_dev, dloss_dev, N, H, V, VocabRange{0, V},
+                       opt, dX_dev, dX_dtype, dW_dev, dW_dtype, workspace_dev, workspace_bytes,
+                       stream_ptr);
+}
 
-  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
-  int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
-  float* deriv = at<float>(workspace_dev, pl.off_deriv);
-  float* gs = at<float>(workspace_dev, pl.off_gs);
-  float* c1 = at<float>(workspace_dev, pl.off_c1);
-  float* oh = at<float>(workspace_dev, pl.off_oh);
-  uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
-  uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
-  const uint64_t* keys = sort_passes(N) % 2 == 0 ? keys_a : keys_b;   // where the sort ends
-  float* part_head = at<float>(workspace_dev, pl.off_head);
-  float* part_tail = at<float>(workspace_dev, pl.off_tail);
-  BlockStats* blocks = at<BlockStats>(workspace_dev, pl.off_blocks);
-  float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] plain scale, [1] = 1
-  int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
-  uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
-  float* dXp = at<float>(workspace_dev, pl.off_dXp);
-  float* dWs = at<float>(workspace_dev, pl.off_dWs);
-  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
-  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
-  // The plain path stores G = p·d and applies one scalar scale afterwards; label
-  // smoothing, Z-loss or a per-row upstream gradient need G scaled row by row.
-  const bool general = opt->label_smoothing > 0.0f || opt->z_loss > 0.0f ||
-                       opt->reduction == LCE_REDUCE_NONE;
-  const float* gemm_scale = general ? scalars + 1 : scalars;
-
-  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, opt->ignore_index, opt->softcap,
-                          opt->logit_scale, state, key, nullptr, deriv, blocks, stream));
-  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(blocks, pl.nb_prep, dloss_dev, opt->reduction == LCE_REDUCE_MEAN,
-                                opt->logit_scale, scalars, counts, stream));
-  LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
-                          scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
-                          general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
-  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
-
-  for (int c = 0; c < pl.nchunks; ++c) {
-    const int64_t v_begin = (int64_t)c * pl.Vc;
-    const int64_t chunk_len = std::min<int64_t>(pl.Vc, V - v_begin);
-    const int n_vt = (int)ceil_div(chunk_len, kTile);
-
-    GradParams gp{};
-    gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
-    gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
-    gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
-    pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
-    gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
-    gp.gs = general ? gs : nullptr; gp.c1 = c1;
-    gp.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
-    LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
-
-    ChunkGemmParams cp{};
-    cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
-    cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
-    cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
-    cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
-    cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
-    LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
-    if (dW_dtype == LCE_BF16) {
-      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
-                                v_begin + chunk_len, part_head, part_tail, stream));
-      LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
-                               chunk_len * H, stream));
-    }
-  }
-  if (dW_dtype == LCE_F32)
-    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
-                              static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, oh, W, gemm_scale, dX_dev,
-                             dX_dtype == LCE_BF16, stream));
-  return LCE_OK;
+lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
+                              const int64_t* labels_dev, const float* lse_dev,
+                              const float* dloss_dev, int64_t N, int64_t H, int64_t V_shard,
+                              int64_t vocab_offset, int64_t vocab_total, const lce_options* opt,
+                              void* dX_part_dev, lce_dtype dX_dtype, void* dW_shard_dev,
+                              lce_dtype dW_dtype, void* workspace_dev, size_t workspace_bytes,
+                              void* stream_ptr) {
+  if (!shape_ok(N, H, V_shard) || !range_ok(V_shard, vocab_offset, vocab_total))
+    return LCE_ERR_SHAPE;
+  return backward_impl(X_dev, W_shard_dev, labels_dev, lse_dev, dloss_dev, N, H, V_shard,
+                       VocabRange{vocab_offset, vocab_total}, opt, dX_part_dev, dX_dtype,
+                       dW_shard_dev, dW_dtype, workspace_dev, workspace_bytes, stream_ptr);
 }
 
 }  // extern "C"

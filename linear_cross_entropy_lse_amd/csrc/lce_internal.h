@@ -66,12 +66,25 @@ hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream);
 // Row-wise kernels (lce_rows.hip).
 struct BlockStats {  // per-block partial of the row scan, combined in a fixed order
   double loss_sum;
-  int32_t n_valid;
-  int32_t n_bad;
+  int32_t n_valid;   // rows with label != ignore_index
+  int32_t n_bad;     // ... whose label is outside [0, V_total)
+  int32_t n_owned;   // valid rows whose label lies in this call's vocabulary rows
+  int32_t pad;
 };
 
+// Vocabulary rows a call works on: W holds rows [v_lo, v_lo + V) of a
+// vocabulary of V_total rows (v_lo = 0, V_total = V without sharding).
+struct VocabRange {
+  int64_t v_lo;
+  int64_t V_total;
+};
+
+// Labels are checked against [0, V_total); a valid row is "owned" when its
+// label lies in [v_lo, v_lo + V).  Owned rows get the target logit, its
+// softcap derivative and the local label (y − v_lo) as sort key; other rows
+// get target 0, derivative 0 and key INT_MAX.
 hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* labels,
-                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           int64_t N, int64_t H, int64_t V, VocabRange vr, int64_t ignore_index,
                            float softcap, float logit_scale, int32_t* row_state,
                            int32_t* row_key, float* target, float* target_deriv,
                            BlockStats* blocks, hipStream_t stream);
@@ -85,18 +98,31 @@ struct LossTerms {
   const float* part_z;   // [S, N] or null (e = 0)
 };
 
+// loss and blocks may be null (a vocabulary shard's partials need neither);
+// zsum, when not null, receives the merged Σ_v z_v of each row (needs
+// terms.part_z).
 hipError_t launch_lse_finalize(const float* part_m, const float* part_s, int S, int64_t N,
                                const int32_t* row_state, const float* target,
                                const LossTerms& terms, float* lse, float* loss,
-                               BlockStats* blocks, hipStream_t stream);
+                               BlockStats* blocks, float* zsum, hipStream_t stream);
 int lse_finalize_blocks(int64_t N);
+
+// Merge of g vocabulary shards' row partials, in shard order: lse_parts,
+// target_parts and zsum_parts are [g, N] (zsum_parts may be null when
+// terms.eps_over_v is 0).  Writes lse, loss and per-block statistics like
+// lse_finalize; labels are checked against [0, V_total).
+hipError_t launch_shard_merge(const float* lse_parts, const float* target_parts,
+                              const float* zsum_parts, int g, const int64_t* labels, int64_t N,
+                              int64_t V_total, int64_t ignore_index, const LossTerms& terms,
+                              float* lse, float* loss, BlockStats* blocks, hipStream_t stream);
 
 // reduced = Σ loss / n_valid (divide = 1) or Σ loss (divide = 0).
 hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, int divide, float* reduced,
                                 int32_t* n_valid, int32_t* bad_flag, hipStream_t stream);
 
 // scalars[0] = a·dloss / n_valid (divide = 1) or a·dloss (divide = 0), the
-// upstream scale of the plain path; scalars[1] = 1.  counts as below.
+// upstream scale of the plain path; scalars[1] = 1.  counts[0] = n_valid,
+// counts[1] = owned rows (the rows that get sorted).
 hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const float* dloss,
                                  int divide, float logit_scale, float* scalars, int32_t* counts,
                                  hipStream_t stream);
@@ -119,7 +145,8 @@ int sort_passes(int64_t N);        // merge passes after the block sort
 hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* keys_a,
                                 uint64_t* keys_b, hipStream_t stream);
 
-// dX_i = sx·dX_acc_i − oh_i·w_{y_i} (valid rows), 0 (ignored), NaN (bad).
+// dX_i = sx·dX_acc_i − oh_i·w_{key_i} (owned rows), sx·dX_acc_i (valid rows
+// whose label lies in another shard), 0 (ignored), NaN (bad).
 hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
                               const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,

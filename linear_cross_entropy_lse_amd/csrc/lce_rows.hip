@@ -28,33 +28,37 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---------------------------------------------------------------------------
 // Row classification and the target logit.  One wave per row.
-//   row_state:    0 ignored, 1 valid, 2 label out of range
-//   row_key:      label for valid rows, INT_MAX otherwise (sort key)
-//   target:       scaled, softcapped target logit (valid rows), else 0
-//   target_deriv: 1 − tanh²(t_raw / c) at the target (1 without softcap),
-//                 t_raw = a·(x_i · w_{y_i})
-//   blocks:       per-block counts of non-ignored and bad rows
+//   row_state:    0 ignored, 1 valid, 2 label outside [0, V_total)
+//   row_key:      y − v_lo for owned rows (valid, label in this call's
+//                 vocabulary rows), INT_MAX otherwise (sort key)
+//   target:       scaled, softcapped target logit (owned rows), else 0
+//   target_deriv: 1 − tanh²(t_raw / c) at the target (1 without softcap) for
+//                 owned rows, else 0; t_raw = a·(x_i · w_{y_i})
+//   blocks:       per-block counts of non-ignored, bad and owned rows
 // ---------------------------------------------------------------------------
 constexpr int kRowsPerPrepBlock = 4;
 
 __global__ void __launch_bounds__(256)
 row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                 const int64_t* __restrict__ labels, int64_t N, int64_t H, int64_t V,
-                int64_t ignore_index, float softcap, float logit_scale,
+                VocabRange vr, int64_t ignore_index, float softcap, float logit_scale,
                 int32_t* __restrict__ row_state, int32_t* __restrict__ row_key,
                 float* __restrict__ target, float* __restrict__ target_deriv,
                 BlockStats* __restrict__ blocks) {
-  __shared__ int counts[kRowsPerPrepBlock][2];
+  __shared__ int counts[kRowsPerPrepBlock][3];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerPrepBlock + wave;
   int st = kRowIgnored;
+  bool owned = false;
   if (row < N) {
     const int64_t y = labels[row];
-    st = (y == ignore_index) ? kRowIgnored : ((y >= 0 && y < V) ? kRowValid : kRowBad);
-    float t = 0.0f, d = 1.0f;
-    if (st == kRowValid) {
+    st = (y == ignore_index) ? kRowIgnored : ((y >= 0 && y < vr.V_total) ? kRowValid : kRowBad);
+    const int64_t yl = y - vr.v_lo;
+    owned = st == kRowValid && yl >= 0 && yl < V;
+    float t = 0.0f, d = 0.0f;
+    if (owned) {
       const uint16_t* xr = X + row * H;
-      const uint16_t* wr = W + y * H;
+      const uint16_t* wr = W + yl * H;
       float dot = 0.0f;
       for (int64_t c = lane; c < H / 8; c += 64) {
         const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c * 8);
@@ -72,11 +76,12 @@ row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
         d = 1.0f - th * th;
       } else {
         t = dot;
+        d = 1.0f;
       }
     }
     if (lane == 0) {
       row_state[row] = st;
-      if (row_key) row_key[row] = (st == kRowValid) ? (int32_t)y : INT_MAX;
+      if (row_key) row_key[row] = owned ? (int32_t)yl : INT_MAX;
       if (target) target[row] = t;
       if (target_deriv) target_deriv[row] = d;
     }
@@ -84,24 +89,29 @@ row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
   if (lane == 0) {
     counts[wave][0] = (st != kRowIgnored);
     counts[wave][1] = (st == kRowBad);
+    counts[wave][2] = owned;
   }
   __syncthreads();
   if (threadIdx.x == 0 && blocks) {
-    int nv = 0, nb = 0;
-    for (int w = 0; w < kRowsPerPrepBlock; ++w) { nv += counts[w][0]; nb += counts[w][1]; }
-    blocks[blockIdx.x] = BlockStats{0.0, nv, nb};
+    int nv = 0, nb = 0, no = 0;
+    for (int w = 0; w < kRowsPerPrepBlock; ++w) {
+      nv += counts[w][0];
+      nb += counts[w][1];
+      no += counts[w][2];
+    }
+    blocks[blockIdx.x] = BlockStats{0.0, nv, nb, no, 0};
   }
 }
 
 int row_prep_blocks(int64_t N) { return (int)((N + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock); }
 
 hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* labels,
-                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           int64_t N, int64_t H, int64_t V, VocabRange vr, int64_t ignore_index,
                            float softcap, float logit_scale, int32_t* row_state,
                            int32_t* row_key, float* target, float* target_deriv,
                            BlockStats* blocks, hipStream_t stream) {
   hipLaunchKernelGGL(row_prep_kernel, dim3(row_prep_blocks(N)), dim3(256), 0, stream, X, W,
-                     labels, N, H, V, ignore_index, softcap, logit_scale, row_state, row_key,
+                     labels, N, H, V, vr, ignore_index, softcap, logit_scale, row_state, row_key,
                      target, target_deriv, blocks);
   return hipGetLastError();
 }
@@ -114,47 +124,21 @@ hipError_t launch_row_prep(const uint16_t* X, const uint16_t* W, const int64_t* 
 // ---------------------------------------------------------------------------
 constexpr int kFinThreads = 256;
 
-__global__ void __launch_bounds__(kFinThreads)
-lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ part_s, int S,
-                    int64_t N, const int32_t* __restrict__ row_state,
-                    const float* __restrict__ target, LossTerms terms,
-                    float* __restrict__ lse_out, float* __restrict__ loss_out,
-                    BlockStats* __restrict__ blocks) {
+// Loss of one row from its LSE, target logit t and logit sum zs.
+__device__ __forceinline__ float row_loss(int st, float lse, float t, float zs,
+                                          const LossTerms& terms) {
+  if (st == kRowBad) return __builtin_nanf("");
+  if (st != kRowValid) return 0.0f;
+  float l = fmaf(-terms.one_minus_eps, t, lse);
+  if (terms.eps_over_v != 0.0f) l = fmaf(-terms.eps_over_v, zs, l);
+  return fmaf(terms.z_loss * lse, lse, l);
+}
+
+// Fixed-shape tree over the block's rows; thread 0 stores the block's total.
+__device__ void store_block_stats(double lossv, int nv, int nb, BlockStats* __restrict__ blocks) {
   __shared__ double ssum[kFinThreads];
   __shared__ int scnt[kFinThreads][2];
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * kFinThreads + tid;
-  double lossv = 0.0;
-  int nv = 0, nb = 0;
-  if (row < N) {
-    const float NEG_INF = -__builtin_inff();
-    float m = NEG_INF;
-    for (int s = 0; s < S; ++s) m = fmaxf(m, part_m[(int64_t)s * N + row]);
-    float sum = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = part_m[(int64_t)s * N + row];
-      if (ms != NEG_INF) sum += part_s[(int64_t)s * N + row] * exp2f(ms - m);
-    }
-    const float lse = (m + log2f(sum)) * kLn2;
-    const int st = row_state[row];
-    float l = 0.0f;
-    if (st == kRowValid) {
-      l = fmaf(-terms.one_minus_eps, target[row], lse);
-      if (terms.part_z) {
-        float zs = 0.0f;
-        for (int s = 0; s < S; ++s) zs += terms.part_z[(int64_t)s * N + row];
-        l = fmaf(-terms.eps_over_v, zs, l);
-      }
-      l = fmaf(terms.z_loss * lse, lse, l);
-    } else if (st == kRowBad) {
-      l = __builtin_nanf("");
-    }
-    lse_out[row] = lse;
-    loss_out[row] = l;
-    lossv = (double)l;
-    nv = st != kRowIgnored;
-    nb = st == kRowBad;
-  }
   ssum[tid] = lossv;
   scnt[tid][0] = nv;
   scnt[tid][1] = nb;
@@ -167,7 +151,41 @@ lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ 
     }
     __syncthreads();
   }
-  if (tid == 0) blocks[blockIdx.x] = BlockStats{ssum[0], scnt[0][0], scnt[0][1]};
+  if (tid == 0) blocks[blockIdx.x] = BlockStats{ssum[0], scnt[0][0], scnt[0][1], 0, 0};
+}
+
+__global__ void __launch_bounds__(kFinThreads)
+lse_finalize_kernel(const float* __restrict__ part_m, const float* __restrict__ part_s, int S,
+                    int64_t N, const int32_t* __restrict__ row_state,
+                    const float* __restrict__ target, LossTerms terms,
+                    float* __restrict__ lse_out, float* __restrict__ loss_out,
+                    BlockStats* __restrict__ blocks, float* __restrict__ zsum_out) {
+  const int64_t row = (int64_t)blockIdx.x * kFinThreads + threadIdx.x;
+  double lossv = 0.0;
+  int nv = 0, nb = 0;
+  if (row < N) {
+    const float NEG_INF = -__builtin_inff();
+    float m = NEG_INF;
+    for (int s = 0; s < S; ++s) m = fmaxf(m, part_m[(int64_t)s * N + row]);
+    float sum = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = part_m[(int64_t)s * N + row];
+      if (ms != NEG_INF) sum += part_s[(int64_t)s * N + row] * exp2f(ms - m);
+    }
+    const float lse = (m + log2f(sum)) * kLn2;
+    float zs = 0.0f;
+    if (terms.part_z)
+      for (int s = 0; s < S; ++s) zs += terms.part_z[(int64_t)s * N + row];
+    const int st = row_state[row];
+    const float l = row_loss(st, lse, target[row], zs, terms);
+    lse_out[row] = lse;
+    if (loss_out) loss_out[row] = l;
+    if (zsum_out) zsum_out[row] = zs;
+    lossv = (double)l;
+    nv = st != kRowIgnored;
+    nb = st == kRowBad;
+  }
+  if (blocks) store_block_stats(lossv, nv, nb, blocks);
 }
 
 int lse_finalize_blocks(int64_t N) { return (int)((N + kFinThreads - 1) / kFinThreads); }
@@ -175,48 +193,106 @@ int lse_finalize_blocks(int64_t N) { return (int)((N + kFinThreads - 1) / kFinTh
 hipError_t launch_lse_finalize(const float* part_m, const float* part_s, int S, int64_t N,
                                const int32_t* row_state, const float* target,
                                const LossTerms& terms, float* lse, float* loss,
-                               BlockStats* blocks, hipStream_t stream) {
+                               BlockStats* blocks, float* zsum, hipStream_t stream) {
   hipLaunchKernelGGL(lse_finalize_kernel, dim3(lse_finalize_blocks(N)), dim3(kFinThreads), 0,
-                     stream, part_m, part_s, S, N, row_state, target, terms, lse, loss, blocks);
+                     stream, part_m, part_s, S, N, row_state, target, terms, lse, loss, blocks,
+                     zsum);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Merge of vocabulary shards (AI-infra KB page M011, §07: with the vocabulary
+// split over ranks the max, exp-sum and target score of a row are made global
+// before its loss is formed; §05: the (max, sum-exp) merge, here with one
+// block per shard).  Shard k reports its row LSE L_k = log Σ_{v in k} e^{z_v}
+// (natural log), its target part (the target logit on the owning shard, else
+// 0) and its logit sum; they are combined in shard order:
+//   LSE = m + log Σ_k e^{L_k − m},  m = max_k L_k;  t = Σ_k t_k;  Σz = Σ_k zs_k.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kFinThreads)
+shard_merge_kernel(const float* __restrict__ lse_parts, const float* __restrict__ target_parts,
+                   const float* __restrict__ zsum_parts, int g, const int64_t* __restrict__ labels,
+                   int64_t N, int64_t V_total, int64_t ignore_index, LossTerms terms,
+                   float* __restrict__ lse_out, float* __restrict__ loss_out,
+                   BlockStats* __restrict__ blocks) {
+  const int64_t row = (int64_t)blockIdx.x * kFinThreads + threadIdx.x;
+  double lossv = 0.0;
+  int nv = 0, nb = 0;
+  if (row < N) {
+    const float NEG_INF = -__builtin_inff();
+    float m = NEG_INF;
+    for (int k = 0; k < g; ++k) m = fmaxf(m, lse_parts[(int64_t)k * N + row]);
+    float sum = 0.0f, t = 0.0f, zs = 0.0f;
+    for (int k = 0; k < g; ++k) {
+      const float lk = lse_parts[(int64_t)k * N + row];
+      if (lk != NEG_INF) sum += exp2f((lk - m) * kLog2e);
+      t += target_parts[(int64_t)k * N + row];
+      if (zsum_parts) zs += zsum_parts[(int64_t)k * N + row];
+    }
+    const float lse = m == NEG_INF ? NEG_INF : m + log2f(sum) * kLn2;
+    const int64_t y = labels[row];
+    const int st = (y == ignore_index) ? kRowIgnored
+                                       : ((y >= 0 && y < V_total) ? kRowValid : kRowBad);
+    const float l = row_loss(st, lse, t, zs, terms);
+    lse_out[row] = lse;
+    loss_out[row] = l;
+    lossv = (double)l;
+    nv = st != kRowIgnored;
+    nb = st == kRowBad;
+  }
+  store_block_stats(lossv, nv, nb, blocks);
+}
+
+hipError_t launch_shard_merge(const float* lse_parts, const float* target_parts,
+                              const float* zsum_parts, int g, const int64_t* labels, int64_t N,
+                              int64_t V_total, int64_t ignore_index, const LossTerms& terms,
+                              float* lse, float* loss, BlockStats* blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(shard_merge_kernel, dim3(lse_finalize_blocks(N)), dim3(kFinThreads), 0,
+                     stream, lse_parts, target_parts, zsum_parts, g, labels, N, V_total,
+                     ignore_index, terms, lse, loss, blocks);
   return hipGetLastError();
 }
 
 // Fixed-order reduction of the block statistics by one workgroup.
 __device__ void reduce_blocks(const BlockStats* __restrict__ blocks, int nblocks, double& sum,
-                              int& nv, int& nb) {
+                              int& nv, int& nb, int& no) {
   __shared__ double ssum[256];
-  __shared__ int scnt[256][2];
+  __shared__ int scnt[256][3];
   const int tid = threadIdx.x;
   double a = 0.0;
-  int v = 0, b = 0;
+  int v = 0, b = 0, w = 0;
   for (int i = tid; i < nblocks; i += 256) {
     a += blocks[i].loss_sum;
     v += blocks[i].n_valid;
     b += blocks[i].n_bad;
+    w += blocks[i].n_owned;
   }
   ssum[tid] = a;
   scnt[tid][0] = v;
   scnt[tid][1] = b;
+  scnt[tid][2] = w;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (tid < o) {
       ssum[tid] += ssum[tid + o];
       scnt[tid][0] += scnt[tid + o][0];
       scnt[tid][1] += scnt[tid + o][1];
+      scnt[tid][2] += scnt[tid + o][2];
     }
     __syncthreads();
   }
   sum = ssum[0];
   nv = scnt[0][0];
   nb = scnt[0][1];
+  no = scnt[0][2];
 }
 
 __global__ void __launch_bounds__(256)
 mean_finalize_kernel(const BlockStats* __restrict__ blocks, int nblocks, int divide,
                      float* reduced, int32_t* n_valid, int32_t* bad_flag) {
   double sum;
-  int nv, nb;
-  reduce_blocks(blocks, nblocks, sum, nv, nb);
+  int nv, nb, no;
+  reduce_blocks(blocks, nblocks, sum, nv, nb, no);
   if (threadIdx.x == 0) {
     if (divide) *reduced = nv > 0 ? (float)(sum / (double)nv) : 0.0f;
     else *reduced = (float)sum;
@@ -234,21 +310,21 @@ hipError_t launch_mean_finalize(const BlockStats* blocks, int nblocks, int divid
 
 // scalars[0] = a·dloss / n_valid (divide; 0 when no row has a target) or
 // a·dloss, the upstream scale of the plain gradient path; scalars[1] = 1.
-// counts[0] = n_valid, counts[1] = valid rows with an in-range label (the rows
-// that get sorted).
+// counts[0] = n_valid, counts[1] = owned rows (valid, label among this call's
+// vocabulary rows: the rows that get sorted).
 __global__ void __launch_bounds__(256)
 scale_finalize_kernel(const BlockStats* __restrict__ blocks, int nblocks,
                       const float* __restrict__ dloss, int divide, float logit_scale,
                       float* scalars, int32_t* counts) {
   double sum;
-  int nv, nb;
-  reduce_blocks(blocks, nblocks, sum, nv, nb);
+  int nv, nb, no;
+  reduce_blocks(blocks, nblocks, sum, nv, nb, no);
   if (threadIdx.x == 0) {
     const float base = divide ? (nv > 0 ? __fdiv_rn(*dloss, (float)nv) : 0.0f) : *dloss;
     scalars[0] = base * logit_scale;
     scalars[1] = 1.0f;
     counts[0] = nv;
-    counts[1] = nv - nb;
+    counts[1] = no;
   }
 }
 
@@ -384,17 +460,24 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
   const int st = row_state[row];
   const float s = *sx;
   const float e = oh[row];
-  const int64_t y = (st == kRowValid) ? row_key[row] : 0;
+  const int32_t key = st == kRowValid ? row_key[row] : INT_MAX;
+  const bool owned = key != INT_MAX;          // the label is one of W's rows
+  const int64_t y = owned ? key : 0;
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (st == kRowValid) {
       const float4 v = *reinterpret_cast<const float4*>(dX_acc + row * H + h);
       const float a[4] = {v.x, v.y, v.z, v.w};
-      const u32x2 wv = *reinterpret_cast<const u32x2*>(W + y * H + h);
-      const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
-                           __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
+      if (owned) {
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(W + y * H + h);
+        const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
+                             __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = fmaf(s, a[q], -e * w4[q]);
+        for (int q = 0; q < 4; ++q) o[q] = fmaf(s, a[q], -e * w4[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = s * a[q];
+      }
     } else if (st == kRowBad) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __builtin_nanf("");

@@ -142,3 +142,44 @@ def test_ex_null_options_and_shapes(lib):
     o = opts()
     assert fwd_ex(lib, ctypes.byref(o), H=12) == _lib.LCE_ERR_SHAPE
     assert bwd_ex(lib, ctypes.byref(o), V=0) == _lib.LCE_ERR_SHAPE
+
+
+# Vocabulary-shard calls: argument checks that return before any launch.
+
+
+def shard_fwd(lib, o, N=8, H=16, Vs=10, off=0, total=40, lse=FAKE, tgt=FAKE, zs=None):
+    return lib.lce_shard_forward(FAKE, FAKE, FAKE, N, H, Vs, off, total, o, lse, tgt, zs,
+                                 FAKE, 1 << 20, None)
+
+
+def shard_bwd(lib, o, N=8, H=16, Vs=10, off=0, total=40):
+    return lib.lce_shard_backward(FAKE, FAKE, FAKE, FAKE, FAKE, N, H, Vs, off, total, o, FAKE,
+                                  _lib.LCE_F32, FAKE, _lib.LCE_F32, FAKE, 1 << 30, None)
+
+
+def shard_merge(lib, o, g=2, N=8, total=40, zs=None):
+    return lib.lce_shard_merge(FAKE, FAKE, zs, g, FAKE, N, total, o, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, 1 << 20, None)
+
+
+@pytest.mark.parametrize("off,Vs,total", [(-1, 10, 40), (31, 10, 40), (0, 10, 9),
+                                          (0, 10, 1 << 31)])
+def test_shard_calls_reject_bad_vocabulary_ranges(lib, off, Vs, total):
+    o = opts()
+    assert shard_fwd(lib, ctypes.byref(o), Vs=Vs, off=off, total=total) == _lib.LCE_ERR_SHAPE
+    assert shard_bwd(lib, ctypes.byref(o), Vs=Vs, off=off, total=total) == _lib.LCE_ERR_SHAPE
+
+
+def test_shard_calls_argument_checks(lib):
+    o = opts()
+    assert shard_fwd(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    assert shard_fwd(lib, ctypes.byref(o), lse=None) == _lib.LCE_ERR_INVALID_ARG
+    assert shard_fwd(lib, ctypes.byref(o), tgt=FAKE + 2) == _lib.LCE_ERR_ALIGNMENT
+    assert shard_fwd(lib, ctypes.byref(o), N=0, lse=None, tgt=None) == _lib.LCE_OK
+    assert shard_bwd(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    assert shard_merge(lib, ctypes.byref(o), g=0) == _lib.LCE_ERR_INVALID_ARG
+    assert shard_merge(lib, ctypes.byref(o), total=0) == _lib.LCE_ERR_SHAPE
+    smooth = opts(label_smoothing=0.1)
+    assert shard_merge(lib, ctypes.byref(smooth)) == _lib.LCE_ERR_INVALID_ARG   # no Σz parts
+    assert lib.lce_shard_merge_workspace_bytes(-1) == 0
+    assert lib.lce_shard_merge_workspace_bytes(1 << 20) >= 4096 * 24
