@@ -436,3 +436,63 @@ def backward_shard(X: np.ndarray, W_shard: np.ndarray, labels: np.ndarray, lse: 
     dZ = dZ * softcap_derivative(Z, c) * a * scale[:, None]
     dZ[bad_mask(labels, V_total, ignore_index)] = np.nan
     return dZ @ W_shard, dZ.T @ X
+
+
+# --------------------------------------------------------------------------- #
+# Row-chunked forward with the gradient formed in the same pass (reading R18)
+# --------------------------------------------------------------------------- #
+# [CCE-blog] §二 (the FLCE pipeline of Liger, also [Liger] §3.2): the rows are
+# cut into chunks; for each chunk the logits block is formed, its loss is
+# computed and the logit gradient is written in place of the logits, then
+# projected back at once (dX rows = dZ_chunk · W, dW accumulated over the
+# chunks) before the next chunk starts.  The gradient needs the upstream
+# scalar, which the pages apply in the real backward.
+#   R18 the upstream gradient (scalar, or one value per row for "none") is an
+#       input of the fused call, so dX and dW come out fully scaled; the
+#       result equals forward_ex followed by backward_ex for every chunk
+#       size (the chunking only changes the schedule).
+def forward_backward_chunked(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
+                             opts: Dict[str, object], chunk_rows: int):
+    """(forward dict, dX, dW) computed chunk by chunk of `chunk_rows` rows."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, V = X.shape[0], W.shape[0]
+    ignore_index = int(opts["ignore_index"])
+    a, c = float(opts["logit_scale"]), float(opts["softcap"])
+    e, lam = float(opts["label_smoothing"]), float(opts["z_loss"])
+    valid = valid_mask(labels, ignore_index)
+    bad = bad_mask(labels, V, ignore_index)
+    n_valid = int(valid.sum())          # known before the first chunk (R4)
+    scale = row_scale(labels, dloss, n_valid, opts)
+    lse = np.zeros(N)
+    loss = np.zeros(N)
+    dX = np.zeros_like(X)
+    dW = np.zeros_like(W)
+    for r0 in range(0, N, max(1, int(chunk_rows))):
+        r1 = min(N, r0 + max(1, int(chunk_rows)))
+        Xb, yb = X[r0:r1], labels[r0:r1]
+        Z = a * logits(Xb, W)                        # the chunk's logits block
+        Zc = apply_softcap(Z, c)
+        lse_b = row_logsumexp(Zc)
+        ok = valid[r0:r1] & ~bad[r0:r1]
+        t = np.zeros(r1 - r0)
+        t[ok] = Zc[np.nonzero(ok)[0], yb[ok]]
+        l_b = lse_b - (1.0 - e) * t - (e / V) * Zc.sum(axis=1) + lam * lse_b * lse_b
+        l_b = np.where(valid[r0:r1], l_b, 0.0)
+        l_b[bad[r0:r1]] = np.nan
+        lse[r0:r1], loss[r0:r1] = lse_b, l_b
+        # The gradient takes the place of the logits block.
+        onehot = (yb[:, None] == np.arange(V)[None, :]).astype(np.float64)
+        G = (1.0 + 2.0 * lam * lse_b)[:, None] * np.exp(Zc - lse_b[:, None]) \
+            - (1.0 - e) * onehot - e / V
+        G = G * softcap_derivative(Z, c) * a * scale[r0:r1, None]
+        G[bad[r0:r1]] = np.nan
+        dX[r0:r1] = G @ W
+        dW += G.T @ Xb
+    total = loss.sum()
+    if opts["reduction"] == "mean":
+        reduced = total / n_valid if n_valid > 0 else 0.0
+    else:
+        reduced = total
+    return {"lse": lse, "loss": loss, "n_valid": n_valid, "reduced": reduced}, dX, dW

@@ -285,3 +285,60 @@ def test_shard_pins_catch_mutation(name, monkeypatch):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# --------------------------------------------------------------------------- #
+# Row-chunked forward with gradient: planted mistakes must be caught by its
+# pins.
+# --------------------------------------------------------------------------- #
+from tests import test_oracle_fused as PF  # noqa: E402
+
+FUSED_PINS = [
+    lambda: PF.test_matches_torch_autograd(0.0),
+    lambda: PF.test_equals_forward_then_backward(PF.OPTS[1], 4),
+    lambda: PF.test_equals_forward_then_backward(PF.OPTS[0], 11),
+]
+
+_orig_fused = O.forward_backward_chunked
+
+
+def _fused_dw_overwritten(X, W, labels, dloss, opts, chunk_rows):
+    # dW keeps only the last chunk's contribution.
+    N = len(labels)
+    last0 = (N - 1) // chunk_rows * chunk_rows
+    f, dX, _ = _orig_fused(X, W, labels, dloss, opts, chunk_rows)
+    _, _, dW_last = _orig_fused(np.asarray(X)[last0:], W, np.asarray(labels)[last0:],
+                                dloss, opts, chunk_rows)
+    return f, dX, dW_last
+
+
+def _fused_mean_per_chunk(X, W, labels, dloss, opts, chunk_rows):
+    # Each chunk normalised by its own valid count instead of the batch's.
+    labels = np.asarray(labels)
+    outs = []
+    for r0 in range(0, len(labels), chunk_rows):
+        outs.append(_orig_fused(np.asarray(X)[r0:r0 + chunk_rows], W, labels[r0:r0 + chunk_rows],
+                                dloss, opts, chunk_rows))
+    f = _orig_fused(X, W, labels, dloss, opts, chunk_rows)[0]
+    dX = np.concatenate([o[1] for o in outs])
+    dW = sum(o[2] for o in outs)
+    return f, dX, dW
+
+
+FUSED_MUTATIONS = {
+    "dw_not_accumulated": ("forward_backward_chunked", _fused_dw_overwritten),
+    "mean_per_chunk": ("forward_backward_chunked", _fused_mean_per_chunk),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_MUTATIONS))
+def test_fused_pins_catch_mutation(name, monkeypatch):
+    attr, fn = FUSED_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in FUSED_PINS:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
