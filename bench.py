@@ -48,6 +48,8 @@ def parse():
                     help="run one plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--shards", type=int, default=8,
                     help="also time one vocabulary shard of V/shards rows (0: skip)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip timing the row-chunked forward-and-backward call")
     return ap.parse_args()
 
 
@@ -157,6 +159,52 @@ def time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, 
             "tokens_per_s": round(N / (ms / 1e3), 1), "tflops": round(tf, 1),
             "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4),
             "note": "one rank's shard forward + shard backward, collectives excluded"}
+
+
+def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, sptr,
+               stream):
+    """The row-chunked call that forms the gradient in the forward pass (three
+    N·H·V contractions), on the same inputs, timed apart from the step."""
+    import ctypes
+    import torch
+    import lce_inputs as L
+    N, H, V = w.N, w.H, w.V
+    opt = _lib.make_options(L.IGNORE_INDEX, float(w.softcap))
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+    ws_n = lib.lce_fused_workspace_bytes(N, H, V, gcode)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=X.device)
+
+    def fstep():
+        st = lib.lce_forward_backward(X.data_ptr(), W.data_ptr(), y.data_ptr(), dloss.data_ptr(),
+                                      N, H, V, ctypes.byref(opt), loss.data_ptr(), lse.data_ptr(),
+                                      mean.data_ptr(), nval.data_ptr(), bad.data_ptr(),
+                                      dX.data_ptr(), gcode, dW.data_ptr(), gcode, ws.data_ptr(),
+                                      ws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_forward_backward: {_lib.status_string(st)}")
+
+    log("[bench] row-chunked forward-and-backward call")
+    for _ in range(args.warmup):
+        fstep()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        fstep()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    del ws
+    return {"ms_per_step": round(ms, 3),
+            "ms_per_step_median_q20_q80": [round(q, 3) for q in quantiles(step_ms)],
+            "tokens_per_s": round(N / (ms / 1e3), 1),
+            "tflops_8nhv": round(8 * N * H * V / (ms / 1e3) / 1e12, 1),
+            "tflops_executed_6nhv": round(6 * N * H * V / (ms / 1e3) / 1e12, 1),
+            "workspace_bytes": int(ws_n),
+            "mean_loss": float(mean.item()),
+            "note": "lce_forward_backward: row chunks of at most H rows, logits block kept in "
+                    "bf16, gradient formed in the forward pass; not the headline path"}
 
 
 def main():
@@ -269,6 +317,12 @@ def main():
         if k in kernels:
             per_kernel[k]["tflops"] = round(units * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
 
+    headline_mean = float(mean.item())
+    fused = None
+    if not args.no_fused:
+        fused = time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode,
+                           sptr, stream)
+
     shard = None
     if args.shards > 1:
         shard = time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, sptr,
@@ -300,6 +354,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "vocab_shard": shard,
+        "fused_row_chunk": fused,
         "kernels": per_kernel,
         "memory_bytes": {"peak_allocated": int(peak_mem),
                          "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),
@@ -308,7 +363,7 @@ def main():
                          "workspace_forward": int(fws_n), "workspace_backward": int(bws_n),
                          "bf16_logits_never_allocated": int(N * V * 2)},
         "kernel_source_hash": src_hash,
-        "mean_loss": float(mean.item()),
+        "mean_loss": headline_mean,
     }
     print(json.dumps(out), flush=True)
 

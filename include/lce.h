@@ -257,6 +257,39 @@ lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
                               void* workspace_dev, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Forward and backward in one call, row chunk by row chunk (the FLCE
+ * pipeline of Liger: blog "最贵的一层：深入浅出 Liger Kernel 与 Cut
+ * Cross-Entropy", §二, and the Liger Kernel paper page, §3.2).  The rows are
+ * cut into chunks of at most H rows (a multiple of 256); for each chunk the
+ * logits against the whole vocabulary are formed once, kept as a bf16 block
+ * of Nc x V in the workspace (no larger than W), turned into the logit
+ * gradient, and projected back at once: dX rows = dZ_chunk · W, dW += dZᵀ ·
+ * X_chunk.  Three N·H·V contractions instead of the four of lce_forward +
+ * lce_backward, for an Nc x V workspace block.
+ *
+ * Results are those of lce_forward_ex followed by lce_backward_ex with the
+ * same options and dloss (within rounding; the stored block adds one bf16
+ * rounding of exp(z − ref)·d, like the gradient chunk of lce_backward).
+ *   dloss_dev   float [1] (MEAN, SUM) or [N] (NONE), as lce_backward_ex; it is
+ *               needed up front because the gradient is formed in the pass
+ *   outputs     loss/lse/reduced/n_valid/bad_label as lce_forward_ex, dX and
+ *               dW as lce_backward_ex
+ * Not supported: label smoothing together with a softcap
+ * (LCE_ERR_INVALID_ARG), V > 2^21 (LCE_ERR_SHAPE).  Workspace:
+ * lce_fused_workspace_bytes (0 for an invalid shape).
+ */
+size_t lce_fused_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype);
+
+lce_status lce_forward_backward(const void* X_dev, const void* W_dev,
+                                const int64_t* labels_dev, const float* dloss_dev,
+                                int64_t N, int64_t H, int64_t V, const lce_options* opt,
+                                float* loss_dev, float* lse_dev, float* reduced_dev,
+                                int32_t* n_valid_dev, int32_t* bad_label_dev,
+                                void* dX_dev, lce_dtype dX_dtype, void* dW_dev,
+                                lce_dtype dW_dtype, void* workspace_dev,
+                                size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);
 

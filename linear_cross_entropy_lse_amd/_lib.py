@@ -32,7 +32,8 @@ REDUCTIONS = {"mean": LCE_REDUCE_MEAN, "sum": LCE_REDUCE_SUM, "none": LCE_REDUCE
 EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_forward",
             "lce_backward", "lce_options_default", "lce_forward_ex", "lce_backward_ex",
             "lce_shard_forward", "lce_shard_merge_workspace_bytes", "lce_shard_merge",
-            "lce_shard_backward", "lce_status_string", "lce_version", "lce_timing_enable",
+            "lce_shard_backward", "lce_fused_workspace_bytes", "lce_forward_backward",
+            "lce_status_string", "lce_version", "lce_timing_enable",
             "lce_timing_reset", "lce_timing_read")
 
 
@@ -106,6 +107,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_shard_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, opt_p, vp,
                                        ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
     lib.lce_shard_backward.restype = ctypes.c_int
+    lib.lce_fused_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.lce_fused_workspace_bytes.restype = sz
+    lib.lce_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, opt_p, vp, vp, vp, vp, vp,
+                                         vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
+    lib.lce_forward_backward.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -436,3 +442,53 @@ def lce_shard_backward(X, W_shard, labels, lse, dloss, vocab_offset: int, vocab_
                                    _stream(dev))
     _check(st, "lce_shard_backward")
     return dX, dW
+
+
+# --------------------------------------------------------------------------- #
+# Forward and backward in one row-chunked pass
+# --------------------------------------------------------------------------- #
+def lce_fused_workspace_bytes(N: int, H: int, V: int, dW_dtype=None) -> int:
+    return int(load().lce_fused_workspace_bytes(N, H, V, _dtype_code(dW_dtype)))
+
+
+def lce_forward_backward(X, W, labels, dloss=1.0, ignore_index: int = -100, softcap: float = 0.0,
+                         logit_scale: float = 1.0, label_smoothing: float = 0.0,
+                         z_loss: float = 0.0, reduction: str = "mean", dX_dtype=None,
+                         dW_dtype=None, workspace=None):
+    """Forward and backward in one call, row chunk by row chunk (include/lce.h).
+    `dloss` as in lce_backward_ex.  Returns (dict of lce_forward_ex, dX, dW)."""
+    import torch
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    n_d = N if reduction == "none" else 1
+    if not torch.is_tensor(dloss):
+        dloss = torch.full((n_d,), float(dloss), dtype=torch.float32, device=dev)
+    dloss = dloss.to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+    if dloss.numel() != n_d:
+        raise ValueError(f"dloss must hold {n_d} value(s) for reduction {reduction!r}")
+    if n_d == 0:
+        dloss = torch.zeros(1, dtype=torch.float32, device=dev)
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    reduced = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int32, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    dXc, dWc = _dtype_code(dX_dtype), _dtype_code(dW_dtype)
+    dX = torch.empty(N, H, dtype=dX_dtype or torch.float32, device=dev)
+    dW = torch.empty(V, H, dtype=dW_dtype or torch.float32, device=dev)
+    need = lce_fused_workspace_bytes(N, H, V, dW_dtype)
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_forward_backward")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_forward_backward(_ptr(X), _ptr(W), _ptr(labels), dloss.data_ptr(), N, H, V,
+                                     ctypes.byref(opt), _ptr(loss), _ptr(lse), reduced.data_ptr(),
+                                     n_valid.data_ptr(), bad.data_ptr(), _ptr(dX), dXc,
+                                     dW.data_ptr(), dWc, _ptr(workspace), workspace.numel(),
+                                     _stream(dev))
+    _check(st, "lce_forward_backward")
+    return ({"loss": loss, "lse": lse, "reduced": reduced, "n_valid": n_valid, "bad_label": bad},
+            dX, dW)

@@ -22,6 +22,9 @@ namespace {
 // workspace size depends on the shape only.
 constexpr int kTargetCUs = 256;
 constexpr size_t kAlign = 256;
+// The fused variant keeps a Nc x V logits block; its 256-row tiles use 32-bit
+// offsets (256·V·2 bytes < 2^31).
+constexpr int64_t kFusedMaxV = (int64_t)1 << 21;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -136,6 +139,69 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
   p.off_dWs = o;
   if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
+  p.total = std::max<size_t>(o, kAlign);
+  return p;
+}
+
+// Fused row-chunk variant.  Chunk rows: a multiple of 256, at most H (the
+// bf16 logits block Nc x V is then no larger than W), at least 256, at most N
+// rounded up.  The dX tiles of one chunk contract over the whole vocabulary;
+// their K range is split so that one part costs no more than the average
+// work per workgroup (the dW tiles contract over the chunk's rows only).
+struct FusedPlan {
+  int64_t Nc, ldu;
+  int nchunks, T, S, n_vtiles, nt_h, ksplit, nb_prep, nb_fin;
+  size_t off_state, off_key, off_target, off_deriv, off_gs, off_c1, off_oh, off_rrow, off_keys_a,
+      off_keys_b, off_head, off_tail, off_bprep, off_bfin, off_scalars, off_pm, off_ps, off_pz,
+      off_U, off_ref, off_Xs, off_dXp, off_dWacc, total;
+};
+
+FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+  FusedPlan p{};
+  const int64_t Np = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
+  p.Nc = std::min<int64_t>(Np, std::max<int64_t>(kTile, H / kTile * kTile));
+  p.nchunks = (int)ceil_div(std::max<int64_t>(N, 1), p.Nc);
+  p.T = (int)(p.Nc / kTile);
+  p.n_vtiles = (int)ceil_div(V, kTile);
+  p.ldu = (int64_t)p.n_vtiles * kTile;
+  p.S = pick_splits(p.T, p.n_vtiles);
+  p.nt_h = (int)ceil_div(H, kTile);
+  // Average K steps per workgroup: both contractions of the chunk, each
+  // T·nt_h·(V/64) tile-steps, over kTargetCUs workgroups; one dX part must
+  // not exceed it.
+  const int64_t steps = ceil_div(V, kBK);
+  const int64_t avg = std::max<int64_t>(1, 2 * (int64_t)p.T * p.nt_h * steps / kTargetCUs);
+  int64_t ks = std::max<int64_t>(1, ceil_div(steps, avg));
+  ks = std::min<int64_t>(ks, 16);
+  const int64_t D = ceil_div(steps, ks);
+  p.ksplit = (int)ceil_div(steps, D);   // every part holds at least one step
+  p.nb_prep = row_prep_blocks(std::max<int64_t>(N, 1));
+  p.nb_fin = lse_finalize_blocks(Np);
+  size_t o = 0;
+  p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_key = o;     o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_target = o;  o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_deriv = o;   o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_gs = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_c1 = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_oh = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_rrow = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_keys_a = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_keys_b = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_head = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
+  p.off_tail = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
+  p.off_bprep = o;   o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
+  p.off_bfin = o;    o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_fin);
+  p.off_scalars = o; o = align_up(o + 16);
+  p.off_pm = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
+  p.off_ps = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
+  p.off_pz = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
+  p.off_U = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)p.ldu);
+  p.off_ref = o;     o = align_up(o + sizeof(float) * (size_t)p.Nc * 2 * (size_t)p.n_vtiles);
+  p.off_Xs = o;      o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)H);
+  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.ksplit * (size_t)p.Nc * (size_t)H);
+  p.off_dWacc = o;
+  if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)V * (size_t)H);
   p.total = std::max<size_t>(o, kAlign);
   return p;
 }
@@ -374,6 +440,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
+    cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0;
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (dW_dtype == LCE_BF16) {
@@ -386,7 +453,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   if (dW_dtype == LCE_F32)
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, N, H, state, key, oh, W, gemm_scale, dX_dev,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, state, key, oh, W, gemm_scale, nullptr, dX_dev,
                              dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }
@@ -606,6 +673,131 @@ lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
   return backward_impl(X_dev, W_shard_dev, labels_dev, lse_dev, dloss_dev, N, H, V_shard,
                        VocabRange{vocab_offset, vocab_total}, opt, dX_part_dev, dX_dtype,
                        dW_shard_dev, dW_dtype, workspace_dev, workspace_bytes, stream_ptr);
+}
+
+size_t lce_fused_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+  if (!shape_ok(N, H, V) || V > kFusedMaxV || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
+    return 0;
+  return plan_fused(N, H, V, dW_dtype).total;
+}
+
+lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                                const float* dloss_dev, int64_t N, int64_t H, int64_t V,
+                                const lce_options* opt, float* loss_dev, float* lse_dev,
+                                float* reduced_dev, int32_t* n_valid_dev, int32_t* bad_label_dev,
+                                void* dX_dev, lce_dtype dX_dtype, void* dW_dev,
+                                lce_dtype dW_dtype, void* workspace_dev, size_t workspace_bytes,
+                                void* stream_ptr) {
+  if (!shape_ok(N, H, V) || V > kFusedMaxV) return LCE_ERR_SHAPE;
+  if (!options_ok(opt) || !reduced_dev || !n_valid_dev || !dW_dev) return LCE_ERR_INVALID_ARG;
+  // Label smoothing needs the softcap derivative apart from the softmax,
+  // which the stored logits block does not keep.
+  if (opt->label_smoothing > 0.0f && opt->softcap > 0.0f) return LCE_ERR_INVALID_ARG;
+  if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
+    return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !dloss_dev || !loss_dev || !lse_dev ||
+                !dX_dev || !workspace_dev))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(dloss_dev, 4) || !aligned(loss_dev, 4) || !aligned(lse_dev, 4) ||
+      !aligned(reduced_dev, 4) || !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4) ||
+      !aligned(dX_dev, 16) || !aligned(dW_dev, 16) || !aligned(workspace_dev, kAlign))
+    return LCE_ERR_ALIGNMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (N == 0) {
+    LCE_LAUNCH("empty_forward", stream, launch_empty_forward(reduced_dev, n_valid_dev, bad_label_dev, stream));
+    LCE_LAUNCH("fill_zero", stream, launch_fill_zero(dW_dev, V * H * (dW_dtype == LCE_BF16 ? 2 : 4), stream));
+    return LCE_OK;
+  }
+  const FusedPlan pl = plan_fused(N, H, V, dW_dtype);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+
+  int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
+  int32_t* key = at<int32_t>(workspace_dev, pl.off_key);
+  float* target = at<float>(workspace_dev, pl.off_target);
+  float* deriv = at<float>(workspace_dev, pl.off_deriv);
+  float* gs = at<float>(workspace_dev, pl.off_gs);
+  float* c1 = at<float>(workspace_dev, pl.off_c1);
+  float* oh = at<float>(workspace_dev, pl.off_oh);
+  float* rrow = at<float>(workspace_dev, pl.off_rrow);
+  uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
+  uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
+  const uint64_t* keys = sort_passes(N) % 2 == 0 ? keys_a : keys_b;
+  float* part_head = at<float>(workspace_dev, pl.off_head);
+  float* part_tail = at<float>(workspace_dev, pl.off_tail);
+  BlockStats* bprep = at<BlockStats>(workspace_dev, pl.off_bprep);
+  BlockStats* bfin = at<BlockStats>(workspace_dev, pl.off_bfin);
+  float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] a·dloss(/n), [1] = 1
+  int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
+  float* pm = at<float>(workspace_dev, pl.off_pm);
+  float* ps = at<float>(workspace_dev, pl.off_ps);
+  float* pz = at<float>(workspace_dev, pl.off_pz);
+  uint16_t* U = at<uint16_t>(workspace_dev, pl.off_U);
+  float* ref = at<float>(workspace_dev, pl.off_ref);
+  uint16_t* Xs = at<uint16_t>(workspace_dev, pl.off_Xs);
+  float* dXp = at<float>(workspace_dev, pl.off_dXp);
+  float* dW32 = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) : at<float>(workspace_dev, pl.off_dWacc);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev);
+  const uint16_t* W = static_cast<const uint16_t*>(W_dev);
+  const bool smoothing = opt->label_smoothing > 0.0f;
+  const bool fixed = flce_fixed_reference(opt->softcap);
+  const float c2 = opt->softcap * kLog2e;
+  const int64_t dx_es = dX_dtype == LCE_BF16 ? 2 : 4;
+
+  LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, VocabRange{0, V}, opt->ignore_index,
+                          opt->softcap, opt->logit_scale, state, key, target, deriv, bprep, stream));
+  LCE_LAUNCH("scale_finalize", stream, launch_scale_finalize(bprep, pl.nb_prep, dloss_dev, opt->reduction == LCE_REDUCE_MEAN,
+                                opt->logit_scale, scalars, counts, stream));
+  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
+  const LossTerms terms = loss_terms(opt, V, smoothing ? pz : nullptr);
+
+  for (int c = 0; c < pl.nchunks; ++c) {
+    const int64_t r0 = (int64_t)c * pl.Nc;
+    const int64_t nr = std::min<int64_t>(pl.Nc, N - r0);
+    const int T = (int)ceil_div(nr, kTile);
+    FlceParams fp{};
+    fp.X = X + r0 * H; fp.W = W; fp.N = nr; fp.H = H; fp.V = V;
+    fp.T = T; fp.S = pl.S; fp.n_vtiles = pl.n_vtiles;
+    pick_xcd_grid(fp.T, fp.S, fp.tt, fp.ss);
+    fp.softcap = opt->softcap; fp.logit_scale = opt->logit_scale;
+    fp.part_m = pm; fp.part_s = ps; fp.part_z = smoothing ? pz : nullptr;
+    fp.U = U; fp.ldu = pl.ldu; fp.ref = fixed ? nullptr : ref;
+    LCE_LAUNCH("flce_logits", stream, launch_flce_logits(fp, stream));
+    LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, nr, state + r0, target + r0, terms,
+                                lse_dev + r0, loss_dev + r0, bfin + r0 / kTile, nullptr, stream));
+    LCE_LAUNCH("row_coef", stream, launch_row_coef(state + r0, lse_dev + r0, deriv + r0,
+                            opt->reduction == LCE_REDUCE_NONE ? dloss_dev + r0 : nullptr, scalars, nr,
+                            opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss, gs + r0, c1 + r0,
+                            oh + r0, stream));
+    // G = diag(r)·U with the fixed reference (dW from the row-scaled X, dX
+    // rows scaled afterwards); otherwise U is turned into G in place.
+    if (fixed) {
+      LCE_LAUNCH("flce_row_scale", stream, launch_flce_row_scale(X + r0 * H, nr, H, gs + r0, c1 + r0, lse_dev + r0,
+                                        c2, rrow + r0, Xs, stream));
+    } else {
+      LCE_LAUNCH("flce_scale", stream, launch_flce_scale(U, pl.ldu, nr, V, ref, 2 * pl.n_vtiles, c2, lse_dev + r0,
+                                    gs + r0, c1 + r0, (float)((double)opt->label_smoothing / (double)V),
+                                    stream));
+    }
+    ChunkGemmParams cp{};
+    cp.G = U; cp.ldg = pl.ldu; cp.Wc = W; cp.wc_rows = V; cp.X = fixed ? Xs : X + r0 * H;
+    cp.N = nr; cp.H = H; cp.chunk_len = V;
+    cp.nt_tok = T; cp.nt_h = pl.nt_h; cp.nt_v = pl.n_vtiles;
+    cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = scalars + 1;
+    cp.dW_dst = dW32;
+    cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
+    LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
+    LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
+                               scalars + 1, fixed ? rrow + r0 : nullptr,
+                               static_cast<char*>(dX_dev) + r0 * H * dx_es, dX_dtype == LCE_BF16,
+                               stream));
+  }
+  LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(bfin, (int)ceil_div(N, kTile), opt->reduction == LCE_REDUCE_MEAN,
+                                reduced_dev, n_valid_dev, bad_label_dev, stream));
+  LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dW32, 0, V, part_head, part_tail, stream));
+  if (dW_dtype == LCE_BF16)
+    LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dW32, static_cast<uint16_t*>(dW_dev), V * H, stream));
+  return LCE_OK;
 }
 
 }  // extern "C"

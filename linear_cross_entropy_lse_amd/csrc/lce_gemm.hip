@@ -102,6 +102,59 @@ __device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], flo
   }
 }
 
+// End of a (token tile, split) sweep: merge the running (m, s) (and Σ z) of
+// the lane pairs and of the two vocabulary halves, then write one partial
+// per token of the split.  `red` is LDS scratch of 3·256 floats; the caller
+// has drained every load into LDS.
+template <int kMode, bool kZSum>
+__device__ __forceinline__ void store_split_partials(float (&m)[kNI], float (&s)[kNI],
+                                                     float (&zs)[kNI], float* red, int wm, int wn,
+                                                     int lane, int64_t tok0, int split, int64_t N,
+                                                     float zunit, float* part_m, float* part_s,
+                                                     float* part_z) {
+  const float NEG_INF = -__builtin_inff();
+  // Lanes l and l^32 hold the same token column (different vocabulary rows).
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const float m2 = __shfl_xor(m[ni], 32);
+    const float s2 = __shfl_xor(s[ni], 32);
+    const float mn = fmaxf(m[ni], m2);
+    const float mref = mn == NEG_INF ? 0.0f : mn;
+    s[ni] = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
+    m[ni] = mn;
+    if (kZSum) zs[ni] += __shfl_xor(zs[ni], 32);
+  }
+  // Waves wm = 0 and wm = 1 cover the two vocabulary halves of the same tokens.
+  __syncthreads();
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int col = acc_col(wn, ni, lane);
+      red[col] = m[ni];
+      red[kTile + col] = s[ni];
+      if (kZSum) red[2 * kTile + col] = zs[ni];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int col = acc_col(wn, ni, lane);
+      const float m2 = red[col], s2 = red[kTile + col];
+      const float mn = fmaxf(m[ni], m2);
+      const float mref = mn == NEG_INF ? 0.0f : mn;
+      const float ss = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
+      const int64_t tok = tok0 + col;
+      if (tok < N) {
+        part_m[(int64_t)split * N + tok] = mn;
+        part_s[(int64_t)split * N + tok] = ss;
+        // Σ z in natural units: c·Σ tanh (capped) or a·Σ (x·w) (plain).
+        if (kZSum) part_z[(int64_t)split * N + tok] = zunit * (zs[ni] + red[2 * kTile + col]);
+      }
+    }
+  }
+}
+
 template <bool kTail, int kMode, bool kZSum>
 __global__ void __launch_bounds__(kThreads, 1)
 lse_partials_kernel(LseParams p) {
@@ -152,49 +205,10 @@ lse_partials_kernel(LseParams p) {
     lse_fold_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) prefetch has landed
-
-  // Lanes l and l^32 hold the same token column (different vocabulary rows).
-#pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) {
-    const float m2 = __shfl_xor(m[ni], 32);
-    const float s2 = __shfl_xor(s[ni], 32);
-    const float mn = fmaxf(m[ni], m2);
-    const float mref = mn == NEG_INF ? 0.0f : mn;
-    s[ni] = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
-    m[ni] = mn;
-    if (kZSum) zs[ni] += __shfl_xor(zs[ni], 32);
-  }
-  // Waves wm = 0 and wm = 1 cover the two vocabulary halves of the same tokens.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem_raw);
-  if (wm == 1 && lane < 32) {
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int col = acc_col(wn, ni, lane);
-      red[col] = m[ni];
-      red[kTile + col] = s[ni];
-      if (kZSum) red[2 * kTile + col] = zs[ni];
-    }
-  }
-  __syncthreads();
-  if (wm == 0 && lane < 32) {
-    // Σ z in natural units: c·Σ tanh (capped) or a·Σ (x·w) (plain).
-    const float zunit = kMode == kPlain ? p.logit_scale : p.softcap;
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const int col = acc_col(wn, ni, lane);
-      const float m2 = red[col], s2 = red[kTile + col];
-      const float mn = fmaxf(m[ni], m2);
-      const float mref = mn == NEG_INF ? 0.0f : mn;
-      const float ss = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
-      const int64_t tok = tok0 + col;
-      if (tok < p.N) {
-        p.part_m[(int64_t)split * p.N + tok] = mn;
-        p.part_s[(int64_t)split * p.N + tok] = ss;
-        if (kZSum) p.part_z[(int64_t)split * p.N + tok] = zunit * (zs[ni] + red[2 * kTile + col]);
-      }
-    }
-  }
+  store_split_partials<kMode, kZSum>(m, s, zs, reinterpret_cast<float*>(smem_raw), wm, wn, lane,
+                                     tok0, split, p.N,
+                                     kMode == kPlain ? p.logit_scale : p.softcap, p.part_m,
+                                     p.part_s, p.part_z);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,6 +339,170 @@ grad_logits_kernel(GradParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-chunked forward that also keeps every logit of the chunk (the FLCE
+// pipeline of Liger as the blog "最贵的一层：深入浅出 Liger Kernel 与 Cut
+// Cross-Entropy" describes it in §二: the chunk's logits are formed, the loss
+// comes from an online softmax over them, and the gradient is written in
+// their place).  The sweep is the forward's: per (token tile, split) a
+// running (m, s) over the split's vocabulary tiles, written as one partial
+// per token and split.  In the same epilogue each logit is stored as
+// U = 2^(u − ref)·d in bf16 (u the base-2 logit, d the softcap derivative),
+// the exponential shared with the running sum.  The reference is the running
+// max of the lane pair after the tile (kPlain, kCapGeneral; stored per
+// 128-column block for the later rescale) or the fixed c2 (kCapFixed).
+// U lies in [0, 1]; U·2^(ref − lse) is the softmax times d.
+// ---------------------------------------------------------------------------
+template <int kMode, bool kMasked, bool kZSum>
+__device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kNI], float (&m)[kNI],
+                                                     float (&s)[kNI], float (&zs)[kNI], int lim,
+                                                     float k2, float c2, float l2a,
+                                                     __amdgpu_buffer_rsrc_t rs,
+                                                     const uint32_t (&cb)[kNI]) {
+  const float NEG_INF = -__builtin_inff();
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    float mref = c2;
+    if (kMode != kCapFixed) {
+      float zmax = NEG_INF;
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = acc[mi][ni][r];
+          zmax = fmaxf(zmax, (!kMasked || acc_row_const(mi, r) < lim) ? z : NEG_INF);
+        }
+      // One reference for both lanes of the token column, so that a 128-row
+      // block of U has a single scale.
+      zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
+      const float umax = kMode == kPlain ? zmax * l2a
+                                         : (zmax == NEG_INF ? NEG_INF : c2 * tanh_of_scaled(zmax, k2));
+      const float mn = fmaxf(m[ni], umax);
+      mref = mn == NEG_INF ? 0.0f : mn;
+      s[ni] *= exp2_fast(m[ni] - mref);
+      m[ni] = mn;
+    }
+    float sum = 0.0f, zsum = 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float uv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = gq * 4 + q;
+          const float z = acc[mi][ni][r];
+          const bool ok = !kMasked || acc_row_const(mi, r) < lim;
+          float e, u, zt;
+          if (kMode == kPlain) {
+            e = exp2_fast(fmaf(z, l2a, -mref));
+            u = e;
+            zt = z;
+          } else {
+            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+            const float d4 = 4.0f * rr;
+            const float d = fmaf(-d4, rr, d4);                  // 1 − tanh² = 4r(1 − r)
+            e = kMode == kCapFixed ? exp2_fast(-2.0f * c2 * rr)  // 2^(c2·tanh − c2)
+                                   : exp2_fast(fmaf(-2.0f * c2, rr, c2 - mref));
+            u = e * d;
+            zt = fmaf(-2.0f, rr, 1.0f);                         // tanh = 1 − 2r
+          }
+          sum += ok ? e : 0.0f;
+          if (kZSum) zsum += ok ? zt : 0.0f;
+          uv[q] = ok ? u : 0.0f;
+        }
+        u32x2 packed;
+        packed[0] = pack_bf16x2(uv[0], uv[1]);
+        packed[1] = pack_bf16x2(uv[2], uv[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * acc_row_const(mi, gq * 4)), 0, 0);
+      }
+    s[ni] += sum;
+    if (kZSum) zs[ni] += zsum;
+  }
+}
+
+// Reference of tile j for the wave's 128-row half, through the descriptor
+// `rr` of the ref rows tok0.. (rows past N are out of range).  Lanes l and
+// l^32 hold the same value after the fold's pair max and store it to the
+// same address.
+__device__ __forceinline__ void flce_store_ref(__amdgpu_buffer_rsrc_t rr, uint32_t ref_base,
+                                               const float (&m)[kNI], int j, int wm,
+                                               uint32_t ni_stride) {
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni)
+    buffer_store_f32(m[ni], rr, ref_base + ni * ni_stride + (uint32_t)(2 * j + wm) * 4u);
+}
+
+template <bool kTail, int kMode, bool kZSum>
+__global__ void __launch_bounds__(kThreads, 1)
+flce_logits_kernel(FlceParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
+  LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  int ti, split;
+  grid_tile(g, p.T, p.tt, p.ss, ti, split);
+  const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
+  const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
+  const int64_t tok0 = (int64_t)ti * kTile;
+  const float k2 = kMode != kPlain ? 2.0f * kLog2e * p.logit_scale / p.softcap : 0.0f;
+  const float c2 = kMode != kPlain ? p.softcap * kLog2e : 0.0f;
+  const float l2a = kLog2e * p.logit_scale;
+  const int nref = 2 * p.n_vtiles;
+
+  float m[kNI], s[kNI], zs[kNI];
+  uint32_t col_base[kNI];   // byte offset of (token column, lane's first row) in the U rows
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    m[ni] = kMode == kCapFixed ? c2 : -__builtin_inff();
+    s[ni] = 0.0f;
+    zs[ni] = 0.0f;
+    col_base[ni] = (uint32_t)(acc_col(wn, ni, lane) * p.ldu * 2 + acc_row_lane(wm, lane) * 2);
+  }
+  // U rows tok0 .. N − 1; a tile's offsets stay below 256 · ldu · 2 bytes.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.U + tok0 * p.ldu, (p.N - tok0) * p.ldu * 2);
+  // ref rows tok0 .. N − 1 (unused with the fixed reference).
+  const __amdgpu_buffer_rsrc_t rr =
+      make_rsrc(kMode != kCapFixed ? p.ref + tok0 * nref : p.part_m, kMode != kCapFixed ? (p.N - tok0) * nref * 4 : 0);
+  const uint32_t ref_base = (uint32_t)(acc_col(wn, 0, lane) * nref * 4);
+  const uint32_t ref_ni_stride = (uint32_t)(32 * nref * 4);   // 32 token columns per ni
+
+  const int j_mid = (int)(j1 < p.V / kTile ? j1 : (j0 > p.V / kTile ? j0 : p.V / kTile));
+  Sweep sw;
+  f32x16 acc[kMI][kNI];
+  // Tiles below V, then (in a loop of its own, as in the forward) the one
+  // tile that reaches past V.
+  for (int j = j0; j < j_mid; ++j) {
+    const int64_t v0 = (int64_t)j * kTile;
+    zero_acc(acc);
+    gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
+                                               p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
+    uint32_t cb[kNI];
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(v0 * 2);
+    flce_fold_store_tile<kMode, false, kZSum>(acc, m, s, zs, 0, k2, c2, l2a, rs, cb);
+    if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
+  }
+  for (int j = j_mid; j < j1; ++j) {
+    const int64_t v0 = (int64_t)j * kTile;
+    zero_acc(acc);
+    gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
+                                               p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
+    uint32_t cb[kNI];
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(v0 * 2);
+    const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
+    flce_fold_store_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a, rs, cb);
+    if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  store_split_partials<kMode, kZSum>(m, s, zs, reinterpret_cast<float*>(smem_raw), wm, wn, lane,
+                                     tok0, split, p.N,
+                                     kMode == kPlain ? p.logit_scale : p.softcap, p.part_m,
+                                     p.part_s, p.part_z);
+}
+
+// ---------------------------------------------------------------------------
 // Backward, steps 2 and 3 for one vocabulary chunk, in one persistent launch.
 //
 //   dX tile (256 tokens x 256 hidden): dX_acc (+)= G[:, chunk] · W[chunk, :]
@@ -346,19 +524,28 @@ grad_logits_kernel(GradParams p) {
 // on consecutive tile ids, and every tile has exactly one owner, so the dX
 // read-modify-write needs no synchronisation.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, LCE_LDS uint16_t* smem,
-                                              int wm, int wn, int lane) {
+// dX tile id g = part · (nt_tok · nt_h) + tile: K steps [part·D, (part+1)·D)
+// of the chunk, D = ceil(steps / ksplit), into partial buffer `part`.  The
+// host picks ksplit so that every part holds at least one step.
+__device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, int64_t D,
+                                              LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
-  const int64_t tok0 = (int64_t)(g / p.nt_h) * kTile;
-  const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
-  const int64_t k_end = (p.chunk_len + kBK - 1) / kBK * kBK;
-  gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, 0, k_end, p.wc_rows,
+  const int n_tiles = p.nt_tok * p.nt_h;
+  const int part = g / n_tiles;
+  const int t = g - part * n_tiles;
+  const int64_t tok0 = (int64_t)(t / p.nt_h) * kTile;
+  const int64_t h0 = (int64_t)(t % p.nt_h) * kTile;
+  const int64_t steps = (p.chunk_len + kBK - 1) / kBK;
+  const int64_t k0 = (int64_t)part * D * kBK;
+  const int64_t k_end = (part + 1) * D < steps ? (part + 1) * D * kBK : steps * kBK;
+  gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, k0, k_end, p.wc_rows,
                                 smem, acc);
   // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
   // past H are pushed out of range.  The 64 previous values of one mi row
   // block are loaded together, so a tile costs 4 round trips, not 256.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dX_acc + tok0 * p.H, (p.N - tok0) * p.H * 4);
+  float* dst = p.dX_acc + (int64_t)part * p.dx_part_stride;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + tok0 * p.H, (p.N - tok0) * p.H * 4);
   const uint32_t rowb = (uint32_t)(p.H * 4);
   uint32_t cbase[kNI];
 #pragma unroll
@@ -390,6 +577,7 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, L
   }
 }
 
+template <bool kDwAcc>
 __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, float sc,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
   f32x16 acc[kMI][kNI];
@@ -401,18 +589,41 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
   // columns at or past H are pushed out of range.
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW_dst + vt0 * p.H, (p.chunk_len - vt0) * p.H * 4);
   const uint32_t rowb = (uint32_t)(p.H * 4);
+  uint32_t cbase[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     const int64_t h = h0 + acc_col(wn, ni, lane);
-    const uint32_t cb = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
+    cbase[ni] = h < p.H ? (uint32_t)acc_row_lane(wm, lane) * rowb + (uint32_t)h * 4u : kOutOfRange;
+  }
+  if (kDwAcc) {
+    // Read-modify-write, the 64 previous values of one mi row block together.
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < kMI; ++mi) {
+      float prev[kNI][16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        buffer_store_f32(sc * acc[mi][ni][r], rs, cb + (uint32_t)acc_row_const(mi, r) * rowb);
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          prev[ni][r] = buffer_load_f32(rs, cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          buffer_store_f32(fmaf(sc, acc[mi][ni][r], prev[ni][r]), rs,
+                           cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          buffer_store_f32(sc * acc[mi][ni][r], rs, cbase[ni] + (uint32_t)acc_row_const(mi, r) * rowb);
   }
 }
 
+template <bool kDwAcc>
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_gemm_kernel(ChunkGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -420,13 +631,14 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
-  const int n_dx = p.nt_tok * p.nt_h, n_dw = p.nt_v * p.nt_h;
+  const int n_dx = p.nt_tok * p.nt_h * p.ksplit, n_dw = p.nt_v * p.nt_h;
   const int dx_lo = (int)((int64_t)xcd * n_dx / kXcds);
   const int nx = (int)((int64_t)(xcd + 1) * n_dx / kXcds) - dx_lo;
   const int dw_lo = (int)((int64_t)xcd * n_dw / kXcds);
   const int nw = (int)((int64_t)(xcd + 1) * n_dw / kXcds) - dw_lo;
-  // Cost of a tile in K steps: D for dX tiles, E for dW tiles.
-  const int64_t D = (p.chunk_len + kBK - 1) / kBK, E = (p.N + kBK - 1) / kBK;
+  // Cost of a tile in K steps: D for dX tiles (one K part), E for dW tiles.
+  const int64_t D = ((p.chunk_len + kBK - 1) / kBK + p.ksplit - 1) / p.ksplit;
+  const int64_t E = (p.N + kBK - 1) / kBK;
   const int rx = nx % kCusPerXcd;                 // workgroups holding one extra dX tile
   const int64_t per_wg = ((int64_t)nx * D + (int64_t)nw * E) / kCusPerXcd;
   const int64_t heavy_budget = per_wg - (int64_t)(nx / kCusPerXcd + 1) * D;
@@ -434,13 +646,15 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
   const int nw_light = nw - nw_heavy;
 
-  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile(p, dx_lo + t, smem, wm, wn, lane);
+  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile(p, dx_lo + t, D, smem, wm, wn, lane);
   const float sc = *p.scale;
   if (li >= rx) {
     const int nl = kCusPerXcd - rx;
-    for (int t = li - rx; t < nw_light; t += nl) chunk_dw_tile(p, dw_lo + t, sc, smem, wm, wn, lane);
+    for (int t = li - rx; t < nw_light; t += nl)
+      chunk_dw_tile<kDwAcc>(p, dw_lo + t, sc, smem, wm, wn, lane);
   } else {
-    for (int t = li; t < nw_heavy; t += rx) chunk_dw_tile(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
+    for (int t = li; t < nw_heavy; t += rx)
+      chunk_dw_tile<kDwAcc>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
   }
 }
 
@@ -473,6 +687,36 @@ hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+bool flce_fixed_reference(float softcap) { return softcap > 0.0f && softcap * kLog2e < 60.0f; }
+
+hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream) {
+  const int grid = p.T * p.S;
+  const bool tail = p.H % kBK != 0, zsum = p.part_z != nullptr;
+  const int mode = p.softcap <= 0.0f ? kPlain
+                   : (flce_fixed_reference(p.softcap) ? kCapFixed : kCapGeneral);
+#define LCE_FLCE_LAUNCH(T_, M_, Z_) \
+  hipLaunchKernelGGL((flce_logits_kernel<T_, M_, Z_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_FLCE_MODES(T_, Z_)                               \
+  do {                                                       \
+    if (mode == kPlain) LCE_FLCE_LAUNCH(T_, kPlain, Z_);       \
+    else if (mode == kCapFixed) LCE_FLCE_LAUNCH(T_, kCapFixed, Z_); \
+    else LCE_FLCE_LAUNCH(T_, kCapGeneral, Z_);               \
+  } while (0)
+  // Σ z only serves label smoothing, which the fused call takes without a
+  // softcap only.
+  if (zsum && mode != kPlain) return hipErrorInvalidValue;
+  if (tail) {
+    if (zsum) LCE_FLCE_LAUNCH(true, kPlain, true);
+    else LCE_FLCE_MODES(true, false);
+  } else {
+    if (zsum) LCE_FLCE_LAUNCH(false, kPlain, true);
+    else LCE_FLCE_MODES(false, false);
+  }
+#undef LCE_FLCE_MODES
+#undef LCE_FLCE_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
   const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f, gen = p.gs != nullptr;
@@ -494,7 +738,10 @@ hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
   const int grid = kXcds * kCusPerXcd;
-  hipLaunchKernelGGL(chunk_gemm_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.dw_accumulate)
+    hipLaunchKernelGGL(chunk_gemm_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(chunk_gemm_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -57,9 +57,42 @@ struct ChunkGemmParams {
   float* dX_acc;       // fp32 [N, H]
   const float* scale;  // device scalar dloss / n_valid
   float* dW_dst;       // fp32 [chunk_len, H] (row v_local)
+  // Split of each dX tile's K range (the chunk's vocabulary) into ksplit
+  // parts; part k goes to dX_acc + k·dx_part_stride.  1 without splitting.
+  int ksplit;
+  int64_t dx_part_stride;
+  int dw_accumulate;   // 1: dW_dst += s·Gᵀ·X instead of =
+};
+
+// Row-chunked forward with the logit gradient formed in the same pass: the
+// logits of `N` rows (one chunk) against the whole vocabulary.  Per (token
+// tile, split) the (m, s) partials as in LseParams, and every logit as
+// U = 2^(u − ref)·d in bf16 ([N, ldu], columns past V written 0), u the
+// base-2 (scaled, capped) logit, d the softcap derivative (1 without), ref
+// the reference below.
+struct FlceParams {
+  const uint16_t* X;   // bf16 [N, H] (the chunk's rows)
+  const uint16_t* W;   // bf16 [V, H]
+  int64_t N, H, V;
+  int T, S, n_vtiles;
+  int tt, ss;
+  float softcap;
+  float logit_scale;
+  float* part_m;       // [S, N]
+  float* part_s;       // [S, N]
+  float* part_z;       // [S, N] or null
+  uint16_t* U;         // bf16 [N, ldu]
+  int64_t ldu;         // n_vtiles · 256
+  // Reference of each row's 128-column block (base 2), [N, 2·n_vtiles]: the
+  // running max of the row's split up to and including that block's tile.
+  // Null selects the fixed reference c·log2(e) (softcap with c·log2(e) < 60).
+  float* ref;
 };
 
 hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream);
+hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream);
+// True when the fused forward's logits use the fixed reference c·log2(e).
+bool flce_fixed_reference(float softcap);
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream);
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream);
 
@@ -146,11 +179,28 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
                                 uint64_t* keys_b, hipStream_t stream);
 
 // dX_i = sx·dX_acc_i − oh_i·w_{key_i} (owned rows), sx·dX_acc_i (valid rows
-// whose label lies in another shard), 0 (ignored), NaN (bad).
-hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
-                              const int32_t* row_state, const int32_t* row_key,
+// whose label lies in another shard), 0 (ignored), NaN (bad).  dX_acc_i is
+// the sum of n_parts partial buffers part_stride floats apart, taken in part
+// order.  sx is the device scalar sx[0], or sx_rows[i] when sx_rows is not
+// null.
+hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
+                              int64_t H, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
-                              void* dX, int dX_bf16, hipStream_t stream);
+                              const float* sx_rows, void* dX, int dX_bf16, hipStream_t stream);
+
+// Fused forward, generic reference: in place, U[i][v] becomes the gradient
+// G = gs_i·(c1_i·U·2^(ref_i,v/128 − lse_i·log2 e) − eps_over_v) for v < V and
+// 0 for V <= v < ldu.  ref == null: the fixed reference c2 for every block.
+hipError_t launch_flce_scale(uint16_t* U, int64_t ldu, int64_t N, int64_t V, const float* ref,
+                             int nref, float c2, const float* lse, const float* gs,
+                             const float* c1, float eps_over_v, hipStream_t stream);
+
+// Fused forward, fixed reference: r_i = gs_i·c1_i·2^(c2 − lse_i·log2 e), and
+// Xs_i = bf16(r_i·x_i).  The gradient is then G = diag(r)·U, so dW = Uᵀ·Xs
+// and dX = diag(r)·(U·W).
+hipError_t launch_flce_row_scale(const uint16_t* X, int64_t N, int64_t H, const float* gs,
+                                 const float* c1, const float* lse, float c2, float* r,
+                                 uint16_t* Xs, hipStream_t stream);
 
 // One-hot part of dW from the sorted keys, in chunks of kSegRows sorted rows;
 // part_head / part_tail hold seg_chunks(N) x H floats each.

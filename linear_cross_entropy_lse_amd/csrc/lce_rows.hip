@@ -452,13 +452,14 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
 // when G already carries each row's scale.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
-                   const int32_t* __restrict__ row_state, const int32_t* __restrict__ row_key,
-                   const float* __restrict__ oh, const uint16_t* __restrict__ W,
-                   const float* __restrict__ sx, void* __restrict__ dX, int dX_bf16) {
+dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_stride, int64_t N,
+                   int64_t H, const int32_t* __restrict__ row_state,
+                   const int32_t* __restrict__ row_key, const float* __restrict__ oh,
+                   const uint16_t* __restrict__ W, const float* __restrict__ sx,
+                   const float* __restrict__ sx_rows, void* __restrict__ dX, int dX_bf16) {
   const int64_t row = blockIdx.x;
   const int st = row_state[row];
-  const float s = *sx;
+  const float s = sx_rows ? sx_rows[row] : *sx;
   const float e = oh[row];
   const int32_t key = st == kRowValid ? row_key[row] : INT_MAX;
   const bool owned = key != INT_MAX;          // the label is one of W's rows
@@ -466,7 +467,14 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (st == kRowValid) {
-      const float4 v = *reinterpret_cast<const float4*>(dX_acc + row * H + h);
+      float4 v = *reinterpret_cast<const float4*>(dX_acc + row * H + h);
+      for (int k = 1; k < n_parts; ++k) {
+        const float4 w = *reinterpret_cast<const float4*>(dX_acc + k * part_stride + row * H + h);
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+      }
       const float a[4] = {v.x, v.y, v.z, v.w};
       if (owned) {
         const u32x2 wv = *reinterpret_cast<const u32x2*>(W + y * H + h);
@@ -494,12 +502,77 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int64_t N, int64_t H,
   }
 }
 
-hipError_t launch_dx_finalize(const float* dX_acc, int64_t N, int64_t H,
-                              const int32_t* row_state, const int32_t* row_key,
+hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
+                              int64_t H, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
-                              void* dX, int dX_bf16, hipStream_t stream) {
-  hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, N, H,
-                     row_state, row_key, oh, W, sx, dX, dX_bf16);
+                              const float* sx_rows, void* dX, int dX_bf16, hipStream_t stream) {
+  hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, n_parts,
+                     part_stride, N, H, row_state, row_key, oh, W, sx, sx_rows, dX, dX_bf16);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused row-chunk variant: turn the stored U = 2^(u − ref)·d of a chunk into
+// the logit gradient (see launch_flce_scale), 8 bf16 values per thread; a
+// 128-column block shares one reference, so one exponential serves a thread.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+flce_scale_kernel(uint16_t* __restrict__ U, int64_t ldu, int64_t V, const float* __restrict__ ref,
+                  int nref, float c2, const float* __restrict__ lse, const float* __restrict__ gs,
+                  const float* __restrict__ c1, float eps_over_v) {
+  const int64_t row = blockIdx.y;
+  const int64_t col0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (col0 >= ldu) return;
+  const float g = gs[row];
+  const float r = ref ? ref[row * nref + col0 / 128] : c2;
+  const float f = g * c1[row] * exp2f(r - lse[row] * kLog2e);
+  const float eb = g * eps_over_v;
+  uint16_t* p = U + row * ldu + col0;
+  const u32x4 in = *reinterpret_cast<const u32x4*>(p);
+  u32x4 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = fmaf(f, __uint_as_float(in[q] << 16), -eb);
+    const float hi = fmaf(f, __uint_as_float(in[q] & 0xffff0000u), -eb);
+    const bool ok_lo = col0 + 2 * q < V, ok_hi = col0 + 2 * q + 1 < V;
+    out[q] = pack_bf16x2(ok_lo ? lo : 0.0f, ok_hi ? hi : 0.0f);
+  }
+  *reinterpret_cast<u32x4*>(p) = out;
+}
+
+hipError_t launch_flce_scale(uint16_t* U, int64_t ldu, int64_t N, int64_t V, const float* ref,
+                             int nref, float c2, const float* lse, const float* gs,
+                             const float* c1, float eps_over_v, hipStream_t stream) {
+  const int64_t per_block = 256 * 8;
+  hipLaunchKernelGGL(flce_scale_kernel, dim3((unsigned)((ldu + per_block - 1) / per_block), (unsigned)N),
+                     dim3(256), 0, stream, U, ldu, V, ref, nref, c2, lse, gs, c1, eps_over_v);
+  return hipGetLastError();
+}
+
+// Fixed-reference form: r_i = gs_i·c1_i·2^(c2 − lse_i·log2 e), Xs_i = bf16(r_i·x_i).
+__global__ void __launch_bounds__(256)
+flce_row_scale_kernel(const uint16_t* __restrict__ X, int64_t H, const float* __restrict__ gs,
+                      const float* __restrict__ c1, const float* __restrict__ lse, float c2,
+                      float* __restrict__ r_out, uint16_t* __restrict__ Xs) {
+  const int64_t row = blockIdx.x;
+  const float r = gs[row] * c1[row] * exp2f(c2 - lse[row] * kLog2e);
+  if (threadIdx.x == 0) r_out[row] = r;
+  for (int64_t h = (int64_t)threadIdx.x * 8; h < H; h += 256 * 8) {
+    const u32x4 in = *reinterpret_cast<const u32x4*>(X + row * H + h);
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      out[q] = pack_bf16x2(r * __uint_as_float(in[q] << 16),
+                           r * __uint_as_float(in[q] & 0xffff0000u));
+    *reinterpret_cast<u32x4*>(Xs + row * H + h) = out;
+  }
+}
+
+hipError_t launch_flce_row_scale(const uint16_t* X, int64_t N, int64_t H, const float* gs,
+                                 const float* c1, const float* lse, float c2, float* r,
+                                 uint16_t* Xs, hipStream_t stream) {
+  hipLaunchKernelGGL(flce_row_scale_kernel, dim3((unsigned)N), dim3(256), 0, stream, X, H, gs, c1,
+                     lse, c2, r, Xs);
   return hipGetLastError();
 }
 

@@ -183,3 +183,32 @@ def test_shard_calls_argument_checks(lib):
     assert shard_merge(lib, ctypes.byref(smooth)) == _lib.LCE_ERR_INVALID_ARG   # no Σz parts
     assert lib.lce_shard_merge_workspace_bytes(-1) == 0
     assert lib.lce_shard_merge_workspace_bytes(1 << 20) >= 4096 * 24
+
+
+# Fused forward + backward: argument checks that return before any launch.
+def fused(lib, o, N=8, H=16, V=40, dW=_lib.LCE_F32):
+    wsb = lib.lce_fused_workspace_bytes(N, H, V, dW)
+    return lib.lce_forward_backward(FAKE, FAKE, FAKE, FAKE, N, H, V, o, FAKE, FAKE, FAKE, FAKE, 0,
+                                    FAKE, _lib.LCE_F32, FAKE, dW, FAKE, max(wsb, 256), None)
+
+
+def test_fused_argument_checks(lib):
+    o = opts()
+    assert fused(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    assert fused(lib, ctypes.byref(o), H=12) == _lib.LCE_ERR_SHAPE
+    assert fused(lib, ctypes.byref(o), V=(1 << 21) + 1) == _lib.LCE_ERR_SHAPE
+    assert fused(lib, ctypes.byref(o), dW=7) == _lib.LCE_ERR_INVALID_ARG
+    both = opts(softcap=30.0, label_smoothing=0.1)
+    assert fused(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_fused_workspace_bytes(8, 12, 40, 0) == 0
+    assert lib.lce_fused_workspace_bytes(8, 16, (1 << 21) + 1, 0) == 0
+
+
+@pytest.mark.parametrize("N,H,V", [(8192, 2304, 256128), (8192, 4096, 128256),
+                                   (32768, 3584, 152064), (16384, 4096, 32000)])
+def test_fused_workspace_is_one_logits_block(lib, N, H, V):
+    # One bf16 block of at most H rows by V columns (no larger than W), dX
+    # partials and O(N) row data: below the N x V logits.
+    ws = lib.lce_fused_workspace_bytes(N, H, V, _lib.LCE_F32)
+    assert 0 < ws < N * V * 2
+    assert ws <= 2 * H * V + 16 * 4 * H * H + 64 * N + (64 << 20)
