@@ -42,9 +42,10 @@ bool shape_ok(int64_t N, int64_t H, int64_t V) {
   return N >= 0 && N < INT_MAX && H >= 8 && H < (1 << 20) && H % 8 == 0 && V >= 1 && V < INT_MAX;
 }
 
-// Vocabulary splits of the persistent (token tile, split) grids.
+// Vocabulary splits of the persistent (token tile, split) grids: as many as
+// fit T·S <= kTargetCUs, so the grid is one wave of workgroups.
 int pick_splits(int T, int n_vtiles) {
-  int S = (int)ceil_div(kTargetCUs, T);
+  int S = kTargetCUs / std::max(T, 1);
   S = std::max(1, std::min(S, n_vtiles));
   return S;
 }
@@ -143,9 +144,10 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   return p;
 }
 
-// Fused row-chunk variant.  Chunk rows: a multiple of 256, at most H (the
-// bf16 logits block Nc x V is then no larger than W), at least 256, at most N
-// rounded up.  The dX tiles of one chunk contract over the whole vocabulary;
+// Fused row-chunk variant.  Chunk rows: 256 times a power of two, at most H
+// (the bf16 logits block Nc x V is then no larger than W), at least 256, at
+// most N rounded up; a power-of-two count of token tiles divides the 256
+// workgroups of the grid evenly.  The dX tiles of one chunk contract over the whole vocabulary;
 // their K range is split so that one part costs no more than the average
 // work per workgroup (the dW tiles contract over the chunk's rows only).
 struct FusedPlan {
@@ -159,7 +161,9 @@ struct FusedPlan {
 FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   FusedPlan p{};
   const int64_t Np = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
-  p.Nc = std::min<int64_t>(Np, std::max<int64_t>(kTile, H / kTile * kTile));
+  int64_t tiles = 1;
+  while (tiles * 2 * kTile <= H) tiles *= 2;
+  p.Nc = std::min<int64_t>(Np, tiles * kTile);
   p.nchunks = (int)ceil_div(std::max<int64_t>(N, 1), p.Nc);
   p.T = (int)(p.Nc / kTile);
   p.n_vtiles = (int)ceil_div(V, kTile);
@@ -193,9 +197,12 @@ FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_bprep = o;   o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
   p.off_bfin = o;    o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_fin);
   p.off_scalars = o; o = align_up(o + 16);
-  p.off_pm = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
-  p.off_ps = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
-  p.off_pz = o;      o = align_up(o + sizeof(float) * (size_t)p.Nc * p.S);
+  // Split partials: a shorter last chunk takes more splits (S·rows stays
+  // below kTargetCUs·256).
+  const size_t part = (size_t)kTargetCUs * kTile;
+  p.off_pm = o;      o = align_up(o + sizeof(float) * part);
+  p.off_ps = o;      o = align_up(o + sizeof(float) * part);
+  p.off_pz = o;      o = align_up(o + sizeof(float) * part);
   p.off_U = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)p.ldu);
   p.off_ref = o;     o = align_up(o + sizeof(float) * (size_t)p.Nc * 2 * (size_t)p.n_vtiles);
   p.off_Xs = o;      o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)H);
@@ -757,13 +764,13 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     const int T = (int)ceil_div(nr, kTile);
     FlceParams fp{};
     fp.X = X + r0 * H; fp.W = W; fp.N = nr; fp.H = H; fp.V = V;
-    fp.T = T; fp.S = pl.S; fp.n_vtiles = pl.n_vtiles;
+    fp.T = T; fp.S = pick_splits(T, pl.n_vtiles); fp.n_vtiles = pl.n_vtiles;
     pick_xcd_grid(fp.T, fp.S, fp.tt, fp.ss);
     fp.softcap = opt->softcap; fp.logit_scale = opt->logit_scale;
     fp.part_m = pm; fp.part_s = ps; fp.part_z = smoothing ? pz : nullptr;
     fp.U = U; fp.ldu = pl.ldu; fp.ref = fixed ? nullptr : ref;
     LCE_LAUNCH("flce_logits", stream, launch_flce_logits(fp, stream));
-    LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, nr, state + r0, target + r0, terms,
+    LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, fp.S, nr, state + r0, target + r0, terms,
                                 lse_dev + r0, loss_dev + r0, bfin + r0 / kTile, nullptr, stream));
     LCE_LAUNCH("row_coef", stream, launch_row_coef(state + r0, lse_dev + r0, deriv + r0,
                             opt->reduction == LCE_REDUCE_NONE ? dloss_dev + r0 : nullptr, scalars, nr,
