@@ -496,3 +496,70 @@ def forward_backward_chunked(X: np.ndarray, W: np.ndarray, labels: np.ndarray, d
     else:
         reduced = total
     return {"lse": lse, "loss": loss, "n_valid": n_valid, "reduced": reduced}, dX, dW
+
+
+# --------------------------------------------------------------------------- #
+# Gradient filtering (reading R19; opt-in, not exact)
+# --------------------------------------------------------------------------- #
+# [CCE-blog] §三: in bf16 training a softmax entry below 2^-12 is lost to
+# rounding once it is accumulated into the gradient, and only a tiny share of
+# a row's entries is above it, so CCE skips every tile of the backward whose
+# entries all lie below the threshold.  [M011] §06 keeps this apart from the
+# memory idea: filtering drops gradient terms, and an unfiltered reference is
+# kept for comparison.
+#   R19 the tile is a block of 256 token rows by 256 vocabulary columns
+#       (aligned to multiples of 256 in both indices); the value compared is
+#       the dense positive part of the logit gradient, (1 + 2l·LSE_i)·p_iv,
+#       over the block's rows that have a target (NaN counts as above); a
+#       block whose values are all below eps loses that dense part in both
+#       contractions, while the one-hot term is always kept.  Label smoothing
+#       (whose −e/V term is not small relative to the threshold in sum) is
+#       not combined with filtering.
+def filter_block_max(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.ndarray,
+                     opts: Dict[str, object], tile: int = 256) -> np.ndarray:
+    """Per (token block, vocabulary block): max over rows with a target of
+    (1 + 2l·LSE)·p (NaN if any such value is NaN), −inf for blocks without
+    such rows."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, V = X.shape[0], W.shape[0]
+    a, c, lam = float(opts["logit_scale"]), float(opts["softcap"]), float(opts["z_loss"])
+    Zc = apply_softcap(a * logits(X, W), c)
+    P = (1.0 + 2.0 * lam * lse)[:, None] * np.exp(Zc - lse[:, None])
+    P[~valid_mask(labels, int(opts["ignore_index"]))] = -np.inf
+    nb_r, nb_c = -(-N // tile), -(-V // tile)
+    out = np.full((nb_r, nb_c), -np.inf)
+    for bi in range(nb_r):
+        for bj in range(nb_c):
+            blk = P[bi * tile:(bi + 1) * tile, bj * tile:(bj + 1) * tile]
+            out[bi, bj] = np.nan if np.isnan(blk).any() else blk.max()
+    return out
+
+
+def backward_filtered(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
+                      opts: Dict[str, object], eps: float, tile: int = 256):
+    """(dX, dW) with the dense gradient part of every block whose values all
+    lie below eps removed (R19)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    if float(opts["label_smoothing"]) > 0:
+        raise ValueError("gradient filtering is not combined with label smoothing (R19)")
+    N, V = X.shape[0], W.shape[0]
+    fwd = forward_ex(X, W, labels, opts)
+    lse = fwd["lse"]
+    scale = row_scale(labels, dloss, fwd["n_valid"], opts)
+    a, c, lam = float(opts["logit_scale"]), float(opts["softcap"]), float(opts["z_loss"])
+    Z = a * logits(X, W)
+    Zc = apply_softcap(Z, c)
+    dense = (1.0 + 2.0 * lam * lse)[:, None] * np.exp(Zc - lse[:, None])
+    bm = filter_block_max(X, W, labels, lse, opts, tile)
+    for bi in range(bm.shape[0]):
+        for bj in range(bm.shape[1]):
+            if bm[bi, bj] < eps:                     # NaN compares False: kept
+                dense[bi * tile:(bi + 1) * tile, bj * tile:(bj + 1) * tile] = 0.0
+    onehot = (labels[:, None] == np.arange(V)[None, :]).astype(np.float64)
+    G = (dense - onehot) * softcap_derivative(Z, c) * a * scale[:, None]
+    G[bad_mask(labels, V, int(opts["ignore_index"]))] = np.nan
+    return G @ W, G.T @ X
