@@ -50,6 +50,8 @@ def parse():
                     help="also time one vocabulary shard of V/shards rows (0: skip)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip timing the row-chunked forward-and-backward call")
+    ap.add_argument("--filter-eps", type=float, default=2.0 ** -12,
+                    help="also time the step with the (non-exact) gradient filter (0: skip)")
     return ap.parse_args()
 
 
@@ -207,6 +209,60 @@ def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, 
                     "bf16, gradient formed in the forward pass; not the headline path"}
 
 
+def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, fws,
+                  fws_n, sptr, stream, step_ms_exact):
+    """The step with the opt-in gradient filter at threshold args.filter_eps
+    (forward, then the filtered backward), and how far its gradients are from
+    the exact ones of the same step."""
+    import ctypes
+    import torch
+    import lce_inputs as L
+    N, H, V = w.N, w.H, w.V
+    opt = _lib.make_options(L.IGNORE_INDEX, float(w.softcap), filter_eps=args.filter_eps)
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+    bws_n = lib.lce_backward_workspace_bytes(N, H, V, gcode)
+    bws = torch.empty(bws_n, dtype=torch.uint8, device=X.device)
+    dXe, dWe = dX.clone(), dW.clone()          # exact gradients of the last timed step
+
+    def fstep():
+        st = lib.lce_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
+                             float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
+                             nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        st = lib.lce_backward_ex(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                                 dloss.data_ptr(), N, H, V, ctypes.byref(opt), dX.data_ptr(),
+                                 gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_backward_ex: {_lib.status_string(st)}")
+
+    log(f"[bench] step with the gradient filter at {args.filter_eps:.3g}")
+    for _ in range(args.warmup):
+        fstep()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        fstep()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+
+    def rel(a, b):
+        return float(torch.linalg.vector_norm((a.float() - b.float()).ravel()) /
+                     torch.linalg.vector_norm(b.float().ravel()))
+    out = {"filter_eps": args.filter_eps, "ms_per_step": round(ms, 3),
+           "tokens_per_s": round(N / (ms / 1e3), 1),
+           "speedup_vs_exact_step": round(step_ms_exact / ms, 3),
+           "dX_rel_l2_vs_exact": rel(dX, dXe), "dW_rel_l2_vs_exact": rel(dW, dWe),
+           "note": "opt-in, not exact: gradient blocks whose softmax values all lie below "
+                   "filter_eps are skipped in both contractions; not the headline path"}
+    dX.copy_(dXe)
+    dW.copy_(dWe)
+    del bws, dXe, dWe
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -318,6 +374,11 @@ def main():
             per_kernel[k]["tflops"] = round(units * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
 
     headline_mean = float(mean.item())
+    filtered = None
+    if args.filter_eps > 0:
+        filtered = time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW,
+                                 gcode, fws, fws_n, sptr, stream, ms_per_step)
+
     fused = None
     if not args.no_fused:
         fused = time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode,
@@ -355,6 +416,7 @@ def main():
         "cpu_baseline": cpu,
         "vocab_shard": shard,
         "fused_row_chunk": fused,
+        "gradient_filter": filtered,
         "kernels": per_kernel,
         "memory_bytes": {"peak_allocated": int(peak_mem),
                          "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),

@@ -147,7 +147,24 @@ typedef struct {
   float label_smoothing;  /* e in [0, 1] (default 0) */
   float z_loss;           /* l, finite and >= 0 (default 0) */
   int32_t reduction;      /* an lce_reduction (default LCE_REDUCE_MEAN) */
+  float filter_eps;       /* gradient filter threshold, finite and >= 0 (default 0:
+                             exact).  See below. */
 } lce_options;
+
+/*
+ * Gradient filter (opt-in, not exact).  The blog "最贵的一层：深入浅出 Liger
+ * Kernel 与 Cut Cross-Entropy" (§三) describes CCE skipping every backward tile
+ * whose softmax entries all lie below 2^-12, since in bf16 training such terms
+ * vanish in rounding once accumulated; the AI-infra KB page M011 (§06) warns
+ * that this drops gradient terms and is separate from the memory saving.
+ * With filter_eps > 0, lce_backward_ex and lce_shard_backward skip, in both
+ * gradient contractions, every block of 256 token rows by 256 vocabulary
+ * columns (aligned to multiples of 256) whose values (1 + 2l·LSE_i)·p_iv over
+ * rows with a target all lie below filter_eps.  The recomputation of the
+ * logits still runs in full and the one-hot term is always applied exactly.
+ * Not combined with label smoothing (LCE_ERR_INVALID_ARG); lce_forward_backward
+ * refuses filter_eps > 0; the forward calls ignore it.
+ */
 
 /* Fill *opt with the defaults listed above (host call). */
 void lce_options_default(lce_options* opt);

@@ -41,16 +41,18 @@ class Options(ctypes.Structure):
     """lce_options (include/lce.h)."""
     _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
                 ("logit_scale", ctypes.c_float), ("label_smoothing", ctypes.c_float),
-                ("z_loss", ctypes.c_float), ("reduction", ctypes.c_int32)]
+                ("z_loss", ctypes.c_float), ("reduction", ctypes.c_int32),
+                ("filter_eps", ctypes.c_float)]
 
 
 def make_options(ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
                  label_smoothing: float = 0.0, z_loss: float = 0.0,
-                 reduction: str = "mean") -> Options:
+                 reduction: str = "mean", filter_eps: float = 0.0) -> Options:
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}, got {reduction!r}")
     return Options(int(ignore_index), float(softcap), float(logit_scale),
-                   float(label_smoothing), float(z_loss), REDUCTIONS[reduction])
+                   float(label_smoothing), float(z_loss), REDUCTIONS[reduction],
+                   float(filter_eps))
 
 
 class KernelTiming(ctypes.Structure):
@@ -298,11 +300,14 @@ def lce_forward_ex(X, W, labels, ignore_index: int = -100, softcap: float = 0.0,
 
 def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap: float = 0.0,
                     logit_scale: float = 1.0, label_smoothing: float = 0.0, z_loss: float = 0.0,
-                    reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None):
+                    reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
+                    filter_eps: float = 0.0):
     """Backward with the loss variants.  `dloss`: a scalar (mean, sum) or an
-    [N] tensor of per-row upstream gradients (none).  Returns (dX, dW)."""
+    [N] tensor of per-row upstream gradients (none).  filter_eps > 0 turns on
+    the (non-exact) gradient filter.  Returns (dX, dW)."""
     import torch
-    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
+                       filter_eps)
     X, W, labels = _prep(X, W, labels)
     N, H = X.shape
     V = W.shape[0]
@@ -407,11 +412,13 @@ def lce_shard_merge(lse_parts, target_parts, labels, vocab_total: int, zsum_part
 def lce_shard_backward(X, W_shard, labels, lse, dloss, vocab_offset: int, vocab_total: int,
                        ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
                        label_smoothing: float = 0.0, z_loss: float = 0.0,
-                       reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None):
+                       reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
+                       filter_eps: float = 0.0):
     """Backward of one vocabulary shard given the merged LSE.  Returns
     (dX share [N, H], dW rows of the shard [V_shard, H])."""
     import torch
-    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction)
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
+                       filter_eps)
     X, W_shard, labels = _prep(X, W_shard, labels)
     N, H = X.shape
     Vs = W_shard.shape[0]

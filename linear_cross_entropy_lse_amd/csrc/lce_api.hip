@@ -32,10 +32,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool options_ok(const lce_options* o) {
   if (!o) return false;
   const bool finite = std::isfinite(o->softcap) && std::isfinite(o->logit_scale) &&
-                      std::isfinite(o->label_smoothing) && std::isfinite(o->z_loss);
+                      std::isfinite(o->label_smoothing) && std::isfinite(o->z_loss) &&
+                      std::isfinite(o->filter_eps);
   return finite && o->logit_scale > 0.0f && o->label_smoothing >= 0.0f &&
          o->label_smoothing <= 1.0f && o->z_loss >= 0.0f && o->reduction >= LCE_REDUCE_MEAN &&
-         o->reduction <= LCE_REDUCE_NONE;
+         o->reduction <= LCE_REDUCE_NONE && o->filter_eps >= 0.0f;
 }
 
 bool shape_ok(int64_t N, int64_t H, int64_t V) {
@@ -100,7 +101,7 @@ struct BwdPlan {
   int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
   int64_t Vc, ldg;
   size_t off_state, off_key, off_deriv, off_gs, off_c1, off_oh, off_keys_a, off_keys_b, off_head,
-      off_tail, off_blocks, off_scalars, off_G, off_dXp, off_dWs, total;
+      off_tail, off_blocks, off_scalars, off_flags, off_G, off_dXp, off_dWs, total;
 };
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
@@ -136,6 +137,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_tail = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
   p.off_scalars = o; o = align_up(o + 16);
+  p.off_flags = o;   o = align_up(o + sizeof(uint32_t) * (size_t)p.T * (size_t)p.n_vtiles_chunk);
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)N * (size_t)p.ldg);
   p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
   p.off_dWs = o;
@@ -374,6 +376,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
                          lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
   if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
+  if (opt->filter_eps > 0.0f && opt->label_smoothing > 0.0f) return LCE_ERR_INVALID_ARG;
   if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
     return LCE_ERR_INVALID_ARG;
   if (!dW_dev) return LCE_ERR_INVALID_ARG;
@@ -408,6 +411,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] plain scale, [1] = 1
   int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
   uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
+  uint32_t* flags = opt->filter_eps > 0.0f ? at<uint32_t>(workspace_dev, pl.off_flags) : nullptr;
   float* dXp = at<float>(workspace_dev, pl.off_dXp);
   float* dWs = at<float>(workspace_dev, pl.off_dWs);
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
@@ -440,6 +444,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
     gp.gs = general ? gs : nullptr; gp.c1 = c1;
     gp.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);
+    gp.flags = reinterpret_cast<uint8_t*>(flags); gp.filter_eps = opt->filter_eps;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 
     ChunkGemmParams cp{};
@@ -447,7 +452,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
-    cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0;
+    cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (dW_dtype == LCE_BF16) {
@@ -553,6 +558,7 @@ void lce_options_default(lce_options* opt) {
   opt->label_smoothing = 0.0f;
   opt->z_loss = 0.0f;
   opt->reduction = LCE_REDUCE_MEAN;
+  opt->filter_eps = 0.0f;
 }
 
 lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
@@ -700,6 +706,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
   // Label smoothing needs the softcap derivative apart from the softmax,
   // which the stored logits block does not keep.
   if (opt->label_smoothing > 0.0f && opt->softcap > 0.0f) return LCE_ERR_INVALID_ARG;
+  if (opt->filter_eps > 0.0f) return LCE_ERR_INVALID_ARG;
   if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
     return LCE_ERR_INVALID_ARG;
   if (N > 0 && (!X_dev || !W_dev || !labels_dev || !dloss_dev || !loss_dev || !lse_dev ||
@@ -793,6 +800,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = scalars + 1;
     cp.dW_dst = dW32;
     cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
+    cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
                                scalars + 1, fixed ? rrow + r0 : nullptr,

@@ -224,12 +224,16 @@ lse_partials_kernel(LseParams p) {
 // General form: G = gsc[ni]·(c1[ni]·p − eps_v)·d with the row's scale gsc (0
 // ignored, NaN bad) and Z-loss factor c1.  kMasked: the tile reaches past V
 // and rows with row_const >= lim are written as 0.
-template <bool kCapped, bool kMasked, bool kGen>
-__device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
+// kFilter: also report whether any value of the dense part compared by the
+// gradient filter, (1 + 2l·LSE)·p over rows with a target, is not below
+// `feps` (NaN counts as not below).
+template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false>
+__device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
                                                 const float (&gsc)[kNI], const float (&c1)[kNI],
                                                 float eps_v, __amdgpu_buffer_rsrc_t rs,
                                                 const uint32_t (&cb)[kNI], int lim, float k2,
-                                                float c2, float l2a) {
+                                                float c2, float l2a, float feps = 0.0f) {
+  bool active = false;
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
@@ -241,27 +245,41 @@ __device__ __forceinline__ void grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
         for (int q = 0; q < 4; ++q) {
           const int r = gq * 4 + q;
           const float z = acc[mi][ni][r];
-          float val;
+          float val, pr;
           if (kCapped) {
             const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
             const float d4 = 4.0f * rr;
-            const float pr = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
+            pr = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
             const float d = fmaf(-d4, rr, d4);
             val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) * d : pr * d;
           } else {
-            const float pr = exp2_fast(fmaf(z, l2a, off[ni]));
+            pr = exp2_fast(fmaf(z, l2a, off[ni]));
             val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
           }
           gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
+          if (kFilter) {
+            // Plain form: ignored rows have pr = 0, bad rows NaN.
+            const float fv = kGen ? (gsc[ni] != 0.0f ? c1[ni] * pr : 0.0f) : pr;
+            active |= (!kMasked || acc_row_const(mi, r) < lim) && !(fv < feps);
+          }
         }
         u32x2 packed;
         packed[0] = pack_bf16x2(gv[0], gv[1]);
         packed[1] = pack_bf16x2(gv[2], gv[3]);
         __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * acc_row_const(mi, gq * 4)), 0, 0);
       }
+  return active;
 }
 
-template <bool kTail, bool kCapped, bool kGen>
+// Filter flag of one wave's quarter of tile (ti, j): byte `wave` of word
+// ti·n_vtiles + j, written by lane 0.
+__device__ __forceinline__ void store_filter_flag(uint8_t* flags, bool active, int ti, int j,
+                                                  int n_vtiles, int wave, int lane) {
+  const bool any = __builtin_amdgcn_ballot_w64(active) != 0;
+  if (lane == 0) flags[((int64_t)ti * n_vtiles + j) * 4 + wave] = any ? 1 : 0;
+}
+
+template <bool kTail, bool kCapped, bool kGen, bool kFilter>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -321,7 +339,9 @@ grad_logits_kernel(GradParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
-    grad_store_tile<kCapped, false, kGen>(acc, off, gsc, c1, p.eps_over_v, rs, cb, 0, k2, c2, l2a);
+    const bool act = grad_store_tile<kCapped, false, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
+                                                                    cb, 0, k2, c2, l2a, p.filter_eps);
+    if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;
@@ -333,7 +353,9 @@ grad_logits_kernel(GradParams p) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    grad_store_tile<kCapped, true, kGen>(acc, off, gsc, c1, p.eps_over_v, rs, cb, lim, k2, c2, l2a);
+    const bool act = grad_store_tile<kCapped, true, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
+                                                                   cb, lim, k2, c2, l2a, p.filter_eps);
+    if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
@@ -527,6 +549,7 @@ flce_logits_kernel(FlceParams p) {
 // dX tile id g = part · (nt_tok · nt_h) + tile: K steps [part·D, (part+1)·D)
 // of the chunk, D = ceil(steps / ksplit), into partial buffer `part`.  The
 // host picks ksplit so that every part holds at least one step.
+template <bool kFilter>
 __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, int64_t D,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
   f32x16 acc[kMI][kNI];
@@ -539,8 +562,26 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
   const int64_t steps = (p.chunk_len + kBK - 1) / kBK;
   const int64_t k0 = (int64_t)part * D * kBK;
   const int64_t k_end = (part + 1) * D < steps ? (part + 1) * D * kBK : steps * kBK;
-  gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, k0, k_end, p.wc_rows,
-                                smem, acc);
+  if (kFilter) {
+    // Gradient filter (one K part): only the runs of vocabulary tiles with a
+    // value above the threshold for this token tile.
+    // Every value here is wave-uniform (kept in scalar registers).
+    const uint32_t* fr = p.flags + (int64_t)(t / p.nt_h) * p.nt_v;
+    const int nv = p.nt_v;
+    int j = 0;
+    while (true) {
+      while (j < nv && __builtin_amdgcn_readfirstlane(fr[j]) == 0u) ++j;
+      if (j >= nv) break;
+      const int ja = j;
+      while (j < nv && __builtin_amdgcn_readfirstlane(fr[j]) != 0u) ++j;
+      const int64_t kb = (int64_t)j * kTile < k_end ? (int64_t)j * kTile : k_end;
+      gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H,
+                                    (int64_t)ja * kTile, kb, p.wc_rows, smem, acc);
+    }
+  } else {
+    gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, k0, k_end, p.wc_rows,
+                                  smem, acc);
+  }
   // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
   // past H are pushed out of range.  The 64 previous values of one mi row
   // block are loaded together, so a tile costs 4 round trips, not 256.
@@ -577,14 +618,31 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
   }
 }
 
-template <bool kDwAcc>
+template <bool kDwAcc, bool kFilter>
 __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, float sc,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
   const int64_t h0 = (int64_t)(g % p.nt_h) * kTile;
-  gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem, acc);
+  if (kFilter) {
+    // Gradient filter: only the runs of token tiles with a value above the
+    // threshold in this vocabulary tile.
+    const uint32_t* fc = p.flags + g / p.nt_h;
+    const int nt = p.nt_tok, nv = p.nt_v;
+    int t = 0;
+    while (true) {
+      while (t < nt && __builtin_amdgcn_readfirstlane(fc[(int64_t)t * nv]) == 0u) ++t;
+      if (t >= nt) break;
+      const int ta = t;
+      while (t < nt && __builtin_amdgcn_readfirstlane(fc[(int64_t)t * nv]) != 0u) ++t;
+      const int64_t kb = (int64_t)t * kTile < p.N ? (int64_t)t * kTile : p.N;
+      gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, (int64_t)ta * kTile,
+                                   kb, p.N, smem, acc);
+    }
+  } else {
+    gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem, acc);
+  }
   // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
   // columns at or past H are pushed out of range.
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW_dst + vt0 * p.H, (p.chunk_len - vt0) * p.H * 4);
@@ -623,7 +681,7 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
   }
 }
 
-template <bool kDwAcc>
+template <bool kDwAcc, bool kFilter>
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_gemm_kernel(ChunkGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -646,15 +704,15 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
   const int nw_light = nw - nw_heavy;
 
-  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile(p, dx_lo + t, D, smem, wm, wn, lane);
+  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter>(p, dx_lo + t, D, smem, wm, wn, lane);
   const float sc = *p.scale;
   if (li >= rx) {
     const int nl = kCusPerXcd - rx;
     for (int t = li - rx; t < nw_light; t += nl)
-      chunk_dw_tile<kDwAcc>(p, dw_lo + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + t, sc, smem, wm, wn, lane);
   } else {
     for (int t = li; t < nw_heavy; t += rx)
-      chunk_dw_tile<kDwAcc>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
   }
 }
 
@@ -720,17 +778,23 @@ hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream) {
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
   const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f, gen = p.gs != nullptr;
-#define LCE_GRAD_LAUNCH(T_, C_, G_) \
-  hipLaunchKernelGGL((grad_logits_kernel<T_, C_, G_>), dim3(grid), dim3(kThreads), 0, stream, p)
-#define LCE_GRAD_TC(G_)                                   \
-  do {                                                    \
-    if (tail && capped) LCE_GRAD_LAUNCH(true, true, G_);  \
-    else if (tail) LCE_GRAD_LAUNCH(true, false, G_);      \
-    else if (capped) LCE_GRAD_LAUNCH(false, true, G_);    \
-    else LCE_GRAD_LAUNCH(false, false, G_);               \
+  const bool filt = p.flags != nullptr;
+#define LCE_GRAD_LAUNCH(T_, C_, G_, F_) \
+  hipLaunchKernelGGL((grad_logits_kernel<T_, C_, G_, F_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_GRAD_TC(G_, F_)                                   \
+  do {                                                        \
+    if (tail && capped) LCE_GRAD_LAUNCH(true, true, G_, F_);  \
+    else if (tail) LCE_GRAD_LAUNCH(true, false, G_, F_);      \
+    else if (capped) LCE_GRAD_LAUNCH(false, true, G_, F_);    \
+    else LCE_GRAD_LAUNCH(false, false, G_, F_);               \
   } while (0)
-  if (gen) LCE_GRAD_TC(true);
-  else LCE_GRAD_TC(false);
+  if (filt) {
+    if (gen) LCE_GRAD_TC(true, true);
+    else LCE_GRAD_TC(false, true);
+  } else {
+    if (gen) LCE_GRAD_TC(true, false);
+    else LCE_GRAD_TC(false, false);
+  }
 #undef LCE_GRAD_TC
 #undef LCE_GRAD_LAUNCH
   return hipGetLastError();
@@ -738,10 +802,15 @@ hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
   const int grid = kXcds * kCusPerXcd;
-  if (p.dw_accumulate)
-    hipLaunchKernelGGL(chunk_gemm_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  // The filtered form reads one flag word per tile and K part; it serves the
+  // recompute path only (one K part, dW written once).
+  if (p.flags && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
+  if (p.flags)
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (p.dw_accumulate)
+    hipLaunchKernelGGL((chunk_gemm_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(chunk_gemm_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

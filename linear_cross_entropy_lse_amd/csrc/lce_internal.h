@@ -39,6 +39,11 @@ struct GradParams {
   const float* gs;           // [N] per-row scale s_i·a (0 ignored, NaN bad)
   const float* c1;           // [N] 1 + 2l·LSE_i
   float eps_over_v;          // e / V
+  // Gradient filter: when flags is not null, byte w of word ti·n_vtiles + j
+  // is set to 1 if wave w of tile (ti, j) holds a value of (1 + 2l·LSE)·p,
+  // over rows with a target, that is not below filter_eps, else 0.
+  uint8_t* flags;
+  float filter_eps;
 };
 
 // dX and dW contractions of one vocabulary chunk, in one persistent launch of
@@ -62,6 +67,9 @@ struct ChunkGemmParams {
   int ksplit;
   int64_t dx_part_stride;
   int dw_accumulate;   // 1: dW_dst += s·Gᵀ·X instead of =
+  // Gradient filter words [nt_tok, nt_v] (non-zero: the tile's dense part is
+  // kept); null: every tile is kept.  Only with ksplit = 1.
+  const uint32_t* flags;
 };
 
 // Row-chunked forward with the logit gradient formed in the same pass: the

@@ -212,3 +212,14 @@ def test_fused_workspace_is_one_logits_block(lib, N, H, V):
     ws = lib.lce_fused_workspace_bytes(N, H, V, _lib.LCE_F32)
     assert 0 < ws < N * V * 2
     assert ws <= 2 * H * V + 16 * 4 * H * H + 64 * N + (64 << 20)
+
+
+def test_filter_option_checks(lib):
+    for bad in (dict(filter_eps=-1e-3), dict(filter_eps=float("nan")), dict(filter_eps=float("inf"))):
+        o = opts(**bad)
+        assert fwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+        assert bwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+    both = opts(filter_eps=2.0 ** -12, label_smoothing=0.1)
+    assert bwd_ex(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
+    assert fused(lib, ctypes.byref(opts(filter_eps=2.0 ** -12))) == _lib.LCE_ERR_INVALID_ARG
+    assert opts().filter_eps == 0.0
