@@ -7,7 +7,9 @@ reduced loss rel err <= 1e-4, dX and dW rel-L2 err <= 1e-3 in float32 and
 chunks hold 256 rows and every case runs several chunks with a ragged last
 one; they cover the three ways the stored logits are referenced (no
 softcap, a softcap small enough for the fixed reference, a large one) and
-every option the call takes.  The full-size case runs the Gemma-2 2B head.
+every option the call takes.  The full-size cases run the four large
+workloads (Liger example, Llama-3 8B, Gemma-2 2B, long Qwen2.5) against the
+stored oracle values.
 """
 import os
 
@@ -126,13 +128,15 @@ def test_fused_rejects_smoothing_with_softcap(lce):
         lce.lce_forward_backward(X, W, y, 1.0, softcap=30.0, label_smoothing=0.1)
 
 
-def test_fused_gemma_fullsize(lce):
-    """Gemma-2 2B head in one fused call against the stored oracle values."""
-    gold = np.load(os.path.join(HERE, "golden", "fullsize_gemma2_2b.npz"))
-    w = L.WORKLOADS["gemma2_2b"]
+@pytest.mark.parametrize("name", ["gemma2_2b", "llama3_8b", "liger", "qwen25_long"])
+def test_fused_fullsize(lce, name):
+    """Each large workload in one fused call against the stored oracle values
+    (every row's LSE and loss, sampled dX and dW rows)."""
+    gold = np.load(os.path.join(HERE, "golden", f"fullsize_{name}.npz"))
+    w = L.WORKLOADS[name]
     X, W, y = L.make_inputs(w)
     assert L.fingerprint(X, W, y) == str(gold["fingerprint"])
-    print("[fused] gemma2_2b full size", flush=True)
+    print(f"[fused] {name} full size: N={w.N} H={w.H} V={w.V} softcap={w.softcap}", flush=True)
     dev = "cuda"
     out, dX, dW = lce.lce_forward_backward(X.to(dev), W.to(dev), y.to(dev), 1.0,
                                            softcap=w.softcap)
@@ -143,7 +147,7 @@ def test_fused_gemma_fullsize(lce):
     mean, gmean = float(out["reduced"]), float(gold["mean"])
     e_dx = rel_l2(dX[torch.from_numpy(gold["dx_rows"]).to(dev)].cpu(), gold["dX"])
     e_dw = rel_l2(dW[torch.from_numpy(gold["dw_rows"]).to(dev)].cpu(), gold["dW"])
-    print(f"[fused] gemma: lse {e_lse:.2e} loss {e_loss:.2e} mean rel "
+    print(f"[fused] {name}: lse {e_lse:.2e} loss {e_loss:.2e} mean rel "
           f"{abs(mean - gmean) / abs(gmean):.2e} dX {e_dx:.2e} dW {e_dw:.2e}", flush=True)
     assert e_lse <= LSE_ATOL and e_loss <= LSE_ATOL
     assert abs(mean - gmean) <= RED_RTOL * abs(gmean)
