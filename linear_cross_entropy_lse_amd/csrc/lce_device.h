@@ -245,6 +245,95 @@ struct DtlMNMajorTile {
   }
 };
 
+// ----------------------------------------------------------------------------
+// Blocked layout of the logit-gradient chunk G.  For token tile t and
+// chunk-local vocabulary tile j, the 256 x 256 block sits at element
+// (t·nvt + j)·65536 and is stored as 4 sub-blocks of 64 vocabulary columns,
+// each 256 token rows of 64 contiguous values:
+//   G[tok][v] at (t·nvt + j)·65536 + (v%256 / 64)·16384 + (tok%256)·64 + v%64.
+// Every pipeline step of both contractions then reads contiguous memory: a
+// 64-column K step of dX (tokens x vocabulary) is one 32 KiB sub-block, a
+// 64-row K step of dW (vocabulary x tokens) four 8 KiB pieces.  Rows of the
+// last token tile past N are stored as zeros by the writer.
+// ----------------------------------------------------------------------------
+constexpr int64_t kGBlockElems = (int64_t)kTile * kTile;  // one 256 x 256 block
+constexpr int64_t kGSubElems = (int64_t)kTile * kBK;      // one 256 x 64 sub-block
+
+// K-major reader of blocked G for the dX contraction: rows are the tokens of
+// one token tile, K the chunk's vocabulary.  init(G, nvt, tok0, ...): the
+// second argument is the chunk's count of vocabulary tiles.
+struct DtlKMajorBlockedG {
+  rsrc_t rsrc;
+  uint32_t voff, row_step;
+  int32_t wave;
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t nvt, int64_t row0,
+                                       int64_t /*rows_total*/, int64_t /*k_total*/, int tid) {
+    rsrc = make_rsrc_raw(base + (row0 / kTile) * nvt * kGBlockElems, nvt * kGBlockElems * 2);
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = wave * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    voff = (uint32_t)(row * kBK * 2 + c * 16);
+    row_step = (uint32_t)(32 * kBK * 2);
+  }
+  struct Step {
+    uint32_t base;
+  };
+  // K step k0 (a multiple of 64) is sub-block k0 / 64 of the token tile.
+  __device__ __forceinline__ Step prepare(int64_t k0) const {
+    return Step{voff + (uint32_t)(k0 / kBK) * (uint32_t)(kGSubElems * 2)};
+  }
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
+    dtl16(rsrc, stage + wave * 512 + i * 2048, st.base + i * row_step);
+  }
+  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+    const Step st = prepare(k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue(st, stage, i);
+  }
+};
+
+// MN-major reader of blocked G for the dW contraction: M is the chunk-local
+// vocabulary tile starting at col0 (a multiple of 256), K the tokens.  Same
+// lane-to-LDS mapping as DtlMNMajorTile (LDS row k, swizzled 16-byte chunk
+// c of 8 columns); only the global address differs.  init(G, nvt, col0, ...).
+struct DtlMNMajorBlockedG {
+  const uint16_t* base;
+  int64_t nvt, vt;
+  uint32_t voff, row_step;
+  int32_t wave;
+  __device__ __forceinline__ void init(const uint16_t* base_, int64_t nvt_, int64_t col0,
+                                       int64_t /*cols_total*/, int64_t /*k_total*/, int tid) {
+    base = base_;
+    nvt = nvt_;
+    vt = col0 / kTile;
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = 2 * wave + (lane >> 5);  // + 8i for block 4i + wave
+    const int c = (lane & 31) ^ ((row & 3) << 2);
+    voff = (uint32_t)((c >> 3) * kGSubElems * 2 + row * kBK * 2 + (c & 7) * 16);
+    row_step = (uint32_t)(8 * kBK * 2);
+  }
+  struct Step {
+    rsrc_t rsrc;
+  };
+  // K step k0 (64 tokens of token tile k0 / 256): a descriptor from the
+  // step's first row to the end of the block.
+  __device__ __forceinline__ Step prepare(int64_t k0) const {
+    const int64_t blk = ((k0 / kTile) * nvt + vt) * kGBlockElems;
+    const int64_t first = (k0 % kTile) * kBK;
+    return Step{make_rsrc_raw(base + blk + first, (kGBlockElems - first) * 2)};
+  }
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
+    dtl16(st.rsrc, stage + wave * 512 + i * 2048, voff + i * row_step);
+  }
+  __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
+    const Step st = prepare(k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue(st, stage, i);
+  }
+};
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -376,16 +465,23 @@ struct Sweep {
 // caller issues other memory operations between two tiles, so a preloaded
 // tile waits for all of them (vmcnt 0) instead of only for its step 0.  The
 // caller waits for vmcnt 0 after the sweep before reusing the LDS.
-template <bool kAmn, bool kBmn, bool kTail, bool kSweep = false, bool kWaitAll = false>
+//
+// kABlk: A is the blocked gradient chunk (DtlKMajorBlockedG / DtlMNMajorBlockedG);
+// `lda` is then the chunk's count of vocabulary tiles.
+template <bool kAmn, bool kBmn, bool kTail, bool kSweep = false, bool kWaitAll = false,
+          bool kABlk = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_t a_row0,
                                           int64_t a_rows, const uint16_t* B, int64_t ldb,
                                           int64_t b_row0, int64_t b_rows, int64_t k_begin,
                                           int64_t k_end, int64_t k_total, LCE_LDS uint16_t* smem,
                                           f32x16 (&acc)[kMI][kNI], Sweep* sw = nullptr,
                                           int64_t next_a_row0 = -1) {
-  typedef typename std::conditional<kAmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LA;
+  typedef typename std::conditional<
+      kABlk, typename std::conditional<kAmn, DtlMNMajorBlockedG, DtlKMajorBlockedG>::type,
+      typename std::conditional<kAmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type>::type LA;
   typedef typename std::conditional<kBmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LB;
   static_assert(!kSweep || (!kAmn && !kBmn), "the sweep prefetch handles K-major operands");
+  static_assert(!kSweep || !kABlk, "the sweep prefetch reads row-major operands");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int nsteps = (int)((k_end - k_begin + kBK - 1) / kBK);

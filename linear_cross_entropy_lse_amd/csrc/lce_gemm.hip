@@ -227,7 +227,10 @@ lse_partials_kernel(LseParams p) {
 // kFilter: also report whether any value of the dense part compared by the
 // gradient filter, (1 + 2l·LSE)·p over rows with a target, is not below
 // `feps` (NaN counts as not below).
-template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false>
+// kBlk: the store offsets follow the blocked G layout (sub-block mi/2, column
+// (mi%2)·32 + 8gq within it); otherwise row-major with row offsets
+// acc_row_const(mi, 4gq).
+template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false, bool kBlk = false>
 __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
                                                 const float (&gsc)[kNI], const float (&c1)[kNI],
                                                 float eps_v, __amdgpu_buffer_rsrc_t rs,
@@ -266,7 +269,9 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
         u32x2 packed;
         packed[0] = pack_bf16x2(gv[0], gv[1]);
         packed[1] = pack_bf16x2(gv[2], gv[3]);
-        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * acc_row_const(mi, gq * 4)), 0, 0);
+        const uint32_t eo = kBlk ? (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 8 * gq)
+                                 : (uint32_t)acc_row_const(mi, gq * 4);
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * eo), 0, 0);
       }
   return active;
 }
@@ -317,10 +322,15 @@ grad_logits_kernel(GradParams p) {
       gsc[ni] = 1.0f;
       c1[ni] = 1.0f;
     }
-    col_base[ni] = (uint32_t)(col * p.ldg * 2 + acc_row_lane(wm, lane) * 2);
+    // Blocked G (see DtlKMajorBlockedG): this lane's 4 consecutive vocabulary
+    // rows r0 = acc_row_lane + acc_row_const(mi, 4gq) lie in sub-block
+    // 2wm + mi/2 at column (mi%2)·32 + 8gq + 4(lane/32) of token row col.
+    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + col * kBK + 4 * (lane >> 5)) * 2);
   }
-  // G rows tok0 .. N − 1; a tile's offsets stay below 256 · ldg · 2 bytes.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + tok0 * p.ldg, (p.N - tok0) * p.ldg * 2);
+  // The whole token tile, padding rows past N included (they get zeros, which
+  // the dW contraction reads).
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + (int64_t)ti * p.n_vtiles * kGBlockElems,
+                                              p.n_vtiles * kGBlockElems * 2);
 
   // Chunk-local tiles j < j_mid lie below V; the tile that reaches past V (at
   // most one) runs in a loop of its own with the masked store.
@@ -338,8 +348,8 @@ grad_logits_kernel(GradParams p) {
                                                j + 1 < j1 ? p.v_begin + vloc0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
-    const bool act = grad_store_tile<kCapped, false, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
+    const bool act = grad_store_tile<kCapped, false, kGen, kFilter, true>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                     cb, 0, k2, c2, l2a, p.filter_eps);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
@@ -351,9 +361,9 @@ grad_logits_kernel(GradParams p) {
                                                smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(vloc0 * 2);
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    const bool act = grad_store_tile<kCapped, true, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
+    const bool act = grad_store_tile<kCapped, true, kGen, kFilter, true>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                    cb, lim, k2, c2, l2a, p.filter_eps);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
@@ -549,9 +559,11 @@ flce_logits_kernel(FlceParams p) {
 // dX tile id g = part · (nt_tok · nt_h) + tile: K steps [part·D, (part+1)·D)
 // of the chunk, D = ceil(steps / ksplit), into partial buffer `part`.  The
 // host picks ksplit so that every part holds at least one step.
-template <bool kFilter>
+template <bool kFilter, bool kGBlk>
 __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, int64_t D,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
+  // Blocked G: the A reader takes the chunk's count of vocabulary tiles.
+  const int64_t lda = kGBlk ? (int64_t)p.nt_v : p.ldg;
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   const int n_tiles = p.nt_tok * p.nt_h;
@@ -575,12 +587,13 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
       const int ja = j;
       while (j < nv && __builtin_amdgcn_readfirstlane(fr[j]) != 0u) ++j;
       const int64_t kb = (int64_t)j * kTile < k_end ? (int64_t)j * kTile : k_end;
-      gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H,
-                                    (int64_t)ja * kTile, kb, p.wc_rows, smem, acc);
+      gemm_tile<false, true, false, false, false, kGBlk>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H,
+                                                         (int64_t)ja * kTile, kb, p.wc_rows, smem,
+                                                         acc);
     }
   } else {
-    gemm_tile<false, true, false>(p.G, p.ldg, tok0, p.N, p.Wc, p.H, h0, p.H, k0, k_end, p.wc_rows,
-                                  smem, acc);
+    gemm_tile<false, true, false, false, false, kGBlk>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H, k0,
+                                                       k_end, p.wc_rows, smem, acc);
   }
   // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
   // past H are pushed out of range.  The 64 previous values of one mi row
@@ -618,9 +631,10 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
   }
 }
 
-template <bool kDwAcc, bool kFilter>
+template <bool kDwAcc, bool kFilter, bool kGBlk>
 __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, float sc,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
+  const int64_t lda = kGBlk ? (int64_t)p.nt_v : p.ldg;
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
@@ -637,11 +651,12 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
       const int ta = t;
       while (t < nt && __builtin_amdgcn_readfirstlane(fc[(int64_t)t * nv]) != 0u) ++t;
       const int64_t kb = (int64_t)t * kTile < p.N ? (int64_t)t * kTile : p.N;
-      gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, (int64_t)ta * kTile,
-                                   kb, p.N, smem, acc);
+      gemm_tile<true, true, false, false, false, kGBlk>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H,
+                                                        (int64_t)ta * kTile, kb, p.N, smem, acc);
     }
   } else {
-    gemm_tile<true, true, false>(p.G, p.ldg, vt0, p.ldg, p.X, p.H, h0, p.H, 0, p.N, p.N, smem, acc);
+    gemm_tile<true, true, false, false, false, kGBlk>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H, 0,
+                                                      p.N, p.N, smem, acc);
   }
   // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
   // columns at or past H are pushed out of range.
@@ -681,7 +696,7 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
   }
 }
 
-template <bool kDwAcc, bool kFilter>
+template <bool kDwAcc, bool kFilter, bool kGBlk>
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_gemm_kernel(ChunkGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -704,15 +719,15 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
   const int nw_light = nw - nw_heavy;
 
-  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter>(p, dx_lo + t, D, smem, wm, wn, lane);
+  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter, kGBlk>(p, dx_lo + t, D, smem, wm, wn, lane);
   const float sc = *p.scale;
   if (li >= rx) {
     const int nl = kCusPerXcd - rx;
     for (int t = li - rx; t < nw_light; t += nl)
-      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter, kGBlk>(p, dw_lo + t, sc, smem, wm, wn, lane);
   } else {
     for (int t = li; t < nw_heavy; t += rx)
-      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter, kGBlk>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
   }
 }
 
@@ -804,13 +819,18 @@ hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
   const int grid = kXcds * kCusPerXcd;
   // The filtered form reads one flag word per tile and K part; it serves the
   // recompute path only (one K part, dW written once).
-  if (p.flags && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
+  // The blocked G comes from the logit-gradient kernel (recompute path: one
+  // K part, dW written once); the fused call's logits block is row-major.
+  if ((p.flags || p.g_blocked) && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
+  if (p.flags && !p.g_blocked) return hipErrorInvalidValue;
   if (p.flags)
-    hipLaunchKernelGGL((chunk_gemm_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else if (p.g_blocked)
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if (p.dw_accumulate)
-    hipLaunchKernelGGL((chunk_gemm_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<true, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_gemm_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

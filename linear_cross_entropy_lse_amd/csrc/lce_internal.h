@@ -32,7 +32,10 @@ struct GradParams {
   float logit_scale;
   const float* lse;          // [N]
   const int32_t* row_state;  // [N]
-  uint16_t* G;               // bf16 [N, ldg]
+  // bf16, blocked: block (token tile t, chunk-local vocabulary tile j) at
+  // element (t·n_vtiles + j)·65536, as 4 sub-blocks of 256 token rows by 64
+  // columns; rows past N hold zeros.  ldg is unused.
+  uint16_t* G;
   int64_t ldg;
   // General form (label smoothing, Z-loss, per-row upstream gradient):
   // G = gs_i·(c1_i·p − eps_over_v)·d; null gs selects the plain G = p·d.
@@ -70,6 +73,9 @@ struct ChunkGemmParams {
   // Gradient filter words [nt_tok, nt_v] (non-zero: the tile's dense part is
   // kept); null: every tile is kept.  Only with ksplit = 1.
   const uint32_t* flags;
+  // 1: G is in the blocked layout the logit-gradient kernel writes (256 x 256
+  // blocks, nt_v per token tile; ldg is then unused); 0: row-major [N, ldg].
+  int g_blocked;
 };
 
 // Row-chunked forward with the logit gradient formed in the same pass: the
