@@ -93,7 +93,8 @@ def test_fullsize_against_oracle(lce, name):
     # workspace, and nothing the size of the logits.
     ws = lce.lce_backward_workspace_bytes(w.N, w.H, w.V)
     outputs = w.N * w.H * 4 + w.V * w.H * 4 + 5 * w.N * 4
-    assert peak <= ws + outputs + (1 << 20), (peak, ws, outputs)
+    # (slack for the caching allocator's rounding of each allocation)
+    assert peak <= ws + outputs + (8 << 20), (peak, ws, outputs)
     # The workspace is O(N·H + V·H): one bf16 gradient chunk no larger than W
     # and the float32 dX accumulator.
     assert ws <= 2 * w.V * w.H + 4 * w.N * w.H + (64 << 20), ws
