@@ -266,7 +266,7 @@ def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, d
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+        print("bench.py: this benchmark measures one GPU only (no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
