@@ -454,7 +454,6 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
     cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
-    cp.g_blocked = 1;
     cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (dW_dtype == LCE_BF16) {
@@ -802,7 +801,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = scalars + 1;
     cp.dW_dst = dW32;
     cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
-    cp.flags = nullptr; cp.g_blocked = 0;
+    cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
                                scalars + 1, fixed ? rrow + r0 : nullptr,

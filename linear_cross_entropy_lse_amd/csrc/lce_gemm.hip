@@ -445,7 +445,9 @@ __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kN
         u32x2 packed;
         packed[0] = pack_bf16x2(uv[0], uv[1]);
         packed[1] = pack_bf16x2(uv[2], uv[3]);
-        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * acc_row_const(mi, gq * 4)), 0, 0);
+        // Blocked layout (as the recompute path's gradient chunk).
+        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 8 * gq);
+        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * eo), 0, 0);
       }
     s[ni] += sum;
     if (kZSum) zs[ni] += zsum;
@@ -489,10 +491,13 @@ flce_logits_kernel(FlceParams p) {
     m[ni] = kMode == kCapFixed ? c2 : -__builtin_inff();
     s[ni] = 0.0f;
     zs[ni] = 0.0f;
-    col_base[ni] = (uint32_t)(acc_col(wn, ni, lane) * p.ldu * 2 + acc_row_lane(wm, lane) * 2);
+    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + acc_col(wn, ni, lane) * kBK + 4 * (lane >> 5)) * 2);
   }
-  // U rows tok0 .. N − 1; a tile's offsets stay below 256 · ldu · 2 bytes.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.U + tok0 * p.ldu, (p.N - tok0) * p.ldu * 2);
+  // U is blocked like the recompute path's gradient chunk: the token tile's
+  // n_vtiles blocks, rows past N included (their values are finite and meet
+  // only zero rows of X in the dW contraction).
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.U + (int64_t)ti * p.n_vtiles * kGBlockElems,
+                                              p.n_vtiles * kGBlockElems * 2);
   // ref rows tok0 .. N − 1 (unused with the fixed reference).
   const __amdgpu_buffer_rsrc_t rr =
       make_rsrc(kMode != kCapFixed ? p.ref + tok0 * nref : p.part_m, kMode != kCapFixed ? (p.N - tok0) * nref * 4 : 0);
@@ -511,7 +516,7 @@ flce_logits_kernel(FlceParams p) {
                                                p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(v0 * 2);
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     flce_fold_store_tile<kMode, false, kZSum>(acc, m, s, zs, 0, k2, c2, l2a, rs, cb);
     if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
   }
@@ -522,7 +527,7 @@ flce_logits_kernel(FlceParams p) {
                                                p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(v0 * 2);
+    for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
     flce_fold_store_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a, rs, cb);
     if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
@@ -559,11 +564,10 @@ flce_logits_kernel(FlceParams p) {
 // dX tile id g = part · (nt_tok · nt_h) + tile: K steps [part·D, (part+1)·D)
 // of the chunk, D = ceil(steps / ksplit), into partial buffer `part`.  The
 // host picks ksplit so that every part holds at least one step.
-template <bool kFilter, bool kGBlk>
+template <bool kFilter>
 __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, int64_t D,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
-  // Blocked G: the A reader takes the chunk's count of vocabulary tiles.
-  const int64_t lda = kGBlk ? (int64_t)p.nt_v : p.ldg;
+  const int64_t lda = p.nt_v;   // blocked G: its reader takes the count of vocabulary tiles
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   const int n_tiles = p.nt_tok * p.nt_h;
@@ -587,12 +591,12 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
       const int ja = j;
       while (j < nv && __builtin_amdgcn_readfirstlane(fr[j]) != 0u) ++j;
       const int64_t kb = (int64_t)j * kTile < k_end ? (int64_t)j * kTile : k_end;
-      gemm_tile<false, true, false, false, false, kGBlk>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H,
+      gemm_tile<false, true, false, false, false, true>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H,
                                                          (int64_t)ja * kTile, kb, p.wc_rows, smem,
                                                          acc);
     }
   } else {
-    gemm_tile<false, true, false, false, false, kGBlk>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H, k0,
+    gemm_tile<false, true, false, false, false, true>(p.G, lda, tok0, p.N, p.Wc, p.H, h0, p.H, k0,
                                                        k_end, p.wc_rows, smem, acc);
   }
   // dX_acc rows tok0.. through a descriptor that ends at row N; columns at or
@@ -631,10 +635,10 @@ __device__ __forceinline__ void chunk_dx_tile(const ChunkGemmParams& p, int g, i
   }
 }
 
-template <bool kDwAcc, bool kFilter, bool kGBlk>
+template <bool kDwAcc, bool kFilter>
 __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, float sc,
                                               LCE_LDS uint16_t* smem, int wm, int wn, int lane) {
-  const int64_t lda = kGBlk ? (int64_t)p.nt_v : p.ldg;
+  const int64_t lda = p.nt_v;   // blocked G: its reader takes the count of vocabulary tiles
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   const int64_t vt0 = (int64_t)(g / p.nt_h) * kTile;
@@ -651,11 +655,11 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
       const int ta = t;
       while (t < nt && __builtin_amdgcn_readfirstlane(fc[(int64_t)t * nv]) != 0u) ++t;
       const int64_t kb = (int64_t)t * kTile < p.N ? (int64_t)t * kTile : p.N;
-      gemm_tile<true, true, false, false, false, kGBlk>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H,
+      gemm_tile<true, true, false, false, false, true>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H,
                                                         (int64_t)ta * kTile, kb, p.N, smem, acc);
     }
   } else {
-    gemm_tile<true, true, false, false, false, kGBlk>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H, 0,
+    gemm_tile<true, true, false, false, false, true>(p.G, lda, vt0, p.ldg, p.X, p.H, h0, p.H, 0,
                                                       p.N, p.N, smem, acc);
   }
   // dW rows vt0.. of the chunk through a descriptor that ends at chunk_len;
@@ -696,7 +700,7 @@ __device__ __forceinline__ void chunk_dw_tile(const ChunkGemmParams& p, int g, f
   }
 }
 
-template <bool kDwAcc, bool kFilter, bool kGBlk>
+template <bool kDwAcc, bool kFilter>
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_gemm_kernel(ChunkGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -719,15 +723,15 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
   const int nw_light = nw - nw_heavy;
 
-  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter, kGBlk>(p, dx_lo + t, D, smem, wm, wn, lane);
+  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter>(p, dx_lo + t, D, smem, wm, wn, lane);
   const float sc = *p.scale;
   if (li >= rx) {
     const int nl = kCusPerXcd - rx;
     for (int t = li - rx; t < nw_light; t += nl)
-      chunk_dw_tile<kDwAcc, kFilter, kGBlk>(p, dw_lo + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + t, sc, smem, wm, wn, lane);
   } else {
     for (int t = li; t < nw_heavy; t += rx)
-      chunk_dw_tile<kDwAcc, kFilter, kGBlk>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
+      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
   }
 }
 
@@ -819,18 +823,15 @@ hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
   const int grid = kXcds * kCusPerXcd;
   // The filtered form reads one flag word per tile and K part; it serves the
   // recompute path only (one K part, dW written once).
-  // The blocked G comes from the logit-gradient kernel (recompute path: one
-  // K part, dW written once); the fused call's logits block is row-major.
-  if ((p.flags || p.g_blocked) && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
-  if (p.flags && !p.g_blocked) return hipErrorInvalidValue;
+  // The filtered form reads one flag word per tile and K part: recompute path
+  // only (one K part, dW written once).
+  if (p.flags && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
   if (p.flags)
-    hipLaunchKernelGGL((chunk_gemm_kernel<false, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-  else if (p.g_blocked)
-    hipLaunchKernelGGL((chunk_gemm_kernel<false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else if (p.dw_accumulate)
-    hipLaunchKernelGGL((chunk_gemm_kernel<true, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_gemm_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_gemm_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -53,7 +53,10 @@ struct GradParams {
 // kXcds x kCusPerXcd workgroups: nt_tok·nt_h tiles of dX_acc (+)= G · W_chunk
 // and nt_v·nt_h tiles of dW_chunk = s·Gᵀ·X.
 struct ChunkGemmParams {
-  const uint16_t* G;   // bf16 [N, ldg], chunk-local vocabulary columns (0 past V)
+  // bf16, blocked (see DtlKMajorBlocked): nt_v blocks of 256 x 256 per token
+  // tile, chunk-local vocabulary columns (0 past V), padding rows past N
+  // finite.  ldg = 256·nt_v.
+  const uint16_t* G;
   int64_t ldg;
   const uint16_t* Wc;  // W + v_begin · H
   int64_t wc_rows;     // V − v_begin (rows of W readable from Wc)
@@ -73,9 +76,6 @@ struct ChunkGemmParams {
   // Gradient filter words [nt_tok, nt_v] (non-zero: the tile's dense part is
   // kept); null: every tile is kept.  Only with ksplit = 1.
   const uint32_t* flags;
-  // 1: G is in the blocked layout the logit-gradient kernel writes (256 x 256
-  // blocks, nt_v per token tile; ldg is then unused); 0: row-major [N, ldg].
-  int g_blocked;
 };
 
 // Row-chunked forward with the logit gradient formed in the same pass: the
@@ -95,7 +95,7 @@ struct FlceParams {
   float* part_m;       // [S, N]
   float* part_s;       // [S, N]
   float* part_z;       // [S, N] or null
-  uint16_t* U;         // bf16 [N, ldu]
+  uint16_t* U;         // bf16, blocked like ChunkGemmParams::G (n_vtiles blocks per token tile)
   int64_t ldu;         // n_vtiles · 256
   // Reference of each row's 128-column block (base 2), [N, 2·n_vtiles]: the
   // running max of the row's split up to and including that block's tile.
@@ -202,9 +202,10 @@ hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_str
                               const float* oh, const uint16_t* W, const float* sx,
                               const float* sx_rows, void* dX, int dX_bf16, hipStream_t stream);
 
-// Fused forward, generic reference: in place, U[i][v] becomes the gradient
-// G = gs_i·(c1_i·U·2^(ref_i,v/128 − lse_i·log2 e) − eps_over_v) for v < V and
-// 0 for V <= v < ldu.  ref == null: the fixed reference c2 for every block.
+// Fused forward, generic reference: in place (blocked layout), U[i][v]
+// becomes the gradient G = gs_i·(c1_i·U·2^(ref_i,v/128 − lse_i·log2 e) −
+// eps_over_v) for rows i < N and v < V, 0 for V <= v < ldu; padding rows stay
+// as they are.  ref == null: the fixed reference c2 for every block.
 hipError_t launch_flce_scale(uint16_t* U, int64_t ldu, int64_t N, int64_t V, const float* ref,
                              int nref, float c2, const float* lse, const float* gs,
                              const float* c1, float eps_over_v, hipStream_t stream);

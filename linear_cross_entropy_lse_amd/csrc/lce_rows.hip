@@ -513,21 +513,26 @@ hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_str
 
 // ---------------------------------------------------------------------------
 // Fused row-chunk variant: turn the stored U = 2^(u − ref)·d of a chunk into
-// the logit gradient (see launch_flce_scale), 8 bf16 values per thread; a
-// 128-column block shares one reference, so one exponential serves a thread.
+// the logit gradient (see launch_flce_scale).  U is blocked: each thread takes
+// 16 consecutive bytes, 8 columns of one token row inside a 64-column
+// sub-block, so one reference (one exponential) serves a thread.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-flce_scale_kernel(uint16_t* __restrict__ U, int64_t ldu, int64_t V, const float* __restrict__ ref,
-                  int nref, float c2, const float* __restrict__ lse, const float* __restrict__ gs,
+flce_scale_kernel(uint16_t* __restrict__ U, int64_t nvt, int64_t N, int64_t V, int64_t total,
+                  const float* __restrict__ ref, int nref, float c2,
+                  const float* __restrict__ lse, const float* __restrict__ gs,
                   const float* __restrict__ c1, float eps_over_v) {
-  const int64_t row = blockIdx.y;
-  const int64_t col0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (col0 >= ldu) return;
+  const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (o >= total) return;
+  const int64_t blk = o / 65536, rem = o % 65536;
+  const int64_t row = blk / nvt * 256 + (rem % 16384) / 64;
+  if (row >= N) return;
+  const int64_t col0 = blk % nvt * 256 + rem / 16384 * 64 + rem % 64;
   const float g = gs[row];
   const float r = ref ? ref[row * nref + col0 / 128] : c2;
   const float f = g * c1[row] * exp2f(r - lse[row] * kLog2e);
   const float eb = g * eps_over_v;
-  uint16_t* p = U + row * ldu + col0;
+  uint16_t* p = U + o;
   const u32x4 in = *reinterpret_cast<const u32x4*>(p);
   u32x4 out;
 #pragma unroll
@@ -543,9 +548,11 @@ flce_scale_kernel(uint16_t* __restrict__ U, int64_t ldu, int64_t V, const float*
 hipError_t launch_flce_scale(uint16_t* U, int64_t ldu, int64_t N, int64_t V, const float* ref,
                              int nref, float c2, const float* lse, const float* gs,
                              const float* c1, float eps_over_v, hipStream_t stream) {
-  const int64_t per_block = 256 * 8;
-  hipLaunchKernelGGL(flce_scale_kernel, dim3((unsigned)((ldu + per_block - 1) / per_block), (unsigned)N),
-                     dim3(256), 0, stream, U, ldu, V, ref, nref, c2, lse, gs, c1, eps_over_v);
+  const int64_t nvt = ldu / 256;
+  const int64_t total = (N + 255) / 256 * 256 * ldu;
+  const int64_t threads = total / 8;
+  hipLaunchKernelGGL(flce_scale_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, U, nvt, N, V, total, ref, nref, c2, lse, gs, c1, eps_over_v);
   return hipGetLastError();
 }
 
