@@ -113,3 +113,28 @@ def test_filter_refused_with_smoothing(lce):
     lse = lce.lce_forward_ex(X, W, y)["lse"]
     with pytest.raises(lce.LceError):
         lce.lce_backward_ex(X, W, y, lse, 1.0, label_smoothing=0.1, filter_eps=1e-3)
+
+
+def test_filter_with_vocabulary_shards(lce):
+    """Shards cut at multiples of 256 keep the filter blocks intact, so the
+    filtered shard gradients add up to the filtered whole-vocabulary ones."""
+    w = L.Workload("filter", N=700, H=64, V=3000, labels="zipf", ignore_frac=0.1, seed=7700)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 6.0).to(torch.bfloat16)
+    o = O.options()
+    X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+    f = O.forward_ex(X64, W64, y64, o)
+    eps = pick_threshold(O.filter_block_max(X64, W64, y64, f["lse"], o))
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    lse = lce.lce_forward_ex(Xd, Wd, yd)["lse"]
+    edges = [0, 1024, 2048, 3000]
+    dX, dWs = None, []
+    for a, b in zip(edges[:-1], edges[1:]):
+        gx, gw = lce.lce_shard_backward(Xd, Wd[a:b], yd, lse, 1.0, a, 3000, filter_eps=eps)
+        dX = gx if dX is None else dX + gx
+        dWs.append(gw)
+    torch.cuda.synchronize()
+    rX, rW = O.backward_filtered(X64, W64, y64, 1.0, o, eps)
+    assert rel_l2(dX.cpu(), rX) <= GRAD_RTOL
+    assert rel_l2(torch.cat(dWs).cpu(), rW) <= GRAD_RTOL

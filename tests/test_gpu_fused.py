@@ -52,6 +52,8 @@ CASES = [
     (800, 64, 5003, dict(softcap=30.0, logit_scale=1.3, reduction="none")),
     (513, 72, 900, dict(label_smoothing=0.1, z_loss=1e-2, reduction="sum")),
     (300, 64, 777, dict(logit_scale=0.6, reduction="none", label_smoothing=0.05)),
+    (100, 64, 300, dict(softcap=20.0)),                            # N < 256, one partial tile
+    (257, 8, 40, dict(z_loss=1e-2)),                               # tiny H and V
 ]
 
 
