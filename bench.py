@@ -203,6 +203,10 @@ def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, 
             "tokens_per_s": round(N / (ms / 1e3), 1),
             "tflops_8nhv": round(8 * N * H * V / (ms / 1e3) / 1e12, 1),
             "tflops_executed_6nhv": round(6 * N * H * V / (ms / 1e3) / 1e12, 1),
+            "frac_of_bf16_dense_peak_8nhv": round(8 * N * H * V / (ms / 1e3) / 1e12 /
+                                                  BF16_DENSE_PEAK_TFLOPS, 4),
+            "frac_of_bf16_dense_peak_executed": round(6 * N * H * V / (ms / 1e3) / 1e12 /
+                                                      BF16_DENSE_PEAK_TFLOPS, 4),
             "workspace_bytes": int(ws_n),
             "mean_loss": float(mean.item()),
             "note": "lce_forward_backward: row chunks of at most H rows, logits block kept in "
