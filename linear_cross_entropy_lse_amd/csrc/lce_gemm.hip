@@ -554,12 +554,13 @@ flce_logits_kernel(FlceParams p) {
 // Schedule: kXcds x kCusPerXcd workgroups, one per compute unit; workgroup b
 // runs on XCD b % kXcds.  Each XCD owns a contiguous range of dX tile ids and
 // of dW tile ids (neighbouring ids share G, W and X slices in its L2).  Inside
-// an XCD the dX tiles (K = chunk length, long) are dealt round-robin, so the
-// first rx workgroups hold one more of them; the dW tiles (K = N) are dealt
-// round-robin as well, the rx heavier workgroups taking only what balances
-// the cost (K steps) of the two groups.  Concurrent workgroups therefore work
-// on consecutive tile ids, and every tile has exactly one owner, so the dX
-// read-modify-write needs no synchronisation.
+// an XCD the kind of tile with more K steps (dX: the chunk's vocabulary; dW:
+// the tokens) is dealt round-robin, so the first rl workgroups hold one more
+// of it; the other kind is dealt round-robin as well, the rl heavier
+// workgroups taking only what balances the cost (K steps) of the two groups.
+// Concurrent workgroups therefore work on consecutive tile ids, and every
+// tile has exactly one owner, so the read-modify-writes need no
+// synchronisation.
 // ---------------------------------------------------------------------------
 // dX tile id g = part · (nt_tok · nt_h) + tile: K steps [part·D, (part+1)·D)
 // of the chunk, D = ceil(steps / ksplit), into partial buffer `part`.  The
@@ -716,23 +717,38 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   // Cost of a tile in K steps: D for dX tiles (one K part), E for dW tiles.
   const int64_t D = ((p.chunk_len + kBK - 1) / kBK + p.ksplit - 1) / p.ksplit;
   const int64_t E = (p.N + kBK - 1) / kBK;
-  const int rx = nx % kCusPerXcd;                 // workgroups holding one extra dX tile
-  const int64_t per_wg = ((int64_t)nx * D + (int64_t)nw * E) / kCusPerXcd;
-  const int64_t heavy_budget = per_wg - (int64_t)(nx / kCusPerXcd + 1) * D;
-  const int h_k = (rx == 0 || heavy_budget <= 0) ? 0 : (int)((heavy_budget + E / 2) / E);
-  const int nw_heavy = (int)((int64_t)rx * h_k < nw ? (int64_t)rx * h_k : nw);
-  const int nw_light = nw - nw_heavy;
-
-  for (int t = li; t < nx; t += kCusPerXcd) chunk_dx_tile<kFilter>(p, dx_lo + t, D, smem, wm, wn, lane);
+  // The longer kind of tile is dealt first, round-robin; the workgroups that
+  // hold one more of it (the first rl) take fewer of the shorter kind, so the
+  // K steps per workgroup come out nearly equal.
+  const bool dw_long = E > D;
+  const int nl_t = dw_long ? nw : nx, ns_t = dw_long ? nx : nw;
+  const int64_t cl = dw_long ? E : D, cs = dw_long ? D : E;
+  const int rl = nl_t % kCusPerXcd;
+  const int64_t per_wg = ((int64_t)nl_t * cl + (int64_t)ns_t * cs) / kCusPerXcd;
+  const int64_t heavy_budget = per_wg - (int64_t)(nl_t / kCusPerXcd + 1) * cl;
+  const int h_k = (rl == 0 || heavy_budget <= 0) ? 0 : (int)((heavy_budget + cs / 2) / cs);
+  const int ns_heavy = (int)((int64_t)rl * h_k < ns_t ? (int64_t)rl * h_k : ns_t);
+  const int ns_light = ns_t - ns_heavy;
   const float sc = *p.scale;
-  if (li >= rx) {
-    const int nl = kCusPerXcd - rx;
-    for (int t = li - rx; t < nw_light; t += nl)
-      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + t, sc, smem, wm, wn, lane);
+
+  // This workgroup's share of each kind: ids start, start + stride, ... below
+  // limit, after `offset` (long kind: round-robin; short kind: the light
+  // workgroups share the first ns_light ids, the heavy ones the rest).
+  int l_start = li, l_stride = kCusPerXcd, l_limit = nl_t;
+  int s_start, s_stride, s_limit, s_offset = 0;
+  if (li >= rl) {
+    s_start = li - rl; s_stride = kCusPerXcd - rl; s_limit = ns_light;
   } else {
-    for (int t = li; t < nw_heavy; t += rx)
-      chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + nw_light + t, sc, smem, wm, wn, lane);
+    s_start = li; s_stride = rl; s_limit = ns_heavy; s_offset = ns_light;
   }
+  const int x_start = dw_long ? s_start : l_start, x_stride = dw_long ? s_stride : l_stride;
+  const int x_limit = dw_long ? s_limit : l_limit, x_offset = dw_long ? s_offset : 0;
+  const int w_start = dw_long ? l_start : s_start, w_stride = dw_long ? l_stride : s_stride;
+  const int w_limit = dw_long ? l_limit : s_limit, w_offset = dw_long ? 0 : s_offset;
+  for (int t = x_start; t < x_limit; t += x_stride)
+    chunk_dx_tile<kFilter>(p, dx_lo + x_offset + t, D, smem, wm, wn, lane);
+  for (int t = w_start; t < w_limit; t += w_stride)
+    chunk_dw_tile<kDwAcc, kFilter>(p, dw_lo + w_offset + t, sc, smem, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -823,8 +839,6 @@ hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream) {
   const int grid = kXcds * kCusPerXcd;
   // The filtered form reads one flag word per tile and K part; it serves the
   // recompute path only (one K part, dW written once).
-  // The filtered form reads one flag word per tile and K part: recompute path
-  // only (one K part, dW written once).
   if (p.flags && (p.ksplit != 1 || p.dw_accumulate)) return hipErrorInvalidValue;
   if (p.flags)
     hipLaunchKernelGGL((chunk_gemm_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
