@@ -563,3 +563,72 @@ def backward_filtered(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
     G = (dense - onehot) * softcap_derivative(Z, c) * a * scale[:, None]
     G[bad_mask(labels, V, int(opts["ignore_index"]))] = np.nan
     return G @ W, G.T @ X
+
+
+# --------------------------------------------------------------------------- #
+# Vocabulary order for the gradient filter (reading R20)
+# --------------------------------------------------------------------------- #
+# [CCE-blog] §三: alongside the filter, the forward records every vocabulary
+# entry's average logit and the backward moves the frequently large ("hot")
+# entries next to each other, so that the blocks it skips are whole ones more
+# often.
+#   R20 the average is over the rows whose label is not the ignore index, of
+#       the plain logit x_i·w_v (before logit scale and softcap, both of which
+#       are increasing); with no such row every average is 0.  Entries are
+#       ordered by decreasing average, equal averages by increasing index, a
+#       NaN average before every number.  The backward with an order is the
+#       backward of the vocabulary relabelled by it: position j holds entry
+#       order[j], a label y becomes the position of y, filter blocks are cut
+#       in positions, and each dW row is returned to its entry.
+def vocab_mean_logit(X: np.ndarray, W: np.ndarray, labels: np.ndarray,
+                     ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+    """Average logit of every vocabulary entry over the rows with a target."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    rows = valid_mask(np.asarray(labels, dtype=np.int64), ignore_index)
+    n = int(rows.sum())
+    if n == 0:
+        return np.zeros(W.shape[0])
+    return logits(X[rows], W).sum(axis=0) / n
+
+
+def vocab_order(mean_logit: np.ndarray) -> np.ndarray:
+    """Entries by decreasing average logit; ties by index; NaN first."""
+    m = np.asarray(mean_logit, dtype=np.float64)
+    idx = np.arange(m.shape[0])
+    nan = np.isnan(m)
+    # lexsort: last key is the primary one.
+    return np.lexsort((idx, -np.where(nan, 0.0, m), ~nan)).astype(np.int64)
+
+
+def backward_sorted(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
+                    opts: Dict[str, object], order: np.ndarray, eps: float = 0.0,
+                    tile: int = 256):
+    """(dX, dW) of the backward on the vocabulary relabelled by `order`
+    (R20), filtered with threshold eps when eps > 0 (R19)."""
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    order = np.asarray(order, dtype=np.int64)
+    V = W.shape[0]
+    if not np.array_equal(np.sort(order), np.arange(V)):
+        raise ValueError("order must be a permutation of the vocabulary")
+    position = np.empty(V, dtype=np.int64)
+    position[order] = np.arange(V)
+    ign = int(opts["ignore_index"])
+    ignored = labels == ign
+    moved = ~ignored & (labels >= 0) & (labels < V)
+    lab = labels.copy()
+    lab[moved] = position[labels[moved]]
+    # A position may equal a non-negative ignore index: the relabelled problem
+    # marks its ignored rows with a value no label or position takes.
+    ign_pos = min(int(labels.min(initial=0)), 0) - 1
+    lab[ignored] = ign_pos
+    o_pos = dict(opts, ignore_index=ign_pos)
+    W_pos = W[order]
+    if eps > 0:
+        dX, dW_pos = backward_filtered(X, W_pos, lab, dloss, o_pos, eps, tile)
+    else:
+        dX, dW_pos = backward_ex(X, W_pos, lab, dloss, o_pos)
+    dW = np.empty_like(dW_pos)
+    dW[order] = dW_pos
+    return dX, dW

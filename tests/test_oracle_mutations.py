@@ -342,3 +342,74 @@ def test_fused_pins_catch_mutation(name, monkeypatch):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# --------------------------------------------------------------------------- #
+# Vocabulary order: planted mistakes must be caught by its pins.
+# --------------------------------------------------------------------------- #
+from tests import test_oracle_sorting as PO  # noqa: E402
+
+ORDER_PINS = [
+    PO.test_mean_logit_by_loops,
+    PO.test_order_elementwise,
+    PO.test_order_of_duplicate_entries,
+    lambda: PO.test_any_order_without_filter_is_the_plain_backward(dict(softcap=2.5, z_loss=0.02)),
+    PO.test_bruteforce_blocks_in_positions,
+]
+
+_orig_mean_logit = O.vocab_mean_logit
+_orig_order = O.vocab_order
+_orig_sorted = O.backward_sorted
+
+
+def _ml_all_rows(X, W, labels, ignore_index=-100):
+    # Averages over every row, ignored ones included.
+    return _orig_mean_logit(X, W, np.zeros_like(np.asarray(labels)), ignore_index)
+
+
+def _order_ascending(mean_logit):
+    return _orig_order(-np.asarray(mean_logit))
+
+
+def _order_ties_reversed(mean_logit):
+    m = np.asarray(mean_logit)
+    idx = np.arange(len(m))
+    return np.lexsort((-idx, -m)).astype(np.int64)
+
+
+def _sorted_dw_in_positions(X, W, labels, dloss, opts, order, eps=0.0, tile=256):
+    # dW rows left in positions instead of returned to their entries.
+    dX, dW = _orig_sorted(X, W, labels, dloss, opts, order, eps, tile)
+    return dX, dW[np.asarray(order)]
+
+
+def _sorted_labels_not_moved(X, W, labels, dloss, opts, order, eps=0.0, tile=256):
+    # The reordered W is used with the original labels.
+    W = np.asarray(W, dtype=np.float64)
+    dX, dW_pos = _orig_sorted(X, W[np.asarray(order)], labels, dloss, opts,
+                              np.arange(W.shape[0]), eps, tile)
+    dW = np.empty_like(dW_pos)
+    dW[np.asarray(order)] = dW_pos
+    return dX, dW
+
+
+ORDER_MUTATIONS = {
+    "mean_over_all_rows": ("vocab_mean_logit", _ml_all_rows),
+    "ascending": ("vocab_order", _order_ascending),
+    "ties_reversed": ("vocab_order", _order_ties_reversed),
+    "dw_left_in_positions": ("backward_sorted", _sorted_dw_in_positions),
+    "labels_not_moved": ("backward_sorted", _sorted_labels_not_moved),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ORDER_MUTATIONS))
+def test_order_pins_catch_mutation(name, monkeypatch):
+    attr, fn = ORDER_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in ORDER_PINS:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
