@@ -214,17 +214,25 @@ def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, 
 
 
 def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, fws,
-                  fws_n, sptr, stream, step_ms_exact):
+                  fws_n, sptr, stream, step_ms_exact, sort=False):
     """The step with the opt-in gradient filter at threshold args.filter_eps
     (forward, then the filtered backward), and how far its gradients are from
-    the exact ones of the same step."""
+    the exact ones of the same step.  sort=True: the step also orders the
+    vocabulary by average logit (lce_vocab_order) and runs the filtered
+    backward on that order (lce_backward_sorted)."""
     import ctypes
     import torch
     import lce_inputs as L
     N, H, V = w.N, w.H, w.V
     opt = _lib.make_options(L.IGNORE_INDEX, float(w.softcap), filter_eps=args.filter_eps)
     dloss = torch.ones(1, dtype=torch.float32, device=X.device)
-    bws_n = lib.lce_backward_workspace_bytes(N, H, V, gcode)
+    if sort:
+        bws_n = lib.lce_backward_sorted_workspace_bytes(N, H, V, gcode)
+        ows_n = lib.lce_vocab_order_workspace_bytes(N, H, V)
+        ows = torch.empty(ows_n, dtype=torch.uint8, device=X.device)
+        order = torch.empty(V, dtype=torch.int32, device=X.device)
+    else:
+        bws_n = lib.lce_backward_workspace_bytes(N, H, V, gcode)
     bws = torch.empty(bws_n, dtype=torch.uint8, device=X.device)
     dXe, dWe = dX.clone(), dW.clone()          # exact gradients of the last timed step
 
@@ -234,13 +242,27 @@ def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, d
                              nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
         if st:
             raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        if sort:
+            st = lib.lce_vocab_order(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V,
+                                     L.IGNORE_INDEX, None, order.data_ptr(), ows.data_ptr(),
+                                     ows_n, sptr)
+            if st:
+                raise RuntimeError(f"lce_vocab_order: {_lib.status_string(st)}")
+            st = lib.lce_backward_sorted(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                                         dloss.data_ptr(), N, H, V, ctypes.byref(opt),
+                                         order.data_ptr(), dX.data_ptr(), gcode, dW.data_ptr(),
+                                         gcode, bws.data_ptr(), bws_n, sptr)
+            if st:
+                raise RuntimeError(f"lce_backward_sorted: {_lib.status_string(st)}")
+            return
         st = lib.lce_backward_ex(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
                                  dloss.data_ptr(), N, H, V, ctypes.byref(opt), dX.data_ptr(),
                                  gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n, sptr)
         if st:
             raise RuntimeError(f"lce_backward_ex: {_lib.status_string(st)}")
 
-    log(f"[bench] step with the gradient filter at {args.filter_eps:.3g}")
+    log(f"[bench] step with the gradient filter at {args.filter_eps:.3g}"
+        + (", vocabulary ordered by average logit" if sort else ""))
     for _ in range(args.warmup):
         fstep()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -261,6 +283,10 @@ def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, d
            "dX_rel_l2_vs_exact": rel(dX, dXe), "dW_rel_l2_vs_exact": rel(dW, dWe),
            "note": "opt-in, not exact: gradient blocks whose softmax values all lie below "
                    "filter_eps are skipped in both contractions; not the headline path"}
+    if sort:
+        out["note"] += ("; the step also orders the vocabulary by average logit and cuts the "
+                        "blocks in that order (the seeded weights carry no such structure)")
+        del ows, order
     dX.copy_(dXe)
     dW.copy_(dWe)
     del bws, dXe, dWe
@@ -378,10 +404,13 @@ def main():
             per_kernel[k]["tflops"] = round(units * N * H * V * args.steps / (kernels[k][1] / 1e3) / 1e12, 1)
 
     headline_mean = float(mean.item())
-    filtered = None
+    filtered = filtered_sorted = None
     if args.filter_eps > 0:
         filtered = time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW,
                                  gcode, fws, fws_n, sptr, stream, ms_per_step)
+        filtered_sorted = time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad,
+                                        dX, dW, gcode, fws, fws_n, sptr, stream, ms_per_step,
+                                        sort=True)
 
     fused = None
     if not args.no_fused:
@@ -421,6 +450,7 @@ def main():
         "vocab_shard": shard,
         "fused_row_chunk": fused,
         "gradient_filter": filtered,
+        "gradient_filter_sorted": filtered_sorted,
         "kernels": per_kernel,
         "memory_bytes": {"peak_allocated": int(peak_mem),
                          "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),

@@ -199,6 +199,64 @@ lce_status lce_backward_ex(const void* X_dev, const void* W_dev,
                            void* stream);
 
 /*
+ * Vocabulary order for the gradient filter.  The blog "最贵的一层：深入浅出
+ * Liger Kernel 与 Cut Cross-Entropy" (§三) pairs CCE's gradient filter with a
+ * vocabulary sort: each entry's average logit is recorded, and the backward
+ * places the entries that are often large next to each other, so that whole
+ * blocks fall below the threshold more often.
+ *
+ * lce_vocab_order computes, for every entry v, the average of the plain logit
+ * x_i·w_v over the rows whose label is not ignore_index (0 for every entry
+ * when there is no such row; logit scale and softcap are left out, both being
+ * increasing), as w_v·x̄ with x̄ the fp32 mean of those rows, and writes the
+ * entries by decreasing average, equal averages by increasing index, NaN
+ * averages first.
+ *   X_dev, W_dev, labels_dev, N, H, V, ignore_index   as lce_forward
+ *   mean_logit_dev  float [V] device, the averages; may be NULL
+ *   order_dev       int32 [V] device, order_dev[j] = the entry at position j
+ *   workspace       lce_vocab_order_workspace_bytes(N, H, V) bytes, 256-byte
+ *                   aligned, caller-owned (0 for an invalid shape)
+ * Errors as lce_forward (W_dev and order_dev must not be NULL).  The sums are
+ * taken in a fixed order, so the result is reproducible bit for bit.
+ */
+size_t lce_vocab_order_workspace_bytes(int64_t N, int64_t H, int64_t V);
+
+lce_status lce_vocab_order(const void* X_dev, const void* W_dev,
+                           const int64_t* labels_dev, int64_t N, int64_t H,
+                           int64_t V, int64_t ignore_index, float* mean_logit_dev,
+                           int32_t* order_dev, void* workspace_dev,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Backward on a reordered vocabulary: the result of lce_backward_ex on the
+ * vocabulary relabelled by order_dev (position j holds entry order_dev[j];
+ * each label moves to its entry's position), with every dW row returned to
+ * its entry.  Without the filter this is lce_backward_ex's result up to the
+ * order of fp32 additions in dX; with filter_eps > 0 the 256-column blocks of
+ * the filter are cut in positions, so an order that gathers the large
+ * entries (lce_vocab_order) lets it skip more blocks.
+ *   order_dev   int32 [V] device, a permutation of [0, V) (NULL:
+ *               LCE_ERR_INVALID_ARG); with entries repeated or out of range
+ *               the gradients are undefined, but no memory outside the
+ *               arguments and the workspace is touched
+ *   workspace   lce_backward_sorted_workspace_bytes(N, H, V, dW_dtype) bytes:
+ *               lce_backward_workspace_bytes plus one chunk of W rows (bf16)
+ *               and of dW rows (fp32)
+ * Other arguments, options and errors as lce_backward_ex.
+ */
+size_t lce_backward_sorted_workspace_bytes(int64_t N, int64_t H, int64_t V,
+                                           lce_dtype dW_dtype);
+
+lce_status lce_backward_sorted(const void* X_dev, const void* W_dev,
+                               const int64_t* labels_dev, const float* lse_dev,
+                               const float* dloss_dev, int64_t N, int64_t H,
+                               int64_t V, const lce_options* opt,
+                               const int32_t* order_dev, void* dX_dev,
+                               lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                               void* workspace_dev, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Vocabulary shards.  The AI-infra KB page M011 (§07) splits the vocabulary
  * columns over ranks: each row's max, exp-sum and target score must be made
  * global before its loss is formed, the hidden-state gradient is the sum of

@@ -33,7 +33,8 @@ EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_
             "lce_backward", "lce_options_default", "lce_forward_ex", "lce_backward_ex",
             "lce_shard_forward", "lce_shard_merge_workspace_bytes", "lce_shard_merge",
             "lce_shard_backward", "lce_fused_workspace_bytes", "lce_forward_backward",
-            "lce_status_string", "lce_version", "lce_timing_enable",
+            "lce_vocab_order_workspace_bytes", "lce_vocab_order",
+            "lce_backward_sorted_workspace_bytes", "lce_backward_sorted", "lce_status_string", "lce_version", "lce_timing_enable",
             "lce_timing_reset", "lce_timing_read")
 
 
@@ -114,6 +115,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, opt_p, vp, vp, vp, vp, vp,
                                          vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
     lib.lce_forward_backward.restype = ctypes.c_int
+    lib.lce_vocab_order_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.lce_vocab_order_workspace_bytes.restype = sz
+    lib.lce_vocab_order.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.lce_vocab_order.restype = ctypes.c_int
+    lib.lce_backward_sorted_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.lce_backward_sorted_workspace_bytes.restype = sz
+    lib.lce_backward_sorted.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, opt_p, vp, vp,
+                                        ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
+    lib.lce_backward_sorted.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -305,9 +315,57 @@ def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap:
     """Backward with the loss variants.  `dloss`: a scalar (mean, sum) or an
     [N] tensor of per-row upstream gradients (none).  filter_eps > 0 turns on
     the (non-exact) gradient filter.  Returns (dX, dW)."""
+    opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
+                       filter_eps)
+    return _backward_with_options(X, W, labels, lse, dloss, opt, reduction, dX_dtype, dW_dtype,
+                                  workspace, None)
+
+
+def lce_backward_sorted(X, W, labels, lse, dloss, order, ignore_index: int = -100,
+                        softcap: float = 0.0, logit_scale: float = 1.0,
+                        label_smoothing: float = 0.0, z_loss: float = 0.0,
+                        reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
+                        filter_eps: float = 0.0):
+    """lce_backward_ex on the vocabulary reordered by `order` (an int32 device
+    permutation of [0, V), e.g. from lce_vocab_order); dW rows come back in
+    entry order.  Returns (dX, dW)."""
     import torch
     opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
                        filter_eps)
+    if not (torch.is_tensor(order) and order.is_cuda and order.dtype == torch.int32
+            and order.dim() == 1 and order.shape[0] == W.shape[0]):
+        raise ValueError("order must be an int32 device tensor of shape [V]")
+    return _backward_with_options(X, W, labels, lse, dloss, opt, reduction, dX_dtype, dW_dtype,
+                                  workspace, order.contiguous())
+
+
+def lce_vocab_order(X, W, labels, ignore_index: int = -100, workspace=None):
+    """Average logit of every vocabulary entry over the rows with a target, and
+    the entries by decreasing average (ties by index).  Returns (mean_logit [V]
+    f32, order [V] i32), device tensors."""
+    import torch
+    X, W, labels = _prep(X, W, labels)
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    mean_logit = torch.empty(V, dtype=torch.float32, device=dev)
+    order = torch.empty(V, dtype=torch.int32, device=dev)
+    need = int(load().lce_vocab_order_workspace_bytes(N, H, V))
+    if need == 0:
+        _check(LCE_ERR_SHAPE, "lce_vocab_order")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().lce_vocab_order(_ptr(X), _ptr(W), _ptr(labels), N, H, V, int(ignore_index),
+                                mean_logit.data_ptr(), order.data_ptr(), _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    _check(st, "lce_vocab_order")
+    return mean_logit, order
+
+
+def _backward_with_options(X, W, labels, lse, dloss, opt, reduction, dX_dtype, dW_dtype,
+                           workspace, order):
+    import torch
+    where = "lce_backward_sorted" if order is not None else "lce_backward_ex"
     X, W, labels = _prep(X, W, labels)
     N, H = X.shape
     V = W.shape[0]
@@ -326,15 +384,24 @@ def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap:
     dXc, dWc = _dtype_code(dX_dtype), _dtype_code(dW_dtype)
     dX = torch.empty(N, H, dtype=dX_dtype or torch.float32, device=dev)
     dW = torch.empty(V, H, dtype=dW_dtype or torch.float32, device=dev)
-    need = lce_backward_workspace_bytes(N, H, V, dW_dtype)
+    if order is None:
+        need = lce_backward_workspace_bytes(N, H, V, dW_dtype)
+    else:
+        need = int(load().lce_backward_sorted_workspace_bytes(N, H, V, dWc))
     if need == 0:
-        _check(LCE_ERR_SHAPE, "lce_backward_ex")
+        _check(LCE_ERR_SHAPE, where)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = load().lce_backward_ex(_ptr(X), _ptr(W), _ptr(labels), _ptr(lse), dloss.data_ptr(),
-                                N, H, V, ctypes.byref(opt), _ptr(dX), dXc, dW.data_ptr(), dWc,
-                                _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, "lce_backward_ex")
+    if order is None:
+        st = load().lce_backward_ex(_ptr(X), _ptr(W), _ptr(labels), _ptr(lse), dloss.data_ptr(),
+                                    N, H, V, ctypes.byref(opt), _ptr(dX), dXc, dW.data_ptr(),
+                                    dWc, _ptr(workspace), workspace.numel(), _stream(dev))
+    else:
+        st = load().lce_backward_sorted(_ptr(X), _ptr(W), _ptr(labels), _ptr(lse),
+                                        dloss.data_ptr(), N, H, V, ctypes.byref(opt),
+                                        order.data_ptr(), _ptr(dX), dXc, dW.data_ptr(), dWc,
+                                        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, where)
     return dX, dW
 
 

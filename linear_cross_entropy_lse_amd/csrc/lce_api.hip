@@ -101,13 +101,17 @@ struct BwdPlan {
   int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
   int64_t Vc, ldg;
   size_t off_state, off_key, off_deriv, off_gs, off_c1, off_oh, off_keys_a, off_keys_b, off_head,
-      off_tail, off_blocks, off_scalars, off_flags, off_G, off_dXp, off_dWs, total;
+      off_tail, off_blocks, off_scalars, off_flags, off_G, off_dXp, off_dWs, off_Wp, off_pos1,
+      off_pkey, total;
 };
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
 // (N·Vc ≤ V·H), with a floor of 4096 columns; chunks are multiples of 256 so
-// tiles never straddle two chunks.
-BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+// tiles never straddle two chunks.  With a vocabulary order (`sorted`) the
+// chunk's W rows are gathered into position order (Wp), its dW rows go through
+// the fp32 chunk buffer, and the label keys are moved to positions (pos1,
+// pkey).
+BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool sorted = false) {
   BwdPlan p{};
   const int64_t Nc = std::max<int64_t>(N, 1);
   p.T = (int)ceil_div(Nc, kTile);
@@ -142,7 +146,34 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.T * kTile * (size_t)p.ldg);
   p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
   p.off_dWs = o;
-  if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
+  if (dW_dtype == LCE_BF16 || sorted) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
+  if (sorted) {
+    p.off_Wp = o;    o = align_up(o + sizeof(uint16_t) * (size_t)p.Vc * (size_t)H);
+    p.off_pos1 = o;  o = align_up(o + sizeof(int32_t) * (size_t)V);
+    p.off_pkey = o;  o = align_up(o + sizeof(int32_t) * (size_t)N);
+  }
+  p.total = std::max<size_t>(o, kAlign);
+  return p;
+}
+
+// Vocabulary order: per-block column sums of X, x̄, the key and its sort
+// word per entry, and the two buffers of the merge sort.
+struct OrderPlan {
+  int64_t nrb;
+  size_t off_part, off_cnt, off_xbar, off_key, off_word, off_keys_a, off_keys_b, total;
+};
+
+OrderPlan plan_order(int64_t N, int64_t H, int64_t V) {
+  OrderPlan p{};
+  p.nrb = mean_row_blocks(N);
+  size_t o = 0;
+  p.off_part = o;    o = align_up(o + sizeof(float) * (size_t)p.nrb * (size_t)H);
+  p.off_cnt = o;     o = align_up(o + sizeof(int32_t) * (size_t)p.nrb);
+  p.off_xbar = o;    o = align_up(o + sizeof(float) * (size_t)H);
+  p.off_key = o;     o = align_up(o + sizeof(float) * (size_t)V);
+  p.off_word = o;    o = align_up(o + sizeof(uint32_t) * (size_t)V);
+  p.off_keys_a = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(V));
+  p.off_keys_b = o;  o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(V));
   p.total = std::max<size_t>(o, kAlign);
   return p;
 }
@@ -371,10 +402,12 @@ lce_status forward_impl(const void* X_dev, const void* W_dev, const int64_t* lab
 
 // Backward over the vocabulary rows W holds ([vr.v_lo, vr.v_lo + V) of
 // vr.V_total): their rows of dW and their share of dX.
+// `order`: null, or a device permutation of [0, V) (the vocabulary order of
+// the sorted backward; full vocabulary only).
 lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
                          const float* lse_dev, const float* dloss_dev, int64_t N, int64_t H,
-                         int64_t V, VocabRange vr, const lce_options* opt, void* dX_dev,
-                         lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                         int64_t V, VocabRange vr, const int32_t* order, const lce_options* opt,
+                         void* dX_dev, lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
   if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
   if (opt->filter_eps > 0.0f && opt->label_smoothing > 0.0f) return LCE_ERR_INVALID_ARG;
@@ -394,7 +427,8 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     LCE_LAUNCH("fill_zero", stream, launch_fill_zero(dW_dev, dw_bytes, stream));
     return LCE_OK;
   }
-  const BwdPlan pl = plan_backward(N, H, V, dW_dtype);
+  const bool sorted = order != nullptr;
+  const BwdPlan pl = plan_backward(N, H, V, dW_dtype, sorted);
   if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
 
   int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
@@ -415,6 +449,9 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   uint32_t* flags = opt->filter_eps > 0.0f ? at<uint32_t>(workspace_dev, pl.off_flags) : nullptr;
   float* dXp = at<float>(workspace_dev, pl.off_dXp);
   float* dWs = at<float>(workspace_dev, pl.off_dWs);
+  uint16_t* Wp = sorted ? at<uint16_t>(workspace_dev, pl.off_Wp) : nullptr;
+  int32_t* pos1 = sorted ? at<int32_t>(workspace_dev, pl.off_pos1) : nullptr;
+  int32_t* pkey = sorted ? at<int32_t>(workspace_dev, pl.off_pkey) : nullptr;
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
   // The plain path stores G = p·d and applies one scalar scale afterwards; label
@@ -430,15 +467,25 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
                           scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
                           general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
-  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(key, N, keys_a, keys_b, stream));
+  // With an order, the one-hot correction of dW works in positions: the label
+  // keys are moved to the positions of the labels before the sort.
+  if (sorted)
+    LCE_LAUNCH("position_keys", stream, launch_position_keys(order, V, key, N, pos1, pkey, stream));
+  LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(sorted ? pkey : key, N, keys_a, keys_b, stream));
 
   for (int c = 0; c < pl.nchunks; ++c) {
     const int64_t v_begin = (int64_t)c * pl.Vc;
     const int64_t chunk_len = std::min<int64_t>(pl.Vc, V - v_begin);
     const int n_vt = (int)ceil_div(chunk_len, kTile);
+    // The chunk's W rows: a slice of W, or (with an order) the rows of the
+    // entries at positions [v_begin, v_begin + chunk_len), gathered.
+    if (sorted)
+      LCE_LAUNCH("gather_rows", stream, launch_gather_rows(W, V, H, order, v_begin, chunk_len, Wp, stream));
+    const uint16_t* Wsrc = sorted ? Wp : W;
+    const int64_t w_begin = sorted ? 0 : v_begin, w_rows = sorted ? chunk_len : V;
 
     GradParams gp{};
-    gp.X = X; gp.W = W; gp.N = N; gp.H = H; gp.V = V; gp.v_begin = v_begin;
+    gp.X = X; gp.W = Wsrc; gp.N = N; gp.H = H; gp.V = w_rows; gp.v_begin = w_begin;
     gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
     gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
     pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
@@ -449,21 +496,26 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
 
     ChunkGemmParams cp{};
-    cp.G = G; cp.ldg = pl.ldg; cp.Wc = W + v_begin * H; cp.wc_rows = V - v_begin; cp.X = X;
+    cp.G = G; cp.ldg = pl.ldg; cp.Wc = Wsrc + w_begin * H; cp.wc_rows = w_rows - w_begin; cp.X = X;
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
     cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
-    cp.dW_dst = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
+    cp.dW_dst = dW_dtype == LCE_F32 && !sorted ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
-    if (dW_dtype == LCE_BF16) {
+    if (sorted) {
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
+                                v_begin + chunk_len, part_head, part_tail, stream));
+      LCE_LAUNCH("scatter_rows", stream, launch_scatter_rows(dWs, V, H, order, v_begin, chunk_len, dW_dev,
+                                  dW_dtype == LCE_BF16, stream));
+    } else if (dW_dtype == LCE_BF16) {
       LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
                                 v_begin + chunk_len, part_head, part_tail, stream));
       LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
                                chunk_len * H, stream));
     }
   }
-  if (dW_dtype == LCE_F32)
+  if (dW_dtype == LCE_F32 && !sorted)
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
   LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, state, key, oh, W, gemm_scale, nullptr, dX_dev,
@@ -671,8 +723,61 @@ lce_status lce_backward_ex(const void* X_dev, const void* W_dev, const int64_t* 
                            size_t workspace_bytes, void* stream_ptr) {
   if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
   return backward_impl(X_dev, W_dev, labels_dev, lse_dev, dloss_dev, N, H, V, VocabRange{0, V},
-                       opt, dX_dev, dX_dtype, dW_dev, dW_dtype, workspace_dev, workspace_bytes,
-                       stream_ptr);
+                       nullptr, opt, dX_dev, dX_dtype, dW_dev, dW_dtype, workspace_dev,
+                       workspace_bytes, stream_ptr);
+}
+
+size_t lce_backward_sorted_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
+  if (!shape_ok(N, H, V) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16)) return 0;
+  return plan_backward(N, H, V, dW_dtype, true).total;
+}
+
+lce_status lce_backward_sorted(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                               const float* lse_dev, const float* dloss_dev, int64_t N, int64_t H,
+                               int64_t V, const lce_options* opt, const int32_t* order_dev,
+                               void* dX_dev, lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
+                               void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if (!order_dev) return LCE_ERR_INVALID_ARG;
+  if (!aligned(order_dev, 4)) return LCE_ERR_ALIGNMENT;
+  return backward_impl(X_dev, W_dev, labels_dev, lse_dev, dloss_dev, N, H, V, VocabRange{0, V},
+                       order_dev, opt, dX_dev, dX_dtype, dW_dev, dW_dtype, workspace_dev,
+                       workspace_bytes, stream_ptr);
+}
+
+size_t lce_vocab_order_workspace_bytes(int64_t N, int64_t H, int64_t V) {
+  if (!shape_ok(N, H, V)) return 0;
+  return plan_order(N, H, V).total;
+}
+
+lce_status lce_vocab_order(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           float* mean_logit_dev, int32_t* order_dev, void* workspace_dev,
+                           size_t workspace_bytes, void* stream_ptr) {
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if (!W_dev || !order_dev || !workspace_dev || (N > 0 && (!X_dev || !labels_dev)))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(mean_logit_dev, 4) || !aligned(order_dev, 4) || !aligned(workspace_dev, kAlign))
+    return LCE_ERR_ALIGNMENT;
+  const OrderPlan pl = plan_order(N, H, V);
+  if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  float* part = at<float>(workspace_dev, pl.off_part);
+  int32_t* cnt = at<int32_t>(workspace_dev, pl.off_cnt);
+  float* xbar = at<float>(workspace_dev, pl.off_xbar);
+  float* key = mean_logit_dev ? mean_logit_dev : at<float>(workspace_dev, pl.off_key);
+  uint32_t* word = at<uint32_t>(workspace_dev, pl.off_word);
+  uint64_t* keys_a = at<uint64_t>(workspace_dev, pl.off_keys_a);
+  uint64_t* keys_b = at<uint64_t>(workspace_dev, pl.off_keys_b);
+  LCE_LAUNCH("vocab_key", stream, launch_vocab_key(static_cast<const uint16_t*>(X_dev), labels_dev, N, H,
+                                           static_cast<const uint16_t*>(W_dev), V, ignore_index,
+                                           part, cnt, xbar, key, word, stream));
+  LCE_LAUNCH("vocab_sort", stream, launch_sort_by_label(reinterpret_cast<const int32_t*>(word), V, keys_a,
+                                                keys_b, stream));
+  LCE_LAUNCH("order_extract", stream, launch_order_extract(sort_passes(V) % 2 == 0 ? keys_a : keys_b, V,
+                                                   order_dev, stream));
+  return LCE_OK;
 }
 
 lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
@@ -685,7 +790,7 @@ lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
   if (!shape_ok(N, H, V_shard) || !range_ok(V_shard, vocab_offset, vocab_total))
     return LCE_ERR_SHAPE;
   return backward_impl(X_dev, W_shard_dev, labels_dev, lse_dev, dloss_dev, N, H, V_shard,
-                       VocabRange{vocab_offset, vocab_total}, opt, dX_part_dev, dX_dtype,
+                       VocabRange{vocab_offset, vocab_total}, nullptr, opt, dX_part_dev, dX_dtype,
                        dW_shard_dev, dW_dtype, workspace_dev, workspace_bytes, stream_ptr);
 }
 

@@ -185,7 +185,7 @@ hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const flo
 
 // Label sort of the valid rows (keys: label << 32 | row, ascending).
 constexpr int kSortBlock = 2048;   // keys sorted per block in LDS
-int sort_padded(int64_t N);        // N rounded up to kSortBlock
+int64_t sort_padded(int64_t N);    // N rounded up to kSortBlock
 int sort_passes(int64_t N);        // merge passes after the block sort
 // Sorted keys end up in keys_a after an even number of passes, else keys_b;
 // each buffer holds sort_padded(N) keys.
@@ -228,6 +228,31 @@ hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const 
                              hipStream_t stream);
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t count, hipStream_t stream);
+
+// Vocabulary order (lce_order.hip).  Average logit of each entry over the
+// rows whose label is not ignore_index: key[v] = w_v·x̄, with x̄ from per-block
+// column sums part [mean_row_blocks(N) x H] and row counts cnt; word[v] maps
+// key[v] to a 32-bit word in decreasing key order (NaN first), ready for
+// launch_sort_by_label.
+constexpr int kMeanRows = 256;
+inline int64_t mean_row_blocks(int64_t N) { return (N + kMeanRows - 1) / kMeanRows; }
+hipError_t launch_vocab_key(const uint16_t* X, const int64_t* labels, int64_t N, int64_t H,
+                            const uint16_t* W, int64_t V, int64_t ignore_index, float* part,
+                            int32_t* cnt, float* xbar, float* key, uint32_t* word,
+                            hipStream_t stream);
+// order[j] = low word of the j-th sorted key.
+hipError_t launch_order_extract(const uint64_t* keys, int64_t V, int32_t* order,
+                                hipStream_t stream);
+// pos1[v] = 1 + position of v in order (0: none); pkey[i] = position of the
+// label key[i], or INT32_MAX.  pos1 holds V entries rounded up to 16 bytes.
+hipError_t launch_position_keys(const int32_t* order, int64_t V, const int32_t* key, int64_t N,
+                                int32_t* pos1, int32_t* pkey, hipStream_t stream);
+// Wp[j] = W[order[j0 + j]] for j < rows (zero row for an out-of-range entry).
+hipError_t launch_gather_rows(const uint16_t* W, int64_t V, int64_t H, const int32_t* order,
+                              int64_t j0, int64_t rows, uint16_t* Wp, hipStream_t stream);
+// dW[order[j0 + j]] = src[j] (fp32 rows) for j < rows, as fp32 or bf16.
+hipError_t launch_scatter_rows(const float* src, int64_t V, int64_t H, const int32_t* order,
+                               int64_t j0, int64_t rows, void* dW, int bf16, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
 

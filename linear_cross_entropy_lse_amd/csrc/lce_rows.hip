@@ -417,7 +417,7 @@ merge_pass_kernel(const uint64_t* __restrict__ in, uint64_t* __restrict__ out, i
   out[g] = v;
 }
 
-int sort_padded(int64_t N) { return (int)((N + kSortBlock - 1) / kSortBlock * kSortBlock); }
+int64_t sort_padded(int64_t N) { return (N + kSortBlock - 1) / kSortBlock * kSortBlock; }
 
 int sort_passes(int64_t N) {
   int passes = 0;

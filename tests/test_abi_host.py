@@ -223,3 +223,67 @@ def test_filter_option_checks(lib):
     assert bwd_ex(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
     assert fused(lib, ctypes.byref(opts(filter_eps=2.0 ** -12))) == _lib.LCE_ERR_INVALID_ARG
     assert opts().filter_eps == 0.0
+
+
+def order_call(lib, X=FAKE, W=FAKE, y=FAKE, N=4, H=8, V=5, mean=FAKE, order=FAKE, ws=FAKE,
+               wsb=None):
+    if wsb is None:
+        wsb = lib.lce_vocab_order_workspace_bytes(max(N, 0), H, V)
+    return lib.lce_vocab_order(X, W, y, N, H, V, -100, mean, order, ws, wsb, None)
+
+
+def sorted_bwd(lib, o, X=FAKE, W=FAKE, y=FAKE, lse=FAKE, dl=FAKE, N=4, H=8, V=5, order=FAKE,
+               dX=FAKE, dXt=0, dW=FAKE, dWt=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.lce_backward_sorted_workspace_bytes(max(N, 0), H, V, dWt if dWt in (0, 1) else 0)
+    return lib.lce_backward_sorted(X, W, y, lse, dl, N, H, V, o, order, dX, dXt, dW, dWt, ws, wsb,
+                                   None)
+
+
+def test_vocab_order_workspace_and_argument_checks(lib):
+    assert lib.lce_vocab_order_workspace_bytes(256, 64, 1000) > 0
+    assert lib.lce_vocab_order_workspace_bytes(256, 12, 1000) == 0
+    assert lib.lce_vocab_order_workspace_bytes(256, 64, 0) == 0
+    # Sort buffers for V keys plus O(N·H / 256 + V) floats: far below W itself.
+    N, H, V = 8192, 2304, 256128
+    assert lib.lce_vocab_order_workspace_bytes(N, H, V) < 32 * V + 4 * (N // 256 + 2) * H + 8192
+    assert order_call(lib, H=12) == _lib.LCE_ERR_SHAPE
+    assert order_call(lib, V=0) == _lib.LCE_ERR_SHAPE
+    assert order_call(lib, W=0) == _lib.LCE_ERR_INVALID_ARG
+    assert order_call(lib, order=0) == _lib.LCE_ERR_INVALID_ARG
+    assert order_call(lib, X=0) == _lib.LCE_ERR_INVALID_ARG
+    assert order_call(lib, y=0) == _lib.LCE_ERR_INVALID_ARG
+    assert order_call(lib, ws=0) == _lib.LCE_ERR_INVALID_ARG
+    assert order_call(lib, X=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
+    assert order_call(lib, y=FAKE + 4) == _lib.LCE_ERR_ALIGNMENT
+    assert order_call(lib, order=FAKE + 2) == _lib.LCE_ERR_ALIGNMENT
+    assert order_call(lib, mean=FAKE + 2) == _lib.LCE_ERR_ALIGNMENT
+    assert order_call(lib, ws=FAKE + 16) == _lib.LCE_ERR_ALIGNMENT
+    assert order_call(lib, wsb=16) == _lib.LCE_ERR_WORKSPACE
+
+
+def test_sorted_backward_workspace_and_argument_checks(lib):
+    for (N, H, V) in [(256, 64, 1000), (8192, 2304, 256128), (32768, 3584, 152064)]:
+        for dt in (0, 1):
+            plain = lib.lce_backward_workspace_bytes(N, H, V, dt)
+            ws = lib.lce_backward_sorted_workspace_bytes(N, H, V, dt)
+            # + one chunk (at most V rounded up to 256 rows) of bf16 W rows and
+            # of fp32 dW rows, + O(N + V)
+            v256 = -(-V // 256) * 256
+            assert plain < ws <= plain + 6 * H * v256 + 4 * (N + V) + 4096
+    assert lib.lce_backward_sorted_workspace_bytes(8, 12, 40, 0) == 0
+    assert lib.lce_backward_sorted_workspace_bytes(8, 16, 40, 5) == 0
+    o = opts()
+    ok = ctypes.byref(o)
+    assert sorted_bwd(lib, ok, H=12) == _lib.LCE_ERR_SHAPE
+    assert sorted_bwd(lib, ok, order=0) == _lib.LCE_ERR_INVALID_ARG
+    assert sorted_bwd(lib, ok, order=FAKE + 2) == _lib.LCE_ERR_ALIGNMENT
+    assert sorted_bwd(lib, None) == _lib.LCE_ERR_INVALID_ARG
+    assert sorted_bwd(lib, ok, dW=0) == _lib.LCE_ERR_INVALID_ARG
+    assert sorted_bwd(lib, ok, dXt=4) == _lib.LCE_ERR_INVALID_ARG
+    assert sorted_bwd(lib, ok, X=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
+    both = opts(filter_eps=2.0 ** -12, label_smoothing=0.1)
+    assert sorted_bwd(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
+    # The plain backward's workspace is too small for the sorted one.
+    assert sorted_bwd(lib, ok, wsb=lib.lce_backward_workspace_bytes(4, 8, 5, 0)) == \
+        _lib.LCE_ERR_WORKSPACE
