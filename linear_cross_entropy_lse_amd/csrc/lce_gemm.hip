@@ -55,6 +55,7 @@ __device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], flo
                                               float (&s)[kNI], float (&zs)[kNI], int lim, float k2,
                                               float c2, float l2a) {
   const float NEG_INF = -__builtin_inff();
+  const float inv2c2 = kMode == kCapFixed ? 0.5f / c2 : 0.0f;
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     float mref = m[ni];
@@ -86,9 +87,10 @@ __device__ __forceinline__ void lse_fold_tile(const f32x16 (&acc)[kMI][kNI], flo
           e = exp2_fast(fmaf(z, l2a, -mref));
           zt = z;
         } else if (kMode == kCapFixed) {
-          const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-          e = exp2_fast(-2.0f * c2 * rr);
-          zt = fmaf(-2.0f, rr, 1.0f);           // tanh = 1 − 2r
+          // q = 2c2·r, as the reciprocal of (2^(z·k2) + 1)/(2c2): e = 2^(−q)
+          const float q = rcp_fast(fmaf(exp2_fast(z * k2), inv2c2, inv2c2));
+          e = exp2_fast(-q);
+          zt = fmaf(-2.0f * inv2c2, q, 1.0f);   // tanh = 1 − 2r = 1 − q/c2
         } else {
           const float t = tanh_of_scaled(z, k2);
           e = exp2_fast(c2 * t - mref);
@@ -250,11 +252,12 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
           const float z = acc[mi][ni][r];
           float val, pr;
           if (kCapped) {
+            // off carries + 2 here: pr4 = 4p, and 4p·r(1 − r) = p·(1 − tanh²).
             const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-            const float d4 = 4.0f * rr;
-            pr = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
-            const float d = fmaf(-d4, rr, d4);
-            val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) * d : pr * d;
+            const float pr4 = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
+            const float dq = fmaf(-rr, rr, rr);
+            val = kGen ? gsc[ni] * fmaf(c1[ni], pr4, -4.0f * eps_v) * dq : pr4 * dq;
+            pr = 0.25f * pr4;   // read by the filter only
           } else {
             pr = exp2_fast(fmaf(z, l2a, off[ni]));
             val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
@@ -312,7 +315,8 @@ grad_logits_kernel(GradParams p) {
     const bool ok = tok < p.N;
     const int st = ok ? p.row_state[tok] : (int)kRowIgnored;
     const float lse2 = ok ? p.lse[tok] * kLog2e : 0.0f;
-    const float o = kCapped ? c2 - lse2 : -lse2;
+    // Capped: + 2 (a factor 4 folded into the exponent; see grad_store_tile).
+    const float o = kCapped ? c2 - lse2 + 2.0f : -lse2;
     if (kGen) {
       off[ni] = o;
       gsc[ni] = ok ? p.gs[tok] : 0.0f;
