@@ -229,10 +229,12 @@ lse_partials_kernel(LseParams p) {
 // kFilter: also report whether any value of the dense part compared by the
 // gradient filter, (1 + 2l·LSE)·p over rows with a target, is not below
 // `feps` (NaN counts as not below).
-// kBlk: the store offsets follow the blocked G layout (sub-block mi/2, column
-// (mi%2)·32 + 8gq within it); otherwise row-major with row offsets
-// acc_row_const(mi, 4gq).
-template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false, bool kBlk = false>
+// Stores follow the blocked G layout.  A lane holds rows 4·(lane/32) + 0..3 of
+// each 8-row group gq of its mi block; lanes l and l + 32 trade halves
+// (permlane32 swap) so that lane l stores the 8 rows of group 2gp and lane
+// l + 32 those of group 2gp + 1, 16 bytes each: sub-block mi/2, column
+// (mi%2)·32 + 16gp (+ 8 from the lane half, carried by cb).
+template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false>
 __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
                                                 const float (&gsc)[kNI], const float (&c1)[kNI],
                                                 float eps_v, __amdgpu_buffer_rsrc_t rs,
@@ -244,37 +246,43 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float gv[4];
+      for (int gp = 0; gp < 2; ++gp) {
+        u32x2 pk[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = gq * 4 + q;
-          const float z = acc[mi][ni][r];
-          float val, pr;
-          if (kCapped) {
-            // off carries + 2 here: pr4 = 4p, and 4p·r(1 − r) = p·(1 − tanh²).
-            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-            const float pr4 = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
-            const float dq = fmaf(-rr, rr, rr);
-            val = kGen ? gsc[ni] * fmaf(c1[ni], pr4, -4.0f * eps_v) * dq : pr4 * dq;
-            pr = 0.25f * pr4;   // read by the filter only
-          } else {
-            pr = exp2_fast(fmaf(z, l2a, off[ni]));
-            val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
+        for (int h = 0; h < 2; ++h) {
+          const int gq = 2 * gp + h;
+          float gv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = gq * 4 + q;
+            const float z = acc[mi][ni][r];
+            float val, pr;
+            if (kCapped) {
+              // off carries + 2 here: pr4 = 4p, and 4p·r(1 − r) = p·(1 − tanh²).
+              const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+              const float pr4 = exp2_fast(fmaf(-2.0f * c2, rr, off[ni]));
+              const float dq = fmaf(-rr, rr, rr);
+              val = kGen ? gsc[ni] * fmaf(c1[ni], pr4, -4.0f * eps_v) * dq : pr4 * dq;
+              pr = 0.25f * pr4;   // read by the filter only
+            } else {
+              pr = exp2_fast(fmaf(z, l2a, off[ni]));
+              val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
+            }
+            gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
+            if (kFilter) {
+              // Plain form: ignored rows have pr = 0, bad rows NaN.
+              const float fv = kGen ? (gsc[ni] != 0.0f ? c1[ni] * pr : 0.0f) : pr;
+              active |= (!kMasked || acc_row_const(mi, r) < lim) && !(fv < feps);
+            }
           }
-          gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
-          if (kFilter) {
-            // Plain form: ignored rows have pr = 0, bad rows NaN.
-            const float fv = kGen ? (gsc[ni] != 0.0f ? c1[ni] * pr : 0.0f) : pr;
-            active |= (!kMasked || acc_row_const(mi, r) < lim) && !(fv < feps);
-          }
+          pk[h][0] = pack_bf16x2(gv[0], gv[1]);
+          pk[h][1] = pack_bf16x2(gv[2], gv[3]);
         }
-        u32x2 packed;
-        packed[0] = pack_bf16x2(gv[0], gv[1]);
-        packed[1] = pack_bf16x2(gv[2], gv[3]);
-        const uint32_t eo = kBlk ? (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 8 * gq)
-                                 : (uint32_t)acc_row_const(mi, gq * 4);
-        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * eo), 0, 0);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+        const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 16 * gp);
+        __builtin_amdgcn_raw_buffer_store_b128(out, rs, (int)(cb[ni] + 2u * eo), 0, 0);
       }
   return active;
 }
@@ -326,10 +334,11 @@ grad_logits_kernel(GradParams p) {
       gsc[ni] = 1.0f;
       c1[ni] = 1.0f;
     }
-    // Blocked G (see DtlKMajorBlockedG): this lane's 4 consecutive vocabulary
-    // rows r0 = acc_row_lane + acc_row_const(mi, 4gq) lie in sub-block
-    // 2wm + mi/2 at column (mi%2)·32 + 8gq + 4(lane/32) of token row col.
-    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + col * kBK + 4 * (lane >> 5)) * 2);
+    // Blocked G (see DtlKMajorBlockedG): after the lane-half swap of
+    // grad_store_tile this lane stores 8 consecutive vocabulary rows of
+    // sub-block 2wm + mi/2 at column (mi%2)·32 + 16gp + 8(lane/32) of token
+    // row col.
+    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + col * kBK + 8 * (lane >> 5)) * 2);
   }
   // The whole token tile, padding rows past N included (they get zeros, which
   // the dW contraction reads).
@@ -353,7 +362,7 @@ grad_logits_kernel(GradParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
-    const bool act = grad_store_tile<kCapped, false, kGen, kFilter, true>(acc, off, gsc, c1, p.eps_over_v, rs,
+    const bool act = grad_store_tile<kCapped, false, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                     cb, 0, k2, c2, l2a, p.filter_eps);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
@@ -367,7 +376,7 @@ grad_logits_kernel(GradParams p) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    const bool act = grad_store_tile<kCapped, true, kGen, kFilter, true>(acc, off, gsc, c1, p.eps_over_v, rs,
+    const bool act = grad_store_tile<kCapped, true, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                    cb, lim, k2, c2, l2a, p.filter_eps);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
