@@ -430,37 +430,45 @@ __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kN
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float uv[4];
+      for (int gp = 0; gp < 2; ++gp) {
+        u32x2 pk[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = gq * 4 + q;
-          const float z = acc[mi][ni][r];
-          const bool ok = !kMasked || acc_row_const(mi, r) < lim;
-          float e, u, zt;
-          if (kMode == kPlain) {
-            e = exp2_fast(fmaf(z, l2a, -mref));
-            u = e;
-            zt = z;
-          } else {
-            const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
-            const float d4 = 4.0f * rr;
-            const float d = fmaf(-d4, rr, d4);                  // 1 − tanh² = 4r(1 − r)
-            e = kMode == kCapFixed ? exp2_fast(-2.0f * c2 * rr)  // 2^(c2·tanh − c2)
-                                   : exp2_fast(fmaf(-2.0f * c2, rr, c2 - mref));
-            u = e * d;
-            zt = fmaf(-2.0f, rr, 1.0f);                         // tanh = 1 − 2r
+        for (int h = 0; h < 2; ++h) {
+          const int gq = 2 * gp + h;
+          float uv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = gq * 4 + q;
+            const float z = acc[mi][ni][r];
+            const bool ok = !kMasked || acc_row_const(mi, r) < lim;
+            float e, u, zt;
+            if (kMode == kPlain) {
+              e = exp2_fast(fmaf(z, l2a, -mref));
+              u = e;
+              zt = z;
+            } else {
+              const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+              const float d4 = 4.0f * rr;
+              const float d = fmaf(-d4, rr, d4);                  // 1 − tanh² = 4r(1 − r)
+              e = kMode == kCapFixed ? exp2_fast(-2.0f * c2 * rr)  // 2^(c2·tanh − c2)
+                                     : exp2_fast(fmaf(-2.0f * c2, rr, c2 - mref));
+              u = e * d;
+              zt = fmaf(-2.0f, rr, 1.0f);                         // tanh = 1 − 2r
+            }
+            sum += ok ? e : 0.0f;
+            if (kZSum) zsum += ok ? zt : 0.0f;
+            uv[q] = ok ? u : 0.0f;
           }
-          sum += ok ? e : 0.0f;
-          if (kZSum) zsum += ok ? zt : 0.0f;
-          uv[q] = ok ? u : 0.0f;
+          pk[h][0] = pack_bf16x2(uv[0], uv[1]);
+          pk[h][1] = pack_bf16x2(uv[2], uv[3]);
         }
-        u32x2 packed;
-        packed[0] = pack_bf16x2(uv[0], uv[1]);
-        packed[1] = pack_bf16x2(uv[2], uv[3]);
-        // Blocked layout (as the recompute path's gradient chunk).
-        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 8 * gq);
-        __builtin_amdgcn_raw_buffer_store_b64(packed, rs, (int)(cb[ni] + 2u * eo), 0, 0);
+        // Blocked layout, 8 rows per lane after the lane-half swap (as the
+        // recompute path's gradient chunk, grad_store_tile).
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+        const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 16 * gp);
+        __builtin_amdgcn_raw_buffer_store_b128(out, rs, (int)(cb[ni] + 2u * eo), 0, 0);
       }
     s[ni] += sum;
     if (kZSum) zs[ni] += zsum;
@@ -504,7 +512,7 @@ flce_logits_kernel(FlceParams p) {
     m[ni] = kMode == kCapFixed ? c2 : -__builtin_inff();
     s[ni] = 0.0f;
     zs[ni] = 0.0f;
-    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + acc_col(wn, ni, lane) * kBK + 4 * (lane >> 5)) * 2);
+    col_base[ni] = (uint32_t)((2 * wm * kGSubElems + acc_col(wn, ni, lane) * kBK + 8 * (lane >> 5)) * 2);
   }
   // U is blocked like the recompute path's gradient chunk: the token tile's
   // n_vtiles blocks, rows past N included (their values are finite and meet
