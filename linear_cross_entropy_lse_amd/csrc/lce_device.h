@@ -3,11 +3,11 @@
 // Tiles: one workgroup of 256 threads (4 waves of 64) computes a 256 x 256
 // fp32 tile C = A · Bᵀ over a K range, 64 K-values per pipeline step.  Each
 // wave owns a 128 x 128 quarter as 4 x 4 blocks of the 32x32x16 bf16 MFMA.
-// Operands are staged through LDS in a K-major layout (each tile row holds 64
-// consecutive K values = 128 bytes), so that one 16-byte LDS read gives a lane
-// its 8-element MFMA fragment.  The 16-byte chunks of a row are XOR-swizzled
-// by the row index to keep the fragment reads and the tile writes free of
-// bank conflicts.
+// Operands are staged through LDS.  A K-major stage holds its 64 K values as
+// two K-halves of 32; in each half a tile row is 64 bytes (four 16-byte
+// chunks), so that one 16-byte LDS read gives a lane its 8-element MFMA
+// fragment.  The chunks of a row are XOR-swizzled by the row index to keep
+// the fragment reads and the tile writes free of bank conflicts.
 //
 // MFMA lane layout (v_mfma_f32_32x32x16_bf16, checked on gfx950):
 //   A fragment: lane l holds A[l % 32][8*(l/32) .. 8*(l/32)+7]
@@ -67,13 +67,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows r
-// and r+8 differ in the low bit so that 16 consecutive rows reading the same
-// logical chunk land in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// K-major LDS stage of one operand: K-half h (K values 32h .. 32h+31) at
+// element h·kHalfElems, 256 rows of 32 values (64 bytes).  The pipeline
+// refills a half as soon as its last slice has been read, so the loads of a
+// step spread over the whole step instead of crowding into one quarter of it.
+// Swizzle: 16-byte chunk c of row r sits at c ^ ((r / 4) % 4); 16 consecutive
+// rows reading one logical chunk then hit 16 distinct 16-byte bank groups
+// (rows r and r + 4k differ in the swizzle, rows r .. r+3 in the 64-byte slot).
+constexpr int kHalfK = kBK / 2;               // K values per half
+constexpr int kHalfElems = kTile * kHalfK;    // bf16 elements per half (16 KiB)
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ swz(row)) << 3);
+__device__ __forceinline__ int lds_off(int half, int row, int chunk) {
+  return half * kHalfElems + row * kHalfK + ((chunk ^ swz(row)) << 3);
 }
 
 // ----------------------------------------------------------------------------
@@ -141,21 +147,22 @@ __device__ __forceinline__ void dtl16(const rsrc_t& rsrc, const void __attribute
 
 // ----------------------------------------------------------------------------
 // Direct-to-LDS K-major loader (buffer_load_dwordx4 ... lds).  One wave
-// instruction fills a 1 KiB block of LDS, lane l writing bytes [16·l, 16·l+16)
-// of it (checked on gfx950: out-of-range lanes write zeros).  Block b holds
-// tile rows 8b .. 8b+7; lane l therefore fetches row 8b + l/8 at physical
-// chunk l % 8, i.e. logical K chunk (l % 8) ^ swz(row), so the LDS image is the
-// same swizzled K-major layout the fragment reads expect.  Each of the 4 waves
-// issues 8 instructions per operand per 64-deep step (blocks 4i + wave).
+// instruction fills a 1 KiB block of one K-half: tile rows 16b .. 16b+15,
+// lane l writing bytes [16·l, 16·l+16) of it (checked on gfx950: out-of-range
+// lanes write zeros), i.e. row 16b + l/4 at physical chunk l % 4, so the lane
+// fetches logical chunk (l % 4) ^ swz(row) of the half.  swz(16b + l/4) =
+// (l/16) % 4 for every block, so a lane's K offset is the same in every block
+// it fills.  A step is 8 instructions per wave: q = 0..3 fill half 0 (blocks
+// 4q + wave), q = 4..7 half 1 (blocks 4(q − 4) + wave).
 // ----------------------------------------------------------------------------
 #define LCE_LDS __attribute__((address_space(3)))
 
 template <bool kTail>
 struct DtlKMajorTile {
   rsrc_t rsrc;
-  uint32_t voff;      // byte offset of this lane's chunk in block `wave`
-  uint32_t row_step;  // bytes between blocks 4i + wave and 4(i+1) + wave (32 rows)
-  int32_t kchunk;     // this lane's logical K offset inside a 64-deep block
+  uint32_t voff;      // byte offset of this lane's chunk in half 0, block `wave`
+  uint32_t row_step;  // bytes between blocks 4j + wave and 4(j+1) + wave (64 rows)
+  int32_t kchunk;     // this lane's K offset inside a half
   int32_t wave;       // wave index, wave-uniform (kept in an SGPR)
   int64_t k_total;
 
@@ -164,36 +171,42 @@ struct DtlKMajorTile {
     rsrc = make_rsrc_raw(base + row0 * ld, (rows_total - row0) * ld * 2);
     const int lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Rows 8(4i + w) + lane/8 all share swz(row) = (lane/8) ^ (w & 1), so the
-    // lane's logical chunk is the same in every block it fills.
-    const int row = wave * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(row);
+    const int row = wave * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(row);
     kchunk = c * 8;
     k_total = k_total_;
     voff = (uint32_t)(row * ld * 2 + c * 16);
-    row_step = (uint32_t)(32 * ld * 2);
+    row_step = (uint32_t)(64 * ld * 2);
   }
-  // Per-step state: the lane's byte offset of the 64-deep K block at k0
-  // (an always-out-of-range offset for chunks past k_total when kTail).
+  // Per-step state: the lane's byte offsets of its chunk in half 0 and half 1
+  // of the 64-deep K block at k0 (kOutOfRange: a zero fill, for chunks past
+  // k_total when kTail, and for steps past the end of the K range).
+  // `row_bytes` moves the step to tile rows further on inside the same
+  // descriptor (the next tile of a sweep).
   struct Step {
-    uint32_t base;
+    uint32_t b0, b1;
   };
-  __device__ __forceinline__ Step prepare(int64_t k0) const {
-    uint32_t base = voff + (uint32_t)(k0 * 2);
-    if (kTail) base = (k0 + kchunk < k_total) ? base : kOutOfRange;
-    return Step{base};
+  __device__ __forceinline__ Step prepare(int64_t k0, uint32_t row_bytes = 0) const {
+    uint32_t b0 = voff + row_bytes + (uint32_t)(k0 * 2), b1 = b0 + kHalfK * 2;
+    if (kTail) {
+      b0 = (k0 + kchunk < k_total) ? b0 : kOutOfRange;
+      b1 = (k0 + kHalfK + kchunk < k_total) ? b1 : kOutOfRange;
+    }
+    return Step{b0, b1};
   }
-  // Enqueue load i (0..7) of the step into `stage`: asynchronous, complete
+  __device__ __forceinline__ Step null_step() const { return Step{kOutOfRange, kOutOfRange}; }
+  // Enqueue load q (0..7) of the step into `stage`: asynchronous, complete
   // once this wave's vmcnt has drained past it.  Without kTail, k_total must
-  // be a multiple of 64 so every chunk is in range.
-  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
-    const uint32_t vo = (kTail && st.base == kOutOfRange) ? kOutOfRange : st.base + i * row_step;
-    dtl16(rsrc, stage + wave * 512 + i * 2048, vo);
+  // be a multiple of 64 so every chunk is in range.  kOutOfRange plus the
+  // block offset (< 2^30) stays out of range.
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int q) const {
+    const int h = q >> 2, j = q & 3;
+    dtl16(rsrc, stage + h * kHalfElems + (j * 4 + wave) * 512, (h ? st.b1 : st.b0) + j * row_step);
   }
   __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
     const Step st = prepare(k0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue(st, stage, i);
+    for (int q = 0; q < 8; ++q) issue(st, stage, q);
   }
 };
 
@@ -235,6 +248,9 @@ struct DtlMNMajorTile {
   __device__ __forceinline__ Step prepare(int64_t k0) const {
     return Step{make_rsrc_raw(base + k0 * ld, (k_total - k0) * ld * 2)};
   }
+  __device__ __forceinline__ Step null_step() const { return Step{make_rsrc_raw(base, 0)}; }
+  // Load q fills K rows 2·wave + 8q and 2·wave + 8q + 1, so q = 0..3 cover
+  // K-half 0 (rows 0..31) and q = 4..7 K-half 1.
   __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
     dtl16(st.rsrc, stage + wave * 512 + i * 2048, voff + i * row_step);
   }
@@ -261,7 +277,9 @@ constexpr int64_t kGSubElems = (int64_t)kTile * kBK;      // one 256 x 64 sub-bl
 
 // K-major reader of blocked G for the dX contraction: rows are the tokens of
 // one token tile, K the chunk's vocabulary.  init(G, nvt, tok0, ...): the
-// second argument is the chunk's count of vocabulary tiles.
+// second argument is the chunk's count of vocabulary tiles.  Same LDS image
+// as DtlKMajorTile; in memory, K-half h of token row r of K step k0 is the
+// 64 bytes at sub-block k0 / 64, row r, column 32h.
 struct DtlKMajorBlockedG {
   rsrc_t rsrc;
   uint32_t voff, row_step;
@@ -271,25 +289,28 @@ struct DtlKMajorBlockedG {
     rsrc = make_rsrc_raw(base + (row0 / kTile) * nvt * kGBlockElems, nvt * kGBlockElems * 2);
     const int lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row = wave * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(row);
+    const int row = wave * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(row);
     voff = (uint32_t)(row * kBK * 2 + c * 16);
-    row_step = (uint32_t)(32 * kBK * 2);
+    row_step = (uint32_t)(64 * kBK * 2);
   }
   struct Step {
-    uint32_t base;
+    uint32_t b0, b1;
   };
   // K step k0 (a multiple of 64) is sub-block k0 / 64 of the token tile.
   __device__ __forceinline__ Step prepare(int64_t k0) const {
-    return Step{voff + (uint32_t)(k0 / kBK) * (uint32_t)(kGSubElems * 2)};
+    const uint32_t b0 = voff + (uint32_t)(k0 / kBK) * (uint32_t)(kGSubElems * 2);
+    return Step{b0, b0 + kHalfK * 2};
   }
-  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
-    dtl16(rsrc, stage + wave * 512 + i * 2048, st.base + i * row_step);
+  __device__ __forceinline__ Step null_step() const { return Step{kOutOfRange, kOutOfRange}; }
+  __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int q) const {
+    const int h = q >> 2, j = q & 3;
+    dtl16(rsrc, stage + h * kHalfElems + (j * 4 + wave) * 512, (h ? st.b1 : st.b0) + j * row_step);
   }
   __device__ __forceinline__ void load(LCE_LDS uint16_t* stage, int64_t k0) const {
     const Step st = prepare(k0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue(st, stage, i);
+    for (int q = 0; q < 8; ++q) issue(st, stage, q);
   }
 };
 
@@ -324,6 +345,7 @@ struct DtlMNMajorBlockedG {
     const int64_t first = (k0 % kTile) * kBK;
     return Step{make_rsrc_raw(base + blk + first, (kGBlockElems - first) * 2)};
   }
+  __device__ __forceinline__ Step null_step() const { return Step{make_rsrc_raw(base, 0)}; }
   __device__ __forceinline__ void issue(const Step& st, LCE_LDS uint16_t* stage, int i) const {
     dtl16(st.rsrc, stage + wave * 512 + i * 2048, voff + i * row_step);
   }
@@ -338,7 +360,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // MFMA fragment of tile rows mbase .. mbase+31, K slice t (16 deep).
-// K-major LDS: one 16-byte read.  MN-major LDS: two ds_read_b64_tr_b16.  That
+// K-major LDS: one 16-byte read (slice t lies in half t / 2, chunks
+// 2·(t % 2) and 2·(t % 2) + 1 for the two lane halves).  MN-major LDS: two ds_read_b64_tr_b16.  That
 // instruction works on groups of 16 lanes: lane k supplies 4 consecutive
 // elements P_k and lane i receives P_{4j + i/4}[i % 4], j = 0..3 (checked on
 // gfx950).  Pointing lane k' at k-row (k0 + k'/4), columns m0 + 4(k' % 4)
@@ -347,7 +370,8 @@ template <bool kMN>
 __device__ __forceinline__ bf16x8 frag_read(const LCE_LDS uint16_t* s, int mbase, int t, int lane) {
   if (!kMN) {
     return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(s + lds_off(mbase + (lane & 31), t * 2 + (lane >> 5))));
+        bf16x8, *reinterpret_cast<const LCE_LDS u32x4*>(
+                    s + lds_off(t >> 1, mbase + (lane & 31), ((t & 1) << 1) | (lane >> 5))));
   } else {
     const int g = lane >> 4, kk = lane & 15;
     const int m = mbase + 16 * (g & 1) + 4 * (kk & 3);
@@ -362,7 +386,8 @@ __device__ __forceinline__ bf16x8 frag_read(const LCE_LDS uint16_t* s, int mbase
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
-constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);   // vmcnt <= 16
+constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);       // vmcnt <= 16
+constexpr int kWaitVm20 = (1 << 14) | 4 | (7 << 4) | (15 << 8);   // vmcnt <= 20
 constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);
 
 // Workgroup barrier without the memory fence __syncthreads() carries (that
@@ -391,14 +416,6 @@ __device__ __forceinline__ void read_frag(Frag& f, const LCE_LDS uint16_t* sA,
   for (int ni = 0; ni < kNI; ++ni) f.b[ni] = frag_read<kBmn>(sB, wn * kWaveTile + ni * 32, t, lane);
 }
 
-__device__ __forceinline__ void mfma_group(const Frag& f, f32x16 (&acc)[kMI][kNI]) {
-#pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
-}
-
 #define LCE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Fragment piece p (0..7) of K slice t: A rows for p < 4, B rows otherwise.
@@ -412,58 +429,77 @@ __device__ __forceinline__ void read_piece(Frag& f, const LCE_LDS uint16_t* sA,
     f.b[p - kMI] = frag_read<kBmn>(sB, wn * kWaveTile + (p - kMI) * 32, t, lane);
 }
 
-#define LCE_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-
-// MFMA group of fragment set `fm` with the 8 fragment reads of K slice t into
-// `fr` interleaved one per MFMA (ds reads 0x100, MFMA 0x008).
-template <bool kAmn, bool kBmn>
-__device__ __forceinline__ void mfma_with_reads(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* sA,
-                                                const LCE_LDS uint16_t* sB, int wm, int wn,
-                                                int lane, int t, f32x16 (&acc)[kMI][kNI]) {
-  read_frag<kAmn, kBmn>(fr, sA, sB, wm, wn, lane, t);
-  mfma_group(fm, acc);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    LCE_SCHED_GROUP(0x008, 1);
-    LCE_SCHED_GROUP(0x100, kAmn || kBmn ? 2 : 1);
-  }
-  LCE_SCHED_GROUP(0x008, 8);
-  LCE_SCHED_FENCE();
-}
-
 // Cross-tile prefetch state of a persistent sweep over A tiles that share one
 // B tile (the forward and the logit-gradient kernels walk the vocabulary
-// tiles of one token tile).  While a tile finishes, its last two pipeline
-// steps issue the first two steps of the next A tile into the stages they
-// free, so those loads are in flight during the caller's epilogue and the
-// next tile starts without a pipeline fill.
+// tiles of one token tile).  The load stream of a tile runs on into the next
+// tile: its last two steps issue that tile's steps 0 and 1, so those loads
+// are in flight during the caller's epilogue and the next tile starts
+// without a pipeline fill.
 struct Sweep {
   int par = 0;             // stage index holding step 0 of the current tile
   bool preloaded = false;  // steps 0 and 1 of the current tile are in flight
 };
 
+// One section of a pipeline step: the 16 MFMAs of fragment set `fm` (one
+// 16-deep K slice), the 8 fragment pieces of K slice t of stage (rA, rB) into
+// `fr`, and 4 loads of one operand's K-half h into `dst` (loads
+// 4h .. 4h+3 of the step state `st`).  The reads go with the first 8 MFMAs,
+// so they land well before the next section multiplies them; the loads go
+// with every fourth MFMA.  Each group is fenced so the compiler keeps the
+// interleave.
+template <bool kAmn, bool kBmn, class L>
+__device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* rA,
+                                             const LCE_LDS uint16_t* rB, int t, const L& ld,
+                                             const typename L::Step& st, LCE_LDS uint16_t* dst,
+                                             int h, int wm, int wn, int lane,
+                                             f32x16 (&acc)[kMI][kNI]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int mi = i >> 2, ni = i & 3;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm.a[mi], fm.b[ni], acc[mi][ni], 0, 0, 0);
+    if (i < 8) read_piece<kAmn, kBmn>(fr, rA, rB, wm, wn, lane, t, i);
+    if ((i & 3) == 3) ld.issue(st, dst, 4 * h + (i >> 2));
+    LCE_SCHED_FENCE();
+  }
+}
+
+// Section boundary: this wave's loads older than its last 16 have landed and
+// its LDS reads are done; then the same for every wave.
+__device__ __forceinline__ void pipe_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitVm16);
+  lds_barrier();
+}
+
 // One 256 x 256 tile C += A·Bᵀ over the K range [k_begin, k_end) (at least
-// one 64-deep step), each operand K-major (kAmn/kBmn false: DtlKMajorTile) or
-// MN-major (true: DtlMNMajorTile), through a two-stage direct-to-LDS
-// pipeline.  LDS: 128 KiB (stage s of A at smem + s·kStageElems, of B at
-// smem + (2 + s)·kStageElems).  For a K-major operand `row0/rows` are its
-// tile rows; for an MN-major one they are its column offset / column count.
+// one 64-deep step), each operand K-major (kAmn/kBmn false) or MN-major
+// (true), through a two-stage direct-to-LDS pipeline.  LDS: 128 KiB (stage s
+// of A at smem + s·kStageElems, of B at smem + (2 + s)·kStageElems).  For a
+// K-major operand `row0/rows` are its tile rows; for an MN-major one they are
+// its column offset / column count.
 //
-// Step k (K slices 0..3 of stage k % 2, fragments f0..f3):
-//   MFMA f0 while reading f2; MFMA f1 while reading f3; MFMA f2;
-//   wait for this wave's loads of stage (k+1) % 2, workgroup barrier;
-//   then 16 (MFMA, load, fragment read) triples, issued in that order and
-//   fenced one by one: the deferred MFMA group f3, the 16 loads of step k + 2
-//   into the stage just consumed, and slices 0 and 1 of the next stage.
-// The MFMA pipe therefore always has independent work while the loads and
-// the LDS reads of the next stage are in flight.
+// A step is four sections of 16 MFMAs, one per 16-deep K slice; the
+// fragments of a slice are read from LDS in the section before the one that
+// multiplies them.  With S the stage of step k (halves h0 = slices 0-1,
+// h1 = slices 2-3) and each step's loads in four groups (h0 of A, h0 of B,
+// h1 of A, h1 of B):
+//   A(k): MFMA slice 0, read slice 1 (S.h0), load step k+1 h1 of B
+//   barrier: every wave has read S.h0; step k's h1 has landed
+//   B(k): MFMA slice 1, read slice 2 (S.h1), load step k+2 h0 of A into S.h0
+//   C(k): MFMA slice 2, read slice 3 (S.h1), load step k+2 h0 of B into S.h0
+//   barrier: every wave has read S.h1; step k+1's h0 has landed
+//   E(k): MFMA slice 3, read slice 0 of step k+1, load step k+2 h1 of A into S.h1
+// Every section thus carries 8 fragment reads (two LDS reads each for an
+// MN-major operand) and 4 loads per wave, and a load has about four sections
+// to land.  Both waits are vmcnt(16), the loads issued after the awaited
+// group.  Steps past the K range load zeros into stages no longer read,
+// which keeps the count fixed.
 //
 // kSweep (K-major operands only, k_begin = 0): `sw` carries the prefetch
-// state; when next_a_row0 >= 0 and the tile has at least two steps, step 0 of
-// the next A tile (rows next_a_row0.., same B) is loaded during the
-// second-to-last step and step 1 after the last step's reads.  kWaitAll: the
-// caller issues other memory operations between two tiles, so a preloaded
-// tile waits for all of them (vmcnt 0) instead of only for its step 0.  The
+// state; when next_a_row0 >= 0 the steps past the K range are steps 0 and 1
+// of the next A tile (rows next_a_row0 > a_row0, within a_rows; same B), so
+// the next call finds them in flight.  kWaitAll: the caller issues other memory operations
+// between two tiles, so a preloaded tile waits for all of them (vmcnt 0).
+// Without kSweep the tile drains its loads before returning; with it the
 // caller waits for vmcnt 0 after the sweep before reusing the LDS.
 //
 // kABlk: A is the blocked gradient chunk (DtlKMajorBlockedG / DtlMNMajorBlockedG);
@@ -480,140 +516,93 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
       kABlk, typename std::conditional<kAmn, DtlMNMajorBlockedG, DtlKMajorBlockedG>::type,
       typename std::conditional<kAmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type>::type LA;
   typedef typename std::conditional<kBmn, DtlMNMajorTile, DtlKMajorTile<kTail>>::type LB;
+  typedef typename LA::Step StA;
+  typedef typename LB::Step StB;
   static_assert(!kSweep || (!kAmn && !kBmn), "the sweep prefetch handles K-major operands");
   static_assert(!kSweep || !kABlk, "the sweep prefetch reads row-major operands");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int nsteps = (int)((k_end - k_begin + kBK - 1) / kBK);
   const int par = kSweep ? sw->par : 0;
-  // In sweep mode the prefetch loads are always issued (a fixed code path);
-  // without a next tile they carry an always-out-of-range offset and only
-  // zero-fill stages this tile no longer reads.
-  const bool prefetch = kSweep && next_a_row0 >= 0 && nsteps >= 2;
+  const bool prefetch = kSweep && next_a_row0 >= 0;
   LA la;
   LB lb;
   la.init(A, lda, a_row0, a_rows, k_total, tid);
   lb.init(B, ldb, b_row0, b_rows, k_total, tid);
-  LCE_LDS uint16_t* sA0 = smem + par * kStageElems;
-  LCE_LDS uint16_t* sA1 = smem + (par ^ 1) * kStageElems;
-  LCE_LDS uint16_t* sB0 = smem + (2 + par) * kStageElems;
-  LCE_LDS uint16_t* sB1 = smem + (2 + (par ^ 1)) * kStageElems;
+  // Sweep: the next A tile lies next_a_row0 − a_row0 rows further on, inside
+  // the descriptor of this one (it ends at a_rows).
+  const uint32_t next_bytes = prefetch ? (uint32_t)((next_a_row0 - a_row0) * lda * 2) : 0u;
+  // Stage of stream step s: A at smem + ((par + s) % 2)·kStageElems.
+  auto stA = [&](int s) { return smem + ((par ^ s) & 1) * kStageElems; };
+  auto stB = [&](int s) { return smem + (2 + ((par ^ s) & 1)) * kStageElems; };
+  // Loader state of stream step s: this tile's steps, then (sweep with a next
+  // tile) that tile's steps 0 and 1, else zero fills.
+  auto stepA = [&](int s) -> StA {
+    if (s < nsteps) return la.prepare(k_begin + (int64_t)s * kBK);
+    if constexpr (kSweep) {
+      if (prefetch) return la.prepare((int64_t)(s - nsteps) * kBK, next_bytes);
+    }
+    return la.null_step();
+  };
+  auto stepB = [&](int s) -> StB {
+    if (s < nsteps) return lb.prepare(k_begin + (int64_t)s * kBK);
+    if constexpr (kSweep) {
+      if (prefetch) return lb.prepare((int64_t)(s - nsteps) * kBK);
+    }
+    return lb.null_step();
+  };
   if (kSweep && sw->preloaded) {
-    // Steps 0 and 1 (16 loads each per wave) were issued by the previous tile.
-    if (kWaitAll || nsteps < 2) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm16);
-    lds_barrier();
+    // Steps 0 and 1 (28 loads per wave, as below) were issued by the previous tile.
+    if (kWaitAll) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm20);
   } else {
     lds_barrier();  // every wave is done with the LDS of the previous tile
-    la.load(sA0, k_begin);
-    lb.load(sB0, k_begin);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    lds_barrier();
-    if (nsteps > 1) {
-      la.load(sA1, k_begin + kBK);
-      lb.load(sB1, k_begin + kBK);
+    // Steps 0 and 1 in steady-state order, except step 1's h1 of B, which
+    // section A of step 0 issues.
+    const StA a0 = stepA(0), a1 = stepA(1);
+    const StB b0 = stepB(0), b1 = stepB(1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) la.issue(a0, stA(0), 4 * h + q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lb.issue(b0, stB(0), 4 * h + q);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) la.issue(a1, stA(1), q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lb.issue(b1, stB(1), q);
+#pragma unroll
+    for (int q = 4; q < 8; ++q) la.issue(a1, stA(1), q);
+    __builtin_amdgcn_s_waitcnt(kWaitVm20);   // step 0's h0 has landed
   }
-  LA ln;  // loader of the next A tile (sweep mode)
-  if (kSweep) ln.init(A, lda, prefetch ? next_a_row0 : a_row0, a_rows, k_total, tid);
+  lds_barrier();
   Frag f0, f1, f2, f3;
-  read_frag<kAmn, kBmn>(f0, sA0, sB0, wm, wn, lane, 0);
-  read_frag<kAmn, kBmn>(f1, sA0, sB0, wm, wn, lane, 1);
+  read_frag<kAmn, kBmn>(f0, stA(0), stB(0), wm, wn, lane, 0);
   LCE_SCHED_FENCE();
-  int k = 0;
-  for (; k + 2 < nsteps; ++k) {
-    const bool odd = k & 1;
-    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
-    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
-    const LCE_LDS uint16_t* na = odd ? sA0 : sA1;
-    const LCE_LDS uint16_t* nb = odd ? sB0 : sB1;
-    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
-    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
-    mfma_group(f2, acc);
-    LCE_SCHED_FENCE();
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of the next stage landed
-    lds_barrier();                          // ... and every other wave's
-    const typename LA::Step sta = la.prepare(k_begin + (int64_t)(k + 2) * kBK);
-    const typename LB::Step stb = lb.prepare(k_begin + (int64_t)(k + 2) * kBK);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mi = i >> 2, ni = i & 3;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
-      if (i < 8)
-        la.issue(sta, ca, i);
-      else
-        lb.issue(stb, cb, i - 8);
-      read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
-      LCE_SCHED_FENCE();
-    }
-  }
-  if (k + 1 < nsteps) {  // second-to-last step: nothing of this tile left to load
-    const bool odd = k & 1;
-    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
-    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
-    const LCE_LDS uint16_t* na = odd ? sA0 : sA1;
-    const LCE_LDS uint16_t* nb = odd ? sB0 : sB1;
-    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
-    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
-    mfma_group(f2, acc);
-    LCE_SCHED_FENCE();
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    lds_barrier();
-    if constexpr (kSweep) {  // step 0 of the next tile into the stage just consumed
-      typename LA::Step sta = ln.prepare(0);
-      typename LB::Step stb = lb.prepare(0);
-      if (!prefetch) sta.base = stb.base = kOutOfRange;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
-        if (i < 8)
-          ln.issue(sta, ca, i);
-        else
-          lb.issue(stb, cb, i - 8);
-        read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
-        LCE_SCHED_FENCE();
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3.a[mi], f3.b[ni], acc[mi][ni], 0, 0, 0);
-        read_piece<kAmn, kBmn>(i < 8 ? f0 : f1, na, nb, wm, wn, lane, i >> 3, i & 7);
-        LCE_SCHED_FENCE();
-      }
-    }
-    ++k;
-  }
-  {  // last step
-    const bool odd = k & 1;
-    LCE_LDS uint16_t* ca = odd ? sA1 : sA0;
-    LCE_LDS uint16_t* cb = odd ? sB1 : sB0;
-    mfma_with_reads<kAmn, kBmn>(f0, f2, ca, cb, wm, wn, lane, 2, acc);
-    mfma_with_reads<kAmn, kBmn>(f1, f3, ca, cb, wm, wn, lane, 3, acc);
-    if constexpr (kSweep) {  // every wave has read this stage: step 1 of the next tile goes here
-      lds_barrier();
-      typename LA::Step sta = ln.prepare(kBK);
-      typename LB::Step stb = lb.prepare(kBK);
-      if (!prefetch) sta.base = stb.base = kOutOfRange;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2.a[mi], f2.b[ni], acc[mi][ni], 0, 0, 0);
-        if (i < 8)
-          ln.issue(sta, ca, i);
-        else
-          lb.issue(stb, cb, i - 8);
-        LCE_SCHED_FENCE();
-      }
-    } else {
-      mfma_group(f2, acc);
-    }
-    mfma_group(f3, acc);
+  StB bnext = stepB(1);  // step k+1 of B, for section A of step k
+  for (int k = 0; k < nsteps; ++k) {
+    LCE_LDS uint16_t* ca = stA(k);
+    LCE_LDS uint16_t* cb = stB(k);
+    LCE_LDS uint16_t* na = stA(k + 1);
+    LCE_LDS uint16_t* nb = stB(k + 1);
+    const StA a2 = stepA(k + 2);
+    const StB b2 = stepB(k + 2);
+    pipe_section<kAmn, kBmn>(f0, f1, ca, cb, 1, lb, bnext, nb, 1, wm, wn, lane, acc);
+    pipe_barrier();
+    pipe_section<kAmn, kBmn>(f1, f2, ca, cb, 2, la, a2, ca, 0, wm, wn, lane, acc);
+    pipe_section<kAmn, kBmn>(f2, f3, ca, cb, 3, lb, b2, cb, 0, wm, wn, lane, acc);
+    pipe_barrier();
+    // In the last step this reads step k+1's half 0 all the same: zero fills
+    // or the next tile's first slice, landed by the barrier above and unused.
+    pipe_section<kAmn, kBmn>(f3, f0, na, nb, 0, la, a2, ca, 1, wm, wn, lane, acc);
+    bnext = b2;
   }
   if (kSweep) {
     sw->par = (par + nsteps) & 1;  // stage of the next tile's step 0
     sw->preloaded = prefetch;
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the zero fills past the K range
   }
 }
 
