@@ -388,6 +388,7 @@ __device__ __forceinline__ bf16x8 frag_read(const LCE_LDS uint16_t* s, int mbase
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 constexpr int kWaitVm16 = (1 << 14) | (7 << 4) | (15 << 8);       // vmcnt <= 16
 constexpr int kWaitVm20 = (1 << 14) | 4 | (7 << 4) | (15 << 8);   // vmcnt <= 20
+constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);                 // vmcnt <= 8
 constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);
 
 // Workgroup barrier without the memory fence __syncthreads() carries (that
@@ -443,11 +444,11 @@ struct Sweep {
 // One section of a pipeline step: the 16 MFMAs of fragment set `fm` (one
 // 16-deep K slice), the 8 fragment pieces of K slice t of stage (rA, rB) into
 // `fr`, and 4 loads of one operand's K-half h into `dst` (loads
-// 4h .. 4h+3 of the step state `st`).  The reads go with the first 8 MFMAs,
+// 4h .. 4h+3 of the step state `st`, when `load`).  The reads go with the first 8 MFMAs,
 // so they land well before the next section multiplies them; the loads go
 // with every fourth MFMA.  Each group is fenced so the compiler keeps the
 // interleave.
-template <bool kAmn, bool kBmn, class L>
+template <bool kAmn, bool kBmn, bool kLoad, class L>
 __device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* rA,
                                              const LCE_LDS uint16_t* rB, int t, const L& ld,
                                              const typename L::Step& st, LCE_LDS uint16_t* dst,
@@ -458,15 +459,17 @@ __device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE
     const int mi = i >> 2, ni = i & 3;
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm.a[mi], fm.b[ni], acc[mi][ni], 0, 0, 0);
     if (i < 8) read_piece<kAmn, kBmn>(fr, rA, rB, wm, wn, lane, t, i);
-    if ((i & 3) == 3) ld.issue(st, dst, 4 * h + (i >> 2));
+    if (kLoad && (i & 3) == 3) ld.issue(st, dst, 4 * h + (i >> 2));
     LCE_SCHED_FENCE();
   }
 }
 
-// Section boundary: this wave's loads older than its last 16 have landed and
-// its LDS reads are done; then the same for every wave.
+// Section boundary: this wave's loads older than its last kNewer (16, 8 or
+// 0: the loads issued after the awaited group) have landed and its LDS reads
+// are done; then the same for every wave.
+template <int kNewer>
 __device__ __forceinline__ void pipe_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitVm16);
+  __builtin_amdgcn_s_waitcnt(kNewer >= 16 ? kWaitVm16 : (kNewer >= 8 ? kWaitVm8 : kWaitVm0));
   lds_barrier();
 }
 
@@ -490,17 +493,19 @@ __device__ __forceinline__ void pipe_barrier() {
 //   E(k): MFMA slice 3, read slice 0 of step k+1, load step k+2 h1 of A into S.h1
 // Every section thus carries 8 fragment reads (two LDS reads each for an
 // MN-major operand) and 4 loads per wave, and a load has about four sections
-// to land.  Both waits are vmcnt(16), the loads issued after the awaited
-// group.  Steps past the K range load zeros into stages no longer read,
-// which keeps the count fixed.
+// to land.  Each wait counts the loads issued after the awaited group: 16
+// inside the K range.  A sweep keeps that count to the end (its last tile
+// loads zeros for the steps past the range); a single tile peels its last
+// two steps, which load nothing and wait for 8 or 0.  The last step still
+// reads the next step's first slice, unused.
 //
 // kSweep (K-major operands only, k_begin = 0): `sw` carries the prefetch
 // state; when next_a_row0 >= 0 the steps past the K range are steps 0 and 1
 // of the next A tile (rows next_a_row0 > a_row0, within a_rows; same B), so
 // the next call finds them in flight.  kWaitAll: the caller issues other memory operations
 // between two tiles, so a preloaded tile waits for all of them (vmcnt 0).
-// Without kSweep the tile drains its loads before returning; with it the
-// caller waits for vmcnt 0 after the sweep before reusing the LDS.
+// Without a next tile every load has landed when the tile returns; after a
+// sweep the caller waits for vmcnt 0 before reusing the LDS.
 //
 // kABlk: A is the blocked gradient chunk (DtlKMajorBlockedG / DtlMNMajorBlockedG);
 // `lda` is then the chunk's count of vocabulary tiles.
@@ -536,7 +541,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
   auto stA = [&](int s) { return smem + ((par ^ s) & 1) * kStageElems; };
   auto stB = [&](int s) { return smem + (2 + ((par ^ s) & 1)) * kStageElems; };
   // Loader state of stream step s: this tile's steps, then (sweep with a next
-  // tile) that tile's steps 0 and 1, else zero fills.
+  // tile) that tile's steps 0 and 1.  Past those, a sweep loads zeros into
+  // stages no longer read; a single tile loads nothing (its tail steps).
   auto stepA = [&](int s) -> StA {
     if (s < nsteps) return la.prepare(k_begin + (int64_t)s * kBK);
     if constexpr (kSweep) {
@@ -568,41 +574,57 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
 #pragma unroll
       for (int q = 0; q < 4; ++q) lb.issue(b0, stB(0), 4 * h + q);
     }
+    if (kSweep || nsteps > 1) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) la.issue(a1, stA(1), q);
+      for (int q = 0; q < 4; ++q) la.issue(a1, stA(1), q);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lb.issue(b1, stB(1), q);
+      for (int q = 0; q < 4; ++q) lb.issue(b1, stB(1), q);
 #pragma unroll
-    for (int q = 4; q < 8; ++q) la.issue(a1, stA(1), q);
-    __builtin_amdgcn_s_waitcnt(kWaitVm20);   // step 0's h0 has landed
+      for (int q = 4; q < 8; ++q) la.issue(a1, stA(1), q);
+      __builtin_amdgcn_s_waitcnt(kWaitVm20);   // step 0's h0 has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    }
   }
   lds_barrier();
   Frag f0, f1, f2, f3;
   read_frag<kAmn, kBmn>(f0, stA(0), stB(0), wm, wn, lane, 0);
   LCE_SCHED_FENCE();
   StB bnext = stepB(1);  // step k+1 of B, for section A of step k
-  for (int k = 0; k < nsteps; ++k) {
+  // Step k; L1 / L2: steps k+1 / k+2 are loaded (compile-time flags, so no
+  // branch sits between the MFMAs).
+  auto step = [&](int k, auto L1, auto L2) {
+    constexpr bool l1 = decltype(L1)::value, l2 = decltype(L2)::value;
     LCE_LDS uint16_t* ca = stA(k);
     LCE_LDS uint16_t* cb = stB(k);
     LCE_LDS uint16_t* na = stA(k + 1);
     LCE_LDS uint16_t* nb = stB(k + 1);
     const StA a2 = stepA(k + 2);
     const StB b2 = stepB(k + 2);
-    pipe_section<kAmn, kBmn>(f0, f1, ca, cb, 1, lb, bnext, nb, 1, wm, wn, lane, acc);
-    pipe_barrier();
-    pipe_section<kAmn, kBmn>(f1, f2, ca, cb, 2, la, a2, ca, 0, wm, wn, lane, acc);
-    pipe_section<kAmn, kBmn>(f2, f3, ca, cb, 3, lb, b2, cb, 0, wm, wn, lane, acc);
-    pipe_barrier();
-    // In the last step this reads step k+1's half 0 all the same: zero fills
-    // or the next tile's first slice, landed by the barrier above and unused.
-    pipe_section<kAmn, kBmn>(f3, f0, na, nb, 0, la, a2, ca, 1, wm, wn, lane, acc);
+    pipe_section<kAmn, kBmn, l1>(f0, f1, ca, cb, 1, lb, bnext, nb, 1, wm, wn, lane, acc);
+    pipe_barrier<l1 ? 16 : 0>();
+    pipe_section<kAmn, kBmn, l2>(f1, f2, ca, cb, 2, la, a2, ca, 0, wm, wn, lane, acc);
+    pipe_section<kAmn, kBmn, l2>(f2, f3, ca, cb, 3, lb, b2, cb, 0, wm, wn, lane, acc);
+    pipe_barrier<(l1 ? 8 : 0) + (l2 ? 8 : 0)>();
+    pipe_section<kAmn, kBmn, l2>(f3, f0, na, nb, 0, la, a2, ca, 1, wm, wn, lane, acc);
     bnext = b2;
+  };
+  const std::true_type yes{};
+  const std::false_type no{};
+  int k = 0;
+  if constexpr (kSweep) {
+    // The stream runs on into the next tile's steps 0 and 1, or, after the
+    // last tile, loads zeros into stages no longer read (one code path for
+    // every tile keeps the accumulators in place).
+    for (; k < nsteps; ++k) step(k, yes, yes);
+  } else {
+    for (; k + 2 < nsteps; ++k) step(k, yes, yes);
+    if (k + 1 < nsteps) step(k++, yes, no);
+    step(k, no, no);
   }
   if (kSweep) {
     sw->par = (par + nsteps) & 1;  // stage of the next tile's step 0
     sw->preloaded = prefetch;
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the zero fills past the K range
   }
 }
 
