@@ -448,16 +448,19 @@ struct Sweep {
 // so they land well before the next section multiplies them; the loads go
 // with every fourth MFMA.  Each group is fenced so the compiler keeps the
 // interleave.
-template <bool kAmn, bool kBmn, bool kLoad, class L>
+template <bool kAmn, bool kBmn, bool kLoad, class L, bool kZeroC = false>
 __device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* rA,
                                              const LCE_LDS uint16_t* rB, int t, const L& ld,
                                              const typename L::Step& st, LCE_LDS uint16_t* dst,
                                              int h, int wm, int wn, int lane,
                                              f32x16 (&acc)[kMI][kNI]) {
+  const f32x16 zero = {};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int mi = i >> 2, ni = i & 3;
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm.a[mi], fm.b[ni], acc[mi][ni], 0, 0, 0);
+    // kZeroC: the tile's first K slice starts from zero instead of acc.
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm.a[mi], fm.b[ni], kZeroC ? zero : acc[mi][ni],
+                                                          0, 0, 0);
     if (i < 8) read_piece<kAmn, kBmn>(fr, rA, rB, wm, wn, lane, t, i);
     if (kLoad && (i & 3) == 3) ld.issue(st, dst, 4 * h + (i >> 2));
     LCE_SCHED_FENCE();
@@ -499,7 +502,8 @@ __device__ __forceinline__ void pipe_barrier() {
 // two steps, which load nothing and wait for 8 or 0.  The last step still
 // reads the next step's first slice, unused.
 //
-// kSweep (K-major operands only, k_begin = 0): `sw` carries the prefetch
+// kSweep (K-major operands only, k_begin = 0): the tile overwrites acc
+// (C = A·Bᵀ; its first K slice starts from zero) and `sw` carries the prefetch
 // state; when next_a_row0 >= 0 the steps past the K range are steps 0 and 1
 // of the next A tile (rows next_a_row0 > a_row0, within a_rows; same B), so
 // the next call finds them in flight.  kWaitAll: the caller issues other memory operations
@@ -593,15 +597,15 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
   StB bnext = stepB(1);  // step k+1 of B, for section A of step k
   // Step k; L1 / L2: steps k+1 / k+2 are loaded (compile-time flags, so no
   // branch sits between the MFMAs).
-  auto step = [&](int k, auto L1, auto L2) {
-    constexpr bool l1 = decltype(L1)::value, l2 = decltype(L2)::value;
+  auto step = [&](int k, auto L1, auto L2, auto Z) {
+    constexpr bool l1 = decltype(L1)::value, l2 = decltype(L2)::value, z = decltype(Z)::value;
     LCE_LDS uint16_t* ca = stA(k);
     LCE_LDS uint16_t* cb = stB(k);
     LCE_LDS uint16_t* na = stA(k + 1);
     LCE_LDS uint16_t* nb = stB(k + 1);
     const StA a2 = stepA(k + 2);
     const StB b2 = stepB(k + 2);
-    pipe_section<kAmn, kBmn, l1>(f0, f1, ca, cb, 1, lb, bnext, nb, 1, wm, wn, lane, acc);
+    pipe_section<kAmn, kBmn, l1, LB, z>(f0, f1, ca, cb, 1, lb, bnext, nb, 1, wm, wn, lane, acc);
     pipe_barrier<l1 ? 16 : 0>();
     pipe_section<kAmn, kBmn, l2>(f1, f2, ca, cb, 2, la, a2, ca, 0, wm, wn, lane, acc);
     pipe_section<kAmn, kBmn, l2>(f2, f3, ca, cb, 3, lb, b2, cb, 0, wm, wn, lane, acc);
@@ -615,12 +619,14 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
   if constexpr (kSweep) {
     // The stream runs on into the next tile's steps 0 and 1, or, after the
     // last tile, loads zeros into stages no longer read (one code path for
-    // every tile keeps the accumulators in place).
-    for (; k < nsteps; ++k) step(k, yes, yes);
+    // every tile keeps the accumulators in place).  Step 0 starts the
+    // accumulators from zero.
+    step(k++, yes, yes, yes);
+    for (; k < nsteps; ++k) step(k, yes, yes, no);
   } else {
-    for (; k + 2 < nsteps; ++k) step(k, yes, yes);
-    if (k + 1 < nsteps) step(k++, yes, no);
-    step(k, no, no);
+    for (; k + 2 < nsteps; ++k) step(k, yes, yes, no);
+    if (k + 1 < nsteps) step(k++, yes, no, no);
+    step(k, no, no, no);
   }
   if (kSweep) {
     sw->par = (par + nsteps) & 1;  // stage of the next tile's step 0

@@ -192,7 +192,6 @@ lse_partials_kernel(LseParams p) {
   Sweep sw;
   f32x16 acc[kMI][kNI];
   for (int j = j0; j < j_mid; ++j) {
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true>(p.W, p.H, (int64_t)j * kTile, p.V, p.X, p.H, tok0, p.N, 0,
                                          p.H, p.H, smem, acc, &sw,
                                          j + 1 < j1 ? (int64_t)(j + 1) * kTile : -1);
@@ -200,7 +199,6 @@ lse_partials_kernel(LseParams p) {
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H, smem,
                                          acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
@@ -355,7 +353,6 @@ grad_logits_kernel(GradParams p) {
   f32x16 acc[kMI][kNI];
   for (int j = j0; j < j_mid; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;      // chunk-local vocabulary row
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true, true>(p.W, p.H, p.v_begin + vloc0, p.V, p.X, p.H, tok0, p.N,
                                                0, p.H, p.H, smem, acc, &sw,
                                                j + 1 < j1 ? p.v_begin + vloc0 + kTile : -1);
@@ -369,7 +366,6 @@ grad_logits_kernel(GradParams p) {
   for (int j = j_mid; j < j1; ++j) {
     const int64_t vloc0 = (int64_t)j * kTile;
     const int64_t v0 = p.v_begin + vloc0;
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H, p.H,
                                                smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
@@ -532,7 +528,6 @@ flce_logits_kernel(FlceParams p) {
   // tile that reaches past V.
   for (int j = j0; j < j_mid; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
                                                p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
@@ -543,7 +538,6 @@ flce_logits_kernel(FlceParams p) {
   }
   for (int j = j_mid; j < j1; ++j) {
     const int64_t v0 = (int64_t)j * kTile;
-    zero_acc(acc);
     gemm_tile<false, false, kTail, true, true>(p.W, p.H, v0, p.V, p.X, p.H, tok0, p.N, 0, p.H,
                                                p.H, smem, acc, &sw, j + 1 < j1 ? v0 + kTile : -1);
     uint32_t cb[kNI];
