@@ -54,6 +54,8 @@ CASES = [
     (300, 64, 777, dict(logit_scale=0.6, reduction="none", label_smoothing=0.05)),
     (100, 64, 300, dict(softcap=20.0)),                            # N < 256, one partial tile
     (257, 8, 40, dict(z_loss=1e-2)),                               # tiny H and V
+    (64, 64, 700, dict()),                                         # one-step dW tiles (K = 64 rows)
+    (128, 192, 640, dict(softcap=30.0)),                           # two-step dW, three-step logits
 ]
 
 

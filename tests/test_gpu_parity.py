@@ -107,6 +107,27 @@ def test_irregular_shapes(lce, N, H, V, softcap):
     check(g, *oracle_all(X, W, y, softcap), what=f"N={N} H={H} V={V} c={softcap}")
 
 
+# The pipelined tile loop has separate code for tiles of one, two and three
+# or more 64-deep K-steps (its last two steps load nothing unless a sweep
+# runs on into the next tile), and for a K that is not a multiple of 64.
+# K is H in the forward and the logit-gradient pass, N in the dW contraction
+# and the chunk's vocabulary in the dX contraction (one chunk at these sizes).
+@pytest.mark.parametrize("N,H,V,softcap", [
+    (64, 64, 64, 0.0),          # one step in every contraction
+    (128, 128, 128, 0.0),       # two steps
+    (192, 192, 192, 30.0),      # three steps, fixed-reference softcap
+    (256, 256, 256, 0.0),       # four steps
+    (320, 264, 200, 0.0),       # five steps with a K tail (264 = 4·64 + 8); ragged vocabulary
+    (64, 128, 3000, 1.5),       # sweeps over 12 vocabulary tiles with one-step dW tiles
+    (192, 64, 130, 0.0),        # one-step forward, three-step dW, three-step dX (130 = 2·64 + 2)
+])
+def test_pipeline_step_counts(lce, N, H, V, softcap):
+    X, W, y = synth(N, H, V, seed=3000 + N + H + V, softcap=softcap)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    g = run_gpu(lce, X, W, y, softcap)
+    check(g, *oracle_all(X, W, y, softcap), what=f"steps N={N} H={H} V={V} c={softcap}")
+
+
 def test_bf16_gradients(lce):
     X, W, y = synth(400, 128, 3000, seed=7, softcap=2.0)
     W = (W.float() * 4.0).to(torch.bfloat16)
