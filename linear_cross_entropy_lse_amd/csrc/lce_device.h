@@ -443,11 +443,12 @@ struct Sweep {
 
 // One section of a pipeline step: the 16 MFMAs of fragment set `fm` (one
 // 16-deep K slice), the 8 fragment pieces of K slice t of stage (rA, rB) into
-// `fr`, and 4 loads of one operand's K-half h into `dst` (loads
-// 4h .. 4h+3 of the step state `st`, when `load`).  The reads go with the first 8 MFMAs,
-// so they land well before the next section multiplies them; the loads go
-// with every fourth MFMA.  Each group is fenced so the compiler keeps the
-// interleave.
+// `fr`, and (kLoad) 4 loads of one operand's K-half h into `dst`, loads
+// 4h .. 4h+3 of the step state `st`.  The reads go with the first 8 MFMAs, so
+// they land well before the next section multiplies them; the loads go with
+// every fourth MFMA.  Each group is fenced so the compiler keeps the
+// interleave.  kZeroC: the MFMAs start from zero instead of acc (the first K
+// slice of a tile).
 template <bool kAmn, bool kBmn, bool kLoad, class L, bool kZeroC = false>
 __device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE_LDS uint16_t* rA,
                                              const LCE_LDS uint16_t* rB, int t, const L& ld,
@@ -458,7 +459,6 @@ __device__ __forceinline__ void pipe_section(const Frag& fm, Frag& fr, const LCE
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int mi = i >> 2, ni = i & 3;
-    // kZeroC: the tile's first K slice starts from zero instead of acc.
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm.a[mi], fm.b[ni], kZeroC ? zero : acc[mi][ni],
                                                           0, 0, 0);
     if (i < 8) read_piece<kAmn, kBmn>(fr, rA, rB, wm, wn, lane, t, i);
@@ -506,8 +506,9 @@ __device__ __forceinline__ void pipe_barrier() {
 // (C = A·Bᵀ; its first K slice starts from zero) and `sw` carries the prefetch
 // state; when next_a_row0 >= 0 the steps past the K range are steps 0 and 1
 // of the next A tile (rows next_a_row0 > a_row0, within a_rows; same B), so
-// the next call finds them in flight.  kWaitAll: the caller issues other memory operations
-// between two tiles, so a preloaded tile waits for all of them (vmcnt 0).
+// the next call finds them in flight.  kWaitAll: the caller issues other
+// memory operations between two tiles, so a preloaded tile waits for all of
+// them (vmcnt 0).
 // Without a next tile every load has landed when the tile returns; after a
 // sweep the caller waits for vmcnt 0 before reusing the LDS.
 //
