@@ -209,7 +209,7 @@ def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, 
                                                       BF16_DENSE_PEAK_TFLOPS, 4),
             "workspace_bytes": int(ws_n),
             "mean_loss": float(mean.item()),
-            "note": "lce_forward_backward: row chunks of at most H rows, logits block kept in "
+            "note": "lce_forward_backward: row chunks of at most 2H rows and half the rows, logits block kept in "
                     "bf16, gradient formed in the forward pass; not the headline path"}
 
 

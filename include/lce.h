@@ -336,9 +336,10 @@ lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
  * Forward and backward in one call, row chunk by row chunk (the FLCE
  * pipeline of Liger: blog "最贵的一层：深入浅出 Liger Kernel 与 Cut
  * Cross-Entropy", §二, and the Liger Kernel paper page, §3.2).  The rows are
- * cut into chunks of at most H rows (a multiple of 256); for each chunk the
- * logits against the whole vocabulary are formed once, kept as a bf16 block
- * of Nc x V in the workspace (no larger than W), turned into the logit
+ * cut into chunks of at most 2H rows and at most half the rows (a power-of-two
+ * count of 256-row tiles, at least one); for each chunk the logits against
+ * the whole vocabulary are formed once, kept as a bf16 block of Nc x V in the
+ * workspace (at most twice the size of W), turned into the logit
  * gradient, and projected back at once: dX rows = dZ_chunk · W, dW += dZᵀ ·
  * X_chunk.  Three N·H·V contractions instead of the four of lce_forward +
  * lce_backward, for an Nc x V workspace block.

@@ -195,8 +195,13 @@ struct FusedPlan {
 FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   FusedPlan p{};
   const int64_t Np = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
+  // Chunk: the largest power-of-two count of 256-row tiles that is at most
+  // 2H rows (its bf16 logits block at most twice the size of W) and, from
+  // two tiles of rows on, at most half the rows (the call never holds every
+  // row's logits at once).
+  const int64_t lim = std::min<int64_t>(2 * H, Np >= 2 * kTile ? Np / 2 : Np);
   int64_t tiles = 1;
-  while (tiles * 2 * kTile <= H) tiles *= 2;
+  while (tiles * 2 * kTile <= lim) tiles *= 2;
   p.Nc = std::min<int64_t>(Np, tiles * kTile);
   p.nchunks = (int)ceil_div(std::max<int64_t>(N, 1), p.Nc);
   p.T = (int)(p.Nc / kTile);
