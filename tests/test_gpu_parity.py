@@ -128,6 +128,33 @@ def test_pipeline_step_counts(lce, N, H, V, softcap):
     check(g, *oracle_all(X, W, y, softcap), what=f"steps N={N} H={H} V={V} c={softcap}")
 
 
+# Logits in the hundreds: e^z overflows a float from z ≈ 88.7, so the forward
+# must keep its running maximum, rescale its running sums when the maximum
+# rises in a later vocabulary tile (the ramp puts the largest logits in the
+# last tiles), and merge split partials whose maxima differ by hundreds.
+# V = 20000 gives 79 vocabulary tiles, 2–3 per split, a partial last tile and
+# ~30 backward vocabulary chunks; H = 72 has a K tail.  Softcap 100 takes the
+# general path (max pass on the raw logits), 30 the fixed reference with the
+# tanh saturated.
+@pytest.mark.parametrize("softcap,ramp", [
+    (0.0, False),
+    (0.0, True),
+    (100.0, False),
+    (100.0, True),
+    (30.0, True),
+])
+def test_large_logits(lce, softcap, ramp):
+    N, H, V = 2300, 72, 20000
+    X, W, y = synth(N, H, V, seed=4100 + int(softcap) + int(ramp), softcap=softcap)
+    Wf = W.float() * 200.0      # logit std ≈ 34, extremes ≈ ±200 (±260 with the ramp)
+    if ramp:
+        Wf *= torch.linspace(0.25, 1.5, V).unsqueeze(1)
+    W = Wf.to(torch.bfloat16)
+    g = run_gpu(lce, X, W, y, softcap)
+    check(g, *oracle_all(X, W, y, softcap), what=f"large logits c={softcap} ramp={ramp}")
+    assert bool(torch.isfinite(g["lse"]).all())
+
+
 def test_bf16_gradients(lce):
     X, W, y = synth(400, 128, 3000, seed=7, softcap=2.0)
     W = (W.float() * 4.0).to(torch.bfloat16)
