@@ -460,10 +460,14 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
   // The plain path stores G = p·d and applies one scalar scale afterwards; label
-  // smoothing, Z-loss or a per-row upstream gradient need G scaled row by row.
+  // smoothing, Z-loss or a per-row upstream gradient need the general form.
+  // While every row has the same scale (no per-row upstream gradient, no
+  // Z-loss), that scale stays a scalar applied in fp32 after the contractions
+  // in the general form too, so the bf16 rounding of G never sees it.
   const bool general = opt->label_smoothing > 0.0f || opt->z_loss > 0.0f ||
                        opt->reduction == LCE_REDUCE_NONE;
-  const float* gemm_scale = general ? scalars + 1 : scalars;
+  const bool unit = opt->reduction != LCE_REDUCE_NONE && opt->z_loss == 0.0f;
+  const float* gemm_scale = unit ? scalars : scalars + 1;
 
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
                           opt->logit_scale, state, key, nullptr, deriv, blocks, stream));
@@ -471,7 +475,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
                                 opt->logit_scale, scalars, counts, stream));
   LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
                           scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
-                          general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
+                          unit, general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
   // With an order, the one-hot correction of dW works in positions: the label
   // keys are moved to the positions of the labels before the sort.
   if (sorted)
@@ -868,6 +872,13 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
   const bool fixed = flce_fixed_reference(opt->softcap);
   const float c2 = opt->softcap * kLog2e;
   const int64_t dx_es = dX_dtype == LCE_BF16 ? 2 : 4;
+  // In-place rescale with one scale for every row (no per-row upstream
+  // gradient, no Z-loss): G = 2^(ref − lse)·U carries the row's class only, and
+  // the scale is applied in fp32 to the dX rows and dW tiles.  Folded into G
+  // before its bf16 rounding, it would move a softmax value near 1 off the
+  // exactly representable 1.
+  const bool unit = !fixed && opt->reduction != LCE_REDUCE_NONE && opt->z_loss == 0.0f;
+  const float* post_scale = unit ? scalars : scalars + 1;
 
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, VocabRange{0, V}, opt->ignore_index,
                           opt->softcap, opt->logit_scale, state, key, target, deriv, bprep, stream));
@@ -892,8 +903,8 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
                                 lse_dev + r0, loss_dev + r0, bfin + r0 / kTile, nullptr, stream));
     LCE_LAUNCH("row_coef", stream, launch_row_coef(state + r0, lse_dev + r0, deriv + r0,
                             opt->reduction == LCE_REDUCE_NONE ? dloss_dev + r0 : nullptr, scalars, nr,
-                            opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss, gs + r0, c1 + r0,
-                            oh + r0, stream));
+                            opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss, unit, gs + r0,
+                            c1 + r0, oh + r0, stream));
     // G = diag(r)·U with the fixed reference (dW from the row-scaled X, dX
     // rows scaled afterwards); otherwise U is turned into G in place.
     if (fixed) {
@@ -908,13 +919,13 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.G = U; cp.ldg = pl.ldu; cp.Wc = W; cp.wc_rows = V; cp.X = fixed ? Xs : X + r0 * H;
     cp.N = nr; cp.H = H; cp.chunk_len = V;
     cp.nt_tok = T; cp.nt_h = pl.nt_h; cp.nt_v = pl.n_vtiles;
-    cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = scalars + 1;
+    cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = post_scale;
     cp.dW_dst = dW32;
     cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
     cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
-                               scalars + 1, fixed ? rrow + r0 : nullptr,
+                               post_scale, fixed ? rrow + r0 : nullptr,
                                static_cast<char*>(dX_dev) + r0 * H * dx_es, dX_dtype == LCE_BF16,
                                stream));
   }

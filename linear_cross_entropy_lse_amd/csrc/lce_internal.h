@@ -177,11 +177,13 @@ hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const fl
 // Per-row gradient coefficients: gs_i (row scale, times a), c1_i = 1 + 2l·LSE_i
 // and oh_i = gs_i·(1 − e)·d_i (the one-hot coefficient, d_i the softcap
 // derivative at the target).  Row scale: dloss_rows[i] when dloss_rows is not
-// null, else the scalar scalars[0] / a.
+// null, else the scalar scalars[0] (a included).  unit: the caller applies the
+// scalar scalars[0] after the contractions, so gs_i is written as the row's
+// class alone (1 valid, 0 ignored, NaN bad); oh_i keeps the full scale.
 hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
                            const float* dloss_rows, const float* scalars, int64_t N,
-                           float logit_scale, float one_minus_eps, float z_loss, float* gs,
-                           float* c1, float* oh, hipStream_t stream);
+                           float logit_scale, float one_minus_eps, float z_loss, int unit,
+                           float* gs, float* c1, float* oh, hipStream_t stream);
 
 // Label sort of the valid rows (keys: label << 32 | row, ascending).
 constexpr int kSortBlock = 2048;   // keys sorted per block in LDS

@@ -341,26 +341,26 @@ __global__ void __launch_bounds__(256)
 row_coef_kernel(const int32_t* __restrict__ row_state, const float* __restrict__ lse,
                 const float* __restrict__ target_deriv, const float* __restrict__ dloss_rows,
                 const float* __restrict__ scalars, int64_t N, float logit_scale,
-                float one_minus_eps, float z_loss, float* __restrict__ gs, float* __restrict__ c1,
-                float* __restrict__ oh) {
+                float one_minus_eps, float z_loss, int unit, float* __restrict__ gs,
+                float* __restrict__ c1, float* __restrict__ oh) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
   const int st = row_state[i];
   float g = 0.0f;
   if (st == kRowValid) g = dloss_rows ? dloss_rows[i] * logit_scale : scalars[0];
   else if (st == kRowBad) g = __builtin_nanf("");
-  if (gs) gs[i] = g;
+  if (gs) gs[i] = unit ? (st == kRowValid ? 1.0f : (st == kRowBad ? __builtin_nanf("") : 0.0f)) : g;
   if (c1) c1[i] = fmaf(2.0f * z_loss, lse[i], 1.0f);
   oh[i] = st == kRowValid ? g * one_minus_eps * target_deriv[i] : 0.0f;
 }
 
 hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
                            const float* dloss_rows, const float* scalars, int64_t N,
-                           float logit_scale, float one_minus_eps, float z_loss, float* gs,
-                           float* c1, float* oh, hipStream_t stream) {
+                           float logit_scale, float one_minus_eps, float z_loss, int unit,
+                           float* gs, float* c1, float* oh, hipStream_t stream) {
   hipLaunchKernelGGL(row_coef_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
                      row_state, lse, target_deriv, dloss_rows, scalars, N, logit_scale,
-                     one_minus_eps, z_loss, gs, c1, oh);
+                     one_minus_eps, z_loss, unit, gs, c1, oh);
   return hipGetLastError();
 }
 

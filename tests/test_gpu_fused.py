@@ -85,6 +85,30 @@ def test_fused_against_oracle(lce, N, H, V, opts):
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
 
 
+# Logits in the hundreds, largest in the last vocabulary tiles: the stored
+# block's per-block reference (running maximum) rises across the sweep and
+# every block is rescaled by its own 2^(ref − lse).  Five row chunks.
+@pytest.mark.parametrize("softcap", [0.0, 100.0, 30.0])
+def test_fused_large_logits(lce, softcap):
+    N, H, V = 1100, 72, 20000
+    w = L.Workload("fused", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1,
+                   seed=6500 + int(softcap))
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 200.0 * torch.linspace(0.25, 1.5, V).unsqueeze(1)).to(torch.bfloat16)
+    print(f"[fused] large logits c={softcap}", flush=True)
+    out, dX, dW = lce.lce_forward_backward(X.cuda(), W.cuda(), y.cuda(), 1.0, softcap=softcap)
+    torch.cuda.synchronize()
+    f, rdX, rdW = O.forward_backward_chunked(L.to_f64(X), L.to_f64(W), y.numpy(), 1.0,
+                                             O.options(softcap=softcap), 256)
+    assert int(out["n_valid"]) == f["n_valid"]
+    np.testing.assert_allclose(out["lse"].cpu().numpy(), f["lse"], rtol=0, atol=LSE_ATOL)
+    np.testing.assert_allclose(out["loss"].cpu().numpy(), f["loss"], rtol=0, atol=LSE_ATOL)
+    assert abs(float(out["reduced"]) - f["reduced"]) <= RED_RTOL * abs(f["reduced"])
+    e_dx, e_dw = rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW)
+    print(f"[fused] dX rel {e_dx:.2e} dW rel {e_dw:.2e}", flush=True)
+    assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+
+
 def test_fused_matches_separate_calls(lce):
     """Same inputs through lce_forward_ex + lce_backward_ex: equal within rounding."""
     w = L.Workload("fused", N=1100, H=128, V=4000, labels="zipf", ignore_frac=0.1, seed=61)

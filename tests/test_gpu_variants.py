@@ -79,6 +79,37 @@ def test_variants_against_oracle(lce, N, H, V, opts):
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
 
 
+# Logits in the hundreds, so each row's softmax is dominated by one entry
+# near 1.  With one scale for every row (mean or sum, no Z-loss) the general
+# form keeps that scale out of the bf16 gradient chunk, as the plain form
+# does, so the dominant value rounds to the exactly representable 1.
+@pytest.mark.parametrize("opts", [
+    dict(label_smoothing=0.1),
+    dict(label_smoothing=0.1, logit_scale=0.8, reduction="sum"),
+    dict(softcap=100.0, label_smoothing=0.05),
+])
+def test_variants_large_logits(lce, opts):
+    N, H, V = 1100, 72, 20000
+    w = L.Workload("variant", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1, seed=4500)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 200.0 * torch.linspace(0.25, 1.5, V).unsqueeze(1)).to(torch.bfloat16)
+    print(f"[variants] large logits {opts}", flush=True)
+    Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
+    out = lce.lce_forward_ex(Xd, Wd, yd, **opts)
+    dX, dW = lce.lce_backward_ex(Xd, Wd, yd, out["lse"], 0.61, **opts)
+    torch.cuda.synchronize()
+    o = O.options(**opts)
+    X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+    f = O.forward_ex(X64, W64, y64, o)
+    rdX, rdW = O.backward_ex(X64, W64, y64, 0.61, o)
+    np.testing.assert_allclose(out["lse"].cpu().numpy(), f["lse"], rtol=0, atol=LSE_ATOL)
+    np.testing.assert_allclose(out["loss"].cpu().numpy(), f["loss"], rtol=0, atol=LSE_ATOL)
+    assert abs(float(out["reduced"]) - f["reduced"]) <= RED_RTOL * abs(f["reduced"])
+    e_dx, e_dw = rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW)
+    print(f"[variants] dX rel {e_dx:.2e} dW rel {e_dw:.2e}", flush=True)
+    assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+
+
 def test_defaults_match_plain_entry_points_bitwise(lce):
     w = L.Workload("v", N=400, H=128, V=3000, labels="uniform", ignore_frac=0.1, seed=77)
     X, W, y = (t.cuda() for t in L.make_inputs(w))
