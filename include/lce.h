@@ -107,8 +107,9 @@ lce_status lce_forward(const void* X_dev, const void* W_dev,
  * The logits are recomputed tile by tile from X, W and the LSE.  The dense
  * part of dZ is rounded to bf16 for the two gradient contractions, which
  * accumulate in float32; the one-hot part (−1 at the target, times the
- * softcap derivative there) is applied exactly in float32.  The workspace
- * holds one bf16 vocabulary chunk of dZ (never the whole N×V matrix).
+ * softcap derivative there) is applied exactly in float32, and so is the
+ * scale dloss / n_valid, after the contractions.  The workspace holds one
+ * bf16 vocabulary chunk of dZ (never the whole N×V matrix).
  */
 lce_status lce_backward(const void* X_dev, const void* W_dev,
                         const int64_t* labels_dev, const float* lse_dev,
@@ -188,7 +189,9 @@ lce_status lce_forward_ex(const void* X_dev, const void* W_dev,
  * Backward with options.  Arguments as lce_backward, plus `opt`; dloss_dev
  * holds one float (MEAN, SUM) or N floats (NONE: the upstream gradient of
  * each row's loss; ignored rows' entries are not used).  The workspace size
- * is the one lce_backward_workspace_bytes returns.
+ * is the one lce_backward_workspace_bytes returns.  A scale that every row
+ * shares (MEAN or SUM without Z-loss) is applied in float32 after the
+ * contractions; per-row factors (NONE, Z-loss) are part of the bf16 dZ.
  */
 lce_status lce_backward_ex(const void* X_dev, const void* W_dev,
                            const int64_t* labels_dev, const float* lse_dev,
