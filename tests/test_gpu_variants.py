@@ -110,6 +110,23 @@ def test_variants_large_logits(lce, opts):
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
 
 
+def test_mean_and_sum_differ_by_the_valid_count(lce):
+    # One scale shared by every row is applied after the contractions, so the
+    # sum reduction's gradients are the mean's times n_valid, up to the float
+    # rounding of that scalar (not the bf16 rounding of the gradient chunk).
+    w = L.Workload("variant", N=700, H=72, V=3000, labels="uniform", ignore_frac=0.1, seed=4600)
+    X, W, y = (t.cuda() for t in L.make_inputs(w))
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    for opts in (dict(label_smoothing=0.1), dict(softcap=80.0), dict()):
+        fm = lce.lce_forward_ex(X, W, y, **opts)
+        dXm, dWm = lce.lce_backward_ex(X, W, y, fm["lse"], 1.0, **opts)
+        dXs, dWs = lce.lce_backward_ex(X, W, y, fm["lse"], 1.0, reduction="sum", **opts)
+        torch.cuda.synchronize()
+        n = int(fm["n_valid"])
+        assert rel_l2(dXs.cpu(), dXm.cpu() * n) <= 1e-6, opts
+        assert rel_l2(dWs.cpu(), dWm.cpu() * n) <= 1e-6, opts
+
+
 def test_defaults_match_plain_entry_points_bitwise(lce):
     w = L.Workload("v", N=400, H=128, V=3000, labels="uniform", ignore_frac=0.1, seed=77)
     X, W, y = (t.cuda() for t in L.make_inputs(w))
