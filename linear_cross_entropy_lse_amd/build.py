@@ -37,18 +37,26 @@ def compile_flags(extra=()):
 def build(verbose: bool = False, out: str = LIB_PATH, extra=()) -> str:
     """Compile every HIP source and link liblce.so.  Always rebuilds."""
     cc = hipcc()
-    objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *compile_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                          if "packed-fp32-ops" not in l)
-        if res.returncode != 0:
+        return src, obj, cmd, res.returncode, msgs
+
+    # The sources are independent translation units: compile them side by side.
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    objs = []
+    for src, obj, cmd, rc, msgs in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
         if verbose and msgs.strip():
             print(msgs)
