@@ -354,6 +354,53 @@ def backward_ex(X: np.ndarray, W: np.ndarray, labels: np.ndarray, dloss,
 
 
 
+def logit_gradient_parts(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.ndarray,
+                         scale: np.ndarray, opts: Dict[str, object],
+                         vocab_rows: Optional[np.ndarray] = None):
+    """The gradient of logit_gradient_ex as its two terms, (dense, onehot):
+    the softmax term s_i·a·((1 + 2l·LSE_i)·p_v − e/V)·d and the target term
+    −s_i·a·(1 − e)·[v = y_i]·d ([CCE-blog] §二 and [M011] §06: dZ = p −
+    onehot; the variant terms as in logit_gradient_ex).  Their sum is the
+    gradient.  Rows with a bad label are NaN in both.  A method that applies
+    the target term apart from the rest (exactly, or through another path)
+    can be checked term by term with these."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    a, e, lam = float(opts["logit_scale"]), float(opts["label_smoothing"]), float(opts["z_loss"])
+    c = float(opts["softcap"])
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    Z = a * logits(X, W[cols])
+    Zc = apply_softcap(Z, c)
+    P = np.exp(Zc - lse[:, None])
+    factor = softcap_derivative(Z, c) * a * np.asarray(scale, dtype=np.float64)[:, None]
+    dense = ((1.0 + 2.0 * lam * lse)[:, None] * P - e / V) * factor
+    onehot = -(1.0 - e) * (labels[:, None] == cols[None, :]) * factor
+    bad = bad_mask(labels, V, int(opts["ignore_index"]))
+    dense[bad] = np.nan
+    onehot[bad] = np.nan
+    return dense, onehot
+
+
+def dX_rows_parts(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
+                  lse_rows: np.ndarray, scale_rows: np.ndarray, opts: Dict[str, object]):
+    """(dense, onehot) parts of dX for a subset of rows: each term of the
+    row's logit gradient contracted with W ([M011] §06: dH = dZ·W)."""
+    W = np.asarray(W, dtype=np.float64)
+    dense, onehot = logit_gradient_parts(X_rows, W, labels_rows, lse_rows, scale_rows, opts)
+    return dense @ W, onehot @ W
+
+
+def dW_vocab_rows_parts(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.ndarray,
+                        scale: np.ndarray, vocab_rows: np.ndarray, opts: Dict[str, object]):
+    """(dense, onehot) parts of dW[v] for selected vocabulary rows, summed
+    over every token row ([M011] §06: dW = dZᵀ·H); needs every row's LSE."""
+    X = np.asarray(X, dtype=np.float64)
+    dense, onehot = logit_gradient_parts(X, W, labels, lse, scale, opts, vocab_rows=vocab_rows)
+    return dense.T @ X, onehot.T @ X
+
+
 # --------------------------------------------------------------------------- #
 # Vocabulary shards (reading R17)
 # --------------------------------------------------------------------------- #
