@@ -58,7 +58,9 @@ typedef enum {
   LCE_ERR_SHAPE = 2,       /* N, H or V outside the limits above (H % 8 != 0 included) */
   LCE_ERR_ALIGNMENT = 3,   /* a pointer breaks the alignment rules above */
   LCE_ERR_WORKSPACE = 4,   /* workspace_bytes is below the size the query returns */
-  LCE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+  LCE_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+  LCE_ERR_SCRATCH_LIMIT = 6 /* lce_forward_noalloc: the shape needs more than the
+                               library's fixed scratch (lce_forward_noalloc_max_bytes) */
 } lce_status;
 
 typedef enum {
@@ -368,6 +370,32 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev,
                                 void* dX_dev, lce_dtype dX_dtype, void* dW_dev,
                                 lce_dtype dW_dtype, void* workspace_dev,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Forward without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it).  Same arguments, kernels and results as lce_forward, bit for
+ * bit, minus the workspace: the call runs in a scratch array the library
+ * holds in device memory, one per device (lce_forward_noalloc_max_bytes()
+ * bytes, 16 MiB, held until the process ends).  The array's device address
+ * is looked up on the first call on each device.  A shape whose forward
+ * workspace (lce_forward_workspace_bytes) exceeds that size returns
+ * LCE_ERR_SCRATCH_LIMIT before anything is launched; with the forward's
+ * plan that is N above roughly 800 000 rows.  The call itself allocates
+ * nothing: no hipMalloc, no host or library allocation on the device.
+ * Every call on one device shares that device's array, and each call
+ * overwrites it before reading it, so nothing carries over between calls;
+ * but calls that overlap in time on one device (concurrent streams, several
+ * host threads) race on it and give undefined results.  Serialise them.
+ */
+size_t lce_forward_noalloc_max_bytes(void);
+
+lce_status lce_forward_noalloc(const void* X_dev, const void* W_dev,
+                               const int64_t* labels_dev, int64_t N, int64_t H,
+                               int64_t V, int64_t ignore_index, float softcap,
+                               float* loss_dev, float* lse_dev, float* mean_dev,
+                               int32_t* n_valid_dev, int32_t* bad_label_dev,
+                               void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);

@@ -21,6 +21,7 @@ LCE_ERR_SHAPE = 2
 LCE_ERR_ALIGNMENT = 3
 LCE_ERR_WORKSPACE = 4
 LCE_ERR_HIP = 5
+LCE_ERR_SCRATCH_LIMIT = 6
 LCE_F32 = 0
 LCE_BF16 = 1
 LCE_REDUCE_MEAN = 0
@@ -34,8 +35,9 @@ EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_
             "lce_shard_forward", "lce_shard_merge_workspace_bytes", "lce_shard_merge",
             "lce_shard_backward", "lce_fused_workspace_bytes", "lce_forward_backward",
             "lce_vocab_order_workspace_bytes", "lce_vocab_order",
-            "lce_backward_sorted_workspace_bytes", "lce_backward_sorted", "lce_status_string", "lce_version", "lce_timing_enable",
-            "lce_timing_reset", "lce_timing_read")
+            "lce_backward_sorted_workspace_bytes", "lce_backward_sorted",
+            "lce_forward_noalloc_max_bytes", "lce_forward_noalloc", "lce_status_string",
+            "lce_version", "lce_timing_enable", "lce_timing_reset", "lce_timing_read")
 
 
 class Options(ctypes.Structure):
@@ -124,6 +126,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_backward_sorted.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, opt_p, vp, vp,
                                         ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]
     lib.lce_backward_sorted.restype = ctypes.c_int
+    lib.lce_forward_noalloc_max_bytes.argtypes = []
+    lib.lce_forward_noalloc_max_bytes.restype = sz
+    lib.lce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                        vp, vp, vp, vp, vp, vp]
+    lib.lce_forward_noalloc.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []

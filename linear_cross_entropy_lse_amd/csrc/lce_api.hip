@@ -332,6 +332,36 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
 
 #define LCE_LAUNCH(name, stream, call) LCE_TRY(timed(name, stream, [&]() { return call; }))
 
+// ---------------------------------------------------------------------------
+// Library-held scratch of lce_forward_noalloc: one fixed array per device,
+// shared by every call on that device.  Host code never passes the array's
+// name to a kernel (in host code it is only a stand-in for the symbol); it
+// passes the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_for_current_device(void** ptr) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *ptr = ptrs[dev];
+  return hipSuccess;
+}
+
 bool range_ok(int64_t V, int64_t v_lo, int64_t V_total) {
   return v_lo >= 0 && V_total < INT_MAX && v_lo <= V_total - V;
 }
@@ -598,8 +628,40 @@ const char* lce_status_string(lce_status status) {
     case LCE_ERR_ALIGNMENT: return "misaligned pointer (X/W/dX/dW 16 B, labels 8 B, workspace 256 B)";
     case LCE_ERR_WORKSPACE: return "workspace smaller than the size query returns";
     case LCE_ERR_HIP: return "HIP runtime error";
+    case LCE_ERR_SCRATCH_LIMIT:
+      return "shape needs more scratch than lce_forward_noalloc holds (lce_forward_noalloc_max_bytes)";
   }
   return "unknown status";
+}
+
+size_t lce_forward_noalloc_max_bytes(void) { return kScratchBytes; }
+
+lce_status lce_forward_noalloc(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
+                               int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                               float softcap, float* loss_dev, float* lse_dev, float* mean_dev,
+                               int32_t* n_valid_dev, int32_t* bad_label_dev, void* stream_ptr) {
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  if (!mean_dev || !n_valid_dev) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!X_dev || !W_dev || !labels_dev || !loss_dev || !lse_dev))
+    return LCE_ERR_INVALID_ARG;
+  if (!aligned(X_dev, 16) || !aligned(W_dev, 16) || !aligned(labels_dev, 8) ||
+      !aligned(loss_dev, 4) || !aligned(lse_dev, 4) || !aligned(mean_dev, 4) ||
+      !aligned(n_valid_dev, 4) || !aligned(bad_label_dev, 4))
+    return LCE_ERR_ALIGNMENT;
+  // The size check comes before any HIP call, so an oversized shape is
+  // refused without touching a device.
+  if (N > 0 && plan_forward(N, H, V).total > kScratchBytes) return LCE_ERR_SCRATCH_LIMIT;
+  lce_options opt;
+  lce_options_default(&opt);
+  opt.ignore_index = ignore_index;
+  opt.softcap = softcap;
+  FwdOut out{};
+  out.loss = loss_dev; out.lse = lse_dev; out.reduced = mean_dev;
+  out.n_valid = n_valid_dev; out.bad_label = bad_label_dev;
+  void* ws = nullptr;
+  if (N > 0 && scratch_for_current_device(&ws) != hipSuccess) return LCE_ERR_HIP;
+  return forward_impl(X_dev, W_dev, labels_dev, N, H, V, VocabRange{0, V}, &opt, out, ws,
+                      kScratchBytes, stream_ptr);
 }
 
 size_t lce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V) {

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.lce_version() >= 100
-    for st in range(6):
+    for st in range(7):
         assert len(lib.lce_status_string(st)) > 0
 
 
@@ -290,3 +290,25 @@ def test_sorted_backward_workspace_and_argument_checks(lib):
     # The plain backward's workspace is too small for the sorted one.
     assert sorted_bwd(lib, ok, wsb=lib.lce_backward_workspace_bytes(4, 8, 5, 0)) == \
         _lib.LCE_ERR_WORKSPACE
+
+
+def test_forward_noalloc_host_checks(lib):
+    """The no-allocation forward refuses bad arguments, and a shape whose
+    workspace exceeds its fixed scratch, before any HIP call."""
+    cap = lib.lce_forward_noalloc_max_bytes()
+    assert cap == 16 << 20
+
+    def na(X=FAKE, W=FAKE, y=FAKE, N=4, H=8, V=5, loss=FAKE, lse=FAKE, mean=FAKE, nv=FAKE):
+        return lib.lce_forward_noalloc(X, W, y, N, H, V, -100, 0.0, loss, lse, mean, nv, None,
+                                       None)
+
+    assert na(H=12) == _lib.LCE_ERR_SHAPE
+    assert na(X=0) == _lib.LCE_ERR_INVALID_ARG
+    assert na(mean=0) == _lib.LCE_ERR_INVALID_ARG
+    assert na(X=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
+    big = 1 << 22
+    assert lib.lce_forward_workspace_bytes(big, 8, 5) > cap
+    assert na(N=big) == _lib.LCE_ERR_SCRATCH_LIMIT
+    # The largest shapes of the benchmark workloads fit.
+    for (N, H, V) in [(8192, 2304, 256128), (32768, 3584, 152064), (16384, 4096, 32000)]:
+        assert lib.lce_forward_workspace_bytes(N, H, V) <= cap
