@@ -504,9 +504,9 @@ __device__ __forceinline__ void pipe_barrier() {
 //
 // kSweep (K-major operands only, k_begin = 0): the tile overwrites acc
 // (C = A·Bᵀ; its first K slice starts from zero) and `sw` carries the prefetch
-// state; when next_a_row0 >= 0 the steps past the K range are steps 0 and 1
-// of the next A tile (rows next_a_row0 > a_row0, within a_rows; same B), so
-// the next call finds them in flight.  kWaitAll: the caller issues other
+// state; when next_a_row0 >= 0 and the tile has at least two steps, the steps
+// past the K range are steps 0 and 1 of the next A tile (rows next_a_row0 >
+// a_row0, within a_rows; same B), so the next call finds them in flight.  kWaitAll: the caller issues other
 // memory operations between two tiles, so a preloaded tile waits for all of
 // them (vmcnt 0).
 // Without a next tile every load has landed when the tile returns; after a
@@ -534,7 +534,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, int64_
   const int wm = wave >> 1, wn = wave & 1;
   const int nsteps = (int)((k_end - k_begin + kBK - 1) / kBK);
   const int par = kSweep ? sw->par : 0;
-  const bool prefetch = kSweep && next_a_row0 >= 0;
+  // The stream runs on into the next tile only when a tile has at least two
+  // steps: a step loads step k+2 two sections ahead, so with one step per tile
+  // (K <= 64) that would skip the next tile's step 0 and load its (absent)
+  // step 1 instead.  A one-step tile starts the next one with its own prologue.
+  const bool prefetch = kSweep && next_a_row0 >= 0 && nsteps >= 2;
   LA la;
   LB lb;
   la.init(A, lda, a_row0, a_rows, k_total, tid);

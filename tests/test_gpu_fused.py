@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import lce_inputs as L
+from tests import fullsize_samples as FS
 from oracle import lce_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +57,8 @@ CASES = [
     (257, 8, 40, dict(z_loss=1e-2)),                               # tiny H and V
     (64, 64, 700, dict()),                                         # one-step dW tiles (K = 64 rows)
     (128, 192, 640, dict(softcap=30.0)),                           # two-step dW, three-step logits
+    (300, 64, 150000, dict()),                                     # one-step logit tiles, 2-3 per split
+    (200, 32, 90000, dict(softcap=30.0)),                          # the same with the fixed reference
 ]
 
 
@@ -180,3 +183,5 @@ def test_fused_fullsize(lce, name):
     assert e_lse <= LSE_ATOL and e_loss <= LSE_ATOL
     assert abs(mean - gmean) <= RED_RTOL * abs(gmean)
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+    S = FS.samples(name, X, W, y, dict(softcap=w.softcap))
+    FS.check(f"fused {name}", dX, dW, S, GRAD_RTOL, 1e-2, log=lambda m: print(m, flush=True))

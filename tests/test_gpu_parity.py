@@ -120,6 +120,12 @@ def test_irregular_shapes(lce, N, H, V, softcap):
     (320, 264, 200, 0.0),       # five steps with a K tail (264 = 4·64 + 8); ragged vocabulary
     (64, 128, 3000, 1.5),       # sweeps over 12 vocabulary tiles with one-step dW tiles
     (192, 64, 130, 0.0),        # one-step forward, three-step dW, three-step dX (130 = 2·64 + 2)
+    # One-step tiles (H <= 64) in sweeps of several vocabulary tiles per split
+    # (one token tile: 256 splits, V / 65536 tiles and more per split): each
+    # tile of such a sweep loads its own first step.
+    (100, 64, 150000, 0.0),
+    (300, 32, 90000, 30.0),
+    (64, 8, 70000, 1.5),
 ])
 def test_pipeline_step_counts(lce, N, H, V, softcap):
     X, W, y = synth(N, H, V, seed=3000 + N + H + V, softcap=softcap)
