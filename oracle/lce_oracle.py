@@ -389,7 +389,10 @@ def dX_rows_parts(X_rows: np.ndarray, W: np.ndarray, labels_rows: np.ndarray,
     row's logit gradient contracted with W ([M011] §06: dH = dZ·W)."""
     W = np.asarray(W, dtype=np.float64)
     dense, onehot = logit_gradient_parts(X_rows, W, labels_rows, lse_rows, scale_rows, opts)
-    return dense @ W, onehot @ W
+    # The target term has at most one non-zero per row (all NaN for a bad
+    # row): only the columns holding one enter its product.
+    cols = np.nonzero((onehot != 0).any(axis=0))[0]
+    return dense @ W, onehot[:, cols] @ W[cols]
 
 
 def dW_vocab_rows_parts(X: np.ndarray, W: np.ndarray, labels: np.ndarray, lse: np.ndarray,

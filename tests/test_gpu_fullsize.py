@@ -9,6 +9,12 @@ them (which calls only the oracle and the seeded input generator):
   * dX on sampled token rows, dW on sampled
     vocabulary rows (incl. the most frequent
     labels and the last vocabulary row)           rel L2 ≤ 1e-3 per sample set
+and, from the oracle at test time (tests/fullsize_samples.py), 1024+ dX rows
+and dW rows from every vocabulary chunk, its boundaries, tile boundaries and
+offsets past 2^31 bytes, checked twice: whole (rel L2 ≤ 1e-3) and as their
+dense part alone, the output minus the oracle's exact one-hot term against the
+oracle's softmax term (rel L2 ≤ 1e-2, the bar of a value that passes through
+bf16 by design), the label-free dW rows as their own set.
 Properties that hold at any size are checked on the whole output: ignored rows
 have loss 0 and dX 0, every LSE is finite, no bad label is flagged, and the
 peak device memory stays far below one N x V logit matrix.
@@ -20,6 +26,7 @@ import pytest
 import torch
 
 import lce_inputs as L
+from tests import fullsize_samples as FS
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +34,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LSE_ATOL = 2e-3
 MEAN_RTOL = 1e-4
 GRAD_RTOL_F32 = 1e-3
+DENSE_RTOL = 1e-2
 FULL = ["liger", "llama3_8b", "gemma2_2b", "qwen25_long"]
 
 
@@ -89,6 +97,9 @@ def test_fullsize_against_oracle(lce, name):
     assert abs(mean - gmean) <= MEAN_RTOL * abs(gmean)
     assert e_dx <= GRAD_RTOL_F32 and e_dw <= GRAD_RTOL_F32
     assert dx_ign_zero
+    S = FS.samples(name, X, W, y, dict(softcap=w.softcap))
+    FS.check(f"fullsize {name}", dX, dW, S, GRAD_RTOL_F32, DENSE_RTOL,
+             log=lambda m: print(m, flush=True))
     # Outputs (dX, dW in float32, five per-row vectors) plus the library's
     # workspace, and nothing the size of the logits.
     ws = lce.lce_backward_workspace_bytes(w.N, w.H, w.V)

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import lce_inputs as L
+from tests import fullsize_samples as FS
 from oracle import lce_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -177,3 +178,5 @@ def test_gemma_eight_shards_fullsize(lce):
     assert e_lse <= LSE_ATOL and e_loss <= LSE_ATOL
     assert abs(mean - gmean) <= RED_RTOL * abs(gmean)
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+    S = FS.samples("gemma2_2b", X, W, y, dict(softcap=w.softcap))
+    FS.check("shards gemma2_2b", dX, dW, S, GRAD_RTOL, 1e-2, log=lambda m: print(m, flush=True))

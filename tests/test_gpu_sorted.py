@@ -25,6 +25,7 @@ import pytest
 import torch
 
 import lce_inputs as L
+from tests import fullsize_samples as FS
 from oracle import lce_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -257,3 +258,5 @@ def test_fullsize_gemma_order_and_sorted_backward(lce):
     e_dw = rel_l2(dW[dw_rows].cpu(), gold["dW"])
     print(f"[sorted] {name}: dX rel {e_dx:.2e} dW rel {e_dw:.2e}", flush=True)
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+    S = FS.samples(name, X, W, y, dict(softcap=w.softcap))
+    FS.check(f"sorted {name}", dX, dW, S, GRAD_RTOL, 1e-2, log=lambda m: print(m, flush=True))

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import lce_inputs as L
+from tests import fullsize_samples as FS
 from oracle import lce_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -198,3 +199,5 @@ def test_gemma_fullsize_variant_sampled(lce):
     e_dw = rel_l2(dW[torch.from_numpy(vrows).to(dev)].cpu(), gw.T @ X64)
     print(f"[variants] gemma full size: dX rel {e_dx:.2e} dW rel {e_dw:.2e}", flush=True)
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+    S = FS.samples("gemma2_2b", X, W, y, opts, dloss.astype(np.float64))
+    FS.check("variants gemma2_2b", dX, dW, S, GRAD_RTOL, 1e-2, log=lambda m: print(m, flush=True))

@@ -413,3 +413,66 @@ def test_order_pins_catch_mutation(name, monkeypatch):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# --------------------------------------------------------------------------- #
+# Gradient split into its softmax and target terms: planted mistakes must be
+# caught by its pins.
+# --------------------------------------------------------------------------- #
+from tests import test_oracle_parts as PP  # noqa: E402
+
+PARTS_PINS = [lambda kw=kw: PP.test_parts_match_autograd_of_their_terms(kw) for kw in PP.CASES]
+PARTS_PINS.append(PP.test_parts_of_a_subset_of_rows_and_bad_labels)
+
+_orig_parts = O.logit_gradient_parts
+
+
+def _parts_smoothing_in_onehot(X, W, labels, lse, scale, opts, vocab_rows=None):
+    # The uniform −e/V term moved from the dense part into the one-hot part.
+    dense, onehot = _orig_parts(X, W, labels, lse, scale, opts, vocab_rows)
+    e = float(opts["label_smoothing"])
+    a = float(opts["logit_scale"])
+    V = np.asarray(W).shape[0]
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    Z = a * O.logits(np.asarray(X, float), np.asarray(W, float)[cols])
+    shift = (e / V) * O.softcap_derivative(Z, float(opts["softcap"])) * a * \
+        np.asarray(scale, float)[:, None]
+    return dense + shift, onehot - shift
+
+
+def _parts_onehot_without_derivative(X, W, labels, lse, scale, opts, vocab_rows=None):
+    # The target term without the softcap derivative at the target.
+    dense, _ = _orig_parts(X, W, labels, lse, scale, opts, vocab_rows)
+    e, a = float(opts["label_smoothing"]), float(opts["logit_scale"])
+    V = np.asarray(W).shape[0]
+    cols = np.arange(V) if vocab_rows is None else np.asarray(vocab_rows)
+    onehot = -(1.0 - e) * (np.asarray(labels)[:, None] == cols[None, :]) * a * \
+        np.asarray(scale, float)[:, None]
+    return dense, onehot
+
+
+def _parts_zloss_factor_dropped(X, W, labels, lse, scale, opts, vocab_rows=None):
+    # The dense term without the Z-loss factor 1 + 2l·LSE.
+    o = dict(opts)
+    o["z_loss"] = 0.0
+    return _orig_parts(X, W, labels, lse, scale, o, vocab_rows)
+
+
+PARTS_MUTATIONS = {
+    "smoothing_in_onehot": ("logit_gradient_parts", _parts_smoothing_in_onehot),
+    "onehot_without_derivative": ("logit_gradient_parts", _parts_onehot_without_derivative),
+    "zloss_factor_dropped": ("logit_gradient_parts", _parts_zloss_factor_dropped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PARTS_MUTATIONS))
+def test_parts_pins_catch_mutation(name, monkeypatch):
+    attr, fn = PARTS_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in PARTS_PINS:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
