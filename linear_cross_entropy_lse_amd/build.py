@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblce.so")
-SOURCES = ["lce_api.hip", "lce_gemm.hip", "lce_rows.hip", "lce_order.hip"]
+SOURCES = ["lce_api.hip", "lce_gemm.hip", "lce_rows.hip", "lce_order.hip", "lce_exact.hip"]
 ARCH = "gfx950"
 
 

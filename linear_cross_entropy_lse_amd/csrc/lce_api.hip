@@ -102,7 +102,8 @@ struct BwdPlan {
   int64_t Vc, ldg;
   size_t off_state, off_key, off_deriv, off_gs, off_c1, off_oh, off_keys_a, off_keys_b, off_head,
       off_tail, off_blocks, off_scalars, off_flags, off_G, off_dXp, off_dWs, off_Wp, off_pos1,
-      off_pkey, total;
+      off_pkey, off_labd, off_labo, off_domcol, off_domc, off_dombase, off_de, off_dkey,
+      off_dkeys_a, off_dkeys_b, off_dcounts, total;
 };
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
@@ -141,6 +142,17 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   p.off_tail = o;    o = align_up(o + sizeof(float) * (size_t)seg_chunks(N) * (size_t)H);
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_prep);
   p.off_scalars = o; o = align_up(o + 16);
+  // Exact entries of the logit-gradient pass and the sort of the dominant ones.
+  p.off_labd = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_labo = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_domcol = o;  o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_domc = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_dombase = o; o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_de = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_dkey = o;    o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_dkeys_a = o; o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_dkeys_b = o; o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_dcounts = o; o = align_up(o + 16);
   p.off_flags = o;   o = align_up(o + sizeof(uint32_t) * (size_t)p.T * (size_t)p.n_vtiles_chunk);
   // Blocked gradient chunk: T token tiles (padded) x Vc columns.
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.T * kTile * (size_t)p.ldg);
@@ -498,6 +510,30 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
                        opt->reduction == LCE_REDUCE_NONE;
   const bool unit = opt->reduction != LCE_REDUCE_NONE && opt->z_loss == 0.0f;
   const float* gemm_scale = unit ? scalars : scalars + 1;
+  // The label's entry and a dominant entry of each row skip the bf16 chunk
+  // and are applied in fp32 (launch_exact_entries): oh comes from their
+  // values, and the dominant entries get a sorted dW correction of their own,
+  // like the one-hot term's.
+  float* lab_dense = at<float>(workspace_dev, pl.off_labd);
+  float* lab_oh = at<float>(workspace_dev, pl.off_labo);
+  int32_t* dom_col = at<int32_t>(workspace_dev, pl.off_domcol);
+  float* dom_coef = at<float>(workspace_dev, pl.off_domc);
+  int32_t* dom_base = at<int32_t>(workspace_dev, pl.off_dombase);
+  float* de = at<float>(workspace_dev, pl.off_de);
+  int32_t* dkey = at<int32_t>(workspace_dev, pl.off_dkey);
+  uint64_t* dkeys_a = at<uint64_t>(workspace_dev, pl.off_dkeys_a);
+  uint64_t* dkeys_b = at<uint64_t>(workspace_dev, pl.off_dkeys_b);
+  const uint64_t* dkeys = sort_passes(N) % 2 == 0 ? dkeys_a : dkeys_b;
+  int32_t* dcounts = at<int32_t>(workspace_dev, pl.off_dcounts);
+  const int32_t* lab_key = sorted ? pkey : key;
+  // oh, de and the sorted dominant keys from the exact entries written so far.
+  auto exact_terms = [&]() -> lce_status {
+    LCE_LAUNCH("exact_coef", stream, launch_exact_coef(state, lab_key, lab_dense, lab_oh, dom_col, dom_coef,
+                                                      unit ? scalars : nullptr, N, oh, de, dkey, stream));
+    LCE_LAUNCH("sort_dominant", stream, launch_sort_by_label(dkey, N, dkeys_a, dkeys_b, stream));
+    LCE_LAUNCH("count_dominant", stream, launch_count_keys(dkeys, N, dcounts, stream));
+    return LCE_OK;
+  };
 
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
                           opt->logit_scale, state, key, nullptr, deriv, blocks, stream));
@@ -505,7 +541,8 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
                                 opt->logit_scale, scalars, counts, stream));
   LCE_LAUNCH("row_coef", stream, launch_row_coef(state, lse_dev, deriv, opt->reduction == LCE_REDUCE_NONE ? dloss_dev : nullptr,
                           scalars, N, opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss,
-                          unit, general ? gs : nullptr, general ? c1 : nullptr, oh, stream));
+                          unit, general ? gs : nullptr, general ? c1 : nullptr, oh, lab_dense,
+                          lab_oh, dom_col, dom_base, stream));
   // With an order, the one-hot correction of dW works in positions: the label
   // keys are moved to the positions of the labels before the sort.
   if (sorted)
@@ -532,7 +569,23 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.gs = general ? gs : nullptr; gp.c1 = c1;
     gp.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);
     gp.flags = reinterpret_cast<uint8_t*>(flags); gp.filter_eps = opt->filter_eps;
+    gp.dom_base = dom_base; gp.key_offset = sorted ? v_begin : 0;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
+    ExactParams ep{};
+    ep.X = X; ep.W = Wsrc; ep.N = N; ep.H = H; ep.V = w_rows;
+    ep.v_begin = w_begin; ep.chunk_len = chunk_len; ep.key_offset = gp.key_offset;
+    ep.n_vtiles = n_vt; ep.softcap = opt->softcap; ep.logit_scale = opt->logit_scale;
+    ep.lse = lse_dev; ep.row_state = state; ep.row_key = lab_key;
+    ep.gs = general ? gs : nullptr; ep.c1 = c1;
+    ep.eps_over_v = gp.eps_over_v; ep.one_minus_eps = 1.0f - opt->label_smoothing;
+    ep.dom_base = dom_base; ep.G = G;
+    ep.lab_dense = lab_dense; ep.lab_oh = lab_oh; ep.dom_col = dom_col; ep.dom_coef = dom_coef;
+    LCE_LAUNCH("exact_entries", stream, launch_exact_entries(ep, stream));
+    // With the filter, exact dense values whose block is skipped are dropped.
+    if (flags)
+      LCE_LAUNCH("filter_exact", stream, launch_filter_exact(flags, n_vt, w_begin, state, lab_key,
+                                                            gp.key_offset, N, lab_dense, dom_col,
+                                                            dom_coef, stream));
 
     ChunkGemmParams cp{};
     cp.G = G; cp.ldg = pl.ldg; cp.Wc = Wsrc + w_begin * H; cp.wc_rows = w_rows - w_begin; cp.X = X;
@@ -542,23 +595,33 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
     cp.dW_dst = dW_dtype == LCE_F32 && !sorted ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
-    if (sorted) {
+    if (sorted || dW_dtype == LCE_BF16) {
+      // This chunk's dW rows are final once corrected: the exact entries of
+      // its labels and dominant entries are all known now.
+      const lce_status st = exact_terms();
+      if (st != LCE_OK) return st;
       LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
                                 v_begin + chunk_len, part_head, part_tail, stream));
-      LCE_LAUNCH("scatter_rows", stream, launch_scatter_rows(dWs, V, H, order, v_begin, chunk_len, dW_dev,
-                                  dW_dtype == LCE_BF16, stream));
-    } else if (dW_dtype == LCE_BF16) {
-      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dWs, v_begin,
+      LCE_LAUNCH("dw_correct", stream, launch_dw_correct(dkeys, dcounts, de, X, N, H, dWs, v_begin,
                                 v_begin + chunk_len, part_head, part_tail, stream));
-      LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
-                               chunk_len * H, stream));
+      if (sorted)
+        LCE_LAUNCH("scatter_rows", stream, launch_scatter_rows(dWs, V, H, order, v_begin, chunk_len, dW_dev,
+                                    dW_dtype == LCE_BF16, stream));
+      else
+        LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dWs, static_cast<uint16_t*>(dW_dev) + v_begin * H,
+                                 chunk_len * H, stream));
     }
   }
-  if (dW_dtype == LCE_F32 && !sorted)
+  if (dW_dtype == LCE_F32 && !sorted) {
+    const lce_status st = exact_terms();
+    if (st != LCE_OK) return st;
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, state, key, oh, W, gemm_scale, nullptr, dX_dev,
-                             dX_dtype == LCE_BF16, stream));
+    LCE_LAUNCH("dw_correct", stream, launch_dw_correct(dkeys, dcounts, de, X, N, H,
+                              static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
+  }
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, state, key, oh, W, gemm_scale, nullptr,
+                             dom_col, de, order, dX_dev, dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }
 
@@ -966,7 +1029,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     LCE_LAUNCH("row_coef", stream, launch_row_coef(state + r0, lse_dev + r0, deriv + r0,
                             opt->reduction == LCE_REDUCE_NONE ? dloss_dev + r0 : nullptr, scalars, nr,
                             opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss, unit, gs + r0,
-                            c1 + r0, oh + r0, stream));
+                            c1 + r0, oh + r0, nullptr, nullptr, nullptr, nullptr, stream));
     // G = diag(r)·U with the fixed reference (dW from the row-scaled X, dX
     // rows scaled afterwards); otherwise U is turned into G in place.
     if (fixed) {
@@ -987,7 +1050,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
-                               post_scale, fixed ? rrow + r0 : nullptr,
+                               post_scale, fixed ? rrow + r0 : nullptr, nullptr, nullptr, nullptr,
                                static_cast<char*>(dX_dev) + r0 * H * dx_es, dX_dtype == LCE_BF16,
                                stream));
   }

@@ -685,6 +685,55 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Value of one logit-gradient entry from its logit z (the same arithmetic in
+// every kernel that forms it).  Plain form (kGen false): G = p·d, `off`
+// folding the row class in (−inf for ignored rows, so G = 0; NaN for rows with
+// a bad label).  General form: G = gsc·(c1·p − eps_v)·d with the row's scale
+// gsc (0 ignored, NaN bad) and Z-loss factor c1.  p is the softmax value and d
+// the softcap derivative (1 without).  Without softcap off = −lse2; with
+// softcap c, r = 1/(2^(z·k2) + 1) gives tanh = 1 − 2r, off = c2 − lse2 + 2,
+// pr4 = 2^(off − 2·c2·r) = 4p, and d = 4r(1 − r).  (k2 = 2a·log2 e / c,
+// c2 = c·log2 e, l2a = a·log2 e, lse2 = LSE·log2 e.)
+template <bool kCapped, bool kGen>
+__device__ __forceinline__ float grad_value(float z, float off, float gsc, float c1, float eps_v,
+                                            float k2, float c2, float l2a, float& pr, float& d) {
+  if (kCapped) {
+    const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
+    const float pr4 = exp2_fast(fmaf(-2.0f * c2, rr, off));
+    const float dq = fmaf(-rr, rr, rr);
+    pr = 0.25f * pr4;
+    d = 4.0f * dq;
+    return kGen ? gsc * fmaf(c1, pr4, -4.0f * eps_v) * dq : pr4 * dq;
+  } else {
+    pr = exp2_fast(fmaf(z, l2a, off));
+    d = 1.0f;
+    return kGen ? gsc * fmaf(c1, pr, -eps_v) : pr;
+  }
+}
+
+// Softmax threshold of a dominant entry: 1/2 + 2^-10, so that two entries of
+// one row can never both lie above it.
+constexpr float kDominantP = 0.5009765625f;
+
+// The raw logit above which an entry's softmax exceeds kDominantP, for a row
+// with exponent offset `off` as in grad_value (+inf when `live` is false:
+// rows without a gradient have no dominant entry).
+template <bool kCapped>
+__device__ __forceinline__ float dominance_threshold(bool live, float off, float k2, float c2,
+                                                     float l2a) {
+  float zthr = __builtin_inff();
+  if (!live) return zthr;
+  const float log2tau = __builtin_log2f(kDominantP);
+  if (kCapped) {
+    // p > τ  <=>  off − 2·c2·r > 2 + log2 τ  <=>  r < R  <=>  z > log2(1/R − 1)/k2.
+    const float R = (off - 2.0f - log2tau) / (2.0f * c2);
+    if (R > 0.0f && R < 1.0f) zthr = log2f(1.0f / R - 1.0f) / k2;
+  } else {
+    zthr = (log2tau - off) / l2a;
+  }
+  return zthr;
+}
+
 // Row classes written by the row-preparation kernels.
 enum RowState : int32_t { kRowIgnored = 0, kRowValid = 1, kRowBad = 2 };
 

@@ -47,6 +47,13 @@ struct GradParams {
   // over rows with a target, that is not below filter_eps, else 0.
   uint8_t* flags;
   float filter_eps;
+  // Dominant entries: for the token of a row with an entry whose softmax
+  // exceeds 1/2 + 2^-10 (at most one per row), the W row of the first of the
+  // 64 rows of the tile that the finding lane holds, plus key_offset (rows
+  // lrow + x, x < 128 with bit 2 clear); untouched otherwise (the host presets
+  // −1).  launch_exact_entries turns it into the entry.
+  int32_t* dom_base;
+  int64_t key_offset;
 };
 
 // dX and dW contractions of one vocabulary chunk, in one persistent launch of
@@ -108,6 +115,45 @@ hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream);
 // True when the fused forward's logits use the fixed reference c·log2(e).
 bool flce_fixed_reference(float softcap);
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream);
+
+// Exact entries of one vocabulary chunk (lce_exact.hip).  Two entries per row
+// do not go through the bf16 gradient chunk: the entry at the row's label,
+// whose p·d nearly cancels the one-hot term when the row predicts its label
+// confidently, and an entry with softmax above 1/2 + 2^-10 (found by the
+// logit-gradient pass, dom_base), which alone carries a large share of the
+// row's gradient.  For each, the logit is recomputed with the MFMA sequence
+// of the tile kernels (so it is the value the forward's LSE and the logit
+// gradient saw, bit for bit), its value is written in fp32, and its place in
+// the chunk G is overwritten with the value of a logit of −inf (0, or −gs·e/V
+// without softcap).  Values in G's units:
+//   lab_dense[i]  the label entry minus the −inf value, lab_oh[i] the one-hot
+//                 term (1 − e)·d·(gs or 1), for rows whose label (row_key −
+//                 key_offset, this call's W rows) lies in the chunk
+//   dom_col[i]    the other entry's W row plus key_offset, dom_coef[i] the
+//                 entry minus the −inf value, for rows whose dom_base lies in
+//                 the chunk (dom_col is preset −1 by the host)
+struct ExactParams {
+  const uint16_t* X;
+  const uint16_t* W;          // this call's W rows (the gathered chunk with an order)
+  int64_t N, H, V;            // V: rows of W
+  int64_t v_begin, chunk_len; // the chunk's rows of W
+  int64_t key_offset;         // row_key − key_offset is a label's row of W
+  int n_vtiles;               // vocabulary tiles of the chunk (G layout)
+  float softcap, logit_scale;
+  const float* lse;
+  const int32_t* row_state;
+  const int32_t* row_key;
+  const float* gs;            // general form (null: plain)
+  const float* c1;
+  float eps_over_v, one_minus_eps;
+  const int32_t* dom_base;
+  uint16_t* G;                // blocked chunk, as GradParams::G
+  float* lab_dense;
+  float* lab_oh;
+  int32_t* dom_col;
+  float* dom_coef;
+};
+hipError_t launch_exact_entries(const ExactParams& p, hipStream_t stream);
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream);
 
 // Row-wise kernels (lce_rows.hip).
@@ -180,10 +226,38 @@ hipError_t launch_scale_finalize(const BlockStats* blocks, int nblocks, const fl
 // null, else the scalar scalars[0] (a included).  unit: the caller applies the
 // scalar scalars[0] after the contractions, so gs_i is written as the row's
 // class alone (1 valid, 0 ignored, NaN bad); oh_i keeps the full scale.
+// lab_dense, lab_oh, dom_col and dom_base, when not null, are preset to 0, 0,
+// −1 and −1 for the exact entries (launch_exact_entries).
 hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
                            const float* dloss_rows, const float* scalars, int64_t N,
                            float logit_scale, float one_minus_eps, float z_loss, int unit,
-                           float* gs, float* c1, float* oh, hipStream_t stream);
+                           float* gs, float* c1, float* oh, float* lab_dense, float* lab_oh,
+                           int32_t* dom_col, int32_t* dom_base, hipStream_t stream);
+
+// Gradient filter with the exact entries of the vocabulary chunk whose W rows
+// are [c_lo, c_lo + 256·n_vt) (in row_key − key_offset space): a row's label
+// or dominant dense value is set to 0 when the 256 x 256 block that holds it
+// has a zero flag word (skipped), as the block's other dense values are.
+hipError_t launch_filter_exact(const uint32_t* flags, int n_vt, int64_t c_lo,
+                               const int32_t* row_state, const int32_t* row_key,
+                               int64_t key_offset, int64_t N, float* lab_dense,
+                               const int32_t* dom_col, float* dom_coef, hipStream_t stream);
+
+// Coefficients of the exact entries for the finalize steps, from the
+// logit-gradient pass's per-row outputs: oh[i] = s·(lab_oh[i] − lab_dense[i])
+// for rows with a label among this call's W rows (row_state valid, row_key !=
+// INT_MAX), else 0; de[i] = −s·dom_coef[i] and dkey[i] = dom_col[i] for rows
+// with a dominant entry (dom_col >= 0), else 0 and INT_MAX.  s = scale[0], or
+// 1 when scale is null.  (dx_finalize and dw_correct subtract oh·w and oh·x,
+// de·w and de·x.)
+hipError_t launch_exact_coef(const int32_t* row_state, const int32_t* row_key,
+                             const float* lab_dense, const float* lab_oh, const int32_t* dom_col,
+                             const float* dom_coef, const float* scale, int64_t N, float* oh,
+                             float* de, int32_t* dkey, hipStream_t stream);
+
+// counts[1] = number of sorted keys (of sort_padded(N)) whose label is not
+// INT_MAX: the rows launch_dw_correct walks.
+hipError_t launch_count_keys(const uint64_t* keys, int64_t N, int32_t* counts, hipStream_t stream);
 
 // Label sort of the valid rows (keys: label << 32 | row, ascending).
 constexpr int kSortBlock = 2048;   // keys sorted per block in LDS
@@ -199,10 +273,13 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
 // the sum of n_parts partial buffers part_stride floats apart, taken in part
 // order.  sx is the device scalar sx[0], or sx_rows[i] when sx_rows is not
 // null.
+// Rows with a dominant entry (dom_col not null, dom_col[i] >= 0) also get
+// − de_i·w_{dom_col[i]} (w_{order[dom_col[i]]} when order is not null).
 hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
                               int64_t H, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
-                              const float* sx_rows, void* dX, int dX_bf16, hipStream_t stream);
+                              const float* sx_rows, const int32_t* dom_col, const float* de,
+                              const int32_t* order, void* dX, int dX_bf16, hipStream_t stream);
 
 // Fused forward, generic reference: in place (blocked layout), U[i][v]
 // becomes the gradient G = gs_i·(c1_i·U·2^(ref_i,v/128 − lse_i·log2 e) −

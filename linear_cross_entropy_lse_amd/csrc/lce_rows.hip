@@ -342,9 +342,15 @@ row_coef_kernel(const int32_t* __restrict__ row_state, const float* __restrict__
                 const float* __restrict__ target_deriv, const float* __restrict__ dloss_rows,
                 const float* __restrict__ scalars, int64_t N, float logit_scale,
                 float one_minus_eps, float z_loss, int unit, float* __restrict__ gs,
-                float* __restrict__ c1, float* __restrict__ oh) {
+                float* __restrict__ c1, float* __restrict__ oh, float* __restrict__ lab_dense,
+                float* __restrict__ lab_oh, int32_t* __restrict__ dom_col,
+                int32_t* __restrict__ dom_base) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
+  if (lab_dense) lab_dense[i] = 0.0f;
+  if (lab_oh) lab_oh[i] = 0.0f;
+  if (dom_col) dom_col[i] = -1;
+  if (dom_base) dom_base[i] = -1;
   const int st = row_state[i];
   float g = 0.0f;
   if (st == kRowValid) g = dloss_rows ? dloss_rows[i] * logit_scale : scalars[0];
@@ -357,10 +363,87 @@ row_coef_kernel(const int32_t* __restrict__ row_state, const float* __restrict__
 hipError_t launch_row_coef(const int32_t* row_state, const float* lse, const float* target_deriv,
                            const float* dloss_rows, const float* scalars, int64_t N,
                            float logit_scale, float one_minus_eps, float z_loss, int unit,
-                           float* gs, float* c1, float* oh, hipStream_t stream) {
+                           float* gs, float* c1, float* oh, float* lab_dense, float* lab_oh,
+                           int32_t* dom_col, int32_t* dom_base, hipStream_t stream) {
   hipLaunchKernelGGL(row_coef_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
                      row_state, lse, target_deriv, dloss_rows, scalars, N, logit_scale,
-                     one_minus_eps, z_loss, unit, gs, c1, oh);
+                     one_minus_eps, z_loss, unit, gs, c1, oh, lab_dense, lab_oh, dom_col, dom_base);
+  return hipGetLastError();
+}
+
+// Filtered blocks and the exact entries (see launch_filter_exact).
+__global__ void __launch_bounds__(256)
+filter_exact_kernel(const uint32_t* __restrict__ flags, int n_vt, int64_t c_lo,
+                    const int32_t* __restrict__ row_state, const int32_t* __restrict__ row_key,
+                    int64_t key_offset, int64_t N, float* __restrict__ lab_dense,
+                    const int32_t* __restrict__ dom_col, float* __restrict__ dom_coef) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N || row_state[i] != kRowValid) return;
+  const int64_t c_hi = c_lo + (int64_t)n_vt * 256;
+  const uint32_t* fr = flags + (i / 256) * n_vt;     // the row's token tile
+  const int32_t key = row_key[i];
+  if (key != INT_MAX) {
+    const int64_t L = (int64_t)key - key_offset;
+    if (L >= c_lo && L < c_hi && fr[(L - c_lo) / 256] == 0u) lab_dense[i] = 0.0f;
+  }
+  const int32_t dc = dom_col[i];
+  if (dc >= 0) {
+    const int64_t L = (int64_t)dc - key_offset;
+    if (L >= c_lo && L < c_hi && fr[(L - c_lo) / 256] == 0u) dom_coef[i] = 0.0f;
+  }
+}
+
+hipError_t launch_filter_exact(const uint32_t* flags, int n_vt, int64_t c_lo,
+                               const int32_t* row_state, const int32_t* row_key,
+                               int64_t key_offset, int64_t N, float* lab_dense,
+                               const int32_t* dom_col, float* dom_coef, hipStream_t stream) {
+  hipLaunchKernelGGL(filter_exact_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     flags, n_vt, c_lo, row_state, row_key, key_offset, N, lab_dense, dom_col,
+                     dom_coef);
+  return hipGetLastError();
+}
+
+// Coefficients of the exact entries (see launch_exact_coef).
+__global__ void __launch_bounds__(256)
+exact_coef_kernel(const int32_t* __restrict__ row_state, const int32_t* __restrict__ row_key,
+                  const float* __restrict__ lab_dense, const float* __restrict__ lab_oh,
+                  const int32_t* __restrict__ dom_col, const float* __restrict__ dom_coef,
+                  const float* __restrict__ scale, int64_t N, float* __restrict__ oh,
+                  float* __restrict__ de, int32_t* __restrict__ dkey) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const float s = scale ? *scale : 1.0f;
+  const bool owned = row_state[i] == kRowValid && row_key[i] != INT_MAX;
+  oh[i] = owned ? s * (lab_oh[i] - lab_dense[i]) : 0.0f;
+  const int32_t c = dom_col[i];
+  de[i] = c >= 0 ? -s * dom_coef[i] : 0.0f;
+  dkey[i] = c >= 0 ? c : INT_MAX;
+}
+
+hipError_t launch_exact_coef(const int32_t* row_state, const int32_t* row_key,
+                             const float* lab_dense, const float* lab_oh, const int32_t* dom_col,
+                             const float* dom_coef, const float* scale, int64_t N, float* oh,
+                             float* de, int32_t* dkey, hipStream_t stream) {
+  hipLaunchKernelGGL(exact_coef_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     row_state, row_key, lab_dense, lab_oh, dom_col, dom_coef, scale, N, oh, de,
+                     dkey);
+  return hipGetLastError();
+}
+
+// First sorted key whose label is INT_MAX (binary search; keys ascending).
+__global__ void count_keys_kernel(const uint64_t* __restrict__ keys, int64_t n,
+                                  int32_t* __restrict__ counts) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int32_t)(keys[mid] >> 32) != INT_MAX && keys[mid] != ~0ull) lo = mid + 1;
+    else hi = mid;
+  }
+  counts[1] = (int32_t)lo;
+}
+
+hipError_t launch_count_keys(const uint64_t* keys, int64_t N, int32_t* counts, hipStream_t stream) {
+  hipLaunchKernelGGL(count_keys_kernel, dim3(1), dim3(1), 0, stream, keys, sort_padded(N), counts);
   return hipGetLastError();
 }
 
@@ -456,7 +539,9 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
                    int64_t H, const int32_t* __restrict__ row_state,
                    const int32_t* __restrict__ row_key, const float* __restrict__ oh,
                    const uint16_t* __restrict__ W, const float* __restrict__ sx,
-                   const float* __restrict__ sx_rows, void* __restrict__ dX, int dX_bf16) {
+                   const float* __restrict__ sx_rows, const int32_t* __restrict__ dom_col,
+                   const float* __restrict__ de, const int32_t* __restrict__ order,
+                   void* __restrict__ dX, int dX_bf16) {
   const int64_t row = blockIdx.x;
   const int st = row_state[row];
   const float s = sx_rows ? sx_rows[row] : *sx;
@@ -464,6 +549,10 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
   const int32_t key = st == kRowValid ? row_key[row] : INT_MAX;
   const bool owned = key != INT_MAX;          // the label is one of W's rows
   const int64_t y = owned ? key : 0;
+  const int32_t dc = (dom_col && st == kRowValid) ? dom_col[row] : -1;
+  const bool dom = dc >= 0;                   // a dominant entry other than the label
+  const int64_t yd = dom ? (order ? order[dc] : dc) : 0;
+  const float ed = dom ? de[row] : 0.0f;
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (st == kRowValid) {
@@ -476,16 +565,23 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
         v.w += w.w;
       }
       const float a[4] = {v.x, v.y, v.z, v.w};
+      float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // the exact terms, − e·w_y − ed·w_yd
       if (owned) {
         const u32x2 wv = *reinterpret_cast<const u32x2*>(W + y * H + h);
         const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
                              __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = fmaf(s, a[q], -e * w4[q]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = s * a[q];
+        for (int q = 0; q < 4; ++q) t[q] = -e * w4[q];
       }
+      if (dom) {
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(W + yd * H + h);
+        const float w4[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
+                             __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = fmaf(-ed, w4[q], t[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = fmaf(s, a[q], t[q]);
     } else if (st == kRowBad) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __builtin_nanf("");
@@ -505,9 +601,11 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
 hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
                               int64_t H, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
-                              const float* sx_rows, void* dX, int dX_bf16, hipStream_t stream) {
+                              const float* sx_rows, const int32_t* dom_col, const float* de,
+                              const int32_t* order, void* dX, int dX_bf16, hipStream_t stream) {
   hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, n_parts,
-                     part_stride, N, H, row_state, row_key, oh, W, sx, sx_rows, dX, dX_bf16);
+                     part_stride, N, H, row_state, row_key, oh, W, sx, sx_rows, dom_col, de, order,
+                     dX, dX_bf16);
   return hipGetLastError();
 }
 
