@@ -201,7 +201,8 @@ struct FusedPlan {
   int nchunks, T, S, n_vtiles, nt_h, ksplit, nb_prep, nb_fin;
   size_t off_state, off_key, off_target, off_deriv, off_gs, off_c1, off_oh, off_rrow, off_keys_a,
       off_keys_b, off_head, off_tail, off_bprep, off_bfin, off_scalars, off_pm, off_ps, off_pz,
-      off_U, off_ref, off_Xs, off_dXp, off_dWacc, total;
+      off_pcz, off_pcb, off_labd, off_labo, off_domcol, off_domc, off_de, off_dkey, off_dkeys_a,
+      off_dkeys_b, off_dcounts, off_U, off_ref, off_Xs, off_dXp, off_dWacc, total;
 };
 
 FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
@@ -254,6 +255,19 @@ FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_pm = o;      o = align_up(o + sizeof(float) * part);
   p.off_ps = o;      o = align_up(o + sizeof(float) * part);
   p.off_pz = o;      o = align_up(o + sizeof(float) * part);
+  // Dominant-entry candidates per split, and the exact entries (as the
+  // recompute path's).
+  p.off_pcz = o;     o = align_up(o + sizeof(float) * part);
+  p.off_pcb = o;     o = align_up(o + sizeof(int32_t) * part);
+  p.off_labd = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_labo = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_domcol = o;  o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_domc = o;    o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_de = o;      o = align_up(o + sizeof(float) * (size_t)N);
+  p.off_dkey = o;    o = align_up(o + sizeof(int32_t) * (size_t)N);
+  p.off_dkeys_a = o; o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_dkeys_b = o; o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
+  p.off_dcounts = o; o = align_up(o + 16);
   p.off_U = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)p.ldu);
   p.off_ref = o;     o = align_up(o + sizeof(float) * (size_t)p.Nc * 2 * (size_t)p.n_vtiles);
   p.off_Xs = o;      o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)H);
@@ -991,6 +1005,18 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
   uint16_t* Xs = at<uint16_t>(workspace_dev, pl.off_Xs);
   float* dXp = at<float>(workspace_dev, pl.off_dXp);
   float* dW32 = dW_dtype == LCE_F32 ? static_cast<float*>(dW_dev) : at<float>(workspace_dev, pl.off_dWacc);
+  float* pcz = at<float>(workspace_dev, pl.off_pcz);
+  int32_t* pcb = at<int32_t>(workspace_dev, pl.off_pcb);
+  float* lab_dense = at<float>(workspace_dev, pl.off_labd);
+  float* lab_oh = at<float>(workspace_dev, pl.off_labo);
+  int32_t* dom_col = at<int32_t>(workspace_dev, pl.off_domcol);
+  float* dom_coef = at<float>(workspace_dev, pl.off_domc);
+  float* de = at<float>(workspace_dev, pl.off_de);
+  int32_t* dkey = at<int32_t>(workspace_dev, pl.off_dkey);
+  uint64_t* dkeys_a = at<uint64_t>(workspace_dev, pl.off_dkeys_a);
+  uint64_t* dkeys_b = at<uint64_t>(workspace_dev, pl.off_dkeys_b);
+  const uint64_t* dkeys = sort_passes(N) % 2 == 0 ? dkeys_a : dkeys_b;
+  int32_t* dcounts = at<int32_t>(workspace_dev, pl.off_dcounts);
   const uint16_t* X = static_cast<const uint16_t*>(X_dev);
   const uint16_t* W = static_cast<const uint16_t*>(W_dev);
   const bool smoothing = opt->label_smoothing > 0.0f;
@@ -1023,13 +1049,35 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     fp.softcap = opt->softcap; fp.logit_scale = opt->logit_scale;
     fp.part_m = pm; fp.part_s = ps; fp.part_z = smoothing ? pz : nullptr;
     fp.U = U; fp.ldu = pl.ldu; fp.ref = fixed ? nullptr : ref;
+    fp.part_cz = pcz; fp.part_cb = pcb;
     LCE_LAUNCH("flce_logits", stream, launch_flce_logits(fp, stream));
     LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, fp.S, nr, state + r0, target + r0, terms,
                                 lse_dev + r0, loss_dev + r0, bfin + r0 / kTile, nullptr, stream));
     LCE_LAUNCH("row_coef", stream, launch_row_coef(state + r0, lse_dev + r0, deriv + r0,
                             opt->reduction == LCE_REDUCE_NONE ? dloss_dev + r0 : nullptr, scalars, nr,
                             opt->logit_scale, 1.0f - opt->label_smoothing, opt->z_loss, unit, gs + r0,
-                            c1 + r0, oh + r0, nullptr, nullptr, nullptr, nullptr, stream));
+                            c1 + r0, oh + r0, lab_dense + r0, lab_oh + r0, dom_col + r0, nullptr,
+                            stream));
+    // The label's entry and a dominant entry of each row leave the stored
+    // block and are applied in fp32 (launch_exact_entries), as in the
+    // recompute backward.
+    ExactParams ep{};
+    ep.X = X + r0 * H; ep.W = W; ep.N = nr; ep.H = H; ep.V = V;
+    ep.v_begin = 0; ep.chunk_len = V; ep.key_offset = 0; ep.n_vtiles = pl.n_vtiles;
+    ep.softcap = opt->softcap; ep.logit_scale = opt->logit_scale;
+    ep.lse = lse_dev + r0; ep.row_state = state + r0; ep.row_key = key + r0;
+    ep.gs = gs + r0; ep.c1 = c1 + r0;
+    ep.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
+    ep.one_minus_eps = 1.0f - opt->label_smoothing;
+    ep.dom_base = nullptr; ep.cand_z = pcz; ep.cand_b = pcb; ep.cand_splits = fp.S;
+    ep.G = U;
+    ep.lab_dense = lab_dense + r0; ep.lab_oh = lab_oh + r0; ep.dom_col = dom_col + r0;
+    ep.dom_coef = dom_coef + r0;
+    LCE_LAUNCH("exact_entries", stream, launch_exact_entries(ep, stream));
+    LCE_LAUNCH("exact_coef", stream, launch_exact_coef(state + r0, key + r0, lab_dense + r0, lab_oh + r0,
+                                                      dom_col + r0, dom_coef + r0,
+                                                      unit ? scalars : nullptr, nr, oh + r0, de + r0,
+                                                      dkey + r0, stream));
     // G = diag(r)·U with the fixed reference (dW from the row-scaled X, dX
     // rows scaled afterwards); otherwise U is turned into G in place.
     if (fixed) {
@@ -1050,13 +1098,16 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
-                               post_scale, fixed ? rrow + r0 : nullptr, nullptr, nullptr, nullptr,
-                               static_cast<char*>(dX_dev) + r0 * H * dx_es, dX_dtype == LCE_BF16,
-                               stream));
+                               post_scale, fixed ? rrow + r0 : nullptr, dom_col + r0, de + r0,
+                               nullptr, static_cast<char*>(dX_dev) + r0 * H * dx_es,
+                               dX_dtype == LCE_BF16, stream));
   }
   LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(bfin, (int)ceil_div(N, kTile), opt->reduction == LCE_REDUCE_MEAN,
                                 reduced_dev, n_valid_dev, bad_label_dev, stream));
   LCE_LAUNCH("dw_correct", stream, launch_dw_correct(keys, counts, oh, X, N, H, dW32, 0, V, part_head, part_tail, stream));
+  LCE_LAUNCH("sort_dominant", stream, launch_sort_by_label(dkey, N, dkeys_a, dkeys_b, stream));
+  LCE_LAUNCH("count_dominant", stream, launch_count_keys(dkeys, N, dcounts, stream));
+  LCE_LAUNCH("dw_correct", stream, launch_dw_correct(dkeys, dcounts, de, X, N, H, dW32, 0, V, part_head, part_tail, stream));
   if (dW_dtype == LCE_BF16)
     LCE_LAUNCH("cast_bf16", stream, launch_cast_bf16(dW32, static_cast<uint16_t*>(dW_dev), V * H, stream));
   return LCE_OK;

@@ -141,11 +141,30 @@ exact_entries_kernel(ExactParams p) {
   }
 
   // ---- a dominant entry: among the 64 rows the finding lane held ----
-  const int32_t db = (in && live) ? p.dom_base[tok] : -1;
+  const float zthr = dominance_threshold<kCapped>(live, o, k2, c2, l2a);
+  int32_t db = -1;
+  if (in && live) {
+    if (p.dom_base) {
+      db = p.dom_base[tok];
+    } else {
+      // The fused forward's per-split candidates: the largest logit (the
+      // smaller row on ties) is dominant if it lies above the threshold.
+      float bz = -__builtin_inff();
+      int32_t bb = -1;
+      for (int sp = 0; sp < p.cand_splits; ++sp) {
+        const float z = p.cand_z[(int64_t)sp * p.N + tok];
+        const int32_t b = p.cand_b[(int64_t)sp * p.N + tok];
+        if (z > bz || (z == bz && b >= 0 && (bb < 0 || b < bb))) {
+          bz = z;
+          bb = b;
+        }
+      }
+      db = bz > zthr ? bb : -1;
+    }
+  }
   const int64_t base = db < 0 ? -1 : (int64_t)db - p.key_offset;
   const bool dom = base >= c_lo && base < c_hi;
   uint64_t todo = __builtin_amdgcn_ballot_w64(dom && lane < kExactRows);
-  const float zthr = dominance_threshold<kCapped>(live, o, k2, c2, l2a);
   while (todo) {
     const int jt = __builtin_ctzll(todo);
     todo &= todo - 1;

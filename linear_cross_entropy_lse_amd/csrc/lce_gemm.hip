@@ -440,16 +440,24 @@ grad_logits_kernel(GradParams p) {
 // 128-column block for the later rescale) or the fixed c2 (kCapFixed).
 // U lies in [0, 1]; U·2^(ref − lse) is the softmax times d.
 // ---------------------------------------------------------------------------
+// Also the candidate of a dominant entry: the lane's largest logit of each
+// token column so far in the split and the W row of the lane's first row of
+// the tile that held it (cz, cbase in LDS, [ni][thread]; row0 is that row for
+// this tile).  A later pass keeps the split's best, and once the LSE is known
+// the exact-entry kernel decides whether it is dominant.
 template <int kMode, bool kMasked, bool kZSum>
 __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kNI], float (&m)[kNI],
                                                      float (&s)[kNI], float (&zs)[kNI], int lim,
                                                      float k2, float c2, float l2a,
                                                      __amdgpu_buffer_rsrc_t rs,
-                                                     const uint32_t (&cb)[kNI]) {
+                                                     const uint32_t (&cb)[kNI],
+                                                     float (*cz)[kThreads], int32_t (*cbase)[kThreads],
+                                                     int tid, int32_t row0) {
   const float NEG_INF = -__builtin_inff();
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     float mref = c2;
+    float zown = NEG_INF;   // the lane's largest logit of the column in this tile
     if (kMode != kCapFixed) {
       float zmax = NEG_INF;
 #pragma unroll
@@ -459,6 +467,7 @@ __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kN
           const float z = acc[mi][ni][r];
           zmax = fmaxf(zmax, (!kMasked || acc_row_const(mi, r) < lim) ? z : NEG_INF);
         }
+      zown = zmax;
       // One reference for both lanes of the token column, so that a 128-row
       // block of U has a single scale.
       zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
@@ -484,6 +493,7 @@ __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kN
             const int r = gq * 4 + q;
             const float z = acc[mi][ni][r];
             const bool ok = !kMasked || acc_row_const(mi, r) < lim;
+            if (kMode == kCapFixed) zown = fmaxf(zown, ok ? z : NEG_INF);
             float e, u, zt;
             if (kMode == kPlain) {
               e = exp2_fast(fmaf(z, l2a, -mref));
@@ -515,6 +525,41 @@ __device__ __forceinline__ void flce_fold_store_tile(const f32x16 (&acc)[kMI][kN
       }
     s[ni] += sum;
     if (kZSum) zs[ni] += zsum;
+    if (zown > cz[ni][tid]) {
+      cz[ni][tid] = zown;
+      cbase[ni][tid] = row0;
+    }
+  }
+}
+
+// End of a fused sweep: the split's dominant-entry candidate of each token,
+// the best of the four lanes that hold its column (lanes l and l^32 of the
+// two waves with the same wn), the larger logit first, then the smaller row.
+__device__ __forceinline__ void flce_store_candidates(const float (*cz)[kThreads],
+                                                      const int32_t (*cbase)[kThreads], int wm,
+                                                      int wn, int lane, int64_t tok0, int split,
+                                                      int64_t N, float* part_cz, int32_t* part_cb) {
+  __syncthreads();
+  if (wm != 0 || lane >= 32) return;
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = tok0 + acc_col(wn, ni, lane);
+    if (tok >= N) continue;
+    const int t0 = wn * 64 + lane, t1 = (2 + wn) * 64 + lane;
+    const int holders[4] = {t0, t0 + 32, t1, t1 + 32};
+    float bz = cz[ni][holders[0]];
+    int32_t bb = cbase[ni][holders[0]];
+#pragma unroll
+    for (int h = 1; h < 4; ++h) {
+      const float z = cz[ni][holders[h]];
+      const int32_t b = cbase[ni][holders[h]];
+      if (z > bz || (z == bz && b >= 0 && (bb < 0 || b < bb))) {
+        bz = z;
+        bb = b;
+      }
+    }
+    part_cz[(int64_t)split * N + tok] = bz;
+    part_cb[(int64_t)split * N + tok] = bb;
   }
 }
 
@@ -534,6 +579,8 @@ template <bool kTail, int kMode, bool kZSum>
 __global__ void __launch_bounds__(kThreads, 1)
 flce_logits_kernel(FlceParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
+  __shared__ float s_cz[kNI][kThreads];      // dominant-entry candidates (see
+  __shared__ int32_t s_cb[kNI][kThreads];    // flce_fold_store_tile)
   LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -556,7 +603,10 @@ flce_logits_kernel(FlceParams p) {
     s[ni] = 0.0f;
     zs[ni] = 0.0f;
     col_base[ni] = (uint32_t)((2 * wm * kGSubElems + acc_col(wn, ni, lane) * kBK + 8 * (lane >> 5)) * 2);
+    s_cz[ni][tid] = -__builtin_inff();
+    s_cb[ni][tid] = -1;
   }
+  const int lrow = acc_row_lane(wm, lane);
   // U is blocked like the recompute path's gradient chunk: the token tile's
   // n_vtiles blocks, rows past N included (their values are finite and meet
   // only zero rows of X in the dW contraction).
@@ -580,7 +630,8 @@ flce_logits_kernel(FlceParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
-    flce_fold_store_tile<kMode, false, kZSum>(acc, m, s, zs, 0, k2, c2, l2a, rs, cb);
+    flce_fold_store_tile<kMode, false, kZSum>(acc, m, s, zs, 0, k2, c2, l2a, rs, cb, s_cz, s_cb, tid,
+                                              (int32_t)(v0 + lrow));
     if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
   }
   for (int j = j_mid; j < j1; ++j) {
@@ -590,8 +641,9 @@ flce_logits_kernel(FlceParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
-    const int lim = (int)(p.V - v0) - acc_row_lane(wm, lane);
-    flce_fold_store_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a, rs, cb);
+    const int lim = (int)(p.V - v0) - lrow;
+    flce_fold_store_tile<kMode, true, kZSum>(acc, m, s, zs, lim, k2, c2, l2a, rs, cb, s_cz, s_cb, tid,
+                                             (int32_t)(v0 + lrow));
     if (kMode != kCapFixed) flce_store_ref(rr, ref_base, m, j, wm, ref_ni_stride);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -599,6 +651,7 @@ flce_logits_kernel(FlceParams p) {
                                      tok0, split, p.N,
                                      kMode == kPlain ? p.logit_scale : p.softcap, p.part_m,
                                      p.part_s, p.part_z);
+  flce_store_candidates(s_cz, s_cb, wm, wn, lane, tok0, split, p.N, p.part_cz, p.part_cb);
 }
 
 // ---------------------------------------------------------------------------

@@ -108,6 +108,11 @@ struct FlceParams {
   // running max of the row's split up to and including that block's tile.
   // Null selects the fixed reference c·log2(e) (softcap with c·log2(e) < 60).
   float* ref;
+  // Dominant-entry candidate of each (split, token), [S, N]: the split's
+  // largest logit of the token and the W row of the first of the 64 rows of
+  // the tile that the lane holding it held (−1: none).
+  float* part_cz;
+  int32_t* part_cb;
 };
 
 hipError_t launch_lse_partials(const LseParams& p, hipStream_t stream);
@@ -147,6 +152,12 @@ struct ExactParams {
   const float* c1;
   float eps_over_v, one_minus_eps;
   const int32_t* dom_base;
+  // Instead of dom_base (null): per-split candidates [cand_splits, N] of the
+  // fused forward (FlceParams::part_cz); the best is dominant when its
+  // softmax exceeds the threshold.
+  const float* cand_z;
+  const int32_t* cand_b;
+  int cand_splits;
   uint16_t* G;                // blocked chunk, as GradParams::G
   float* lab_dense;
   float* lab_oh;

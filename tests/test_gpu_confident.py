@@ -132,3 +132,36 @@ def test_confident_rows_variants(lce, opts):
     e_dx, e_dw = rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW)
     print(f"[confident] {opts}: dX {e_dx:.2e} dW {e_dw:.2e}", flush=True)
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+
+
+@pytest.mark.parametrize("kind,opts", [
+    ("softcap_wrong_label", dict()),                        # fixed reference (softcap 30)
+    ("label_is_top", dict()),                               # no softcap: running reference
+    ("label_is_top_softcap", dict(z_loss=1e-3)),            # fixed reference, per-row factor
+    ("label_is_top", dict(reduction="none")),               # per-row upstream gradients
+])
+def test_confident_rows_fused(lce, kind, opts):
+    """The row-chunked fused call (two row chunks here) on the same regimes."""
+    Z, y, c = confident_case(kind, seed=SEEDS[kind])
+    X, W = inputs_with_logits(Z, seed=7)
+    y[::17] = -100
+    yt = torch.from_numpy(y.astype(np.int64))
+    N = len(y)
+    red = opts.get("reduction", "mean")
+    dloss = (np.random.default_rng(5).standard_normal(N).astype(np.float32) if red == "none"
+             else np.float32(1.0))
+    dev = "cuda"
+    out, dX, dW = lce.lce_forward_backward(X.to(dev), W.to(dev), yt.to(dev),
+                                           torch.from_numpy(np.atleast_1d(dloss)).to(dev),
+                                           softcap=c, **opts)
+    torch.cuda.synchronize()
+    o = O.options(softcap=c, **opts)
+    X64, W64 = L.to_f64(X), L.to_f64(W)
+    f = O.forward_ex(X64, W64, y, o)
+    rdX, rdW = O.backward_ex(X64, W64, y, dloss.astype(np.float64), o)
+    e_lse = float(np.abs(out["lse"].cpu().numpy() - f["lse"]).max())
+    e_dx, e_dw = rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW)
+    print(f"[confident fused] {kind} {opts}: lse {e_lse:.1e} dX {e_dx:.2e} dW {e_dw:.2e}",
+          flush=True)
+    assert e_lse <= LSE_ATOL
+    assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
