@@ -397,6 +397,17 @@ lce_status lce_forward_noalloc(const void* X_dev, const void* W_dev,
                                int32_t* n_valid_dev, int32_t* bad_label_dev,
                                void* stream);
 
+/*
+ * The device a call would run on (host call).  For HIP device `device` (-1:
+ * the current device): the number of compute units, the peak shader clock in
+ * kHz and the architecture name (NUL-terminated, truncated to arch_len bytes;
+ * arch may be NULL).  The dense bf16 MFMA peak of a gfx950 part is
+ * cu_count · clock · 4096 flops per clock and compute unit.  Returns LCE_OK,
+ * LCE_ERR_INVALID_ARG for NULL outputs, or LCE_ERR_HIP.
+ */
+lce_status lce_device_info(int device, int32_t* cu_count, int32_t* clock_khz, char* arch,
+                           int32_t arch_len);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);
 

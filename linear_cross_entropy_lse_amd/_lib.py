@@ -36,7 +36,8 @@ EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_
             "lce_shard_backward", "lce_fused_workspace_bytes", "lce_forward_backward",
             "lce_vocab_order_workspace_bytes", "lce_vocab_order",
             "lce_backward_sorted_workspace_bytes", "lce_backward_sorted",
-            "lce_forward_noalloc_max_bytes", "lce_forward_noalloc", "lce_status_string",
+            "lce_forward_noalloc_max_bytes", "lce_forward_noalloc", "lce_device_info",
+            "lce_status_string",
             "lce_version", "lce_timing_enable", "lce_timing_reset", "lce_timing_read")
 
 
@@ -131,6 +132,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                         vp, vp, vp, vp, vp, vp]
     lib.lce_forward_noalloc.restype = ctypes.c_int
+    lib.lce_device_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_char_p,
+                                    ctypes.c_int32]
+    lib.lce_device_info.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -152,6 +157,15 @@ def status_string(status: int) -> str:
 
 def lce_version() -> int:
     return int(load().lce_version())
+
+
+def lce_device_info(device: int = -1) -> dict:
+    """Compute units, peak shader clock (kHz) and architecture of a device."""
+    cus, clk = ctypes.c_int32(0), ctypes.c_int32(0)
+    arch = ctypes.create_string_buffer(64)
+    _check(load().lce_device_info(int(device), ctypes.byref(cus), ctypes.byref(clk), arch, 64),
+           "lce_device_info")
+    return {"cu_count": cus.value, "clock_khz": clk.value, "arch": arch.value.decode()}
 
 
 def lce_timing_enable(enable: bool = True) -> None:

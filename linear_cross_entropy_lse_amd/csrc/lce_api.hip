@@ -697,6 +697,22 @@ int lce_timing_read(lce_kernel_timing* out, int max_entries) {
   return n;
 }
 
+lce_status lce_device_info(int device, int32_t* cu_count, int32_t* clock_khz, char* arch,
+                           int32_t arch_len) {
+  if (!cu_count || !clock_khz) return LCE_ERR_INVALID_ARG;
+  int dev = device;
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return LCE_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LCE_ERR_HIP;
+  *cu_count = prop.multiProcessorCount;
+  *clock_khz = prop.clockRate;
+  if (arch && arch_len > 0) {
+    std::strncpy(arch, prop.gcnArchName, (size_t)arch_len - 1);
+    arch[arch_len - 1] = 0;
+  }
+  return LCE_OK;
+}
+
 const char* lce_status_string(lce_status status) {
   switch (status) {
     case LCE_OK: return "ok";

@@ -312,3 +312,10 @@ def test_forward_noalloc_host_checks(lib):
     # The largest shapes of the benchmark workloads fit.
     for (N, H, V) in [(8192, 2304, 256128), (32768, 3584, 152064), (16384, 4096, 32000)]:
         assert lib.lce_forward_workspace_bytes(N, H, V) <= cap
+
+
+def test_device_info_argument_checks(lib):
+    """lce_device_info refuses NULL outputs before asking the runtime."""
+    c = ctypes.c_int32(0)
+    assert lib.lce_device_info(-1, None, ctypes.byref(c), None, 0) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_device_info(-1, ctypes.byref(c), None, None, 0) == _lib.LCE_ERR_INVALID_ARG
