@@ -73,11 +73,13 @@ class LceError(RuntimeError):
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load liblce.so and declare its signatures (raises if it is not built)."""
+    """Load liblce.so and declare its signatures (raises if it is not built).
+    The environment variable LCE_LIB selects another build of the library
+    (the checking builds of build.py)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LCE_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"liblce.so is not built ({p}); run "
                            "`python -m linear_cross_entropy_lse_amd.build`")

@@ -634,7 +634,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(dkeys, dcounts, de, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
   }
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, state, key, oh, W, gemm_scale, nullptr,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, V, state, key, oh, W, gemm_scale, nullptr,
                              dom_col, de, order, dX_dev, dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }
@@ -1113,7 +1113,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
     cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
-    LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, state + r0, key + r0, oh + r0, W,
+    LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, V, state + r0, key + r0, oh + r0, W,
                                post_scale, fixed ? rrow + r0 : nullptr, dom_col + r0, de + r0,
                                nullptr, static_cast<char*>(dX_dev) + r0 * H * dx_es,
                                dX_dtype == LCE_BF16, stream));

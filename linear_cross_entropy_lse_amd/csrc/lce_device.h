@@ -734,6 +734,19 @@ __device__ __forceinline__ float dominance_threshold(bool live, float off, float
   return zthr;
 }
 
+// Index checks of the debug build (build.py --debug-checks): LCE_DCHECK(c)
+// is c, and prints the failing check, so that `if (LCE_DCHECK(i < n)) use(i)`
+// skips the access it guards; the product build compiles it to true.
+#ifdef LCE_DEBUG_CHECKS
+__device__ __forceinline__ bool lce_dcheck(bool ok, const char* what, const char* file, int line) {
+  if (!ok) printf("lce check failed: %s (%s:%d)\n", what, file, line);
+  return ok;
+}
+#define LCE_DCHECK(cond) lce_dcheck((cond), #cond, __FILE__, __LINE__)
+#else
+#define LCE_DCHECK(cond) true
+#endif
+
 // Row classes written by the row-preparation kernels.
 enum RowState : int32_t { kRowIgnored = 0, kRowValid = 1, kRowBad = 2 };
 

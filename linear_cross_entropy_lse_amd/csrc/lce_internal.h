@@ -287,7 +287,7 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
 // Rows with a dominant entry (dom_col not null, dom_col[i] >= 0) also get
 // − de_i·w_{dom_col[i]} (w_{order[dom_col[i]]} when order is not null).
 hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
-                              int64_t H, const int32_t* row_state, const int32_t* row_key,
+                              int64_t H, int64_t V, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
                               const float* sx_rows, const int32_t* dom_col, const float* de,
                               const int32_t* order, void* dX, int dX_bf16, hipStream_t stream);

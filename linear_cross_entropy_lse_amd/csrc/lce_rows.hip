@@ -56,7 +56,7 @@ row_prep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const int64_t yl = y - vr.v_lo;
     owned = st == kRowValid && yl >= 0 && yl < V;
     float t = 0.0f, d = 0.0f;
-    if (owned) {
+    if (owned && LCE_DCHECK(H % 8 == 0 && vr.v_lo + V <= vr.V_total)) {
       const uint16_t* xr = X + row * H;
       const uint16_t* wr = W + yl * H;
       float dot = 0.0f;
@@ -536,7 +536,7 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_stride, int64_t N,
-                   int64_t H, const int32_t* __restrict__ row_state,
+                   int64_t H, int64_t V, const int32_t* __restrict__ row_state,
                    const int32_t* __restrict__ row_key, const float* __restrict__ oh,
                    const uint16_t* __restrict__ W, const float* __restrict__ sx,
                    const float* __restrict__ sx_rows, const int32_t* __restrict__ dom_col,
@@ -547,11 +547,11 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
   const float s = sx_rows ? sx_rows[row] : *sx;
   const float e = oh[row];
   const int32_t key = st == kRowValid ? row_key[row] : INT_MAX;
-  const bool owned = key != INT_MAX;          // the label is one of W's rows
+  const bool owned = key != INT_MAX && LCE_DCHECK(key >= 0 && key < V);  // the label is one of W's rows
   const int64_t y = owned ? key : 0;
   const int32_t dc = (dom_col && st == kRowValid) ? dom_col[row] : -1;
-  const bool dom = dc >= 0;                   // a dominant entry other than the label
-  const int64_t yd = dom ? (order ? order[dc] : dc) : 0;
+  const int64_t yd = dc >= 0 ? (order ? order[dc] : dc) : 0;
+  const bool dom = dc >= 0 && LCE_DCHECK(dc < V && yd >= 0 && yd < V);  // a dominant entry other than the label
   const float ed = dom ? de[row] : 0.0f;
   for (int64_t h = (int64_t)threadIdx.x * 4; h < H; h += 1024) {
     float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -599,12 +599,12 @@ dx_finalize_kernel(const float* __restrict__ dX_acc, int n_parts, int64_t part_s
 }
 
 hipError_t launch_dx_finalize(const float* dX_acc, int n_parts, int64_t part_stride, int64_t N,
-                              int64_t H, const int32_t* row_state, const int32_t* row_key,
+                              int64_t H, int64_t V, const int32_t* row_state, const int32_t* row_key,
                               const float* oh, const uint16_t* W, const float* sx,
                               const float* sx_rows, const int32_t* dom_col, const float* de,
                               const int32_t* order, void* dX, int dX_bf16, hipStream_t stream) {
   hipLaunchKernelGGL(dx_finalize_kernel, dim3((unsigned)N), dim3(256), 0, stream, dX_acc, n_parts,
-                     part_stride, N, H, row_state, row_key, oh, W, sx, sx_rows, dom_col, de, order,
+                     part_stride, N, H, V, row_state, row_key, oh, W, sx, sx_rows, dom_col, de, order,
                      dX, dX_bf16);
   return hipGetLastError();
 }
@@ -700,8 +700,8 @@ __device__ __forceinline__ int32_t key_label(uint64_t k) { return (int32_t)(k >>
 
 __global__ void __launch_bounds__(64)
 dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts,
-              const float* __restrict__ oh, const uint16_t* __restrict__ X, int64_t H,
-              float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
+              const float* __restrict__ oh, const uint16_t* __restrict__ X, int64_t n_rows,
+              int64_t H, float* __restrict__ dst, int64_t v_lo, int64_t v_hi,
               float* __restrict__ part_head, float* __restrict__ part_tail) {
   __shared__ int32_t s_row[kSegRows], s_lab[kSegRows];
   __shared__ float s_e[kSegRows];
@@ -713,9 +713,10 @@ dw_seg_kernel(const uint64_t* __restrict__ keys, const int32_t* __restrict__ cou
   const int lane = threadIdx.x;
   if (lane < cnt) {
     const uint64_t k = keys[p0 + lane];
-    s_row[lane] = (int32_t)(uint32_t)k;
+    const bool ok = LCE_DCHECK((int64_t)(uint32_t)k < n_rows);
+    s_row[lane] = ok ? (int32_t)(uint32_t)k : 0;
     s_lab[lane] = key_label(k);
-    s_e[lane] = oh[(uint32_t)k];
+    s_e[lane] = ok ? oh[(uint32_t)k] : 0.0f;
   }
   const int32_t lab_prev = p0 > 0 ? key_label(keys[p0 - 1]) : -1;
   const int32_t lab_next = p0 + cnt < n_ok ? key_label(keys[p0 + cnt]) : -1;
@@ -797,8 +798,8 @@ hipError_t launch_dw_correct(const uint64_t* keys, const int32_t* counts, const 
                              int64_t v_hi, float* part_head, float* part_tail,
                              hipStream_t stream) {
   const dim3 grid((unsigned)seg_chunks(N), (unsigned)((H + 511) / 512));
-  hipLaunchKernelGGL(dw_seg_kernel, grid, dim3(64), 0, stream, keys, counts, oh, X, H, dst, v_lo,
-                     v_hi, part_head, part_tail);
+  hipLaunchKernelGGL(dw_seg_kernel, grid, dim3(64), 0, stream, keys, counts, oh, X, N, H, dst,
+                     v_lo, v_hi, part_head, part_tail);
   hipLaunchKernelGGL(dw_seg_fix_kernel, grid, dim3(64), 0, stream, keys, counts, H, dst, v_lo,
                      v_hi, part_head, part_tail);
   return hipGetLastError();
