@@ -219,10 +219,10 @@ lse_partials_kernel(LseParams p) {
 // tanh = 1 − 2r, p = 2^((c2 − lse2) − 2·c2·r) and 1 − tanh² = 4r(1 − r).
 //
 // The kernel also looks for an entry whose softmax exceeds 1/2 + 2^-10 (at
-// most one per row): a max over each lane's logits of a token column against
-// that column's threshold, and, in the rare tile that holds one, the W row of
-// the lane's first row of the tile goes to GradParams::dom_base.  The exact
-// entries themselves are computed afterwards (launch_exact_entries).
+// most one per row): a max over each lane's softmax values of a token column
+// against 1/2, and, for the rare tile that holds one, the W row of the lane's
+// first row of the tile goes to GradParams::dom_base.  The exact entries
+// themselves are computed afterwards (launch_exact_entries).
 // ---------------------------------------------------------------------------
 // G of one finished tile, as bf16, through the G descriptor (rows past N are
 // out of range).  Plain form (kGen false): G = p·d, off[ni] folding the row
@@ -238,15 +238,16 @@ lse_partials_kernel(LseParams p) {
 // (permlane32 swap) so that lane l stores the 8 rows of group 2gp and lane
 // l + 32 those of group 2gp + 1, 16 bytes each: sub-block mi/2, column
 // (mi%2)·32 + 16gp (+ 8 from the lane half, carried by cb).
-// zmax[ni] gathers the largest logit of each token column among the
-// lane's rows (for the dominance check, grad_find_dominant).
+// pmax[ni] gathers the largest softmax value of each token column among the
+// lane's rows, times 4 with softcap (for the dominance check,
+// grad_find_dominant).
 template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false>
 __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
                                                 const float (&gsc)[kNI], const float (&c1)[kNI],
                                                 float eps_v, __amdgpu_buffer_rsrc_t rs,
                                                 const uint32_t (&cb)[kNI], int lim, float k2,
                                                 float c2, float l2a, float feps,
-                                                float (&zmax)[kNI]) {
+                                                float (&pmax)[kNI]) {
   bool active = false;
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni)
@@ -263,8 +264,7 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
           for (int q = 0; q < 4; ++q) {
             const int r = gq * 4 + q;
             const float z = acc[mi][ni][r];
-            zmax[ni] = fmaxf(zmax[ni], (!kMasked || acc_row_const(mi, r) < lim) ? z : -__builtin_inff());
-            float val, pr;
+            float val, pr, pm;
             if (kCapped) {
               // off carries + 2 here: pr4 = 4p, and 4p·r(1 − r) = p·(1 − tanh²).
               const float rr = rcp_fast(exp2_fast(z * k2) + 1.0f);
@@ -272,11 +272,14 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
               const float dq = fmaf(-rr, rr, rr);
               val = kGen ? gsc[ni] * fmaf(c1[ni], pr4, -4.0f * eps_v) * dq : pr4 * dq;
               pr = 0.25f * pr4;   // read by the filter only
+              pm = pr4;
             } else {
               pr = exp2_fast(fmaf(z, l2a, off[ni]));
               val = kGen ? gsc[ni] * fmaf(c1[ni], pr, -eps_v) : pr;
+              pm = pr;
             }
             gv[q] = (!kMasked || acc_row_const(mi, r) < lim) ? val : 0.0f;
+            pmax[ni] = fmaxf(pmax[ni], (!kMasked || acc_row_const(mi, r) < lim) ? pm : 0.0f);
             if (kFilter) {
               // Plain form: ignored rows have pr = 0, bad rows NaN.
               const float fv = kGen ? (gsc[ni] != 0.0f ? c1[ni] * pr : 0.0f) : pr;
@@ -303,32 +306,50 @@ __device__ __forceinline__ void store_filter_flag(uint8_t* flags, bool active, i
   if (lane == 0) flags[((int64_t)ti * n_vtiles + j) * 4 + wave] = any ? 1 : 0;
 }
 
-// Dominance check of one stored tile: for each token column ni of this lane,
-// whether its largest logit among the lane's rows (zmax, from
-// grad_store_tile) exceeds the column's threshold.  The rare lane that holds
-// one records, for the row's token, the W row of its first row of the tile
-// plus key_offset: row0 + vloc0.  The threshold, the output pointer and row0
-// are read from LDS (dom: [0] the pointer, [1] row0 without the lane's part
-// lrow), so that they take no registers in the epilogue.
-__device__ __forceinline__ void grad_find_dominant(const float (&zmax)[kNI],
-                                                   const float (*zthr)[kThreads],
-                                                   const int64_t* dom, int tid,
-                                                   int64_t tok0, int wn, int lane, int lrow,
-                                                   int64_t vloc0) {
+// Candidates of a dominant entry in one stored tile: for each token column ni
+// of this lane, whether its largest softmax value among the lane's rows
+// (pmax, from grad_store_tile; 4p with softcap) exceeds 1/2.  That is a
+// superset of the entries above 1/2 + 2^-10: the exact-entry kernel
+// recomputes the candidate tile's logits and keeps an entry only if its logit
+// lies above the row's dominance threshold.  A candidate leaves tile number
+// j + 1 in the lane's LDS slot of the column (an LDS max without return, so
+// the epilogue neither waits nor branches); grad_store_candidates turns the
+// slots into W rows after the sweep.  Rows without a gradient (ignored, bad
+// label) have p = 0 or NaN in the plain form and are never candidates; in the
+// general form the exact-entry kernel drops them.
+template <bool kCapped>
+__device__ __forceinline__ void grad_mark_candidates(const float (&pmax)[kNI],
+                                                     uint32_t (*cand)[kThreads], int tid, int j) {
+  const float thr = kCapped ? 2.0f : 0.5f;
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni)
-    if (zmax[ni] > zthr[ni][tid]) {
+    atomicMax(&cand[ni][tid], pmax[ni] > thr ? (uint32_t)(j + 1) : 0u);
+}
+
+// After the sweep: the W row of the lane's first row of the candidate tile,
+// plus key_offset, for the token of each marked column.  The output pointer
+// and v_begin + key_offset come from LDS (dom: [0], [1]), and tok0 from the
+// token tile ti, so that none of them stays in a register through the sweep.
+__device__ __forceinline__ void grad_store_candidates(const uint32_t (*cand)[kThreads],
+                                                      const int64_t* dom, int tid, int ti, int wn,
+                                                      int lane, int lrow) {
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const uint32_t c = cand[ni][tid];
+    if (c != 0u) {
       int32_t* dom_base = reinterpret_cast<int32_t*>(dom[0]);
-      dom_base[tok0 + acc_col(wn, ni, lane)] = (int32_t)(dom[1] + vloc0 + lrow);
+      dom_base[(int64_t)ti * kTile + acc_col(wn, ni, lane)] =
+          (int32_t)(dom[1] + (int64_t)(c - 1u) * kTile + lrow);
     }
+  }
 }
 
 template <bool kTail, bool kCapped, bool kGen, bool kFilter>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
-  __shared__ float s_zthr[kNI][kThreads];   // dominance threshold per token column
-  __shared__ int64_t s_dom[2];              // dom_base and v_begin + key_offset
+  __shared__ uint32_t s_cand[kNI][kThreads];   // candidate tile + 1 per token column (0: none)
+  __shared__ int64_t s_dom[2];                 // dom_base and v_begin + key_offset
   LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -364,9 +385,6 @@ grad_logits_kernel(GradParams p) {
       gsc[ni] = 1.0f;
       c1[ni] = 1.0f;
     }
-    s_zthr[ni][tid] = dominance_threshold<kCapped>(ok && (kGen ? (gsc[ni] != 0.0f && gsc[ni] == gsc[ni])
-                                                                : st == kRowValid),
-                                                    o, k2, c2, l2a);
     // Blocked G (see DtlKMajorBlockedG): after the lane-half swap of
     // grad_store_tile this lane stores 8 consecutive vocabulary rows of
     // sub-block 2wm + mi/2 at column (mi%2)·32 + 16gp + 8(lane/32) of token
@@ -384,6 +402,8 @@ grad_logits_kernel(GradParams p) {
   const int j_mid = (int)(j1 < full_local ? j1 : (j0 > full_local ? j0 : full_local));
   const int lrow = acc_row_lane(wm, lane);
   // (The first tile's prologue barrier orders these LDS writes before any read.)
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) s_cand[ni][tid] = 0u;
   if (tid == 0) {
     s_dom[0] = reinterpret_cast<int64_t>(p.dom_base);
     s_dom[1] = p.v_begin + p.key_offset;
@@ -400,11 +420,11 @@ grad_logits_kernel(GradParams p) {
     uint32_t cb[kNI];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
-    float zmax[kNI] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    float pmax[kNI] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool act = grad_store_tile<kCapped, false, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                     cb, 0, k2, c2, l2a, p.filter_eps,
-                                                                    zmax);
-    grad_find_dominant(zmax, s_zthr, s_dom, tid, tok0, wn, lane, lrow, vloc0);
+                                                                    pmax);
+    grad_mark_candidates<kCapped>(pmax, s_cand, tid, j);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
   for (int j = j_mid; j < j1; ++j) {
@@ -416,14 +436,16 @@ grad_logits_kernel(GradParams p) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     const int lim = (int)(p.V - v0) - lrow;
-    float zmax[kNI] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    float pmax[kNI] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool act = grad_store_tile<kCapped, true, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
                                                                    cb, lim, k2, c2, l2a, p.filter_eps,
-                                                                   zmax);
-    grad_find_dominant(zmax, s_zthr, s_dom, tid, tok0, wn, lane, lrow, vloc0);
+                                                                   pmax);
+    grad_mark_candidates<kCapped>(pmax, s_cand, tid, j);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();   // s_dom, written by thread 0, is read by every thread
+  grad_store_candidates(s_cand, s_dom, tid, ti, wn, lane, lrow);
 }
 
 // ---------------------------------------------------------------------------
