@@ -120,6 +120,7 @@ def cpu_baseline(w, X, W, y, rows):
                                      w.softcap)
         dW = dW_part if dW is None else dW + dW_part
         dt += time.perf_counter() - t0
+        log(f"[bench] CPU oracle: {min(a + 2048, len(idx))} of {len(idx)} rows, {dt:.1f} s")
     what = ("every token row" if full else
             f"{len(idx)} seeded token rows; the full-batch rate is extrapolated from these rows")
     return {"value": round(len(idx) / dt, 3), "unit": "tokens/s", "cores": int(cores),
@@ -355,6 +356,62 @@ def time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, d
     return out
 
 
+def time_filter_hot(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, fws,
+                    fws_n, bws, bws_n, sptr, stream):
+    """The gradient filter where it keeps blocks: the same shape with hot
+    entries, as the vocabulary-order tests build them (every row gains 2 in
+    hidden unit 0, and 1 in 156 vocabulary entries, seeded and scattered, gain
+    2.5 there, so their logits rise by about 5).  Times the exact step on
+    these inputs, then the filtered step unordered and ordered, each against
+    that exact step.  Leaves dX, dW holding the hot inputs' gradients."""
+    import torch
+    import lce_inputs as L
+    N, H, V = w.N, w.H, w.V
+    n_hot = max(1, V // 156)
+    g = torch.Generator().manual_seed(w.seed + 4242)
+    hot = torch.randperm(V, generator=g)[:n_hot].to(X.device)
+    Xh = X.clone()
+    Xh[:, 0] = (Xh[:, 0].float() + 2.0).to(torch.bfloat16)
+    Wh = W.clone()
+    Wh[hot, 0] = (Wh[hot, 0].float() + 2.5).to(torch.bfloat16)
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+
+    def exact_step():
+        st = lib.lce_forward(Xh.data_ptr(), Wh.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
+                             float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
+                             nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        st = lib.lce_backward(Xh.data_ptr(), Wh.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                              dloss.data_ptr(), N, H, V, L.IGNORE_INDEX, float(w.softcap),
+                              dX.data_ptr(), gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n,
+                              sptr)
+        if st:
+            raise RuntimeError(f"lce_backward: {_lib.status_string(st)}")
+
+    log(f"[bench] hot-entry inputs ({n_hot} hot entries): exact step")
+    for _ in range(args.warmup):
+        exact_step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        exact_step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    exact_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    unordered = time_filtered(lib, _lib, args, w, Xh, Wh, y, loss, lse, mean, nval, bad, dX, dW,
+                              gcode, fws, fws_n, sptr, stream, exact_ms)
+    ordered = time_filtered(lib, _lib, args, w, Xh, Wh, y, loss, lse, mean, nval, bad, dX, dW,
+                            gcode, fws, fws_n, sptr, stream, exact_ms, sort=True)
+    for r in (unordered, ordered):
+        r.pop("regime", None)
+    del Xh, Wh
+    return {"inputs": f"seeded inputs of the same shape with {n_hot} hot vocabulary entries "
+                      "(row mean direction +2 in hidden unit 0, hot entries' weights +2.5 there)",
+            "exact_step_ms": round(exact_ms, 3), "unordered": unordered, "ordered": ordered}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -509,6 +566,11 @@ def main():
         shard = time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, sptr,
                                  stream)
 
+    filter_hot = None
+    if args.filter_eps > 0:
+        filter_hot = time_filter_hot(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX,
+                                     dW, gcode, fws, fws_n, bws, bws_n, sptr, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} rows")
@@ -541,6 +603,7 @@ def main():
         "fused_row_chunk": fused,
         "gradient_filter": filtered,
         "gradient_filter_sorted": filtered_sorted,
+        "gradient_filter_hot_entries": filter_hot,
         "kernels": per_kernel,
         "memory_bytes": {"peak_allocated": int(peak_mem),
                          "inputs": int(X.numel() * 2 + W.numel() * 2 + y.numel() * 8),

@@ -59,6 +59,8 @@ CASES = [
     (128, 192, 640, dict(softcap=30.0)),                           # two-step dW, three-step logits
     (300, 64, 150000, dict()),                                     # one-step logit tiles, 2-3 per split
     (200, 32, 90000, dict(softcap=30.0)),                          # the same with the fixed reference
+    (513, 64, 5, dict()),                                          # a handful of classes
+    (600, 64, 3, dict(softcap=30.0, z_loss=1e-3)),
 ]
 
 

@@ -98,6 +98,10 @@ def test_tiny_config(lce):
     (1, 8, 1, 0.0),             # degenerate: one row, one class
     (300, 64, 9000, 0.0),       # several backward vocabulary chunks, split-K for dX
     (700, 48, 5000, 4.0),       # several chunks with softcap and a short K
+    # A handful of classes: the softmax part is most of each gradient row.
+    (513, 64, 5, 0.0),
+    (513, 64, 3, 30.0),
+    (300, 72, 2, 0.0),
 ])
 def test_irregular_shapes(lce, N, H, V, softcap):
     X, W, y = synth(N, H, V, seed=1000 + N + V, softcap=softcap)
