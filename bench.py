@@ -126,7 +126,7 @@ def cpu_baseline(w, X, W, y, rows):
     return {"value": round(len(idx) / dt, 3), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle", "extrapolated": not full,
             "sample": f"{what} of {w.name} (N={w.N}, H={w.H}, V={w.V}): float64 forward, dX "
-                      f"rows and their dW share in {dt:.1f} s"}
+                      f"rows and their dW share in {dt:.3g} s"}
 
 
 def parity_vs_stored(w, out, dX, dW, X, W, y):

@@ -78,6 +78,51 @@ def confident_case(kind, seed):
 SEEDS = {"softcap_wrong_label": 11, "label_is_top": 12, "label_is_top_softcap": 13}
 
 
+def shared_case(kind, seed):
+    """Rows whose softmax mass is shared by two or three large entries
+    (logit 14 each, the others N(0, 1), V = 20000: p ≈ 0.49 each for two,
+    0.33 for three), with the label one of them or none."""
+    N, V = 300, 20000
+    rng = np.random.default_rng(seed)
+    Z = rng.standard_normal((N, V))
+    k = 3 if kind.startswith("three") else 2
+    tops = np.stack([rng.permutation(V)[:k] for _ in range(N)])
+    for j in range(k):
+        Z[np.arange(N), tops[:, j]] = 14.0
+    y = tops[:, 0].copy() if "label" in kind else rng.integers(0, V, N)
+    return Z, y, (30.0 if kind.endswith("softcap") else 0.0)
+
+
+SHARED = {"two_label": 21, "two_label_softcap": 22, "two_other_softcap": 23,
+          "three_label": 24, "three_label_softcap": 25}
+
+
+@pytest.mark.parametrize("kind", sorted(SHARED))
+def test_shared_rows(lce, kind):
+    """Two or three entries share each row's mass: every one of them above a
+    third of it is taken out of the bf16 chunk with the label's entry."""
+    Z, y, c = shared_case(kind, seed=SHARED[kind])
+    X, W = inputs_with_logits(Z, seed=9)
+    y[::13] = -100
+    yt = torch.from_numpy(y.astype(np.int64))
+    dev = "cuda"
+    out = lce.lce_forward(X.to(dev), W.to(dev), yt.to(dev), -100, c)
+    dX, dW = lce.lce_backward(X.to(dev), W.to(dev), yt.to(dev), out["lse"], 1.0, -100, c)
+    N = len(y)
+    o2, dX2, dW2 = lce.lce_forward_backward(X.to(dev), W.to(dev), yt.to(dev),
+                                            torch.ones(1, device=dev), softcap=c)
+    torch.cuda.synchronize()
+    X64, W64 = L.to_f64(X), L.to_f64(W)
+    f = O.forward(X64, W64, y, -100, c)
+    rdX, rdW = O.backward(X64, W64, y, 1.0, -100, c)
+    p = np.exp(O.apply_softcap(X64 @ W64.T, c) - f["lse"][:, None])
+    p_top = np.sort(p, axis=1)[:, ::-1][:, :3].mean(0)
+    e = [rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW), rel_l2(dX2.cpu(), rdX), rel_l2(dW2.cpu(), rdW)]
+    print(f"[shared] {kind}: mean top-3 p {p_top.round(3)} recompute dX {e[0]:.2e} dW {e[1]:.2e} "
+          f"fused dX {e[2]:.2e} dW {e[3]:.2e}", flush=True)
+    assert max(e) <= GRAD_RTOL
+
+
 @pytest.mark.parametrize("kind", sorted(SEEDS))
 def test_confident_rows(lce, kind):
     Z, y, c = confident_case(kind, seed=SEEDS[kind])
