@@ -53,6 +53,8 @@ def parse():
                     help="also time one vocabulary shard of V/shards rows (0: skip)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip timing the row-chunked forward-and-backward call")
+    ap.add_argument("--no-precise", action="store_true",
+                    help="skip timing the step with the precise (two-part) gradient")
     ap.add_argument("--filter-eps", type=float, default=2.0 ** -12,
                     help="also time the step with the (non-exact) gradient filter (0: skip)")
     return ap.parse_args()
@@ -220,6 +222,58 @@ def time_vocab_shard(lib, _lib, args, w, X, W, y, lse, dX, dW, gcode, fws, bws, 
             "tokens_per_s": round(N / (ms / 1e3), 1), "tflops": round(tf, 1),
             "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4),
             "note": "one rank's shard forward + shard backward, collectives excluded"}
+
+
+def time_precise(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, fws,
+                 fws_n, bws, bws_n, sptr, stream, step_ms_exact):
+    """The step with the precise gradient (lce_options.precise: the gradient
+    chunk carried as two bf16 parts, both contractions run on each), and how
+    far its gradients are from the default step's."""
+    import ctypes
+    import torch
+    import lce_inputs as L
+    N, H, V = w.N, w.H, w.V
+    opt = _lib.make_options(L.IGNORE_INDEX, float(w.softcap), precise=True)
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+    dXd, dWd = dX.clone(), dW.clone()   # the default step's gradients
+
+    def pstep():
+        st = lib.lce_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
+                             float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
+                             nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        st = lib.lce_backward_ex(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                                 dloss.data_ptr(), N, H, V, ctypes.byref(opt), dX.data_ptr(),
+                                 gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n, sptr)
+        if st:
+            raise RuntimeError(f"lce_backward_ex: {_lib.status_string(st)}")
+
+    log("[bench] step with the precise gradient")
+    for _ in range(args.warmup):
+        pstep()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        pstep()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+
+    def rel(a, b):
+        return float(torch.linalg.vector_norm((a.float() - b.float()).ravel()) /
+                     torch.linalg.vector_norm(b.float().ravel()))
+    out = {"ms_per_step": round(ms, 3), "tokens_per_s": round(N / (ms / 1e3), 1),
+           "slowdown_vs_default_step": round(ms / step_ms_exact, 3),
+           "dX_rel_l2_default_vs_precise": rel(dXd, dX), "dW_rel_l2_default_vs_precise": rel(dWd, dW),
+           "note": "lce_backward_ex with precise = 1: the gradient chunk as hi + lo bf16 parts, "
+                   "chunks half as wide, both contractions on each part (12·N·H·V flops per step); "
+                   "not the headline path"}
+    dX.copy_(dXd)
+    dW.copy_(dWd)
+    del dXd, dWd
+    return out
 
 
 def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, sptr,
@@ -556,6 +610,11 @@ def main():
                                         dX, dW, gcode, fws, fws_n, sptr, stream, ms_per_step,
                                         sort=True)
 
+    precise = None
+    if not args.no_precise:
+        precise = time_precise(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW,
+                               gcode, fws, fws_n, bws, bws_n, sptr, stream, ms_per_step)
+
     fused = None
     if not args.no_fused:
         fused = time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode,
@@ -601,6 +660,7 @@ def main():
         "cpu_baseline": cpu,
         "vocab_shard": shard,
         "fused_row_chunk": fused,
+        "precise_gradient": precise,
         "gradient_filter": filtered,
         "gradient_filter_sorted": filtered_sorted,
         "gradient_filter_hot_entries": filter_hot,

@@ -152,6 +152,8 @@ typedef struct {
   int32_t reduction;      /* an lce_reduction (default LCE_REDUCE_MEAN) */
   float filter_eps;       /* gradient filter threshold, finite and >= 0 (default 0:
                              exact).  See below. */
+  int32_t precise;        /* 1: the softmax part of dZ is carried as two bf16
+                             parts (default 0).  See below. */
 } lce_options;
 
 /*
@@ -167,6 +169,23 @@ typedef struct {
  * logits still runs in full and the one-hot term is always applied exactly.
  * Not combined with label smoothing (LCE_ERR_INVALID_ARG); lce_forward_backward
  * refuses filter_eps > 0; the forward calls ignore it.
+ */
+
+/*
+ * Precise gradient (opt-in).  The backward carries the softmax part of dZ,
+ * softmax·(1 − tanh²) times the row factors, through a bf16 chunk: each value
+ * is rounded to 2^-9 of itself.  The label's entry and an entry above half of
+ * its row's softmax mass are applied in float32 (they skip the chunk), which
+ * keeps ordinary and confident rows far inside the float32 bar; a row whose
+ * gradient is carried by a few mid-sized entries (two or three entries near
+ * 1/2 or 1/3 of the mass, or a tiny vocabulary) shows the rounding at about
+ * 1e-3 relative.  With precise = 1, lce_backward_ex, lce_backward_sorted and
+ * lce_shard_backward store each value as hi = bf16(g) and lo = bf16(g − hi)
+ * (about 16 significant bits) and run both gradient contractions on each
+ * part: the contractions cost twice as much, and the workspace sizes the
+ * queries return hold both parts (each vocabulary chunk is half as wide).
+ * Not combined with filter_eps > 0 (LCE_ERR_INVALID_ARG); lce_forward_backward
+ * refuses it; the forward calls ignore it.  precise must be 0 or 1.
  */
 
 /* Fill *opt with the defaults listed above (host call). */

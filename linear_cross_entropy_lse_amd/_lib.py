@@ -46,17 +46,18 @@ class Options(ctypes.Structure):
     _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
                 ("logit_scale", ctypes.c_float), ("label_smoothing", ctypes.c_float),
                 ("z_loss", ctypes.c_float), ("reduction", ctypes.c_int32),
-                ("filter_eps", ctypes.c_float)]
+                ("filter_eps", ctypes.c_float), ("precise", ctypes.c_int32)]
 
 
 def make_options(ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
                  label_smoothing: float = 0.0, z_loss: float = 0.0,
-                 reduction: str = "mean", filter_eps: float = 0.0) -> Options:
+                 reduction: str = "mean", filter_eps: float = 0.0,
+                 precise: bool = False) -> Options:
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}, got {reduction!r}")
     return Options(int(ignore_index), float(softcap), float(logit_scale),
                    float(label_smoothing), float(z_loss), REDUCTIONS[reduction],
-                   float(filter_eps))
+                   float(filter_eps), int(bool(precise)))
 
 
 class KernelTiming(ctypes.Structure):
@@ -334,12 +335,13 @@ def lce_forward_ex(X, W, labels, ignore_index: int = -100, softcap: float = 0.0,
 def lce_backward_ex(X, W, labels, lse, dloss, ignore_index: int = -100, softcap: float = 0.0,
                     logit_scale: float = 1.0, label_smoothing: float = 0.0, z_loss: float = 0.0,
                     reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
-                    filter_eps: float = 0.0):
+                    filter_eps: float = 0.0, precise: bool = False):
     """Backward with the loss variants.  `dloss`: a scalar (mean, sum) or an
     [N] tensor of per-row upstream gradients (none).  filter_eps > 0 turns on
-    the (non-exact) gradient filter.  Returns (dX, dW)."""
+    the (non-exact) gradient filter; precise=True carries the gradient chunk
+    as two bf16 parts (twice the contraction work).  Returns (dX, dW)."""
     opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
-                       filter_eps)
+                       filter_eps, precise)
     return _backward_with_options(X, W, labels, lse, dloss, opt, reduction, dX_dtype, dW_dtype,
                                   workspace, None)
 
@@ -348,13 +350,13 @@ def lce_backward_sorted(X, W, labels, lse, dloss, order, ignore_index: int = -10
                         softcap: float = 0.0, logit_scale: float = 1.0,
                         label_smoothing: float = 0.0, z_loss: float = 0.0,
                         reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
-                        filter_eps: float = 0.0):
+                        filter_eps: float = 0.0, precise: bool = False):
     """lce_backward_ex on the vocabulary reordered by `order` (an int32 device
     permutation of [0, V), e.g. from lce_vocab_order); dW rows come back in
     entry order.  Returns (dX, dW)."""
     import torch
     opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
-                       filter_eps)
+                       filter_eps, precise)
     if not (torch.is_tensor(order) and order.is_cuda and order.dtype == torch.int32
             and order.dim() == 1 and order.shape[0] == W.shape[0]):
         raise ValueError("order must be an int32 device tensor of shape [V]")
@@ -503,12 +505,12 @@ def lce_shard_backward(X, W_shard, labels, lse, dloss, vocab_offset: int, vocab_
                        ignore_index: int = -100, softcap: float = 0.0, logit_scale: float = 1.0,
                        label_smoothing: float = 0.0, z_loss: float = 0.0,
                        reduction: str = "mean", dX_dtype=None, dW_dtype=None, workspace=None,
-                       filter_eps: float = 0.0):
+                       filter_eps: float = 0.0, precise: bool = False):
     """Backward of one vocabulary shard given the merged LSE.  Returns
     (dX share [N, H], dW rows of the shard [V_shard, H])."""
     import torch
     opt = make_options(ignore_index, softcap, logit_scale, label_smoothing, z_loss, reduction,
-                       filter_eps)
+                       filter_eps, precise)
     X, W_shard, labels = _prep(X, W_shard, labels)
     N, H = X.shape
     Vs = W_shard.shape[0]

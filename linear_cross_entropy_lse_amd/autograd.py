@@ -15,13 +15,13 @@ from . import _lib
 class LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, X, W, labels, ignore_index=-100, softcap=0.0, logit_scale=1.0,
-                label_smoothing=0.0, z_loss=0.0, reduction="mean", filter_eps=0.0):
+                label_smoothing=0.0, z_loss=0.0, reduction="mean", filter_eps=0.0, precise=False):
         opts = dict(ignore_index=int(ignore_index), softcap=float(softcap),
                     logit_scale=float(logit_scale), label_smoothing=float(label_smoothing),
                     z_loss=float(z_loss), reduction=reduction)
         out = _lib.lce_forward_ex(X, W, labels, **opts)
         ctx.save_for_backward(X, W, labels, out["lse"])
-        ctx.opts = dict(opts, filter_eps=float(filter_eps))
+        ctx.opts = dict(opts, filter_eps=float(filter_eps), precise=bool(precise))
         return out["loss"] if reduction == "none" else out["reduced"]
 
     @staticmethod
@@ -29,16 +29,17 @@ class LinearCrossEntropy(torch.autograd.Function):
         X, W, labels, lse = ctx.saved_tensors
         dX, dW = _lib.lce_backward_ex(X, W, labels, lse, grad.float(), dX_dtype=X.dtype,
                                       dW_dtype=W.dtype, **ctx.opts)
-        return dX, dW, None, None, None, None, None, None, None, None
+        return dX, dW, None, None, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(X, W, labels, ignore_index: int = -100, softcap: float = 0.0,
                          logit_scale: float = 1.0, label_smoothing: float = 0.0,
                          z_loss: float = 0.0, reduction: str = "mean",
-                         filter_eps: float = 0.0):
+                         filter_eps: float = 0.0, precise: bool = False):
     """Cross-entropy of X·Wᵀ over pre-shifted labels without the logits: the
     mean over valid targets (or the sum, or the per-row losses for
     reduction="none") of LSE − (1 − e)·z_y − (e/V)·Σ z + l·LSE².  filter_eps > 0
-    turns on the non-exact gradient filter of the backward."""
+    turns on the non-exact gradient filter of the backward; precise=True its
+    two-part gradient chunk."""
     return LinearCrossEntropy.apply(X, W, labels, ignore_index, softcap, logit_scale,
-                                    label_smoothing, z_loss, reduction, filter_eps)
+                                    label_smoothing, z_loss, reduction, filter_eps, precise)

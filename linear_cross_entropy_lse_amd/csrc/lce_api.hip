@@ -36,7 +36,8 @@ bool options_ok(const lce_options* o) {
                       std::isfinite(o->filter_eps);
   return finite && o->logit_scale > 0.0f && o->label_smoothing >= 0.0f &&
          o->label_smoothing <= 1.0f && o->z_loss >= 0.0f && o->reduction >= LCE_REDUCE_MEAN &&
-         o->reduction <= LCE_REDUCE_NONE && o->filter_eps >= 0.0f;
+         o->reduction <= LCE_REDUCE_NONE && o->filter_eps >= 0.0f &&
+         (o->precise == 0 || o->precise == 1);
 }
 
 bool shape_ok(int64_t N, int64_t H, int64_t V) {
@@ -108,11 +109,14 @@ struct BwdPlan {
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
 // (N·Vc ≤ V·H), with a floor of 4096 columns; chunks are multiples of 256 so
-// tiles never straddle two chunks.  With a vocabulary order (`sorted`) the
+// tiles never straddle two chunks.  `precise`: the chunk holds two bf16 parts
+// (hi, lo) at half the width each (the workspace queries return the larger of
+// the two plans).  With a vocabulary order (`sorted`) the
 // chunk's W rows are gathered into position order (Wp), its dW rows go through
 // the fp32 chunk buffer, and the label keys are moved to positions (pos1,
 // pkey).
-BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool sorted = false) {
+BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool sorted = false,
+                      bool precise = false) {
   BwdPlan p{};
   const int64_t Nc = std::max<int64_t>(N, 1);
   p.T = (int)ceil_div(Nc, kTile);
@@ -120,6 +124,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   // At most 2^21 columns, so a 256-row block of a chunk spans < 2^31 bytes
   // (the 32-bit buffer offsets of the gradient kernels).
   vc = std::min<int64_t>(vc, (int64_t)1 << 21);
+  if (precise) vc /= 2;
   vc = std::max<int64_t>(kTile, vc / kTile * kTile);
   p.nchunks = (int)ceil_div(V, vc);
   p.Vc = ceil_div(ceil_div(V, p.nchunks), kTile) * kTile;
@@ -154,8 +159,10 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   p.off_dkeys_b = o; o = align_up(o + sizeof(uint64_t) * (size_t)sort_padded(N));
   p.off_dcounts = o; o = align_up(o + 16);
   p.off_flags = o;   o = align_up(o + sizeof(uint32_t) * (size_t)p.T * (size_t)p.n_vtiles_chunk);
-  // Blocked gradient chunk: T token tiles (padded) x Vc columns.
-  p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.T * kTile * (size_t)p.ldg);
+  // Blocked gradient chunk: T token tiles (padded) x Vc columns; with
+  // `precise` its lo part follows at G + T·256·ldg.
+  p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.T * kTile * (size_t)p.ldg *
+                                      (precise ? 2 : 1));
   p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
   p.off_dWs = o;
   if (dW_dtype == LCE_BF16 || sorted) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
@@ -471,7 +478,8 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
                          void* dX_dev, lce_dtype dX_dtype, void* dW_dev, lce_dtype dW_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* stream_ptr) {
   if (!options_ok(opt)) return LCE_ERR_INVALID_ARG;
-  if (opt->filter_eps > 0.0f && opt->label_smoothing > 0.0f) return LCE_ERR_INVALID_ARG;
+  if (opt->filter_eps > 0.0f && (opt->label_smoothing > 0.0f || opt->precise))
+    return LCE_ERR_INVALID_ARG;
   if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
     return LCE_ERR_INVALID_ARG;
   if (!dW_dev) return LCE_ERR_INVALID_ARG;
@@ -489,7 +497,8 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     return LCE_OK;
   }
   const bool sorted = order != nullptr;
-  const BwdPlan pl = plan_backward(N, H, V, dW_dtype, sorted);
+  const bool precise = opt->precise != 0;
+  const BwdPlan pl = plan_backward(N, H, V, dW_dtype, sorted, precise);
   if (workspace_bytes < pl.total) return LCE_ERR_WORKSPACE;
 
   int32_t* state = at<int32_t>(workspace_dev, pl.off_state);
@@ -507,6 +516,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   float* scalars = at<float>(workspace_dev, pl.off_scalars);       // [0] plain scale, [1] = 1
   int32_t* counts = at<int32_t>(workspace_dev, pl.off_scalars + 8);
   uint16_t* G = at<uint16_t>(workspace_dev, pl.off_G);
+  uint16_t* G_lo = precise ? G + (size_t)pl.T * kTile * (size_t)pl.ldg : nullptr;
   uint32_t* flags = opt->filter_eps > 0.0f ? at<uint32_t>(workspace_dev, pl.off_flags) : nullptr;
   float* dXp = at<float>(workspace_dev, pl.off_dXp);
   float* dWs = at<float>(workspace_dev, pl.off_dWs);
@@ -584,6 +594,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);
     gp.flags = reinterpret_cast<uint8_t*>(flags); gp.filter_eps = opt->filter_eps;
     gp.dom_base = dom_base; gp.key_offset = sorted ? v_begin : 0;
+    gp.G_lo = G_lo;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
     ExactParams ep{};
     ep.X = X; ep.W = Wsrc; ep.N = N; ep.H = H; ep.V = w_rows;
@@ -592,7 +603,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     ep.lse = lse_dev; ep.row_state = state; ep.row_key = lab_key;
     ep.gs = general ? gs : nullptr; ep.c1 = c1;
     ep.eps_over_v = gp.eps_over_v; ep.one_minus_eps = 1.0f - opt->label_smoothing;
-    ep.dom_base = dom_base; ep.G = G;
+    ep.dom_base = dom_base; ep.G = G; ep.G_lo = G_lo;
     ep.lab_dense = lab_dense; ep.lab_oh = lab_oh; ep.dom_col = dom_col; ep.dom_coef = dom_coef;
     LCE_LAUNCH("exact_entries", stream, launch_exact_entries(ep, stream));
     // With the filter, exact dense values whose block is skipped are dropped.
@@ -609,6 +620,11 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
     cp.dW_dst = dW_dtype == LCE_F32 && !sorted ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
+    if (precise) {
+      // The lo part through the same contractions, added to both results.
+      cp.G = G_lo; cp.accumulate = 1; cp.dw_accumulate = 1;
+      LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
+    }
     if (sorted || dW_dtype == LCE_BF16) {
       // This chunk's dW rows are final once corrected: the exact entries of
       // its labels and dominant entries are all known now.
@@ -764,7 +780,8 @@ size_t lce_forward_workspace_bytes(int64_t N, int64_t H, int64_t V) {
 
 size_t lce_backward_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   if (!shape_ok(N, H, V) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16)) return 0;
-  return plan_backward(N, H, V, dW_dtype).total;
+  return std::max(plan_backward(N, H, V, dW_dtype).total,
+                  plan_backward(N, H, V, dW_dtype, false, true).total);
 }
 
 void lce_options_default(lce_options* opt) {
@@ -776,6 +793,7 @@ void lce_options_default(lce_options* opt) {
   opt->z_loss = 0.0f;
   opt->reduction = LCE_REDUCE_MEAN;
   opt->filter_eps = 0.0f;
+  opt->precise = 0;
 }
 
 lce_status lce_forward(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
@@ -893,7 +911,8 @@ lce_status lce_backward_ex(const void* X_dev, const void* W_dev, const int64_t* 
 
 size_t lce_backward_sorted_workspace_bytes(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   if (!shape_ok(N, H, V) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16)) return 0;
-  return plan_backward(N, H, V, dW_dtype, true).total;
+  return std::max(plan_backward(N, H, V, dW_dtype, true).total,
+                  plan_backward(N, H, V, dW_dtype, true, true).total);
 }
 
 lce_status lce_backward_sorted(const void* X_dev, const void* W_dev, const int64_t* labels_dev,
@@ -976,7 +995,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
   // Label smoothing needs the softcap derivative apart from the softmax,
   // which the stored logits block does not keep.
   if (opt->label_smoothing > 0.0f && opt->softcap > 0.0f) return LCE_ERR_INVALID_ARG;
-  if (opt->filter_eps > 0.0f) return LCE_ERR_INVALID_ARG;
+  if (opt->filter_eps > 0.0f || opt->precise) return LCE_ERR_INVALID_ARG;
   if ((dX_dtype != LCE_F32 && dX_dtype != LCE_BF16) || (dW_dtype != LCE_F32 && dW_dtype != LCE_BF16))
     return LCE_ERR_INVALID_ARG;
   if (N > 0 && (!X_dev || !W_dev || !labels_dev || !dloss_dev || !loss_dev || !lse_dev ||

@@ -120,6 +120,8 @@ exact_entries_kernel(ExactParams p) {
   // What G holds for a logit of −inf: 0, or −gsc·e/V without softcap.
   const float vinf = (!kCapped && kGen) ? -gsc * p.eps_over_v : 0.0f;
   const uint16_t vinf_bits = (uint16_t)f32_to_bf16_bits(vinf);
+  // Its lo part, for a chunk carried as two bf16 parts.
+  const uint16_t vinf_lo = (uint16_t)f32_to_bf16_bits(vinf - bf16_bits_to_f32(vinf_bits));
 
   // ---- the label's entry: the block's diagonal C[j][j] = x_j · w_{y_j} ----
   const int32_t key = (in && st == kRowValid) ? p.row_key[tok] : INT32_MAX;
@@ -136,7 +138,9 @@ exact_entries_kernel(ExactParams p) {
       const float val = grad_value<kCapped, kGen>(z, off, gsc, c1, p.eps_over_v, k2, c2, l2a, pr, d);
       p.lab_dense[tok] = val - vinf;
       p.lab_oh[tok] = (kGen ? gsc : 1.0f) * p.one_minus_eps * d;
-      p.G[g_offset(tok, wrow - c_lo, p.n_vtiles)] = vinf_bits;
+      const int64_t g = g_offset(tok, wrow - c_lo, p.n_vtiles);
+      p.G[g] = vinf_bits;
+      if (p.G_lo) p.G_lo[g] = vinf_lo;
     }
   }
 
@@ -212,7 +216,9 @@ exact_entries_kernel(ExactParams p) {
       const float val = grad_value<kCapped, kGen>(best, off, gsc, c1, p.eps_over_v, k2, c2, l2a, pr, d);
       p.dom_col[tj] = (int32_t)(best_row + p.key_offset);
       p.dom_coef[tj] = val - vinf;
-      p.G[g_offset(tj, best_row - c_lo, p.n_vtiles)] = vinf_bits;
+      const int64_t g = g_offset(tj, best_row - c_lo, p.n_vtiles);
+      p.G[g] = vinf_bits;
+      if (p.G_lo) p.G_lo[g] = vinf_lo;
     }
   }
 }

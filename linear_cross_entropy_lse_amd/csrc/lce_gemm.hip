@@ -240,11 +240,14 @@ lse_partials_kernel(LseParams p) {
 // (mi%2)·32 + 16gp (+ 8 from the lane half, carried by cb).
 // pmax[ni] gathers the largest softmax value of each token column among the
 // lane's rows, times 4 with softcap (for the dominance check,
-// grad_find_dominant).
-template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false>
+// grad_mark_candidates).
+// kSplit (precise gradient): each value g is stored as hi = bf16(g) through
+// rs and lo = bf16(g − hi) through rs_lo, at the same offsets.
+template <bool kCapped, bool kMasked, bool kGen, bool kFilter = false, bool kSplit = false>
 __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], const float (&off)[kNI],
                                                 const float (&gsc)[kNI], const float (&c1)[kNI],
                                                 float eps_v, __amdgpu_buffer_rsrc_t rs,
+                                                __amdgpu_buffer_rsrc_t rs_lo,
                                                 const uint32_t (&cb)[kNI], int lim, float k2,
                                                 float c2, float l2a, float feps,
                                                 float (&pmax)[kNI]) {
@@ -255,7 +258,7 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        u32x2 pk[2];
+        u32x2 pk[2], lo[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int gq = 2 * gp + h;
@@ -288,12 +291,24 @@ __device__ __forceinline__ bool grad_store_tile(const f32x16 (&acc)[kMI][kNI], c
           }
           pk[h][0] = pack_bf16x2(gv[0], gv[1]);
           pk[h][1] = pack_bf16x2(gv[2], gv[3]);
+          if (kSplit) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              lo[h][e] = pack_bf16x2(gv[2 * e] - __uint_as_float(pk[h][e] << 16),
+                                     gv[2 * e + 1] - __uint_as_float(pk[h][e] & 0xffff0000u));
+          }
         }
+        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 16 * gp);
         const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
         const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
-        const uint32_t eo = (uint32_t)((mi >> 1) * kGSubElems + (mi & 1) * 32 + 16 * gp);
         __builtin_amdgcn_raw_buffer_store_b128(out, rs, (int)(cb[ni] + 2u * eo), 0, 0);
+        if (kSplit) {
+          const auto t0 = __builtin_amdgcn_permlane32_swap(lo[0][0], lo[1][0], false, false);
+          const auto t1 = __builtin_amdgcn_permlane32_swap(lo[0][1], lo[1][1], false, false);
+          const u32x4 out_lo = {t0[0], t1[0], t0[1], t1[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(out_lo, rs_lo, (int)(cb[ni] + 2u * eo), 0, 0);
+        }
       }
   return active;
 }
@@ -344,7 +359,7 @@ __device__ __forceinline__ void grad_store_candidates(const uint32_t (*cand)[kTh
   }
 }
 
-template <bool kTail, bool kCapped, bool kGen, bool kFilter>
+template <bool kTail, bool kCapped, bool kGen, bool kFilter, bool kSplit = false>
 __global__ void __launch_bounds__(kThreads, 1)
 grad_logits_kernel(GradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * kStageElems];
@@ -395,6 +410,9 @@ grad_logits_kernel(GradParams p) {
   // the dW contraction reads).
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + (int64_t)ti * p.n_vtiles * kGBlockElems,
                                               p.n_vtiles * kGBlockElems * 2);
+  const __amdgpu_buffer_rsrc_t rs_lo =
+      kSplit ? make_rsrc(p.G_lo + (int64_t)ti * p.n_vtiles * kGBlockElems, p.n_vtiles * kGBlockElems * 2)
+             : rs;
 
   // Chunk-local tiles j < j_mid lie below V; the tile that reaches past V (at
   // most one) runs in a loop of its own with the masked store.
@@ -421,9 +439,8 @@ grad_logits_kernel(GradParams p) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     float pmax[kNI] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bool act = grad_store_tile<kCapped, false, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
-                                                                    cb, 0, k2, c2, l2a, p.filter_eps,
-                                                                    pmax);
+    const bool act = grad_store_tile<kCapped, false, kGen, kFilter, kSplit>(
+        acc, off, gsc, c1, p.eps_over_v, rs, rs_lo, cb, 0, k2, c2, l2a, p.filter_eps, pmax);
     grad_mark_candidates<kCapped>(pmax, s_cand, tid, j);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
@@ -437,9 +454,8 @@ grad_logits_kernel(GradParams p) {
     for (int ni = 0; ni < kNI; ++ni) cb[ni] = col_base[ni] + (uint32_t)(j * kGBlockElems * 2);
     const int lim = (int)(p.V - v0) - lrow;
     float pmax[kNI] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bool act = grad_store_tile<kCapped, true, kGen, kFilter>(acc, off, gsc, c1, p.eps_over_v, rs,
-                                                                   cb, lim, k2, c2, l2a, p.filter_eps,
-                                                                   pmax);
+    const bool act = grad_store_tile<kCapped, true, kGen, kFilter, kSplit>(
+        acc, off, gsc, c1, p.eps_over_v, rs, rs_lo, cb, lim, k2, c2, l2a, p.filter_eps, pmax);
     grad_mark_candidates<kCapped>(pmax, s_cand, tid, j);
     if (kFilter) store_filter_flag(p.flags, act, ti, j, p.n_vtiles, wave, lane);
   }
@@ -950,23 +966,26 @@ hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream) {
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
   const int grid = p.T * p.S;
   const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f, gen = p.gs != nullptr;
-  const bool filt = p.flags != nullptr;
-  if (!p.dom_base) return hipErrorInvalidValue;
-#define LCE_GRAD_LAUNCH(T_, C_, G_, F_) \
-  hipLaunchKernelGGL((grad_logits_kernel<T_, C_, G_, F_>), dim3(grid), dim3(kThreads), 0, stream, p)
-#define LCE_GRAD_TC(G_, F_)                                   \
-  do {                                                        \
-    if (tail && capped) LCE_GRAD_LAUNCH(true, true, G_, F_);  \
-    else if (tail) LCE_GRAD_LAUNCH(true, false, G_, F_);      \
-    else if (capped) LCE_GRAD_LAUNCH(false, true, G_, F_);    \
-    else LCE_GRAD_LAUNCH(false, false, G_, F_);               \
+  const bool filt = p.flags != nullptr, split = p.G_lo != nullptr;
+  if (!p.dom_base || (filt && split)) return hipErrorInvalidValue;
+#define LCE_GRAD_LAUNCH(T_, C_, G_, F_, S_) \
+  hipLaunchKernelGGL((grad_logits_kernel<T_, C_, G_, F_, S_>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define LCE_GRAD_TC(G_, F_, S_)                                   \
+  do {                                                            \
+    if (tail && capped) LCE_GRAD_LAUNCH(true, true, G_, F_, S_);  \
+    else if (tail) LCE_GRAD_LAUNCH(true, false, G_, F_, S_);      \
+    else if (capped) LCE_GRAD_LAUNCH(false, true, G_, F_, S_);    \
+    else LCE_GRAD_LAUNCH(false, false, G_, F_, S_);               \
   } while (0)
   if (filt) {
-    if (gen) LCE_GRAD_TC(true, true);
-    else LCE_GRAD_TC(false, true);
+    if (gen) LCE_GRAD_TC(true, true, false);
+    else LCE_GRAD_TC(false, true, false);
+  } else if (split) {
+    if (gen) LCE_GRAD_TC(true, false, true);
+    else LCE_GRAD_TC(false, false, true);
   } else {
-    if (gen) LCE_GRAD_TC(true, false);
-    else LCE_GRAD_TC(false, false);
+    if (gen) LCE_GRAD_TC(true, false, false);
+    else LCE_GRAD_TC(false, false, false);
   }
 #undef LCE_GRAD_TC
 #undef LCE_GRAD_LAUNCH

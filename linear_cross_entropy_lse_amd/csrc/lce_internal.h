@@ -54,6 +54,9 @@ struct GradParams {
   // −1).  launch_exact_entries turns it into the entry.
   int32_t* dom_base;
   int64_t key_offset;
+  // Precise gradient: when not null, G holds hi = bf16(g) and G_lo, in the
+  // same layout, lo = bf16(g − hi).  Not with flags.
+  uint16_t* G_lo;
 };
 
 // dX and dW contractions of one vocabulary chunk, in one persistent launch of
@@ -159,6 +162,7 @@ struct ExactParams {
   const int32_t* cand_b;
   int cand_splits;
   uint16_t* G;                // blocked chunk, as GradParams::G
+  uint16_t* G_lo;             // its lo part (precise gradient), or null
   float* lab_dense;
   float* lab_oh;
   int32_t* dom_col;

@@ -228,6 +228,23 @@ def test_filter_option_checks(lib):
     assert opts().filter_eps == 0.0
 
 
+def test_precise_option_checks(lib):
+    assert opts().precise == 0
+    for bad in (2, -1):
+        o = opts(precise=bad)
+        assert fwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+        assert bwd_ex(lib, ctypes.byref(o)) == _lib.LCE_ERR_INVALID_ARG
+    # Not with the gradient filter, and not in the fused call.
+    both = opts(precise=1, filter_eps=2.0 ** -12)
+    assert bwd_ex(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
+    assert fused(lib, ctypes.byref(opts(precise=1))) == _lib.LCE_ERR_INVALID_ARG
+    # The workspace the query returns holds the two-part chunk too: the
+    # precise backward gets past its workspace check and stops at the device
+    # (no GPU here), like the plain one.
+    o = opts(precise=1)
+    assert bwd_ex(lib, ctypes.byref(o)) == bwd_ex(lib, ctypes.byref(opts()))
+
+
 def order_call(lib, X=FAKE, W=FAKE, y=FAKE, N=4, H=8, V=5, mean=FAKE, order=FAKE, ws=FAKE,
                wsb=None):
     if wsb is None:
@@ -287,8 +304,9 @@ def test_sorted_backward_workspace_and_argument_checks(lib):
     assert sorted_bwd(lib, ok, X=FAKE + 8) == _lib.LCE_ERR_ALIGNMENT
     both = opts(filter_eps=2.0 ** -12, label_smoothing=0.1)
     assert sorted_bwd(lib, ctypes.byref(both)) == _lib.LCE_ERR_INVALID_ARG
-    # The plain backward's workspace is too small for the sorted one.
-    assert sorted_bwd(lib, ok, wsb=lib.lce_backward_workspace_bytes(4, 8, 5, 0)) == \
+    # A workspace below what the sorted backward needs (its chunk buffers) is
+    # refused before any launch.
+    assert sorted_bwd(lib, ok, wsb=lib.lce_backward_sorted_workspace_bytes(4, 8, 5, 0) // 4) == \
         _lib.LCE_ERR_WORKSPACE
 
 

@@ -1,0 +1,128 @@
+"""The precise gradient (lce_options.precise): the softmax part of dZ carried as
+two bf16 parts, hi = bf16(g) and lo = bf16(g − hi), through both gradient
+contractions.
+
+The gradient is softmax − onehot (blog "最贵的一层：深入浅出 Liger Kernel 与 Cut
+Cross-Entropy", §二; AI-infra KB M011 §06) times the softcap derivative
+(Unsloth fused cross-entropy chapter, §4); precise mode changes only how many
+bits of its softmax part reach the contractions, so every case is checked
+against the same float64 oracle as the default path, at the float32 bar, and
+must come out at least ten times closer than the default path wherever the
+default path's error is above 1e-4 (the bf16 rounding of the chunk is then
+what it measures).
+
+Cases: a handful of classes (the softmax part is most of each row), the
+loss variants with per-row factors, bf16 outputs, several vocabulary chunks
+with ragged tails, one-step tiles (H = 64), a vocabulary order, and a
+vocabulary shard; plus the refusals (with the filter, in the fused call).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lce_inputs as L
+from oracle import lce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+GRAD_RTOL = 1e-3
+GRAD_RTOL_BF16 = 1e-2
+
+
+@pytest.fixture(scope="module")
+def lce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_lse_amd as P
+    P.load()
+    return P
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+CASES = [
+    # N, H, V, W scale, options
+    (513, 64, 5, 4.0, dict()),
+    (600, 72, 3, 4.0, dict(softcap=30.0)),
+    (300, 64, 2, 4.0, dict(z_loss=1e-2, reduction="none")),
+    (700, 48, 5000, 4.0, dict(softcap=4.0)),                      # several chunks, short K
+    (300, 64, 9000, 4.0, dict(label_smoothing=0.1, reduction="sum")),
+    (257, 136, 1003, 4.0, dict(logit_scale=1.3, z_loss=1e-3)),   # K tail, ragged rows
+]
+
+
+def run_case(lce, N, H, V, scale, opts, seed, precise, dtype=torch.float32):
+    w = L.Workload("precise", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1, seed=seed)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * scale).to(torch.bfloat16)
+    red = opts.get("reduction", "mean")
+    rng = np.random.default_rng(seed)
+    dloss = rng.standard_normal(N).astype(np.float32) if red == "none" else np.float32(0.8)
+    dev = "cuda"
+    out = lce.lce_forward_ex(X.to(dev), W.to(dev), y.to(dev), **opts)
+    dX, dW = lce.lce_backward_ex(X.to(dev), W.to(dev), y.to(dev), out["lse"],
+                                 torch.from_numpy(np.atleast_1d(dloss)).to(dev),
+                                 dX_dtype=dtype, dW_dtype=dtype, precise=precise, **opts)
+    torch.cuda.synchronize()
+    o = O.options(**opts)
+    rdX, rdW = O.backward_ex(L.to_f64(X), L.to_f64(W), y.numpy(),
+                             dloss.astype(np.float64) if red == "none" else 0.8, o)
+    return rel_l2(dX.float().cpu(), rdX), rel_l2(dW.float().cpu(), rdW)
+
+
+@pytest.mark.parametrize("N,H,V,scale,opts", CASES)
+def test_precise_against_oracle(lce, N, H, V, scale, opts):
+    seed = 9100 + N + V
+    print(f"[precise] N={N} H={H} V={V} {opts}", flush=True)
+    d = run_case(lce, N, H, V, scale, opts, seed, precise=False)
+    p = run_case(lce, N, H, V, scale, opts, seed, precise=True)
+    print(f"[precise] default dX {d[0]:.2e} dW {d[1]:.2e} | precise dX {p[0]:.2e} dW {p[1]:.2e}",
+          flush=True)
+    assert max(p) <= GRAD_RTOL
+    for a, b in zip(d, p):
+        if a > 1e-4:
+            assert b <= 0.1 * a, (a, b)
+
+
+def test_precise_bf16_outputs(lce):
+    d = run_case(lce, 400, 64, 7, 4.0, dict(softcap=30.0), 9300, precise=True,
+                 dtype=torch.bfloat16)
+    print(f"[precise] bf16 outputs: dX {d[0]:.2e} dW {d[1]:.2e}", flush=True)
+    assert max(d) <= GRAD_RTOL_BF16
+
+
+def test_precise_sorted_and_shard(lce):
+    """The same two-part chunk in the backward on a vocabulary order and in a
+    vocabulary shard's backward."""
+    N, H, V = 300, 64, 2000
+    w = L.Workload("precise", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1, seed=9400)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 6.0).to(torch.bfloat16)
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    out = lce.lce_forward(Xd, Wd, yd, -100, 30.0)
+    X64, W64 = L.to_f64(X), L.to_f64(W)
+    rdX, rdW = O.backward(X64, W64, y.numpy(), 1.0, -100, 30.0)
+    order = torch.from_numpy(np.random.default_rng(3).permutation(V).astype(np.int32)).to(dev)
+    sX, sW = lce.lce_backward_sorted(Xd, Wd, yd, out["lse"], 1.0, order, softcap=30.0,
+                                     precise=True)
+    lo, hi = 700, 1500
+    shX, shW = lce.lce_shard_backward(Xd, Wd[lo:hi].contiguous(), yd, out["lse"], 1.0, lo, V,
+                                      softcap=30.0, precise=True)
+    torch.cuda.synchronize()
+    e = [rel_l2(sX.cpu(), rdX), rel_l2(sW.cpu(), rdW), rel_l2(shW.cpu(), rdW[lo:hi])]
+    print(f"[precise] sorted dX {e[0]:.2e} dW {e[1]:.2e} | shard dW {e[2]:.2e}", flush=True)
+    assert max(e) <= GRAD_RTOL
+
+
+def test_precise_refusals(lce):
+    X = torch.zeros(8, 16, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(40, 16, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(8, dtype=torch.int64, device="cuda")
+    out = lce.lce_forward(X, W, y, -100, 0.0)
+    with pytest.raises(Exception):
+        lce.lce_backward_ex(X, W, y, out["lse"], 1.0, precise=True, filter_eps=2.0 ** -12)
