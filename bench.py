@@ -502,12 +502,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def step():
+    def step(mid_event=None):
         st = lib.lce_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
                              float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
                              nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sptr)
         if st:
             raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        if mid_event is not None:
+            mid_event.record(stream)
         st = lib.lce_backward(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
                               dloss.data_ptr(), N, H, V, L.IGNORE_INDEX, float(w.softcap),
                               dX.data_ptr(), gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n,
@@ -569,6 +571,19 @@ def main():
     kernel_pass_ms = (time.perf_counter() - tk) * 1e3 / args.steps
     P.lce_timing_enable(False)
     kernels = P.lce_timing_read()
+
+    # Forward and backward apart: K more steps with one more event between
+    # the two calls of each step.
+    log(f"[bench] forward/backward pass, {args.steps} steps")
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evf[i][0].record(stream)
+        step(evf[i][1])
+        evf[i][2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evf) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evf) / args.steps
 
     # Dominant kernel and its roofline (algorithmic work per step from
     # GEMM_KERNELS, spread over that kernel's launches).
@@ -657,6 +672,11 @@ def main():
         "device": device,
         "parity": parity,
         "kernel_pass_ms_per_step": round(kernel_pass_ms, 3),
+        "forward_backward_ms": {"forward": round(fwd_ms, 3), "backward": round(bwd_ms, 3),
+                                "forward_tflops": round(2 * N * H * V / (fwd_ms / 1e3) / 1e12, 1),
+                                "backward_tflops": round(6 * N * H * V / (bwd_ms / 1e3) / 1e12, 1),
+                                "note": "a third pass of K steps with an event between the two "
+                                        "calls; forward 2·N·H·V, backward 6·N·H·V flops"},
         "cpu_baseline": cpu,
         "vocab_shard": shard,
         "fused_row_chunk": fused,

@@ -572,6 +572,22 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
   if (sorted)
     LCE_LAUNCH("position_keys", stream, launch_position_keys(order, V, key, N, pos1, pkey, stream));
   LCE_LAUNCH("sort_by_label", stream, launch_sort_by_label(sorted ? pkey : key, N, keys_a, keys_b, stream));
+  // The label entries' values, once for the whole vocabulary (their logits
+  // as the tile kernels form them, from W's own rows); each chunk then only
+  // clears their slots in G.
+  {
+    ExactParams ep{};
+    ep.X = X; ep.W = W; ep.N = N; ep.H = H; ep.V = V;
+    ep.v_begin = 0; ep.chunk_len = V; ep.key_offset = 0;
+    ep.softcap = opt->softcap; ep.logit_scale = opt->logit_scale;
+    ep.lse = lse_dev; ep.row_state = state; ep.row_key = key;
+    ep.gs = general ? gs : nullptr; ep.c1 = c1;
+    ep.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);
+    ep.one_minus_eps = 1.0f - opt->label_smoothing;
+    ep.label_pass = kLabelValues;
+    ep.lab_dense = lab_dense; ep.lab_oh = lab_oh;
+    LCE_LAUNCH("exact_labels", stream, launch_exact_entries(ep, stream));
+  }
 
   for (int c = 0; c < pl.nchunks; ++c) {
     const int64_t v_begin = (int64_t)c * pl.Vc;
@@ -604,6 +620,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     ep.gs = general ? gs : nullptr; ep.c1 = c1;
     ep.eps_over_v = gp.eps_over_v; ep.one_minus_eps = 1.0f - opt->label_smoothing;
     ep.dom_base = dom_base; ep.G = G; ep.G_lo = G_lo;
+    ep.label_pass = kLabelSlots; ep.keys = keys; ep.n_keys = counts + 1;
     ep.lab_dense = lab_dense; ep.lab_oh = lab_oh; ep.dom_col = dom_col; ep.dom_coef = dom_coef;
     LCE_LAUNCH("exact_entries", stream, launch_exact_entries(ep, stream));
     // With the filter, exact dense values whose block is skipped are dropped.

@@ -17,6 +17,10 @@
 // v_mfma_f32_32x32x16_bf16 over K as the tile kernels use, so it is the value
 // the forward's LSE and the logit-gradient tile saw, bit for bit.  That keeps
 // p − 1 of a confident row at the size the LSE itself implies.
+// The backward computes the label entries' values once, over the whole
+// vocabulary; after each chunk's logit-gradient pass it only writes their
+// slots in G (the labels of a chunk are one run of the label-sorted keys) and
+// takes the dominant entries the pass marked.
 #include "lce_device.h"
 #include "lce_internal.h"
 
@@ -87,6 +91,41 @@ __device__ __forceinline__ int64_t g_offset(int64_t tok, int64_t col, int n_vtil
          (tok % kTile) * kBK + col % kBK;
 }
 
+// A token row's terms, as the logit-gradient kernel forms them: exponent
+// offset (plain form: with the row class folded in), row scale, Z-loss
+// factor, whether the row has a gradient, and the value G holds for a logit
+// of −inf there (0, or −gsc·e/V without softcap) with its lo part.
+struct RowTerms {
+  float o, off, gsc, c1;
+  bool live;
+  uint16_t vinf_bits, vinf_lo;
+  float vinf;
+};
+
+template <bool kCapped, bool kGen>
+__device__ __forceinline__ RowTerms row_terms(const ExactParams& p, int64_t tok, float c2) {
+  RowTerms t;
+  const bool in = tok >= 0 && tok < p.N;
+  const int st = in ? p.row_state[tok] : (int)kRowIgnored;
+  const float lse2 = in ? p.lse[tok] * kLog2e : 0.0f;
+  t.o = kCapped ? c2 - lse2 + 2.0f : -lse2;
+  if (kGen) {
+    t.off = t.o;
+    t.gsc = in ? p.gs[tok] : 0.0f;
+    t.c1 = in ? p.c1[tok] : 1.0f;
+    t.live = t.gsc != 0.0f && t.gsc == t.gsc;
+  } else {
+    t.off = st == kRowValid ? t.o : (st == kRowBad ? __builtin_nanf("") : -__builtin_inff());
+    t.gsc = 1.0f;
+    t.c1 = 1.0f;
+    t.live = st == kRowValid;
+  }
+  t.vinf = (!kCapped && kGen) ? -t.gsc * p.eps_over_v : 0.0f;
+  t.vinf_bits = (uint16_t)f32_to_bf16_bits(t.vinf);
+  t.vinf_lo = (uint16_t)f32_to_bf16_bits(t.vinf - bf16_bits_to_f32(t.vinf_bits));
+  return t;
+}
+
 template <bool kCapped, bool kGen>
 __global__ void __launch_bounds__(64)
 exact_entries_kernel(ExactParams p) {
@@ -97,52 +136,74 @@ exact_entries_kernel(ExactParams p) {
   const float l2a = kLog2e * p.logit_scale;
   const int64_t c_lo = p.v_begin, c_hi = p.v_begin + p.chunk_len;
 
-  // This lane's token (column lane % 32 of the block) and its row terms, as
-  // the logit-gradient kernel forms them.
-  const int64_t tok = t0 + (lane & 31);
-  const bool in = tok < p.N;
-  const int st = in ? p.row_state[tok] : (int)kRowIgnored;
-  const float lse2 = in ? p.lse[tok] * kLog2e : 0.0f;
-  const float o = kCapped ? c2 - lse2 + 2.0f : -lse2;
-  float off, gsc, c1;
-  bool live;
-  if (kGen) {
-    off = o;
-    gsc = in ? p.gs[tok] : 0.0f;
-    c1 = in ? p.c1[tok] : 1.0f;
-    live = gsc != 0.0f && gsc == gsc;
-  } else {
-    off = st == kRowValid ? o : (st == kRowBad ? __builtin_nanf("") : -__builtin_inff());
-    gsc = 1.0f;
-    c1 = 1.0f;
-    live = st == kRowValid;
-  }
-  // What G holds for a logit of −inf: 0, or −gsc·e/V without softcap.
-  const float vinf = (!kCapped && kGen) ? -gsc * p.eps_over_v : 0.0f;
-  const uint16_t vinf_bits = (uint16_t)f32_to_bf16_bits(vinf);
-  // Its lo part, for a chunk carried as two bf16 parts.
-  const uint16_t vinf_lo = (uint16_t)f32_to_bf16_bits(vinf - bf16_bits_to_f32(vinf_bits));
-
   // ---- the label's entry: the block's diagonal C[j][j] = x_j · w_{y_j} ----
-  const int32_t key = (in && st == kRowValid) ? p.row_key[tok] : INT32_MAX;
-  const int64_t wrow = key == INT32_MAX ? -1 : (int64_t)key - p.key_offset;
-  const bool lab = wrow >= c_lo && wrow < c_hi;
-  if (__builtin_amdgcn_ballot_w64(lab) != 0) {
-    const f32x16 c = block_logits(lab ? p.W + wrow * p.H : nullptr,
-                                  in ? p.X + tok * p.H : nullptr, p.H, lane);
-    // Row j = lane % 32 of the diagonal sits in lane half (j / 4) % 2.
-    const int j = lane & 31;
-    if (lab && ((j >> 2) & 1) == (lane >> 5)) {
-      const float z = pick(c, ((j >> 3) & 3) * 4 + (j & 3));
-      float pr, d;
-      const float val = grad_value<kCapped, kGen>(z, off, gsc, c1, p.eps_over_v, k2, c2, l2a, pr, d);
-      p.lab_dense[tok] = val - vinf;
-      p.lab_oh[tok] = (kGen ? gsc : 1.0f) * p.one_minus_eps * d;
-      const int64_t g = g_offset(tok, wrow - c_lo, p.n_vtiles);
-      p.G[g] = vinf_bits;
-      if (p.G_lo) p.G_lo[g] = vinf_lo;
+  const int32_t* row_key = p.row_key;
+  if (p.label_pass == kLabelValues) {
+    // Tokens t0 .. t0 + 31 in order: their label entries' values, and (with
+    // G) the value of a logit at −inf in G there.
+    const int64_t ltok = t0 + (lane & 31);
+    int64_t lw = -1;
+    if (ltok < p.N && p.row_state[ltok] == kRowValid && row_key[ltok] != INT32_MAX)
+      lw = (int64_t)row_key[ltok] - p.key_offset;
+    const bool lab = lw >= c_lo && lw < c_hi;
+    if (__builtin_amdgcn_ballot_w64(lab) != 0) {
+      const RowTerms rt = row_terms<kCapped, kGen>(p, lab ? ltok : -1, c2);
+      const f32x16 c = block_logits(lab ? p.W + lw * p.H : nullptr,
+                                    lab ? p.X + ltok * p.H : nullptr, p.H, lane);
+      // Row j = lane % 32 of the diagonal sits in lane half (j / 4) % 2.
+      const int j = lane & 31;
+      if (lab && ((j >> 2) & 1) == (lane >> 5)) {
+        const float z = pick(c, ((j >> 3) & 3) * 4 + (j & 3));
+        float pr, d;
+        const float val = grad_value<kCapped, kGen>(z, rt.off, rt.gsc, rt.c1, p.eps_over_v, k2,
+                                                    c2, l2a, pr, d);
+        p.lab_dense[ltok] = val - rt.vinf;
+        p.lab_oh[ltok] = (kGen ? rt.gsc : 1.0f) * p.one_minus_eps * d;
+        if (p.G) {
+          const int64_t g = g_offset(ltok, lw - c_lo, p.n_vtiles);
+          p.G[g] = rt.vinf_bits;
+          if (p.G_lo) p.G_lo[g] = rt.vinf_lo;
+        }
+      }
+    }
+  } else if (p.label_pass == kLabelSlots) {
+    // The values are known (an earlier kLabelValues pass over the whole
+    // vocabulary); only G's entries at the labels in this chunk are set to
+    // the value of a logit at −inf.  Those rows are one run of the
+    // label-sorted keys: this wave takes keys t0 .. t0 + 31.
+    const int64_t i = t0 + (lane & 31);
+    if (i < *p.n_keys) {
+      const uint64_t k = p.keys[i];
+      const int64_t ltok = (int64_t)(uint32_t)k;
+      const int64_t lw = (int64_t)(uint32_t)(k >> 32) - p.key_offset;
+      if (lw >= c_lo && lw < c_hi) {
+        float vinf = 0.0f;
+        if (!kCapped && kGen) vinf = -p.gs[ltok] * p.eps_over_v;
+        const uint16_t vb = (uint16_t)f32_to_bf16_bits(vinf);
+        const int64_t g = g_offset(ltok, lw - c_lo, p.n_vtiles);
+        p.G[g] = vb;
+        if (p.G_lo) p.G_lo[g] = (uint16_t)f32_to_bf16_bits(vinf - bf16_bits_to_f32(vb));
+      }
     }
   }
+  if (!p.dom_base && !p.cand_z) return;   // no dominant entries in this pass
+
+  // This lane's token in token order (column lane % 32 of the block) and its
+  // row terms, for the dominant entry.  A wave without a candidate in this
+  // chunk stops after reading them.
+  const int64_t tok = t0 + (lane & 31);
+  const bool in = tok < p.N;
+  if (p.dom_base) {
+    const int32_t d0 = in ? p.dom_base[tok] : -1;
+    const int64_t b0 = d0 < 0 ? -1 : (int64_t)d0 - p.key_offset;
+    if (__builtin_amdgcn_ballot_w64(b0 >= c_lo && b0 < c_hi) == 0) return;
+  }
+  const RowTerms tr = row_terms<kCapped, kGen>(p, tok, c2);
+  const float o = tr.o, off = tr.off, gsc = tr.gsc, c1 = tr.c1, vinf = tr.vinf;
+  const bool live = tr.live;
+  const uint16_t vinf_bits = tr.vinf_bits, vinf_lo = tr.vinf_lo;
+  const int32_t key = (in && p.row_state[tok] == kRowValid) ? row_key[tok] : INT32_MAX;
+  const int64_t wrow = key == INT32_MAX ? -1 : (int64_t)key - p.key_offset;   // the label's W row
 
   // ---- a dominant entry: among the 64 rows the finding lane held ----
   const float zthr = dominance_threshold<kCapped>(live, o, k2, c2, l2a);

@@ -47,11 +47,12 @@ struct GradParams {
   // over rows with a target, that is not below filter_eps, else 0.
   uint8_t* flags;
   float filter_eps;
-  // Dominant entries: for the token of a row with an entry whose softmax
-  // exceeds 1/2 + 2^-10 (at most one per row), the W row of the first of the
+  // Dominant-entry candidates: for the token of a row with an entry whose
+  // softmax exceeds 1/2 (at most one per row), the W row of the first of the
   // 64 rows of the tile that the finding lane holds, plus key_offset (rows
   // lrow + x, x < 128 with bit 2 clear); untouched otherwise (the host presets
-  // −1).  launch_exact_entries turns it into the entry.
+  // −1).  launch_exact_entries recomputes those 64 logits and keeps the entry
+  // if its softmax exceeds 1/2 + 2^-10.
   int32_t* dom_base;
   int64_t key_offset;
   // Precise gradient: when not null, G holds hi = bf16(g) and G_lo, in the
@@ -163,11 +164,24 @@ struct ExactParams {
   int cand_splits;
   uint16_t* G;                // blocked chunk, as GradParams::G
   uint16_t* G_lo;             // its lo part (precise gradient), or null
+  // What the pass does for the label entries (kLabelValues, kLabelSlots or
+  // kLabelNone).  kLabelSlots reads the label-sorted keys (row_key << 32 |
+  // row, ascending) and the count of rows with a key in range (*n_keys): the
+  // rows whose labels fall in this chunk are one run of them.
+  int label_pass;
+  const uint64_t* keys;
+  const int32_t* n_keys;
   float* lab_dense;
   float* lab_oh;
   int32_t* dom_col;
   float* dom_coef;
 };
+// ExactParams::label_pass: compute the label entries' values (lab_dense,
+// lab_oh) of tokens in [v_begin, v_begin + chunk_len), and write the value of
+// a logit at −inf into G at them unless G is null; only that write, for the
+// labels in this chunk; or nothing.  The dominant-entry part runs when
+// dom_base or cand_z is set.
+constexpr int kLabelValues = 0, kLabelSlots = 1, kLabelNone = 2;
 hipError_t launch_exact_entries(const ExactParams& p, hipStream_t stream);
 hipError_t launch_chunk_gemm(const ChunkGemmParams& p, hipStream_t stream);
 

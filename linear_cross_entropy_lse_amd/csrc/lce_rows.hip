@@ -455,28 +455,31 @@ hipError_t launch_count_keys(const uint64_t* keys, int64_t N, int32_t* counts, h
 // merges sorted runs pairwise (each output element finds its source by a
 // binary search along the merge path), doubling the run length per pass.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
+// One thread per compare pair (kSortBlock / 2 threads), so each of the
+// network's stages is one exchange and one barrier.
+constexpr int kSortThreads = kSortBlock / 2;
+
+__global__ void __launch_bounds__(kSortThreads)
 sort_block_kernel(const int32_t* __restrict__ row_key, int64_t N, uint64_t* __restrict__ out) {
   __shared__ uint64_t sk[kSortBlock];
   const int64_t base = (int64_t)blockIdx.x * kSortBlock;
-  for (int i = threadIdx.x; i < kSortBlock; i += 256) {
+  for (int i = threadIdx.x; i < kSortBlock; i += kSortThreads) {
     const int64_t row = base + i;
     sk[i] = row < N ? ((uint64_t)(uint32_t)row_key[row] << 32) | (uint64_t)row : ~0ull;
   }
   __syncthreads();
+  const int t = threadIdx.x;   // compare pair t
   for (int k = 2; k <= kSortBlock; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < kSortBlock / 2; t += 256) {
-        const int i = 2 * t - (t & (j - 1));   // lower element of compare pair t
-        const uint64_t a = sk[i], b = sk[i + j];
-        if ((a > b) == ((i & k) == 0)) {
-          sk[i] = b;
-          sk[i + j] = a;
-        }
+      const int i = 2 * t - (t & (j - 1));   // its lower element
+      const uint64_t a = sk[i], b = sk[i + j];
+      if ((a > b) == ((i & k) == 0)) {
+        sk[i] = b;
+        sk[i + j] = a;
       }
       __syncthreads();
     }
-  for (int i = threadIdx.x; i < kSortBlock; i += 256) out[base + i] = sk[i];
+  for (int i = threadIdx.x; i < kSortBlock; i += kSortThreads) out[base + i] = sk[i];
 }
 
 __global__ void __launch_bounds__(256)
@@ -512,8 +515,8 @@ hipError_t launch_sort_by_label(const int32_t* row_key, int64_t N, uint64_t* key
                                 uint64_t* keys_b, hipStream_t stream) {
   const int64_t n = sort_padded(N);
   const int passes = sort_passes(N);
-  hipLaunchKernelGGL(sort_block_kernel, dim3((unsigned)(n / kSortBlock)), dim3(256), 0, stream, row_key,
-                     N, keys_a);
+  hipLaunchKernelGGL(sort_block_kernel, dim3((unsigned)(n / kSortBlock)), dim3(kSortThreads), 0, stream,
+                     row_key, N, keys_a);
   uint64_t* src = keys_a;
   uint64_t* dst = keys_b;
   int64_t run = kSortBlock;
