@@ -110,8 +110,11 @@ lce_status lce_forward(const void* X_dev, const void* W_dev,
  * part of dZ is rounded to bf16 for the two gradient contractions, which
  * accumulate in float32; the one-hot part (−1 at the target, times the
  * softcap derivative there) is applied exactly in float32, and so is the
- * scale dloss / n_valid, after the contractions.  The workspace holds one
- * bf16 vocabulary chunk of dZ (never the whole N×V matrix).
+ * scale dloss / n_valid, after the contractions.  Two entries of each row
+ * skip the bf16 chunk and are applied in float32 with the one-hot part: the
+ * label's, and one whose softmax exceeds 1/2 + 2^-10 if the row has one.
+ * The workspace holds one bf16 vocabulary chunk of dZ (never the whole N×V
+ * matrix).
  */
 lce_status lce_backward(const void* X_dev, const void* W_dev,
                         const int64_t* labels_dev, const float* lse_dev,
