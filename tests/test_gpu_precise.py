@@ -46,6 +46,8 @@ def rel_l2(a, b):
 
 CASES = [
     # N, H, V, W scale, options
+    (1, 8, 1, 4.0, dict()),                                       # one row, one class
+    (3, 16, 2, 4.0, dict(softcap=30.0)),
     (513, 64, 5, 4.0, dict()),
     (600, 72, 3, 4.0, dict(softcap=30.0)),
     (300, 64, 2, 4.0, dict(z_loss=1e-2, reduction="none")),
@@ -117,6 +119,16 @@ def test_precise_sorted_and_shard(lce):
     e = [rel_l2(sX.cpu(), rdX), rel_l2(sW.cpu(), rdW), rel_l2(shW.cpu(), rdW[lo:hi])]
     print(f"[precise] sorted dX {e[0]:.2e} dW {e[1]:.2e} | shard dW {e[2]:.2e}", flush=True)
     assert max(e) <= GRAD_RTOL
+
+
+def test_precise_empty_batch(lce):
+    X = torch.zeros(0, 16, dtype=torch.bfloat16, device="cuda")
+    W = torch.randn(40, 16, device="cuda").to(torch.bfloat16)
+    y = torch.zeros(0, dtype=torch.int64, device="cuda")
+    lse = torch.zeros(0, dtype=torch.float32, device="cuda")
+    dX, dW = lce.lce_backward_ex(X, W, y, lse, 1.0, precise=True)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, 16) and torch.count_nonzero(dW).item() == 0
 
 
 def test_precise_refusals(lce):
