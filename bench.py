@@ -40,8 +40,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gemma2_2b")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on (0: all rows)")
@@ -601,6 +601,10 @@ def main():
                 "avg_launch_ms": round(avg_ms, 4),
                 "algorithmic_flops_per_launch": dom_flops_per_launch,
                 "timing": "hipEvent pair per launch on the launch stream, second timed pass"}
+    if traffic is not None:
+        # Bytes across the L2 boundary per launch (counter summary) over the
+        # same average launch duration.
+        roofline["traffic_gb_per_s"] = round(traffic / (avg_ms / 1e3) / 1e9, 1)
     per_kernel = {k: {"launches_per_step": v[0] / args.steps,
                       "ms_per_step": round(v[1] / args.steps, 4)}
                   for k, v in kernels.items()}
