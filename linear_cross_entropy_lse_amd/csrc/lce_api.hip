@@ -107,27 +107,34 @@ struct BwdPlan {
       off_dkeys_a, off_dkeys_b, off_dcounts, total;
 };
 
-// Chunk width: the bf16 gradient chunk N x Vc is kept no larger than W itself
-// (N·Vc ≤ V·H), with a floor of 4096 columns; chunks are multiples of 256 so
-// tiles never straddle two chunks.  `precise`: the chunk holds two bf16 parts
-// (hi, lo) at half the width each (the workspace queries return the larger of
-// the two plans).  With a vocabulary order (`sorted`) the
-// chunk's W rows are gathered into position order (Wp), its dW rows go through
-// the fp32 chunk buffer, and the label keys are moved to positions (pos1,
-// pkey).
+// Chunk width: the bf16 gradient chunk N x Vc is kept about as large as W
+// (N·Vc ≤ V·H before its width is rounded up to whole 256-column tiles, so
+// that tiles never straddle two chunks), with a floor of 4096 columns and a
+// cap of 2^21 columns (a 256-row block of a chunk then spans < 2^31 bytes, the
+// 32-bit buffer offsets of the gradient kernels).  The number of chunks is
+// the fewest that meets the bound: ceil(N/H) between the floor and the cap,
+// counted before the rounding (rounding the bound down first can add a chunk
+// for a few columns: 5 chunks instead of 4 at N = 4H).  `precise`: the chunk
+// holds two bf16 parts (hi, lo), twice as many chunks of half the width (the
+// workspace queries return the larger of the two plans).  With a vocabulary
+// order (`sorted`) the chunk's W rows are gathered into position order (Wp),
+// its dW rows go through the fp32 chunk buffer, and the label keys are moved
+// to positions (pos1, pkey).
 BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool sorted = false,
                       bool precise = false) {
   BwdPlan p{};
   const int64_t Nc = std::max<int64_t>(N, 1);
   p.T = (int)ceil_div(Nc, kTile);
-  int64_t vc = std::max<int64_t>(4096, (V * H) / Nc);
-  // At most 2^21 columns, so a 256-row block of a chunk spans < 2^31 bytes
-  // (the 32-bit buffer offsets of the gradient kernels).
-  vc = std::min<int64_t>(vc, (int64_t)1 << 21);
-  if (precise) vc /= 2;
-  vc = std::max<int64_t>(kTile, vc / kTile * kTile);
-  p.nchunks = (int)ceil_div(V, vc);
-  p.Vc = ceil_div(ceil_div(V, p.nchunks), kTile) * kTile;
+  const int64_t parts = precise ? 2 : 1, floor_cols = 4096, cap_cols = (int64_t)1 << 21;
+  int64_t n;
+  if (V * H < floor_cols * Nc)
+    n = ceil_div(V * parts, floor_cols);
+  else if (V * H > cap_cols * Nc)
+    n = ceil_div(V * parts, cap_cols);
+  else
+    n = ceil_div(Nc * parts, H);
+  n = std::max<int64_t>(n, 1);
+  p.Vc = ceil_div(ceil_div(V, n), kTile) * kTile;
   p.nchunks = (int)ceil_div(V, p.Vc);
   p.ldg = p.Vc;
   p.n_vtiles_chunk = (int)(p.Vc / kTile);

@@ -37,13 +37,17 @@ ROW_BLOCK = 128
 
 def backward_chunk_columns(N: int, H: int, V: int) -> int:
     """Vocabulary columns per chunk of the backward's bf16 gradient chunk:
-    the widest multiple of 256 with N·Vc <= V·H (at least 4096, at most
-    2^21 columns), then evened out over the chunks it gives."""
-    vc = max(4096, (V * H) // max(N, 1))
-    vc = min(vc, 1 << 21)
-    vc = max(256, vc // 256 * 256)
-    n = -(-V // vc)
-    per = -(-V // n)
+    the fewest chunks with N·Vc <= V·H before the width is rounded up to a
+    multiple of 256 (ceil(N/H) chunks; widths of at least 4096 and at most
+    2^21 columns), evened out over the chunks."""
+    Nc = max(N, 1)
+    if V * H < 4096 * Nc:
+        n = -(-V // 4096)
+    elif V * H > (1 << 21) * Nc:
+        n = -(-V // (1 << 21))
+    else:
+        n = -(-Nc // H)
+    per = -(-V // max(n, 1))
     return -(-per // 256) * 256
 
 
