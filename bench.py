@@ -55,6 +55,8 @@ def parse():
                     help="skip timing the row-chunked forward-and-backward call")
     ap.add_argument("--no-precise", action="store_true",
                     help="skip timing the step with the precise (two-part) gradient")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured as a HIP graph")
     ap.add_argument("--filter-eps", type=float, default=2.0 ** -12,
                     help="also time the step with the (non-exact) gradient filter (0: skip)")
     return ap.parse_args()
@@ -274,6 +276,55 @@ def time_precise(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW
     dW.copy_(dWd)
     del dXd, dWd
     return out
+
+
+def time_graph(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, fws,
+               fws_n, bws, bws_n, step_ms_exact):
+    """The same step (same buffers, same calls) captured once as a HIP graph
+    and replayed: the host no longer launches each kernel, which matters only
+    where a step is short enough for launches to show.  Its outputs must equal,
+    bitwise, those of the headline step just timed on the same inputs."""
+    import torch
+    import lce_inputs as L
+    N, H, V = w.N, w.H, w.V
+    dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+    ref = [t.clone() for t in (loss, lse, mean, nval, dX, dW)]
+
+    def gstep(sp):
+        st = lib.lce_forward(X.data_ptr(), W.data_ptr(), y.data_ptr(), N, H, V, L.IGNORE_INDEX,
+                             float(w.softcap), loss.data_ptr(), lse.data_ptr(), mean.data_ptr(),
+                             nval.data_ptr(), bad.data_ptr(), fws.data_ptr(), fws_n, sp)
+        if st:
+            raise RuntimeError(f"lce_forward: {_lib.status_string(st)}")
+        st = lib.lce_backward(X.data_ptr(), W.data_ptr(), y.data_ptr(), lse.data_ptr(),
+                              dloss.data_ptr(), N, H, V, L.IGNORE_INDEX, float(w.softcap),
+                              dX.data_ptr(), gcode, dW.data_ptr(), gcode, bws.data_ptr(), bws_n, sp)
+        if st:
+            raise RuntimeError(f"lce_backward: {_lib.status_string(st)}")
+
+    log("[bench] the step as a captured HIP graph")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gstep(torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, (loss, lse, mean, nval, dX, dW)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    del g
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(N / (ms / 1e3), 1),
+            "speedup_vs_step": round(step_ms_exact / ms, 3), "bitwise_equal_to_step": same,
+            "note": "lce_forward + lce_backward captured once into a graph and replayed "
+                    "(torch.cuda.CUDAGraph); same work as the headline step, which launches "
+                    "each kernel from the host"}
 
 
 def time_fused(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode, sptr,
@@ -621,6 +672,10 @@ def main():
                       "headline fraction divides by the published 2500 TFLOP/s"}
 
     headline_mean = float(mean.item())
+    graph = None
+    if not args.no_graph:
+        graph = time_graph(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW, gcode,
+                           fws, fws_n, bws, bws_n, ms_per_step)
     filtered = filtered_sorted = None
     if args.filter_eps > 0:
         filtered = time_filtered(lib, _lib, args, w, X, W, y, loss, lse, mean, nval, bad, dX, dW,
@@ -682,6 +737,7 @@ def main():
                                 "note": "a third pass of K steps with an event between the two "
                                         "calls; forward 2·N·H·V, backward 6·N·H·V flops"},
         "cpu_baseline": cpu,
+        "hip_graph": graph,
         "vocab_shard": shard,
         "fused_row_chunk": fused,
         "precise_gradient": precise,

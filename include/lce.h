@@ -40,7 +40,11 @@
  *
  * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns without waiting.  Calls are re-entrant;
- * concurrent calls on different streams need separate workspaces.
+ * concurrent calls on different streams need separate workspaces.  The
+ * forward and backward calls make no allocation, copy, memset or
+ * synchronisation of their own, so they may be captured into a HIP graph on a
+ * capturing stream (the upstream-gradient and other inputs must then live in
+ * device memory the graph reads at replay).
  */
 #ifndef LCE_H_
 #define LCE_H_

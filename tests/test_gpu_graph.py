@@ -1,0 +1,74 @@
+"""The training step captured in a HIP graph.
+
+Every entry point of the step only enqueues kernels on the caller's stream (no
+allocation, copy, memset or synchronisation inside the library), so a
+forward + backward can be captured once and replayed.  The binding allocates
+its outputs and workspace from torch, which serves them from the graph's own
+pool during capture.  The upstream gradient is passed as a device tensor made
+before the capture (a host scalar would be a host-to-device copy inside it).
+
+The graph is replayed several times, with eager work and synchronisations
+between the replays and new inputs copied into the captured input buffers,
+and every replay must equal, bitwise, the eager step on the same inputs.
+"""
+import pytest
+import torch
+
+import lce_inputs as L
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_lse_amd as P
+    P.load()
+    return P
+
+
+def inputs(N, H, V, seed, softcap):
+    w = L.Workload("graph", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1,
+                   softcap=softcap, seed=seed)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    return X.cuda(), W.cuda(), y.cuda()
+
+
+def step(lce, X, W, y, dloss, softcap, precise=False):
+    out = lce.lce_forward(X, W, y, -100, softcap)
+    dX, dW = lce.lce_backward_ex(X, W, y, out["lse"], dloss, -100, softcap, precise=precise)
+    return [out["loss"], out["lse"], out["mean"], out["n_valid"], dX, dW]
+
+
+@pytest.mark.parametrize("N,H,V,softcap,precise", [
+    (600, 136, 5000, 30.0, False),     # several chunks, K tail, ragged rows and vocabulary
+    (256, 64, 1000, 0.0, False),       # the tiny workload's shape
+    (300, 64, 2000, 30.0, True),       # the precise gradient (two contractions per chunk)
+])
+def test_graph_replays_match_eager(lce, N, H, V, softcap, precise):
+    seeds = [21, 22, 23]
+    sets = [inputs(N, H, V, s, softcap) for s in seeds]
+    dloss = torch.tensor(0.7, dtype=torch.float32, device="cuda")
+    print(f"[graph] N={N} H={H} V={V} softcap={softcap} precise={precise}: eager", flush=True)
+    eager = [step(lce, X, W, y, dloss, softcap, precise) for X, W, y in sets]
+    torch.cuda.synchronize()
+    Xb, Wb, yb = (t.clone() for t in sets[0])
+    g = torch.cuda.CUDAGraph()
+    print("[graph] capture", flush=True)
+    with torch.cuda.graph(g):
+        outs = step(lce, Xb, Wb, yb, dloss, softcap, precise)
+    for rep, k in enumerate([0, 1, 2, 1, 0]):
+        X, W, y = sets[k]
+        Xb.copy_(X)
+        Wb.copy_(W)
+        yb.copy_(y)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {rep} on input set {k}", flush=True)
+        for a, b in zip(eager[k], outs):
+            assert torch.equal(a, b)
+        # eager work between replays
+        step(lce, *sets[(k + 1) % 3], dloss, softcap, precise)
+        torch.cuda.synchronize()
