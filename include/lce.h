@@ -34,7 +34,7 @@
  *     no floating-point atomics are used anywhere.
  *
  * Shapes and alignment (checked on the host before anything is launched):
- *   N >= 0 tokens, 1 <= H < 2^20 with H % 8 == 0, 1 <= V < 2^31, N < 2^31;
+ *   0 <= N < 2^31 - 1 tokens, 1 <= H < 2^20 with H % 8 == 0, 1 <= V < 2^31 - 1;
  *   X_dev, W_dev, dX_dev, dW_dev must be 16-byte aligned, labels_dev 8-byte,
  *   workspace_dev 256-byte aligned.
  *
@@ -302,7 +302,7 @@ lce_status lce_backward_sorted(const void* X_dev, const void* W_dev,
  * V_shard) of a vocabulary of vocab_total rows; W_shard_dev points to those
  * rows (bf16 [V_shard, H]).  Labels are global ids, checked against
  * [0, vocab_total).  Shapes as above, with 0 <= vocab_offset and
- * vocab_offset + V_shard <= vocab_total < 2^31 (else LCE_ERR_SHAPE).
+ * vocab_offset + V_shard <= vocab_total < 2^31 - 1 (else LCE_ERR_SHAPE).
  */
 
 /*

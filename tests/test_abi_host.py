@@ -73,6 +73,26 @@ def bwd(lib, X=FAKE, W=FAKE, y=FAKE, lse=FAKE, dl=FAKE, N=4, H=8, V=5, dX=FAKE, 
                             None)
 
 
+def test_shape_limits(lib):
+    """The limits of include/lce.h, on both sides of each bound: H < 2^20,
+    V < 2^31 - 1, N < 2^31 - 1 (workspace queries return 0 for a refused shape)."""
+    big = (1 << 31) - 2
+    for q in (lambda N, H, V: lib.lce_forward_workspace_bytes(N, H, V),
+              lambda N, H, V: lib.lce_backward_workspace_bytes(N, H, V, 0),
+              lambda N, H, V: lib.lce_backward_workspace_bytes(N, H, V, 1)):
+        assert q(4, (1 << 20) - 8, 5) > 0
+        assert q(4, 1 << 20, 5) == 0
+        assert q(4, 8, big) > 0
+        assert q(4, 8, big + 1) == 0
+        assert q(big, 8, 5) > 0
+        assert q(big + 1, 8, 5) == 0
+    assert fwd(lib, H=1 << 20) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, V=big + 1) == _lib.LCE_ERR_SHAPE
+    assert fwd(lib, N=big + 1) == _lib.LCE_ERR_SHAPE
+    assert bwd(lib, H=1 << 20) == _lib.LCE_ERR_SHAPE
+    assert bwd(lib, V=big + 1) == _lib.LCE_ERR_SHAPE
+
+
 def test_forward_error_paths(lib):
     assert fwd(lib, H=12) == _lib.LCE_ERR_SHAPE
     assert fwd(lib, H=0) == _lib.LCE_ERR_SHAPE
