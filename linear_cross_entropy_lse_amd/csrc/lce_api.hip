@@ -99,13 +99,29 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
 }
 
 struct BwdPlan {
-  int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep;
+  int T, nchunks, n_vtiles_chunk, S_chunk, nt_h, nb_prep, ksplit;
   int64_t Vc, ldg;
   size_t off_state, off_key, off_deriv, off_gs, off_c1, off_oh, off_keys_a, off_keys_b, off_head,
       off_tail, off_blocks, off_scalars, off_flags, off_G, off_dXp, off_dWs, off_Wp, off_pos1,
       off_pkey, off_labd, off_labo, off_domcol, off_domc, off_dombase, off_de, off_dkey,
       off_dkeys_a, off_dkeys_b, off_dcounts, total;
 };
+
+// K parts of the dX tiles of a chunk of `steps` 64-deep K steps.  The dX
+// tiles (T token tiles x nt_h hidden tiles) contract over the whole chunk, the
+// dW tiles over the rows; both kinds together hold 2·T·nt_h·steps tile-steps.
+// With few token tiles the dX tiles are too few and too long to spread over
+// the workgroups (at N = 1024 one of them would take three times the average
+// work of a workgroup), so their K range is split until one part costs no
+// more than the average; part k accumulates into its own fp32 buffer and the
+// parts are summed in order at the end.  Every part holds at least one step:
+// the count is ceil(steps / ceil(steps / k)), which the chunk GEMM's own part
+// length ceil(steps / ksplit) reproduces.
+int dx_parts(int64_t steps, int T, int nt_h) {
+  const int64_t avg = std::max<int64_t>(1, 2 * (int64_t)T * nt_h * steps / kTargetCUs);
+  const int64_t ks = std::min<int64_t>(std::max<int64_t>(1, ceil_div(steps, avg)), 16);
+  return (int)ceil_div(steps, ceil_div(steps, ks));
+}
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept about as large as W
 // (N·Vc ≤ V·H before its width is rounded up to whole 256-column tiles, so
@@ -141,6 +157,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   p.S_chunk = pick_splits(p.T, p.n_vtiles_chunk);
   p.nt_h = (int)ceil_div(H, kTile);
   p.nb_prep = row_prep_blocks(Nc);
+  p.ksplit = dx_parts(ceil_div(std::min<int64_t>(p.Vc, V), kBK), p.T, p.nt_h);
   size_t o = 0;
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_key = o;     o = align_up(o + sizeof(int32_t) * (size_t)N);
@@ -170,7 +187,7 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   // `precise` its lo part follows at G + T·256·ldg.
   p.off_G = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.T * kTile * (size_t)p.ldg *
                                       (precise ? 2 : 1));
-  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)N * (size_t)H);
+  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.ksplit * (size_t)N * (size_t)H);
   p.off_dWs = o;
   if (dW_dtype == LCE_BF16 || sorted) o = align_up(o + sizeof(float) * (size_t)p.Vc * (size_t)H);
   if (sorted) {
@@ -596,6 +613,11 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     LCE_LAUNCH("exact_labels", stream, launch_exact_entries(ep, stream));
   }
 
+  // dX partial buffers, all written by the first chunk's chunk GEMM (the
+  // widest chunk) and summed by dx_finalize.  Every chunk's parts are at most
+  // dx_part_steps steps long, so a narrower last chunk has no more parts.
+  const int dx_nparts = flags ? 1 : pl.ksplit;
+  const int64_t dx_part_steps = ceil_div(ceil_div(std::min<int64_t>(pl.Vc, V), kBK), dx_nparts);
   for (int c = 0; c < pl.nchunks; ++c) {
     const int64_t v_begin = (int64_t)c * pl.Vc;
     const int64_t chunk_len = std::min<int64_t>(pl.Vc, V - v_begin);
@@ -641,7 +663,14 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     cp.N = N; cp.H = H; cp.chunk_len = chunk_len;
     cp.nt_tok = pl.T; cp.nt_h = pl.nt_h; cp.nt_v = n_vt;
     cp.accumulate = c > 0; cp.dX_acc = dXp; cp.scale = gemm_scale;
-    cp.ksplit = 1; cp.dx_part_stride = 0; cp.dw_accumulate = 0; cp.flags = flags;
+    // K parts of this chunk's dX tiles: as many parts of at most
+    // dx_part_steps steps as the chunk needs (each part then holds at least
+    // one step; the chunk GEMM's part length ceil(steps / ksplit) gives the
+    // same count).  A narrower last chunk may use fewer parts, which then
+    // accumulate into the first buffers.  The filter's form takes one part.
+    cp.ksplit = flags ? 1 : (int)ceil_div(ceil_div(chunk_len, kBK), dx_part_steps);
+    if (cp.ksplit > dx_nparts) return LCE_ERR_INVALID_ARG;   // cannot happen: chunk 0 is the widest
+    cp.dx_part_stride = N * H; cp.dw_accumulate = 0; cp.flags = flags;
     cp.dW_dst = dW_dtype == LCE_F32 && !sorted ? static_cast<float*>(dW_dev) + v_begin * H : dWs;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
     if (precise) {
@@ -674,7 +703,7 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     LCE_LAUNCH("dw_correct", stream, launch_dw_correct(dkeys, dcounts, de, X, N, H,
                               static_cast<float*>(dW_dev), 0, V, part_head, part_tail, stream));
   }
-  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, 1, 0, N, H, V, state, key, oh, W, gemm_scale, nullptr,
+  LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, dx_nparts, N * H, N, H, V, state, key, oh, W, gemm_scale, nullptr,
                              dom_col, de, order, dX_dev, dX_dtype == LCE_BF16, stream));
   return LCE_OK;
 }

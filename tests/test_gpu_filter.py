@@ -7,8 +7,10 @@ that decision unique, each case puts the threshold in the middle of the
 widest gap (in log scale) between the oracle's block maxima near their
 median and checks that no block maximum lies within 1% of it; the gradients
 must then match the oracle's filtered gradients to the usual bars (rel-L2
-<= 1e-3).  Also: a threshold below every value reproduces the exact path bit
-for bit, one above every value leaves the one-hot term alone, and the
+<= 1e-3).  Also: a threshold below every value reproduces the exact path (dW
+bit for bit; dX up to the order of its sums, since the exact path may split a
+dX tile's vocabulary range into parts summed at the end and the filtered one
+does not), one above every value leaves the one-hot term alone, and the
 filter is refused with label smoothing.
 """
 import numpy as np
@@ -93,7 +95,10 @@ def test_tiny_threshold_is_the_exact_path(lce):
     a = lce.lce_backward_ex(X, W, y, out["lse"], 1.0, softcap=30.0)
     b = lce.lce_backward_ex(X, W, y, out["lse"], 1.0, softcap=30.0, filter_eps=1e-37)
     torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[1], b[1])
+    e = float(torch.linalg.vector_norm(a[0] - b[0]) / torch.linalg.vector_norm(a[0]))
+    print(f"[filter] tiny threshold: dX {e:.1e} from the exact path, dW equal", flush=True)
+    assert e <= 1e-6
 
 
 def test_huge_threshold_leaves_the_onehot_term(lce):

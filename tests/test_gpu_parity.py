@@ -138,6 +138,23 @@ def test_pipeline_step_counts(lce, N, H, V, softcap):
     check(g, *oracle_all(X, W, y, softcap), what=f"steps N={N} H={H} V={V} c={softcap}")
 
 
+# Few token tiles: the dX tiles of a chunk are too few to spread over the
+# workgroups, so their vocabulary range is split into K parts summed at the
+# end.  (N, H, V): 8 chunks of 4096 columns in 8 parts each, the last chunk
+# (3328 columns) in 7; 18 chunks in 16 parts, the last one (368 columns) in
+# 2, with softcap; one chunk in 2 parts at H = 2304 (K tail, 9 hidden tiles).
+@pytest.mark.parametrize("N,H,V,softcap", [
+    (4096, 256, 32000, 0.0),
+    (1100, 64, 70000, 30.0),
+    (2000, 2304, 6000, 30.0),
+])
+def test_split_dx_parts(lce, N, H, V, softcap):
+    X, W, y = synth(N, H, V, seed=3500 + N, softcap=softcap)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    g = run_gpu(lce, X, W, y, softcap)
+    check(g, *oracle_all(X, W, y, softcap), what=f"dX parts N={N} H={H} V={V} c={softcap}")
+
+
 # Logits in the hundreds: e^z overflows a float from z ≈ 88.7, so the forward
 # must keep its running maximum, rescale its running sums when the maximum
 # rises in a later vocabulary tile (the ramp puts the largest logits in the
