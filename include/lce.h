@@ -403,12 +403,13 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev,
  * forbid it).  Same arguments, kernels and results as lce_forward, bit for
  * bit, minus the workspace: the call runs in a scratch array the library
  * holds in device memory, one per device (lce_forward_noalloc_max_bytes()
- * bytes, 16 MiB, held until the process ends).  The array's device address
+ * bytes, 64 MiB, held until the process ends).  The array's device address
  * is looked up on the first call on each device.  A shape whose forward
  * workspace (lce_forward_workspace_bytes) exceeds that size returns
  * LCE_ERR_SCRATCH_LIMIT before anything is launched; with the forward's
- * plan that is N above roughly 800 000 rows.  The call itself allocates
- * nothing: no hipMalloc, no host or library allocation on the device.
+ * plan that is N above roughly 640 000 rows (V of 2048 or more).  The call
+ * itself allocates nothing: no hipMalloc, no host or library allocation on
+ * the device.
  * Every call on one device shares that device's array, and each call
  * overwrites it before reading it, so nothing carries over between calls;
  * but calls that overlap in time on one device (concurrent streams, several

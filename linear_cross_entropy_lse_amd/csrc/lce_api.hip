@@ -80,12 +80,21 @@ struct FwdPlan {
   size_t off_state, off_target, off_pm, off_ps, off_pz, off_blocks, total;
 };
 
+// Forward: the token tiles go in groups of at most kGroupTiles (one launch
+// each), every group split S ways over the vocabulary, so that a full group
+// fills the 256 workgroups of the grid with a 4 x 8 block of (token tiles,
+// splits) on each XCD: per pipeline step an XCD touches 4 X blocks and 8 W
+// blocks.  One launch over every token tile would leave fewer splits as N
+// grows (S = 256 / T) and, past 32 token tiles, blocks of 8 x 4, 16 x 2 or
+// 32 x 1 tiles that share fewer operands in L2.
+constexpr int kGroupTiles = kTargetCUs / 8;
+
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
   (void)H;
   FwdPlan p{};
   p.T = (int)std::max<int64_t>(1, ceil_div(N, kTile));
   p.n_vtiles = (int)ceil_div(V, kTile);
-  p.S = pick_splits(p.T, p.n_vtiles);
+  p.S = pick_splits(std::min(p.T, kGroupTiles), p.n_vtiles);
   p.nb_fin = lse_finalize_blocks(std::max<int64_t>(N, 1));
   size_t o = 0;
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
@@ -106,6 +115,31 @@ struct BwdPlan {
       off_pkey, off_labd, off_labo, off_domcol, off_domc, off_dombase, off_de, off_dkey,
       off_dkeys_a, off_dkeys_b, off_dcounts, total;
 };
+
+// Logit-gradient grid past kGroupTiles token tiles: rounds of 256 / S token
+// tiles x S splits, S in {8, 4, 2, 1} (round_tile), S chosen for the least
+// estimated time: rounds x tiles per split (the slowest workgroup of a round),
+// times the measured cost of the XCD block a round gives each XCD (4 x 8 tiles
+// 1, 8 x 4 1.02, 16 x 2 1.055, 32 x 1 1.25: smaller blocks share fewer
+// operands in L2).  Narrow chunks (large N) have few vocabulary tiles, so the
+// splits that fill a round evenly can matter more than the block.
+int grad_round_splits(int T, int n_vt) {
+  static const int kS[4] = {8, 4, 2, 1};
+  static const double kBlockCost[4] = {1.0, 1.02, 1.055, 1.25};
+  int best = 1;
+  double best_cost = 1e300;
+  for (int i = 0; i < 4; ++i) {
+    const int S = kS[i];
+    if (S > n_vt) continue;
+    const int rt = kTargetCUs / S;
+    const double cost = (double)ceil_div(T, rt) * ceil_div(n_vt, S) * kBlockCost[i];
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
 
 // K parts of the dX tiles of a chunk of `steps` 64-deep K steps.  The dX
 // tiles (T token tiles x nt_h hidden tiles) contract over the whole chunk, the
@@ -396,7 +430,7 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
 // passes the device address hipGetSymbolAddress returns, looked up once per
 // device with that device current.
 // ---------------------------------------------------------------------------
-constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 constexpr int kMaxDevices = 64;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -476,13 +510,17 @@ lce_status forward_impl(const void* X_dev, const void* W_dev, const int64_t* lab
 
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
                           opt->logit_scale, state, nullptr, target, nullptr, nullptr, stream));
-  LseParams lp{};
-  lp.X = X; lp.W = W; lp.N = N; lp.H = H; lp.V = V;
-  lp.T = pl.T; lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
-  lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
-  pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
-  lp.part_m = pm; lp.part_s = ps; lp.part_z = zsum ? pz : nullptr;
-  LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
+  const int64_t group_rows = (int64_t)kGroupTiles * kTile;
+  for (int64_t r0 = 0; r0 < N; r0 += group_rows) {
+    LseParams lp{};
+    lp.X = X + r0 * H; lp.W = W; lp.N = std::min<int64_t>(group_rows, N - r0); lp.H = H; lp.V = V;
+    lp.T = (int)ceil_div(lp.N, kTile); lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
+    lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
+    pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
+    lp.part_m = pm + r0; lp.part_s = ps + r0; lp.part_z = zsum ? pz + r0 : nullptr;
+    lp.ldp = N;
+    LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
+  }
   const LossTerms terms = loss_terms(opt, vr.V_total, zsum ? pz : nullptr);
   LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, terms, out.lse, out.loss,
                               shard ? nullptr : blocks, out.zsum, stream));
@@ -634,6 +672,10 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
     gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
     pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
+    if (pl.T > kGroupTiles) {
+      gp.S = grad_round_splits(pl.T, n_vt);
+      gp.round_tiles = kTargetCUs / gp.S;
+    }
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
     gp.gs = general ? gs : nullptr; gp.c1 = c1;
     gp.eps_over_v = (float)((double)opt->label_smoothing / (double)vr.V_total);

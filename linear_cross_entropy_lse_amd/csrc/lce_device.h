@@ -655,6 +655,21 @@ __device__ __forceinline__ void grid_tile(int g, int T, int tt, int ss, int& ti,
   split = (x / ngt) * ss + local / tt;
 }
 
+// Oversubscribed (token tile, split) grid, in rounds of kXcds·kCusPerXcd
+// workgroups: round r covers token tiles [r·rt, (r + 1)·rt) with every split
+// (rt·S = kXcds·kCusPerXcd), and within the round the workgroups of XCD x
+// (hardware id % 8) take a (rt / 8) x S block of it.  Workgroups start in id
+// order, so the ones resident together form about one round, and each XCD's
+// block shares its X and W blocks in L2.  In the last round ti may pass the
+// last token tile; the caller skips such a workgroup.
+__device__ __forceinline__ void round_tile(int b, int rt, int& ti, int& split) {
+  const int per_round = kXcds * kCusPerXcd;
+  const int r = b / per_round, q = b - r * per_round;
+  const int x = q % kXcds, local = q / kXcds, tt = rt / kXcds;
+  ti = r * rt + x * tt + local % tt;
+  split = local / tt;
+}
+
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMI][kNI]) {
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi)

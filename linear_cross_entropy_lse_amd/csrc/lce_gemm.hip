@@ -112,8 +112,8 @@ template <int kMode, bool kZSum>
 __device__ __forceinline__ void store_split_partials(float (&m)[kNI], float (&s)[kNI],
                                                      float (&zs)[kNI], float* red, int wm, int wn,
                                                      int lane, int64_t tok0, int split, int64_t N,
-                                                     float zunit, float* part_m, float* part_s,
-                                                     float* part_z) {
+                                                     int64_t ldp, float zunit, float* part_m,
+                                                     float* part_s, float* part_z) {
   const float NEG_INF = -__builtin_inff();
   // Lanes l and l^32 hold the same token column (different vocabulary rows).
 #pragma unroll
@@ -148,10 +148,10 @@ __device__ __forceinline__ void store_split_partials(float (&m)[kNI], float (&s)
       const float ss = s[ni] * exp2_fast(m[ni] - mref) + s2 * exp2_fast(m2 - mref);
       const int64_t tok = tok0 + col;
       if (tok < N) {
-        part_m[(int64_t)split * N + tok] = mn;
-        part_s[(int64_t)split * N + tok] = ss;
+        part_m[(int64_t)split * ldp + tok] = mn;
+        part_s[(int64_t)split * ldp + tok] = ss;
         // Σ z in natural units: c·Σ tanh (capped) or a·Σ (x·w) (plain).
-        if (kZSum) part_z[(int64_t)split * N + tok] = zunit * (zs[ni] + red[2 * kTile + col]);
+        if (kZSum) part_z[(int64_t)split * ldp + tok] = zunit * (zs[ni] + red[2 * kTile + col]);
       }
     }
   }
@@ -206,7 +206,7 @@ lse_partials_kernel(LseParams p) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) prefetch has landed
   store_split_partials<kMode, kZSum>(m, s, zs, reinterpret_cast<float*>(smem_raw), wm, wn, lane,
-                                     tok0, split, p.N,
+                                     tok0, split, p.N, p.ldp,
                                      kMode == kPlain ? p.logit_scale : p.softcap, p.part_m,
                                      p.part_s, p.part_z);
 }
@@ -368,9 +368,13 @@ grad_logits_kernel(GradParams p) {
   LCE_LDS uint16_t* smem = (LCE_LDS uint16_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
   int ti, split;
-  grid_tile(g, p.T, p.tt, p.ss, ti, split);
+  if (p.round_tiles > 0) {
+    round_tile(blockIdx.x, p.round_tiles, ti, split);
+    if (ti >= p.T) return;   // past the last token tile (last round only)
+  } else {
+    grid_tile(xcd_remap(blockIdx.x, gridDim.x), p.T, p.tt, p.ss, ti, split);
+  }
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;
@@ -686,7 +690,7 @@ flce_logits_kernel(FlceParams p) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   store_split_partials<kMode, kZSum>(m, s, zs, reinterpret_cast<float*>(smem_raw), wm, wn, lane,
-                                     tok0, split, p.N,
+                                     tok0, split, p.N, p.N,
                                      kMode == kPlain ? p.logit_scale : p.softcap, p.part_m,
                                      p.part_s, p.part_z);
   flce_store_candidates(s_cz, s_cb, wm, wn, lane, tok0, split, p.N, p.part_cz, p.part_cb);
@@ -964,7 +968,11 @@ hipError_t launch_flce_logits(const FlceParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_grad_logits(const GradParams& p, hipStream_t stream) {
-  const int grid = p.T * p.S;
+  const int per_round = kXcds * kCusPerXcd;
+  if (p.round_tiles > 0 && (p.round_tiles % kXcds != 0 || p.round_tiles * p.S != per_round))
+    return hipErrorInvalidValue;
+  const int grid = p.round_tiles > 0 ? (p.T + p.round_tiles - 1) / p.round_tiles * per_round
+                                     : p.T * p.S;
   const bool tail = p.H % kBK != 0, capped = p.softcap > 0.0f, gen = p.gs != nullptr;
   const bool filt = p.flags != nullptr, split = p.G_lo != nullptr;
   if (!p.dom_base || (filt && split)) return hipErrorInvalidValue;

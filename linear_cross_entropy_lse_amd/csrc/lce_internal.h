@@ -15,9 +15,10 @@ struct LseParams {
   int tt, ss;         // XCD sub-grid (see grid_tile); 0 = plain order
   float softcap;
   float logit_scale;  // a > 0: z = a·(x·w) before the softcap
-  float* part_m;      // [S, N] base-2 running max
-  float* part_s;      // [S, N] Σ 2^(u − m)
-  float* part_z;      // [S, N] Σ_v z_v (label smoothing), or null
+  float* part_m;      // [S, ldp] base-2 running max
+  float* part_s;      // [S, ldp] Σ 2^(u − m)
+  float* part_z;      // [S, ldp] Σ_v z_v (label smoothing), or null
+  int64_t ldp;        // floats from one split's partials to the next (>= N)
 };
 
 // Recomputed logit gradient of one vocabulary chunk [v_begin, v_begin + 256·n_vtiles).
@@ -28,6 +29,7 @@ struct GradParams {
   int64_t v_begin;
   int T, S, n_vtiles;
   int tt, ss;
+  int round_tiles;    // > 0: rounds of round_tiles token tiles x S splits (round_tile)
   float softcap;
   float logit_scale;
   const float* lse;          // [N]

@@ -155,6 +155,23 @@ def test_split_dx_parts(lce, N, H, V, softcap):
     check(g, *oracle_all(X, W, y, softcap), what=f"dX parts N={N} H={H} V={V} c={softcap}")
 
 
+# More than 32 token tiles: the forward runs in launches of 32 token tiles
+# (the last one partial), and the logit-gradient grid in rounds of 256 / S
+# token tiles x S splits, whose last round has workgroups past the last token
+# tile.  (N, H, V): 36 token tiles, one chunk of 12 vocabulary tiles (S = 4,
+# one round of 64 tiles); 79 token tiles, two chunks of 10 vocabulary tiles
+# (S = 2, one round of 128 tiles), a K tail and softcap.
+@pytest.mark.parametrize("N,H,V,softcap", [
+    (9000, 64, 3000, 0.0),
+    (20000, 72, 5000, 30.0),
+])
+def test_many_token_tiles(lce, N, H, V, softcap):
+    X, W, y = synth(N, H, V, seed=3700 + N, softcap=softcap)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    g = run_gpu(lce, X, W, y, softcap)
+    check(g, *oracle_all(X, W, y, softcap), what=f"token tiles N={N} H={H} V={V} c={softcap}")
+
+
 # Logits in the hundreds: e^z overflows a float from z ≈ 88.7, so the forward
 # must keep its running maximum, rescale its running sums when the maximum
 # rises in a later vocabulary tile (the ramp puts the largest logits in the
