@@ -159,12 +159,19 @@ int dx_parts(int64_t steps, int T, int nt_h) {
 
 // Chunk width: the bf16 gradient chunk N x Vc is kept about as large as W
 // (N·Vc ≤ V·H before its width is rounded up to whole 256-column tiles, so
-// that tiles never straddle two chunks), with a floor of 4096 columns and a
-// cap of 2^21 columns (a 256-row block of a chunk then spans < 2^31 bytes, the
+// that tiles never straddle two chunks), with a floor (below) and a cap of
+// 2^21 columns (a 256-row block of a chunk then spans < 2^31 bytes, the
 // 32-bit buffer offsets of the gradient kernels).  The number of chunks is
 // the fewest that meets the bound: ceil(N/H) between the floor and the cap,
 // counted before the rounding (rounding the bound down first can add a chunk
-// for a few columns: 5 chunks instead of 4 at N = 4H).  `precise`: the chunk
+// for a few columns: 5 chunks instead of 4 at N = 4H).
+// Floor: a dW tile of the chunk GEMM contracts over all N rows (N/64 steps),
+// and the chunk's work per workgroup is 2·T·nt_h·(Vc/64)/256 steps; a dW tile
+// is no longer than that average when Vc ≥ 32768/nt_h columns.  Narrower
+// chunks leave a few workgroups holding one dW tile each to set the time (at
+// H = 1024, N = 16384: twice the average).  So the floor is 32768/nt_h
+// columns in whole tiles, at least 4096 and at most 16384 (where H ≤ 512, the
+// chunk then holds N·16384 bf16 values at most).  `precise`: the chunk
 // holds two bf16 parts (hi, lo), twice as many chunks of half the width (the
 // workspace queries return the larger of the two plans).  With a vocabulary
 // order (`sorted`) the chunk's W rows are gathered into position order (Wp),
@@ -175,7 +182,10 @@ BwdPlan plan_backward(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype, bool 
   BwdPlan p{};
   const int64_t Nc = std::max<int64_t>(N, 1);
   p.T = (int)ceil_div(Nc, kTile);
-  const int64_t parts = precise ? 2 : 1, floor_cols = 4096, cap_cols = (int64_t)1 << 21;
+  const int64_t nt_h = ceil_div(H, kTile);
+  const int64_t floor_cols = std::max<int64_t>(
+      4096, std::min<int64_t>(16384, ceil_div(ceil_div(32768, nt_h), kTile) * kTile));
+  const int64_t parts = precise ? 2 : 1, cap_cols = (int64_t)1 << 21;
   int64_t n;
   if (V * H < floor_cols * Nc)
     n = ceil_div(V * parts, floor_cols);

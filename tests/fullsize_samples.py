@@ -38,11 +38,14 @@ ROW_BLOCK = 128
 def backward_chunk_columns(N: int, H: int, V: int) -> int:
     """Vocabulary columns per chunk of the backward's bf16 gradient chunk:
     the fewest chunks with N·Vc <= V·H before the width is rounded up to a
-    multiple of 256 (ceil(N/H) chunks; widths of at least 4096 and at most
-    2^21 columns), evened out over the chunks."""
+    multiple of 256 (ceil(N/H) chunks; widths of at least max(4096,
+    32768 / ceil(H/256)) columns in whole tiles, that floor at most 16384, and
+    at most 2^21 columns), evened out over the chunks."""
     Nc = max(N, 1)
-    if V * H < 4096 * Nc:
-        n = -(-V // 4096)
+    nt_h = -(-H // 256)
+    floor_cols = max(4096, min(16384, -(-(-(-32768 // nt_h)) // 256) * 256))
+    if V * H < floor_cols * Nc:
+        n = -(-V // floor_cols)
     elif V * H > (1 << 21) * Nc:
         n = -(-V // (1 << 21))
     else:

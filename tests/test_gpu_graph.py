@@ -43,7 +43,7 @@ def step(lce, X, W, y, dloss, softcap, precise=False):
 
 
 @pytest.mark.parametrize("N,H,V,softcap,precise", [
-    (600, 136, 5000, 30.0, False),     # several chunks, K tail, ragged rows and vocabulary
+    (600, 136, 40000, 30.0, False),    # several chunks, K tail, ragged rows and vocabulary
     (256, 64, 1000, 0.0, False),       # the tiny workload's shape
     (300, 64, 2000, 30.0, True),       # the precise gradient (two contractions per chunk)
 ])

@@ -96,8 +96,8 @@ def test_tiny_config(lce):
     (513, 136, 2100, 1.5),      # softcap that actually bends the logits
     (96, 64, 300, 30.0),        # a single partial tile in both dimensions
     (1, 8, 1, 0.0),             # degenerate: one row, one class
-    (300, 64, 9000, 0.0),       # several backward vocabulary chunks, split-K for dX
-    (700, 48, 5000, 4.0),       # several chunks with softcap and a short K
+    (300, 64, 40000, 0.0),      # several backward vocabulary chunks, split-K for dX
+    (700, 48, 20000, 4.0),      # several chunks with softcap and a short K
     # A handful of classes: the softmax part is most of each gradient row.
     (513, 64, 5, 0.0),
     (513, 64, 3, 30.0),
@@ -140,12 +140,12 @@ def test_pipeline_step_counts(lce, N, H, V, softcap):
 
 # Few token tiles: the dX tiles of a chunk are too few to spread over the
 # workgroups, so their vocabulary range is split into K parts summed at the
-# end.  (N, H, V): 8 chunks of 4096 columns in 8 parts each, the last chunk
-# (3328 columns) in 7; 18 chunks in 16 parts, the last one (368 columns) in
-# 2, with softcap; one chunk in 2 parts at H = 2304 (K tail, 9 hidden tiles).
+# end.  (N, H, V): 2 chunks of 16128 columns in 9 parts each; 4 chunks of
+# 12544 columns in 16 parts, the last one (12368 columns) in 15, with
+# softcap; one chunk in 2 parts at H = 2304 (K tail, 9 hidden tiles).
 @pytest.mark.parametrize("N,H,V,softcap", [
     (4096, 256, 32000, 0.0),
-    (1100, 64, 70000, 30.0),
+    (1100, 64, 50000, 30.0),
     (2000, 2304, 6000, 30.0),
 ])
 def test_split_dx_parts(lce, N, H, V, softcap):
@@ -159,8 +159,8 @@ def test_split_dx_parts(lce, N, H, V, softcap):
 # (the last one partial), and the logit-gradient grid in rounds of 256 / S
 # token tiles x S splits, whose last round has workgroups past the last token
 # tile.  (N, H, V): 36 token tiles, one chunk of 12 vocabulary tiles (S = 4,
-# one round of 64 tiles); 79 token tiles, two chunks of 10 vocabulary tiles
-# (S = 2, one round of 128 tiles), a K tail and softcap.
+# one round of 64 tiles); 79 token tiles, one chunk of 20 vocabulary tiles
+# (S = 8, three rounds of 32 tiles), a K tail and softcap.
 @pytest.mark.parametrize("N,H,V,softcap", [
     (9000, 64, 3000, 0.0),
     (20000, 72, 5000, 30.0),

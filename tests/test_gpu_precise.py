@@ -51,7 +51,7 @@ CASES = [
     (513, 64, 5, 4.0, dict()),
     (600, 72, 3, 4.0, dict(softcap=30.0)),
     (300, 64, 2, 4.0, dict(z_loss=1e-2, reduction="none")),
-    (700, 48, 5000, 4.0, dict(softcap=4.0)),                      # several chunks, short K
+    (700, 48, 20000, 4.0, dict(softcap=4.0)),                     # several chunks, short K
     (300, 64, 9000, 4.0, dict(label_smoothing=0.1, reduction="sum")),
     (257, 136, 1003, 4.0, dict(logit_scale=1.3, z_loss=1e-3)),   # K tail, ragged rows
 ]

@@ -68,7 +68,7 @@ CASES = [
     # N, H, V, shard edges (fractions of V), options
     (257, 72, 1003, [0, 0.3, 0.31, 1.0], dict()),
     (513, 136, 2100, [0, 0.25, 0.5, 0.75, 1.0], dict(softcap=3.0, reduction="sum")),
-    (300, 64, 9000, [0, 0.5, 1.0], dict(softcap=30.0, label_smoothing=0.1, z_loss=1e-3,
+    (300, 64, 40000, [0, 0.5, 1.0], dict(softcap=30.0, label_smoothing=0.1, z_loss=1e-3,
                                          logit_scale=1.3, reduction="none")),
     (96, 48, 700, [0, 0.1, 0.9, 1.0], dict(label_smoothing=0.2)),
 ]

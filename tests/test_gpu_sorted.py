@@ -101,7 +101,7 @@ ORDER_CASES = [
     (256, 64, 1000, 0),
     (700, 72, 3000, 40),
     (100, 8, 40, 0),
-    (2048, 64, 10000, 64),
+    (2048, 64, 40000, 64),
 ]
 
 
@@ -151,10 +151,10 @@ def test_order_ties_and_no_targets(lce):
 def test_identity_order_is_the_plain_backward(lce, dW_dtype):
     """Identity order: the gathered W chunk equals the slice and the dW rows go
     back where they came from, so every operation and its order match."""
-    X, W, y = hot_inputs(2048, 64, 10000, 64, seed=8300)
+    X, W, y = hot_inputs(2048, 64, 40000, 64, seed=8300)
     Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
     lse = lce.lce_forward_ex(Xd, Wd, yd, softcap=30.0)["lse"]
-    ident = torch.arange(10000, dtype=torch.int32, device="cuda")
+    ident = torch.arange(40000, dtype=torch.int32, device="cuda")
     for eps in (0.0, 2.0 ** -12):
         a = lce.lce_backward_ex(Xd, Wd, yd, lse, 0.9, softcap=30.0, dW_dtype=dW_dtype,
                                 filter_eps=eps)
@@ -167,7 +167,7 @@ def test_identity_order_is_the_plain_backward(lce, dW_dtype):
 
 SORTED_CASES = [
     # N, H, V, hot entries, options, filter, dW dtype
-    (2048, 64, 10000, 64, dict(), True, torch.float32),
+    (2048, 64, 40000, 64, dict(), True, torch.float32),
     (700, 64, 3000, 40, dict(softcap=30.0, z_loss=1e-3, reduction="sum"), True, torch.bfloat16),
     (600, 72, 2600, 0, dict(softcap=4.0), False, torch.float32),
     (520, 64, 2100, 30, dict(ignore_index=3, logit_scale=0.8), True, torch.float32),

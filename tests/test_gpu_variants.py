@@ -45,8 +45,8 @@ CASES = [
     (513, 136, 2100, dict(softcap=3.0, logit_scale=0.7, label_smoothing=0.2, z_loss=1e-3,
                           reduction="sum")),
     (600, 200, 1500, dict(z_loss=1e-2, reduction="none")),
-    (300, 64, 9000, dict(softcap=30.0, label_smoothing=0.05, reduction="none")),
-    (700, 48, 5000, dict(softcap=4.0, logit_scale=2.0, reduction="sum")),
+    (300, 64, 40000, dict(softcap=30.0, label_smoothing=0.05, reduction="none")),
+    (700, 48, 20000, dict(softcap=4.0, logit_scale=2.0, reduction="sum")),
     (96, 64, 300, dict(softcap=80.0, label_smoothing=0.3, z_loss=5e-3)),   # general softcap path
 ]
 
