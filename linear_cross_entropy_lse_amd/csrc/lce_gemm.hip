@@ -875,16 +875,31 @@ chunk_gemm_kernel(ChunkGemmParams p) {
   const int64_t D = ((p.chunk_len + kBK - 1) / kBK + p.ksplit - 1) / p.ksplit;
   const int64_t E = (p.N + kBK - 1) / kBK;
   // The longer kind of tile is dealt first, round-robin; the workgroups that
-  // hold one more of it (the first rl) take fewer of the shorter kind, so the
-  // K steps per workgroup come out nearly equal.
+  // hold one more of it (the first rl, "heavy") take h of the shorter kind
+  // each and the others share the rest, with h chosen so that the larger of
+  // the two groups' K steps per workgroup is least.  (Values are uniform over
+  // the workgroup: a scalar loop of at most ns_t / rl + 1 steps.)
   const bool dw_long = E > D;
   const int nl_t = dw_long ? nw : nx, ns_t = dw_long ? nx : nw;
   const int64_t cl = dw_long ? E : D, cs = dw_long ? D : E;
   const int rl = nl_t % kCusPerXcd;
-  const int64_t per_wg = ((int64_t)nl_t * cl + (int64_t)ns_t * cs) / kCusPerXcd;
-  const int64_t heavy_budget = per_wg - (int64_t)(nl_t / kCusPerXcd + 1) * cl;
-  const int h_k = (rl == 0 || heavy_budget <= 0) ? 0 : (int)((heavy_budget + cs / 2) / cs);
-  const int ns_heavy = (int)((int64_t)rl * h_k < ns_t ? (int64_t)rl * h_k : ns_t);
+  int ns_heavy = 0;
+  if (rl > 0) {
+    const int64_t load_h = (int64_t)(nl_t / kCusPerXcd + 1) * cl, load_l = load_h - cl;
+    const int n_light = kCusPerXcd - rl;
+    int64_t best = -1;
+    for (int h = 0;; ++h) {
+      const int c = rl * h < ns_t ? rl * h : ns_t;
+      const int64_t heavy = load_h + (int64_t)h * cs;
+      const int64_t light = load_l + (int64_t)((ns_t - c + n_light - 1) / n_light) * cs;
+      const int64_t load = heavy > light ? heavy : light;
+      if (best < 0 || load < best) {
+        best = load;
+        ns_heavy = c;
+      }
+      if (c >= ns_t) break;
+    }
+  }
   const int ns_light = ns_t - ns_heavy;
   const float sc = *p.scale;
 
