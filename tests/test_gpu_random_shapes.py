@@ -1,0 +1,116 @@
+"""Seeded random shapes and options against the oracle.
+
+The grids depend on the shape in several ways: forward launches of 32 token
+tiles, logit-gradient rounds past 32 token tiles, K parts of the dX tiles
+with few token tiles, the chunk width (bound by W's size, a floor set by H,
+a cap of 2^21 columns), ragged rows, vocabulary and K.  Fixed cases cover
+each rule on its own; these draw (N, H, V, softcap, loss options) from a
+seeded generator over ranges where the rules meet in combinations nobody
+picked by hand, with the oracle cost bounded (N·V ≤ 4e7, N·V·H ≤ 4e9).
+
+Bars: per-row LSE and loss abs ≤ 2e-3, reduced loss rel ≤ 1e-4, dX and dW
+rel-L2 ≤ 1e-3 (float32 outputs), n_valid exact.  The reduced loss also gets
+an absolute allowance of 2^-20 times the mean (or, for the sum, the sum) of
+|LSE|: each row's loss is LSE − z formed in float32, so it carries a few ulps
+of LSE whatever its own size, and where the loss is mostly cancellation (one
+class: LSE = z and only the Z-loss term is left) a purely relative bar on a
+value near zero asks for more than float32 holds.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lce_inputs as L
+from oracle import lce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def log_uniform(rng, lo, hi):
+    return int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+
+
+def draw(k):
+    """Case k: three regimes in turn, (a) any N up to 3000 with vocabularies
+    up to 70000 (several chunks, few token tiles), (b) 33 to 80 token tiles
+    with small vocabularies (forward groups, gradient rounds), (c) H from 512
+    to 1024 with mid-size N and V (chunk-width floor, dX parts, dealing)."""
+    rng = np.random.default_rng(90_000 + k)
+    regime = k % 3
+    while True:
+        if regime == 0:
+            N, H, V = log_uniform(rng, 1, 3000), 8 * int(rng.integers(1, 65)), log_uniform(rng, 1, 70000)
+        elif regime == 1:
+            N, H, V = int(rng.integers(8193, 20481)), 8 * int(rng.integers(1, 33)), log_uniform(rng, 100, 3000)
+        else:
+            N, H, V = log_uniform(rng, 256, 4096), 8 * int(rng.integers(64, 129)), log_uniform(rng, 1000, 20000)
+        if N * V <= 4e7 and N * V * H <= 4e9:
+            break
+    softcap = float(rng.choice([0.0, 0.0, 30.0, 2.5]))
+    opts = {}
+    if rng.random() < 0.5:
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            opts = dict(label_smoothing=0.1)
+        elif kind == 1:
+            opts = dict(z_loss=1e-3, reduction="sum")
+        elif kind == 2:
+            opts = dict(logit_scale=0.7, reduction="none")
+        else:
+            opts = dict(label_smoothing=0.05, z_loss=1e-3)
+    labels = "zipf" if rng.random() < 0.5 else "uniform"
+    return N, H, V, softcap, opts, labels
+
+
+@pytest.fixture(scope="module")
+def lce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_lse_amd as P
+    P.load()
+    return P
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.mark.parametrize("k", range(N_CASES))
+def test_random_shape(lce, k):
+    N, H, V, softcap, opts, labels = draw(k)
+    print(f"[random] case {k}: N={N} H={H} V={V} softcap={softcap} {opts} {labels}", flush=True)
+    w = L.Workload("random", N=N, H=H, V=V, labels=labels, ignore_frac=0.1, softcap=softcap,
+                   seed=91_000 + k)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    red = opts.get("reduction", "mean")
+    rng = np.random.default_rng(92_000 + k)
+    dloss = rng.standard_normal(N).astype(np.float32) if red == "none" else np.float32(0.9)
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    out = lce.lce_forward_ex(Xd, Wd, yd, softcap=softcap, **opts)
+    dX, dW = lce.lce_backward_ex(Xd, Wd, yd, out["lse"],
+                                 torch.from_numpy(np.atleast_1d(dloss)).to(dev),
+                                 softcap=softcap, **opts)
+    torch.cuda.synchronize()
+    o = O.options(softcap=softcap, **opts)
+    X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+    f = O.forward_ex(X64, W64, y64, o)
+    rdX, rdW = O.backward_ex(X64, W64, y64, dloss.astype(np.float64) if red == "none" else 0.9, o)
+    assert int(out["n_valid"]) == f["n_valid"]
+    np.testing.assert_allclose(out["lse"].cpu().numpy(), f["lse"], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(out["loss"].cpu().numpy(), f["loss"], rtol=0, atol=2e-3)
+    if red != "none" and f["n_valid"] > 0:
+        valid = y64 != L.IGNORE_INDEX
+        lse_mass = np.abs(f["lse"][valid]).sum() / (f["n_valid"] if red == "mean" else 1)
+        tol = 1e-4 * abs(f["reduced"]) + 2.0 ** -20 * lse_mass
+        assert abs(float(out["reduced"]) - f["reduced"]) <= tol
+    e = (rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW))
+    print(f"[random] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-3, e
