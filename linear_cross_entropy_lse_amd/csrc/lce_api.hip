@@ -1210,7 +1210,7 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     ep.eps_over_v = (float)((double)opt->label_smoothing / (double)V);
     ep.one_minus_eps = 1.0f - opt->label_smoothing;
     ep.dom_base = nullptr; ep.cand_z = pcz; ep.cand_b = pcb; ep.cand_splits = fp.S;
-    ep.G = U;
+    ep.G = U; ep.g_logits = true;
     ep.lab_dense = lab_dense + r0; ep.lab_oh = lab_oh + r0; ep.dom_col = dom_col + r0;
     ep.dom_coef = dom_coef + r0;
     LCE_LAUNCH("exact_entries", stream, launch_exact_entries(ep, stream));

@@ -123,6 +123,9 @@ __device__ __forceinline__ RowTerms row_terms(const ExactParams& p, int64_t tok,
   t.vinf = (!kCapped && kGen) ? -t.gsc * p.eps_over_v : 0.0f;
   t.vinf_bits = (uint16_t)f32_to_bf16_bits(t.vinf);
   t.vinf_lo = (uint16_t)f32_to_bf16_bits(t.vinf - bf16_bits_to_f32(t.vinf_bits));
+  // In the fused call's stored logits the slot gets the logit value whose
+  // image under the later rescale (G = f·U − gs·e/V) is vinf: 0.
+  if (p.g_logits) t.vinf_bits = t.vinf_lo = 0;
   return t;
 }
 

@@ -166,6 +166,9 @@ struct ExactParams {
   int cand_splits;
   uint16_t* G;                // blocked chunk, as GradParams::G
   uint16_t* G_lo;             // its lo part (precise gradient), or null
+  bool g_logits;              // G holds the fused call's stored logits, turned into the
+                              // gradient afterwards by G = f·U − gs·e/V: a taken entry's
+                              // slot is then set to 0, whose image is the slot value
   // What the pass does for the label entries (kLabelValues, kLabelSlots or
   // kLabelNone).  kLabelSlots reads the label-sorted keys (row_key << 32 |
   // row, ascending) and the count of rows with a key in range (*n_keys): the

@@ -61,6 +61,10 @@ CASES = [
     (200, 32, 90000, dict(softcap=30.0)),                          # the same with the fixed reference
     (513, 64, 5, dict()),                                          # a handful of classes
     (600, 64, 3, dict(softcap=30.0, z_loss=1e-3)),
+    # Label smoothing with a handful of classes: e/V is large, so the slot of
+    # an exactly taken entry must come out of the in-place rescale as −gs·e/V.
+    (300, 64, 2, dict(label_smoothing=0.1)),
+    (400, 376, 5, dict(label_smoothing=0.2, reduction="sum")),
 ]
 
 

@@ -114,3 +114,47 @@ def test_random_shape(lce, k):
     e = (rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW))
     print(f"[random] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
     assert max(e) <= 1e-3, e
+
+
+N_FUSED = 24
+
+
+@pytest.mark.parametrize("k", range(N_FUSED))
+def test_random_shape_fused_call(lce, k):
+    """The row-chunked fused call (its own grids: row chunks of a power of two
+    of 256-row tiles, split-K dX, accumulating dW) on the same kind of draws,
+    against the oracle's forward_backward_chunked.  The call takes label
+    smoothing only without a softcap, so a draw with both drops the smoothing."""
+    N, H, V, softcap, opts, labels = draw(1000 + k)
+    if softcap > 0 and "label_smoothing" in opts:
+        opts = {a: b for a, b in opts.items() if a != "label_smoothing"}
+    print(f"[random fused] case {k}: N={N} H={H} V={V} softcap={softcap} {opts} {labels}",
+          flush=True)
+    w = L.Workload("random", N=N, H=H, V=V, labels=labels, ignore_frac=0.1, softcap=softcap,
+                   seed=93_000 + k)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    red = opts.get("reduction", "mean")
+    rng = np.random.default_rng(94_000 + k)
+    dloss = rng.standard_normal(N).astype(np.float32) if red == "none" else np.float32(0.9)
+    dev = "cuda"
+    out, dX, dW = lce.lce_forward_backward(X.to(dev), W.to(dev), y.to(dev),
+                                           torch.from_numpy(np.atleast_1d(dloss)).to(dev),
+                                           softcap=softcap, **opts)
+    torch.cuda.synchronize()
+    o = O.options(softcap=softcap, **opts)
+    y64 = y.numpy()
+    f, rdX, rdW = O.forward_backward_chunked(L.to_f64(X), L.to_f64(W), y64,
+                                             dloss.astype(np.float64) if red == "none" else 0.9,
+                                             o, 256)
+    assert int(out["n_valid"]) == f["n_valid"]
+    np.testing.assert_allclose(out["lse"].cpu().numpy(), f["lse"], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(out["loss"].cpu().numpy(), f["loss"], rtol=0, atol=2e-3)
+    if red != "none" and f["n_valid"] > 0:
+        valid = y64 != L.IGNORE_INDEX
+        lse_mass = np.abs(f["lse"][valid]).sum() / (f["n_valid"] if red == "mean" else 1)
+        tol = 1e-4 * abs(f["reduced"]) + 2.0 ** -20 * lse_mass
+        assert abs(float(out["reduced"]) - f["reduced"]) <= tol
+    e = (rel_l2(dX.cpu(), rdX), rel_l2(dW.cpu(), rdW))
+    print(f"[random fused] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-3, e
