@@ -287,3 +287,32 @@ def test_random_shape_precise(lce, k):
     for a, b in zip(q, p):
         if a > 1e-4:
             assert b <= 0.1 * a, (a, b)
+
+
+@pytest.mark.parametrize("k", range(N_OTHER))
+def test_random_shape_bf16_outputs(lce, k):
+    """dX and dW emitted in bf16 (bar 1e-2), from the separate calls and the
+    fused call."""
+    N, H, V, softcap, opts, X, W, y, red, dloss, rng = inputs_for(k, 5000)
+    fused = bool(k % 2)
+    if fused and softcap > 0 and "label_smoothing" in opts:
+        opts = {a: b for a, b in opts.items() if a != "label_smoothing"}
+    print(f"[random bf16] case {k}: N={N} H={H} V={V} softcap={softcap} {opts} fused={fused}",
+          flush=True)
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    dl = torch.from_numpy(np.atleast_1d(dloss)).to(dev)
+    if fused:
+        _, dX, dW = lce.lce_forward_backward(Xd, Wd, yd, dl, softcap=softcap, dX_dtype=torch.bfloat16,
+                                             dW_dtype=torch.bfloat16, **opts)
+    else:
+        lse = lce.lce_forward_ex(Xd, Wd, yd, softcap=softcap, **opts)["lse"]
+        dX, dW = lce.lce_backward_ex(Xd, Wd, yd, lse, dl, softcap=softcap, dX_dtype=torch.bfloat16,
+                                     dW_dtype=torch.bfloat16, **opts)
+    torch.cuda.synchronize()
+    assert dX.dtype == torch.bfloat16 and dW.dtype == torch.bfloat16
+    rdX, rdW = oracle_grads(X, W, y, dloss, red, softcap, opts)
+    fx, fw = grad_floors(X, W, y, dloss, red, softcap, opts)
+    e = (rel_l2(dX.float().cpu(), rdX, fx), rel_l2(dW.float().cpu(), rdW, fw))
+    print(f"[random bf16] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-2, e
