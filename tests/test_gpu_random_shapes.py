@@ -316,3 +316,55 @@ def test_random_shape_bf16_outputs(lce, k):
     e = (rel_l2(dX.float().cpu(), rdX, fx), rel_l2(dW.float().cpu(), rdW, fw))
     print(f"[random bf16] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
     assert max(e) <= 1e-2, e
+
+
+def filter_case(k):
+    """Seeded shape, options and threshold for the gradient filter: several
+    256 x 256 blocks in both directions, no label smoothing (refused with the
+    filter), and a threshold in the widest log gap between the oracle's block
+    maxima near their median, at least 1 % from every block maximum, so the
+    float32 skip decisions match the oracle's; a draw without such a gap is
+    drawn again."""
+    for t in range(20):
+        rng = np.random.default_rng(97_000 + 100 * k + t)
+        N = int(rng.integers(300, 3001))
+        H = 8 * int(rng.integers(1, 33))
+        V = log_uniform(rng, 600, 20000)
+        softcap = float(rng.choice([0.0, 30.0, 4.0]))
+        opts = [dict(), dict(z_loss=1e-3, reduction="sum"), dict(logit_scale=1.3)][int(rng.integers(0, 3))]
+        w = L.Workload("random", N=N, H=H, V=V, labels="zipf", ignore_frac=0.1, softcap=softcap,
+                       seed=98_000 + 100 * k + t)
+        X, W, y = L.make_inputs(w)
+        W = (W.float() * float(rng.uniform(4.0, 7.0))).to(torch.bfloat16)
+        o = O.options(softcap=softcap, **opts)
+        X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+        f = O.forward_ex(X64, W64, y64, o)
+        bm = O.filter_block_max(X64, W64, y64, f["lse"], o)
+        v = np.sort(bm[np.isfinite(bm) & (bm > 0)].ravel())
+        if len(v) < 8:
+            continue
+        lo, hi = len(v) // 4, 3 * len(v) // 4
+        gaps = np.log(v[lo + 1:hi + 1]) - np.log(v[lo:hi])
+        j = lo + int(np.argmax(gaps))
+        eps = float(np.sqrt(v[j] * v[j + 1]))
+        if np.all(np.abs(v / eps - 1.0) > 0.01):
+            return N, H, V, softcap, opts, X, W, y, o, eps, bm
+    pytest.skip("no draw with a clear threshold")
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_filter(lce, k):
+    N, H, V, softcap, opts, X, W, y, o, eps, bm = filter_case(k)
+    kept = int((bm >= eps).sum())
+    print(f"[random filter] case {k}: N={N} H={H} V={V} softcap={softcap} {opts} eps={eps:.3e} "
+          f"kept {kept} of {bm.size}", flush=True)
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    lse = lce.lce_forward_ex(Xd, Wd, yd, softcap=softcap, **opts)["lse"]
+    dX, dW = lce.lce_backward_ex(Xd, Wd, yd, lse, 0.9, softcap=softcap, filter_eps=eps, **opts)
+    torch.cuda.synchronize()
+    rX, rW = O.backward_filtered(L.to_f64(X), L.to_f64(W), y.numpy(), 0.9, o, eps)
+    fx, fw = grad_floors(X, W, y, np.float32(0.9), opts.get("reduction", "mean"), softcap, opts)
+    e = (rel_l2(dX.cpu(), rX, fx), rel_l2(dW.cpu(), rW, fw))
+    print(f"[random filter] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-3, e
