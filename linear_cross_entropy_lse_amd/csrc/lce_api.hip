@@ -44,8 +44,11 @@ bool shape_ok(int64_t N, int64_t H, int64_t V) {
   return N >= 0 && N < INT_MAX && H >= 8 && H < (1 << 20) && H % 8 == 0 && V >= 1 && V < INT_MAX;
 }
 
-// Vocabulary splits of the persistent (token tile, split) grids: as many as
-// fit T·S <= kTargetCUs, so the grid is one wave of workgroups.
+// Vocabulary splits of a persistent (token tile, split) grid of T token
+// tiles: as many as fit T·S <= kTargetCUs, so the grid is one wave of
+// workgroups.  The forward calls it with at most kGroupTiles token tiles per
+// launch; the logit-gradient grid past kGroupTiles uses rounds instead
+// (grad_round_splits).
 int pick_splits(int T, int n_vtiles) {
   int S = kTargetCUs / std::max(T, 1);
   S = std::max(1, std::min(S, n_vtiles));

@@ -6,7 +6,8 @@
 
 namespace lce {
 
-// Forward partials: grid T x S, T token tiles of 256, S vocabulary splits.
+// Forward partials of one launch: grid T x S, T token tiles of 256 (at most
+// 32 per launch), S vocabulary splits.
 struct LseParams {
   const uint16_t* X;  // bf16 [N, H]
   const uint16_t* W;  // bf16 [V, H]
