@@ -435,6 +435,21 @@ lce_status lce_forward_noalloc(const void* X_dev, const void* W_dev,
 lce_status lce_device_info(int device, int32_t* cu_count, int32_t* clock_khz, char* arch,
                            int32_t arch_len);
 
+/*
+ * The backward's chunking for these sizes (host call, pure computation, the
+ * plan lce_backward and lce_backward_ex follow): the vocabulary columns per
+ * bf16 gradient chunk (a multiple of 256; the last chunk may be narrower),
+ * the number of chunks, and the K parts the dX tiles of the first chunk are
+ * split into (1 when there are enough token tiles; summed in order at the
+ * end).  precise (0 or 1) selects the plan of lce_options.precise.  Without
+ * the filter and vocabulary order the workspace holds one chunk of
+ * 256·ceil(N/256) x chunk_columns bf16 values (twice with precise) and
+ * dx_parts fp32 copies of dX.  Returns LCE_OK, LCE_ERR_SHAPE (shape out of
+ * range) or LCE_ERR_INVALID_ARG (NULL output, precise not 0 or 1).
+ */
+lce_status lce_backward_plan(int64_t N, int64_t H, int64_t V, int32_t precise,
+                             int64_t* chunk_columns, int32_t* n_chunks, int32_t* dx_parts);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);
 

@@ -37,6 +37,7 @@ EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_
             "lce_vocab_order_workspace_bytes", "lce_vocab_order",
             "lce_backward_sorted_workspace_bytes", "lce_backward_sorted",
             "lce_forward_noalloc_max_bytes", "lce_forward_noalloc", "lce_device_info",
+            "lce_backward_plan",
             "lce_status_string",
             "lce_version", "lce_timing_enable", "lce_timing_reset", "lce_timing_read")
 
@@ -139,6 +140,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_char_p,
                                     ctypes.c_int32]
     lib.lce_device_info.restype = ctypes.c_int
+    lib.lce_backward_plan.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.lce_backward_plan.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -169,6 +173,14 @@ def lce_device_info(device: int = -1) -> dict:
     _check(load().lce_device_info(int(device), ctypes.byref(cus), ctypes.byref(clk), arch, 64),
            "lce_device_info")
     return {"cu_count": cus.value, "clock_khz": clk.value, "arch": arch.value.decode()}
+
+
+def lce_backward_plan(N: int, H: int, V: int, precise: bool = False) -> dict:
+    """The backward's chunking (include/lce.h): chunk_columns, n_chunks, dx_parts."""
+    cols, nch, parts = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().lce_backward_plan(int(N), int(H), int(V), 1 if precise else 0, ctypes.byref(cols),
+                                    ctypes.byref(nch), ctypes.byref(parts)), "lce_backward_plan")
+    return {"chunk_columns": cols.value, "n_chunks": nch.value, "dx_parts": parts.value}
 
 
 def lce_timing_enable(enable: bool = True) -> None:

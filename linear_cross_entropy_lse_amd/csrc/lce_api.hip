@@ -837,11 +837,23 @@ lce_status lce_device_info(int device, int32_t* cu_count, int32_t* clock_khz, ch
   return LCE_OK;
 }
 
+lce_status lce_backward_plan(int64_t N, int64_t H, int64_t V, int32_t precise,
+                             int64_t* chunk_columns, int32_t* n_chunks, int32_t* dx_parts) {
+  if (!chunk_columns || !n_chunks || !dx_parts || (precise != 0 && precise != 1))
+    return LCE_ERR_INVALID_ARG;
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  const BwdPlan pl = plan_backward(N, H, V, LCE_F32, false, precise != 0);
+  *chunk_columns = pl.Vc;
+  *n_chunks = pl.nchunks;
+  *dx_parts = pl.ksplit;
+  return LCE_OK;
+}
+
 const char* lce_status_string(lce_status status) {
   switch (status) {
     case LCE_OK: return "ok";
     case LCE_ERR_INVALID_ARG: return "invalid argument (NULL pointer or enum out of range)";
-    case LCE_ERR_SHAPE: return "shape out of range (need N >= 0, 8 <= H < 2^20, H % 8 == 0, 1 <= V < 2^31)";
+    case LCE_ERR_SHAPE: return "shape out of range (need 0 <= N < 2^31 - 1, 8 <= H < 2^20, H % 8 == 0, 1 <= V < 2^31 - 1)";
     case LCE_ERR_ALIGNMENT: return "misaligned pointer (X/W/dX/dW 16 B, labels 8 B, workspace 256 B)";
     case LCE_ERR_WORKSPACE: return "workspace smaller than the size query returns";
     case LCE_ERR_HIP: return "HIP runtime error";

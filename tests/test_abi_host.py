@@ -93,6 +93,45 @@ def test_shape_limits(lib):
     assert bwd(lib, V=big + 1) == _lib.LCE_ERR_SHAPE
 
 
+def test_backward_plan_matches_the_sampling_mirror(lib):
+    """The chunking the library reports (lce_backward_plan) equals the mirror
+    the full-size tests use to place their samples at chunk boundaries
+    (tests/fullsize_samples.py), and its dX parts follow the rule written
+    out here: split a dX tile's K range until one part is no longer than the
+    average work per workgroup, 2·T·nt_h·steps / 256 K steps, at most 16
+    parts, every part holding a step."""
+    import random
+    from tests import fullsize_samples as FS
+
+    def dx_parts(steps, T, nt_h):
+        avg = max(1, 2 * T * nt_h * steps // 256)
+        ks = min(max(1, -(-steps // avg)), 16)
+        return -(-steps // -(-steps // ks))
+
+    rng = random.Random(11)
+    shapes = [(8192, 2304, 256128), (16384, 4096, 32000), (8192, 4096, 128256), (32768, 3584, 152064),
+              (256, 64, 1000), (1024, 2304, 256128), (16384, 768, 50257), (40, 64, (1 << 21) + 100003)]
+    shapes += [(rng.randint(1, 70000), 8 * rng.randint(1, 1024), rng.randint(1, 300000)) for _ in range(300)]
+    cols, nch, parts = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    for N, H, V in shapes:
+        assert lib.lce_backward_plan(N, H, V, 0, ctypes.byref(cols), ctypes.byref(nch),
+                                     ctypes.byref(parts)) == _lib.LCE_OK
+        vc = FS.backward_chunk_columns(N, H, V)
+        assert cols.value == vc, (N, H, V, cols.value, vc)
+        assert nch.value == -(-V // vc)
+        steps0 = -(-min(vc, V) // 64)
+        assert parts.value == dx_parts(steps0, -(-max(N, 1) // 256), -(-H // 256)), (N, H, V)
+        assert lib.lce_backward_plan(N, H, V, 1, ctypes.byref(cols), ctypes.byref(nch),
+                                     ctypes.byref(parts)) == _lib.LCE_OK
+        assert cols.value % 256 == 0 and cols.value <= vc
+    assert lib.lce_backward_plan(4, 12, 5, 0, ctypes.byref(cols), ctypes.byref(nch),
+                                 ctypes.byref(parts)) == _lib.LCE_ERR_SHAPE
+    assert lib.lce_backward_plan(4, 16, 5, 2, ctypes.byref(cols), ctypes.byref(nch),
+                                 ctypes.byref(parts)) == _lib.LCE_ERR_INVALID_ARG
+    assert lib.lce_backward_plan(4, 16, 5, 0, None, ctypes.byref(nch),
+                                 ctypes.byref(parts)) == _lib.LCE_ERR_INVALID_ARG
+
+
 def test_forward_error_paths(lib):
     assert fwd(lib, H=12) == _lib.LCE_ERR_SHAPE
     assert fwd(lib, H=0) == _lib.LCE_ERR_SHAPE
