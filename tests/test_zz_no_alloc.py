@@ -73,8 +73,11 @@ def inputs(N, H, V, softcap, seed):
 
 
 def test_noalloc_matches_forward_twice_shrinking(lib):
-    # Larger first call (several token tiles, ragged vocabulary), then a smaller one.
-    for (N, H, V, c, seed) in [(1100, 136, 5003, 30.0, 11), (300, 64, 1000, 0.0, 12)]:
+    # Calls of decreasing size: more than 32 token tiles (the forward in two
+    # launches of token tiles), several token tiles with a ragged vocabulary,
+    # then a smaller one.
+    for (N, H, V, c, seed) in [(9000, 64, 3000, 30.0, 10), (1100, 136, 5003, 30.0, 11),
+                               (300, 64, 1000, 0.0, 12)]:
         print(f"[noalloc] N={N} H={H} V={V} softcap={c}", flush=True)
         X, W, y = inputs(N, H, V, c, seed)
         ref = forward_with_workspace(lib, X, W, y, c)
