@@ -368,3 +368,29 @@ def test_random_shape_filter(lce, k):
     e = (rel_l2(dX.cpu(), rX, fx), rel_l2(dW.cpu(), rW, fw))
     print(f"[random filter] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
     assert max(e) <= 1e-3, e
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_vocab_order(lce, k):
+    """lce_vocab_order on seeded shapes (a third of them with hot entries):
+    the averages against the oracle's vocab_mean_logit within the tolerance of
+    tests/test_gpu_sorted.py, and the order valid (a permutation, the GPU's
+    averages never increasing along it, ties by index, the oracle's never
+    increasing beyond tolerance)."""
+    from tests import test_gpu_sorted as S
+    rng = np.random.default_rng(99_000 + k)
+    N, H, V = log_uniform(rng, 1, 6000), 8 * int(rng.integers(1, 65)), log_uniform(rng, 2, 60000)
+    print(f"[random order] case {k}: N={N} H={H} V={V}", flush=True)
+    if k % 3 == 0 and V >= 16:
+        X, W, y = S.hot_inputs(N, H, V, max(1, V // 50), seed=99_500 + k)
+    else:
+        X, W, y = L.make_inputs(L.Workload("random", N=N, H=H, V=V, labels="zipf", ignore_frac=0.1,
+                                           seed=99_500 + k))
+    key, order = lce.lce_vocab_order(X.cuda(), W.cuda(), y.cuda())
+    torch.cuda.synchronize()
+    X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+    ref = O.vocab_mean_logit(X64, W64, y64)
+    tol = S.key_tolerance(X64, W64, y64)
+    kg = key.cpu().numpy()
+    assert (np.abs(kg - ref) <= tol).all()
+    S.check_order(kg, order.cpu().numpy(), ref, tol)
