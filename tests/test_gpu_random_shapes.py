@@ -394,3 +394,59 @@ def test_random_shape_vocab_order(lce, k):
     kg = key.cpu().numpy()
     assert (np.abs(kg - ref) <= tol).all()
     S.check_order(kg, order.cpu().numpy(), ref, tol)
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_bad_labels_and_ignore_index(lce, k):
+    """Seeded shapes with a custom ignore index and a few labels out of range:
+    the bad-label flag, a NaN loss on exactly the bad rows (and a NaN reduced
+    loss), the other rows' losses and LSE against the oracle, finite dX rows
+    for every row that is not bad; with no bad row, the gradients against the
+    oracle under the custom ignore index."""
+    rng = np.random.default_rng(99_800 + k)
+    N, H, V = log_uniform(rng, 2, 4000), 8 * int(rng.integers(1, 65)), log_uniform(rng, 4, 30000)
+    softcap = float(rng.choice([0.0, 30.0]))
+    ignore = int(rng.integers(0, V))                  # a real class index used as the ignore index
+    w = L.Workload("random", N=N, H=H, V=V, labels="uniform", ignore_frac=0.0, softcap=softcap,
+                   seed=99_900 + k)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    y = y.clone()
+    y[torch.from_numpy(rng.random(N) < 0.1)] = ignore
+    n_bad = 0 if k % 3 == 0 else int(rng.integers(1, max(2, N // 50) + 1))
+    bad_rows = rng.choice(N, size=min(n_bad, N), replace=False) if n_bad else np.array([], dtype=np.int64)
+    for r in bad_rows:
+        y[int(r)] = int(V + rng.integers(0, 1000)) if rng.random() < 0.5 else -int(rng.integers(1, 1000))
+        if int(y[int(r)]) == ignore:
+            y[int(r)] = V
+    bad = np.zeros(N, dtype=bool)
+    bad[bad_rows] = True
+    print(f"[random labels] case {k}: N={N} H={H} V={V} softcap={softcap} ignore={ignore} "
+          f"bad={int(bad.sum())}", flush=True)
+    dev = "cuda"
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    out = lce.lce_forward(Xd, Wd, yd, ignore, softcap)
+    dX, dW = lce.lce_backward(Xd, Wd, yd, out["lse"], 0.9, ignore, softcap)
+    torch.cuda.synchronize()
+    loss = out["loss"].cpu().numpy()
+    assert int(out["bad_label"]) == (1 if bad.any() else 0)
+    assert np.isnan(loss[bad]).all() and np.isfinite(loss[~bad]).all()
+    assert np.isfinite(dX.cpu().numpy()[~bad]).all()
+    y_ok = y.clone()
+    y_ok[torch.from_numpy(bad)] = ignore                # the oracle's rows without the bad ones
+    X64, W64 = L.to_f64(X), L.to_f64(W)
+    f = O.forward(X64, W64, y_ok.numpy(), ignore, softcap)
+    valid = (y_ok.numpy() != ignore)
+    np.testing.assert_allclose(out["lse"].cpu().numpy()[~bad], f["lse"][~bad], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(loss[~bad], f["loss"][~bad], rtol=0, atol=2e-3)
+    if bad.any():
+        assert math.isnan(float(out["mean"]))
+        return
+    assert int(out["n_valid"]) == int(valid.sum())
+    if valid.any():
+        assert abs(float(out["mean"]) - f["mean"]) <= 1e-4 * abs(f["mean"]) + 2.0 ** -20 * np.abs(f["lse"][valid]).mean()
+    rdX, rdW = O.backward(X64, W64, y.numpy(), 0.9, ignore, softcap)
+    fx, fw = grad_floors(X, W, y, np.float32(0.9), "mean", softcap, dict(ignore_index=ignore))
+    e = (rel_l2(dX.cpu(), rdX, fx), rel_l2(dW.cpu(), rdW, fw))
+    print(f"[random labels] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-3, e
