@@ -491,3 +491,55 @@ def test_random_shape_combinations(lce, k):
     bar = 1e-3 if combo.endswith("precise") else 1e-2
     print(f"[random combo] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
     assert max(e) <= bar, e
+
+
+def sorted_filter_case(k):
+    """Seeded hot-entry inputs, the oracle's vocabulary order, and a filter
+    threshold in a wide gap of the block maxima taken in that order (the
+    procedure of tests/test_gpu_sorted.py); drawn again without such a gap."""
+    from tests import test_gpu_sorted as S
+    for t in range(20):
+        rng = np.random.default_rng(99_600 + 100 * k + t)
+        N = int(rng.integers(300, 3001))
+        H = 8 * int(rng.integers(1, 33))
+        V = log_uniform(rng, 600, 30000)
+        opts = [dict(), dict(softcap=30.0), dict(softcap=4.0, z_loss=1e-3, reduction="sum")][k % 3]
+        X, W, y = S.hot_inputs(N, H, V, max(2, V // 60), seed=99_700 + 100 * k + t)
+        o = O.options(**opts)
+        X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+        order = O.vocab_order(O.vocab_mean_logit(X64, W64, y64, int(o["ignore_index"])))
+        pos = np.empty(V, dtype=np.int64)
+        pos[order] = np.arange(V)
+        ignored = y64 == int(o["ignore_index"])
+        y_pos = y64.copy()
+        y_pos[~ignored] = pos[y64[~ignored]]
+        y_pos[ignored] = -1000
+        f = O.forward_ex(X64, W64, y64, o)
+        bm = O.filter_block_max(X64, W64[order], y_pos, f["lse"], dict(o, ignore_index=-1000))
+        v = np.sort(bm[np.isfinite(bm) & (bm > 0)].ravel())
+        if len(v) < 8:
+            continue
+        lo, hi = len(v) // 4, 3 * len(v) // 4
+        gaps = np.log(v[lo + 1:hi + 1]) - np.log(v[lo:hi])
+        j = lo + int(np.argmax(gaps))
+        eps = float(np.sqrt(v[j] * v[j + 1]))
+        if np.all(np.abs(v / eps - 1.0) > 0.01):
+            return N, H, V, opts, X, W, y, o, order, eps
+    pytest.skip("no draw with a clear threshold")
+
+
+@pytest.mark.parametrize("k", range(9))
+def test_random_shape_sorted_filter(lce, k):
+    N, H, V, opts, X, W, y, o, order, eps = sorted_filter_case(k)
+    print(f"[random sorted filter] case {k}: N={N} H={H} V={V} {opts} eps={eps:.3e}", flush=True)
+    Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
+    lse = lce.lce_forward_ex(Xd, Wd, yd, **opts)["lse"]
+    od = torch.from_numpy(order.astype(np.int32)).cuda()
+    dX, dW = lce.lce_backward_sorted(Xd, Wd, yd, lse, 0.9, od, filter_eps=eps, **opts)
+    torch.cuda.synchronize()
+    rX, rW = O.backward_sorted(L.to_f64(X), L.to_f64(W), y.numpy(), 0.9, o, order, eps)
+    fx, fw = grad_floors(X, W, y, np.float32(0.9), opts.get("reduction", "mean"),
+                         opts.get("softcap", 0.0), {a: b for a, b in opts.items() if a != "softcap"})
+    e = (rel_l2(dX.cpu(), rX, fx), rel_l2(dW.cpu(), rW, fw))
+    print(f"[random sorted filter] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-3, e
