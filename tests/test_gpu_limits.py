@@ -74,3 +74,41 @@ def test_vocabulary_past_the_chunk_cap(lce, N, H, V, softcap):
           f"dW {e[1]:.2e} label-free dW rows {e[2]:.2e}", flush=True)
     assert e[0] <= 1e-3 and e[1] <= 1e-3
     assert e[2] <= 1e-2
+
+
+@pytest.mark.parametrize("mode", ["sorted", "precise", "shards"])
+def test_past_the_chunk_cap_other_paths(lce, mode):
+    """The same 2^21-column chunks through the sorted backward (a seeded random
+    order: the gathered W chunk and the scattered dW rows span past 2^31
+    bytes), the precise gradient (three chunks of 732 416 columns, two parts
+    each) and two vocabulary shards of uneven size."""
+    N, H, V, softcap = 40, 64, (1 << 21) + 100003, 30.0
+    print(f"[limits] {mode}: N={N} H={H} V={V} softcap={softcap}", flush=True)
+    w = L.Workload("limits", N=N, H=H, V=V, labels="uniform", ignore_frac=0.1, softcap=softcap,
+                   seed=7800)
+    X, W, y = L.make_inputs(w)
+    W = (W.float() * 4.0).to(torch.bfloat16)
+    Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
+    lse = lce.lce_forward(Xd, Wd, yd, -100, softcap)["lse"]
+    if mode == "sorted":
+        order = torch.from_numpy(np.random.default_rng(5).permutation(V).astype(np.int32)).cuda()
+        dX, dW = lce.lce_backward_sorted(Xd, Wd, yd, lse, 1.0, order, softcap=softcap)
+    elif mode == "precise":
+        dX, dW = lce.lce_backward_ex(Xd, Wd, yd, lse, 1.0, softcap=softcap, precise=True)
+    else:
+        cut = 700001
+        ax, aw = lce.lce_shard_backward(Xd, Wd[:cut], yd, lse, 1.0, 0, V, softcap=softcap)
+        bx, bw = lce.lce_shard_backward(Xd, Wd[cut:], yd, lse, 1.0, cut, V, softcap=softcap)
+        dX, dW = ax + bx, torch.cat([aw, bw])
+    torch.cuda.synchronize()
+    dX, dW = dX.cpu().numpy(), dW.cpu().numpy()
+    del Xd, Wd
+    torch.cuda.empty_cache()
+    X64, W64, y64 = L.to_f64(X), L.to_f64(W), y.numpy()
+    rdX, rdW = O.backward(X64, W64, y64, 1.0, -100, softcap)
+    free = np.ones(V, dtype=bool)
+    free[y64[y64 != -100]] = False
+    e = [rel_l2(dX, rdX), rel_l2(dW, rdW), rel_l2(dW[free], rdW[free])]
+    print(f"[limits] {mode}: dX {e[0]:.2e} dW {e[1]:.2e} label-free dW rows {e[2]:.2e}", flush=True)
+    assert e[0] <= 1e-3 and e[1] <= 1e-3
+    assert e[2] <= (1e-4 if mode == "precise" else 1e-2)
