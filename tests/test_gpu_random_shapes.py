@@ -543,3 +543,35 @@ def test_random_shape_sorted_filter(lce, k):
     e = (rel_l2(dX.cpu(), rX, fx), rel_l2(dW.cpu(), rW, fw))
     print(f"[random sorted filter] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
     assert max(e) <= 1e-3, e
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_autograd(lce, k):
+    """The autograd wrapper on seeded shapes and options: the loss it returns
+    (reduced, or per row with reduction "none" and a random upstream gradient
+    through loss.backward) and X.grad, W.grad (bf16, as the inputs) against
+    the oracle (bar 1e-2)."""
+    N, H, V, softcap, opts, X, W, y, red, dloss, rng = inputs_for(k, 7000)
+    print(f"[random autograd] case {k}: N={N} H={H} V={V} softcap={softcap} {opts}", flush=True)
+    Xp = X.cuda().requires_grad_(True)
+    Wp = W.cuda().requires_grad_(True)
+    loss = lce.linear_cross_entropy(Xp, Wp, y.cuda(), softcap=softcap, **opts)
+    if red == "none":
+        loss.backward(torch.from_numpy(dloss).cuda())
+    else:
+        (loss * 0.9).backward()
+    torch.cuda.synchronize()
+    o = O.options(softcap=softcap, **opts)
+    f = O.forward_ex(L.to_f64(X), L.to_f64(W), y.numpy(), o)
+    if red == "none":
+        np.testing.assert_allclose(loss.detach().cpu().numpy(), f["loss"], rtol=0, atol=2e-3)
+    elif f["n_valid"] > 0:
+        valid = y.numpy() != L.IGNORE_INDEX
+        lse_mass = np.abs(f["lse"][valid]).sum() / (f["n_valid"] if red == "mean" else 1)
+        assert abs(float(loss.detach()) - f["reduced"]) <= 1e-4 * abs(f["reduced"]) + 2.0 ** -20 * lse_mass
+    assert Xp.grad.dtype == torch.bfloat16 and Wp.grad.dtype == torch.bfloat16
+    rdX, rdW = oracle_grads(X, W, y, dloss, red, softcap, opts)
+    fx, fw = grad_floors(X, W, y, dloss, red, softcap, opts)
+    e = (rel_l2(Xp.grad.float().cpu(), rdX, fx), rel_l2(Wp.grad.float().cpu(), rdW, fw))
+    print(f"[random autograd] case {k}: dX {e[0]:.2e} dW {e[1]:.2e}", flush=True)
+    assert max(e) <= 1e-2, e
