@@ -80,6 +80,8 @@ void pick_xcd_grid(int T, int S, int& tt, int& ss) {
 
 struct FwdPlan {
   int T, S, n_vtiles, nb_fin;
+  int S_tail;          // splits of the tail launch; 0: no tail
+  int64_t rows_main;   // rows of the groups split S ways (all rows without a tail)
   size_t off_state, off_target, off_pm, off_ps, off_pz, off_blocks, total;
 };
 
@@ -89,7 +91,10 @@ struct FwdPlan {
 // splits) on each XCD: per pipeline step an XCD touches 4 X blocks and 8 W
 // blocks.  One launch over every token tile would leave fewer splits as N
 // grows (S = 256 / T) and, past 32 token tiles, blocks of 8 x 4, 16 x 2 or
-// 32 x 1 tiles that share fewer operands in L2.
+// 32 x 1 tiles that share fewer operands in L2.  Past kGroupTiles tiles, the
+// r = T mod kGroupTiles tiles after the last full group form a tail launch
+// split pick_splits(r) ways: with the groups' S it would take as long as a
+// full group for as few as one token tile.
 constexpr int kGroupTiles = kTargetCUs / 8;
 
 FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
@@ -98,13 +103,18 @@ FwdPlan plan_forward(int64_t N, int64_t H, int64_t V) {
   p.T = (int)std::max<int64_t>(1, ceil_div(N, kTile));
   p.n_vtiles = (int)ceil_div(V, kTile);
   p.S = pick_splits(std::min(p.T, kGroupTiles), p.n_vtiles);
+  const int tail_tiles = p.T > kGroupTiles ? p.T % kGroupTiles : 0;
+  p.rows_main = tail_tiles ? (int64_t)(p.T - tail_tiles) * kTile : N;
+  p.S_tail = tail_tiles ? pick_splits(tail_tiles, p.n_vtiles) : 0;
   p.nb_fin = lse_finalize_blocks(std::max<int64_t>(N, 1));
+  // Split partials: [S, rows_main] for the groups, then [S_tail, N - rows_main].
+  const size_t n_part = (size_t)p.rows_main * p.S + (size_t)(N - p.rows_main) * p.S_tail;
   size_t o = 0;
   p.off_state = o;   o = align_up(o + sizeof(int32_t) * (size_t)N);
   p.off_target = o;  o = align_up(o + sizeof(float) * (size_t)N);
-  p.off_pm = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
-  p.off_ps = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
-  p.off_pz = o;      o = align_up(o + sizeof(float) * (size_t)N * p.S);
+  p.off_pm = o;      o = align_up(o + sizeof(float) * n_part);
+  p.off_ps = o;      o = align_up(o + sizeof(float) * n_part);
+  p.off_pz = o;      o = align_up(o + sizeof(float) * n_part);
   p.off_blocks = o;  o = align_up(o + sizeof(BlockStats) * (size_t)p.nb_fin);
   p.total = std::max<size_t>(o, kAlign);
   return p;
@@ -119,23 +129,31 @@ struct BwdPlan {
       off_dkeys_a, off_dkeys_b, off_dcounts, total;
 };
 
-// Logit-gradient grid past kGroupTiles token tiles: rounds of 256 / S token
-// tiles x S splits, S in {8, 4, 2, 1} (round_tile), S chosen for the least
+// Logit-gradient grid past kGroupTiles token tiles: full rounds of 256 / S
+// token tiles x S splits, S in {8, 4, 2, 1} (round_tile), then the tiles left
+// over in a launch of their own split pick_splits ways (a last round partly
+// filled would take as long as a full one).  S is chosen for the least
 // estimated time: rounds x tiles per split (the slowest workgroup of a round),
 // times the measured cost of the XCD block a round gives each XCD (4 x 8 tiles
 // 1, 8 x 4 1.02, 16 x 2 1.055, 32 x 1 1.25: smaller blocks share fewer
-// operands in L2).  Narrow chunks (large N) have few vocabulary tiles, so the
-// splits that fill a round evenly can matter more than the block.
+// operands in L2), plus the left-over launch's tiles per split.  Only S with
+// at least one full round are considered; with none (fewer vocabulary tiles
+// than 8 and fewer token tiles than a round of fewer splits) the result is 0
+// and the grid is a single launch of T x pick_splits(T) workgroups.  Narrow
+// chunks (large N) have few vocabulary tiles, so the splits that fill a round
+// evenly can matter more than the block.
 int grad_round_splits(int T, int n_vt) {
   static const int kS[4] = {8, 4, 2, 1};
   static const double kBlockCost[4] = {1.0, 1.02, 1.055, 1.25};
-  int best = 1;
+  int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < 4; ++i) {
     const int S = kS[i];
-    if (S > n_vt) continue;
     const int rt = kTargetCUs / S;
-    const double cost = (double)ceil_div(T, rt) * ceil_div(n_vt, S) * kBlockCost[i];
+    if (S > n_vt || T < rt) continue;
+    const int rest = T % rt;
+    double cost = (double)(T / rt) * ceil_div(n_vt, S) * kBlockCost[i];
+    if (rest > 0) cost += (double)ceil_div(n_vt, pick_splits(rest, n_vt));
     if (cost < best_cost) {
       best_cost = cost;
       best = S;
@@ -523,20 +541,37 @@ lce_status forward_impl(const void* X_dev, const void* W_dev, const int64_t* lab
 
   LCE_LAUNCH("row_prep", stream, launch_row_prep(X, W, labels_dev, N, H, V, vr, opt->ignore_index, opt->softcap,
                           opt->logit_scale, state, nullptr, target, nullptr, nullptr, stream));
-  const int64_t group_rows = (int64_t)kGroupTiles * kTile;
-  for (int64_t r0 = 0; r0 < N; r0 += group_rows) {
+  // Launches over the rows [r0, r0 + n) split S ways, partials [S, ldp] from
+  // offset `part` of the partial buffers.
+  auto partials = [&](int64_t r0, int64_t n, int S, size_t part, int64_t ldp) -> hipError_t {
     LseParams lp{};
-    lp.X = X + r0 * H; lp.W = W; lp.N = std::min<int64_t>(group_rows, N - r0); lp.H = H; lp.V = V;
-    lp.T = (int)ceil_div(lp.N, kTile); lp.S = pl.S; lp.n_vtiles = pl.n_vtiles;
+    lp.X = X + r0 * H; lp.W = W; lp.N = n; lp.H = H; lp.V = V;
+    lp.T = (int)ceil_div(n, kTile); lp.S = S; lp.n_vtiles = pl.n_vtiles;
     lp.softcap = opt->softcap; lp.logit_scale = opt->logit_scale;
     pick_xcd_grid(lp.T, lp.S, lp.tt, lp.ss);
-    lp.part_m = pm + r0; lp.part_s = ps + r0; lp.part_z = zsum ? pz + r0 : nullptr;
-    lp.ldp = N;
-    LCE_LAUNCH("lse_partials", stream, launch_lse_partials(lp, stream));
-  }
-  const LossTerms terms = loss_terms(opt, vr.V_total, zsum ? pz : nullptr);
-  LCE_LAUNCH("lse_finalize", stream, launch_lse_finalize(pm, ps, pl.S, N, state, target, terms, out.lse, out.loss,
-                              shard ? nullptr : blocks, out.zsum, stream));
+    lp.part_m = pm + part; lp.part_s = ps + part; lp.part_z = zsum ? pz + part : nullptr;
+    lp.ldp = ldp;
+    return launch_lse_partials(lp, stream);
+  };
+  // Final LSE and loss of the rows [r0, r0 + n) from S partials [S, n] at
+  // offset `part` (r0 is a multiple of 256, the rows of one block of sums).
+  auto finalize = [&](int64_t r0, int64_t n, int S, size_t part) -> hipError_t {
+    const LossTerms terms = loss_terms(opt, vr.V_total, zsum ? pz + part : nullptr);
+    return launch_lse_finalize(pm + part, ps + part, S, n, state + r0, target + r0, terms,
+                               out.lse + r0, out.loss ? out.loss + r0 : nullptr,
+                               shard ? nullptr : blocks + r0 / kTile,
+                               out.zsum ? out.zsum + r0 : nullptr, stream);
+  };
+  const int64_t group_rows = (int64_t)kGroupTiles * kTile, tail_rows = N - pl.rows_main;
+  const size_t tail_part = (size_t)pl.rows_main * pl.S;
+  for (int64_t r0 = 0; r0 < pl.rows_main; r0 += group_rows)
+    LCE_LAUNCH("lse_partials", stream, partials(r0, std::min(group_rows, pl.rows_main - r0), pl.S,
+                                                (size_t)r0, pl.rows_main));
+  if (tail_rows > 0)
+    LCE_LAUNCH("lse_partials", stream, partials(pl.rows_main, tail_rows, pl.S_tail, tail_part, tail_rows));
+  LCE_LAUNCH("lse_finalize", stream, finalize(0, pl.rows_main, pl.S, 0));
+  if (tail_rows > 0)
+    LCE_LAUNCH("lse_finalize", stream, finalize(pl.rows_main, tail_rows, pl.S_tail, tail_part));
   if (!shard)
     LCE_LAUNCH("mean_finalize", stream, launch_mean_finalize(blocks, pl.nb_fin, opt->reduction == LCE_REDUCE_MEAN,
                                   out.reduced, out.n_valid, out.bad_label, stream));
@@ -685,9 +720,15 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.T = pl.T; gp.S = std::min(pl.S_chunk, n_vt); gp.n_vtiles = n_vt;
     gp.softcap = opt->softcap; gp.logit_scale = opt->logit_scale;
     pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
-    if (pl.T > kGroupTiles) {
-      gp.S = grad_round_splits(pl.T, n_vt);
+    // Past kGroupTiles token tiles: full rounds here, the tiles left over in a
+    // second launch (below).
+    int rest_tiles = 0;
+    const int round_splits = pl.T > kGroupTiles ? grad_round_splits(pl.T, n_vt) : 0;
+    if (round_splits > 0) {
+      gp.S = round_splits;
       gp.round_tiles = kTargetCUs / gp.S;
+      rest_tiles = pl.T % gp.round_tiles;
+      gp.T = pl.T - rest_tiles;
     }
     gp.lse = lse_dev; gp.row_state = state; gp.G = G; gp.ldg = pl.ldg;
     gp.gs = general ? gs : nullptr; gp.c1 = c1;
@@ -696,6 +737,12 @@ lce_status backward_impl(const void* X_dev, const void* W_dev, const int64_t* la
     gp.dom_base = dom_base; gp.key_offset = sorted ? v_begin : 0;
     gp.G_lo = G_lo;
     LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
+    if (rest_tiles > 0) {
+      gp.t0 = gp.T; gp.T = rest_tiles; gp.round_tiles = 0;
+      gp.S = pick_splits(rest_tiles, n_vt);
+      pick_xcd_grid(gp.T, gp.S, gp.tt, gp.ss);
+      LCE_LAUNCH("grad_logits", stream, launch_grad_logits(gp, stream));
+    }
     ExactParams ep{};
     ep.X = X; ep.W = Wsrc; ep.N = N; ep.H = H; ep.V = w_rows;
     ep.v_begin = w_begin; ep.chunk_len = chunk_len; ep.key_offset = gp.key_offset;

@@ -375,6 +375,7 @@ grad_logits_kernel(GradParams p) {
   } else {
     grid_tile(xcd_remap(blockIdx.x, gridDim.x), p.T, p.tt, p.ss, ti, split);
   }
+  ti += p.t0;
   const int j0 = (int)((int64_t)split * p.n_vtiles / p.S);
   const int j1 = (int)((int64_t)(split + 1) * p.n_vtiles / p.S);
   const int64_t tok0 = (int64_t)ti * kTile;

@@ -31,6 +31,7 @@ struct GradParams {
   int T, S, n_vtiles;
   int tt, ss;
   int round_tiles;    // > 0: rounds of round_tiles token tiles x S splits (round_tile)
+  int t0;             // first token tile of the launch: it covers tiles [t0, t0 + T)
   float softcap;
   float logit_scale;
   const float* lse;          // [N]

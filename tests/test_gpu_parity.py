@@ -155,15 +155,24 @@ def test_split_dx_parts(lce, N, H, V, softcap):
     check(g, *oracle_all(X, W, y, softcap), what=f"dX parts N={N} H={H} V={V} c={softcap}")
 
 
-# More than 32 token tiles: the forward runs in launches of 32 token tiles
-# (the last one partial), and the logit-gradient grid in rounds of 256 / S
-# token tiles x S splits, whose last round has workgroups past the last token
-# tile.  (N, H, V): 36 token tiles, one chunk of 12 vocabulary tiles (S = 4,
-# one round of 64 tiles); 79 token tiles, one chunk of 20 vocabulary tiles
-# (S = 8, three rounds of 32 tiles), a K tail and softcap.
+# More than 32 token tiles: the forward runs in launches of 32 token tiles x
+# 8 splits and the tiles left over in a launch of their own with more splits;
+# the logit-gradient grid runs in full rounds of 256 / S token tiles x S
+# splits, then the tiles left over in a launch of their own.  (N, H, V):
+#   * 36 token tiles, one chunk of 12 vocabulary tiles: one round of 32 x 8,
+#     then 4 tiles x 12 splits (forward: 32 x 8, then 4 x 12);
+#   * 79 token tiles, one chunk of 20 vocabulary tiles, a K tail and softcap:
+#     one round of 64 x 4, then 15 x 17 (forward: two launches of 32 x 8, then
+#     15 x 17);
+#   * 33 token tiles, the last holding one row: 32 x 8, then 1 x 8 (8
+#     vocabulary tiles) in both;
+#   * 36 token tiles and 4 vocabulary tiles: no full round fits, one gradient
+#     launch of 36 x 4 (forward: 32 x 4, then 4 x 4).
 @pytest.mark.parametrize("N,H,V,softcap", [
     (9000, 64, 3000, 0.0),
     (20000, 72, 5000, 30.0),
+    (8193, 64, 2000, 0.0),
+    (9000, 64, 1000, 30.0),
 ])
 def test_many_token_tiles(lce, N, H, V, softcap):
     X, W, y = synth(N, H, V, seed=3700 + N, softcap=softcap)
