@@ -367,8 +367,10 @@ lce_status lce_shard_backward(const void* X_dev, const void* W_shard_dev,
  * Forward and backward in one call, row chunk by row chunk (the FLCE
  * pipeline of Liger: blog "最贵的一层：深入浅出 Liger Kernel 与 Cut
  * Cross-Entropy", §二, and the Liger Kernel paper page, §3.2).  The rows are
- * cut into chunks of at most 2H rows and at most half the rows (a power-of-two
- * count of 256-row tiles, at least one); for each chunk the logits against
+ * cut into chunks of whole 256-row tiles, at least one, at most 2H rows and,
+ * from two tiles on, at most half the tiles rounded up; as even as whole tiles
+ * allow, their count chosen for the least estimated time (lce_fused_plan
+ * gives the plan); for each chunk the logits against
  * the whole vocabulary are formed once, kept as a bf16 block of Nc x V in the
  * workspace (at most twice the size of W), turned into the logit
  * gradient, and projected back at once: dX rows = dZ_chunk · W, dW += dZᵀ ·
@@ -449,6 +451,18 @@ lce_status lce_device_info(int device, int32_t* cu_count, int32_t* clock_khz, ch
  */
 lce_status lce_backward_plan(int64_t N, int64_t H, int64_t V, int32_t precise,
                              int64_t* chunk_columns, int32_t* n_chunks, int32_t* dx_parts);
+
+/*
+ * The row chunking of lce_forward_backward for these sizes (host call, pure
+ * computation, the plan the call follows): the rows per chunk (a multiple of
+ * 256; the last chunk holds the rest, at least one row), the number of
+ * chunks, and the K parts the dX tiles of a full chunk are split into (a
+ * shorter last chunk may take more).  The workspace holds one bf16 block of
+ * chunk_rows x 256·ceil(V/256) values.  Returns LCE_OK, LCE_ERR_SHAPE (shape
+ * out of range) or LCE_ERR_INVALID_ARG (NULL output).
+ */
+lce_status lce_fused_plan(int64_t N, int64_t H, int64_t V, int64_t* chunk_rows, int32_t* n_chunks,
+                          int32_t* dx_parts);
 
 /* Static, NUL-terminated description of a status code. */
 const char* lce_status_string(lce_status status);

@@ -8,7 +8,7 @@ from ._lib import (LCE_BF16, LCE_F32, LceError, lce_backward,  # noqa: F401
                    lce_backward_ex, lce_backward_plan, lce_backward_sorted, lce_backward_workspace_bytes,
                    lce_device_info,
                    lce_forward, lce_vocab_order,
-                   lce_forward_backward, lce_forward_ex, lce_fused_workspace_bytes,
+                   lce_forward_backward, lce_forward_ex, lce_fused_plan, lce_fused_workspace_bytes,
                    lce_forward_workspace_bytes, lce_shard_backward, lce_shard_forward,
                    lce_shard_merge, lce_timing_enable, lce_timing_read, lce_timing_reset,
                    lce_version, load, make_options, status_string)

@@ -37,7 +37,7 @@ EXPORTED = ("lce_forward_workspace_bytes", "lce_backward_workspace_bytes", "lce_
             "lce_vocab_order_workspace_bytes", "lce_vocab_order",
             "lce_backward_sorted_workspace_bytes", "lce_backward_sorted",
             "lce_forward_noalloc_max_bytes", "lce_forward_noalloc", "lce_device_info",
-            "lce_backward_plan",
+            "lce_backward_plan", "lce_fused_plan",
             "lce_status_string",
             "lce_version", "lce_timing_enable", "lce_timing_reset", "lce_timing_read")
 
@@ -143,6 +143,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lce_backward_plan.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.lce_backward_plan.restype = ctypes.c_int
+    lib.lce_fused_plan.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.lce_fused_plan.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_version.argtypes = []
@@ -181,6 +184,14 @@ def lce_backward_plan(N: int, H: int, V: int, precise: bool = False) -> dict:
     _check(load().lce_backward_plan(int(N), int(H), int(V), 1 if precise else 0, ctypes.byref(cols),
                                     ctypes.byref(nch), ctypes.byref(parts)), "lce_backward_plan")
     return {"chunk_columns": cols.value, "n_chunks": nch.value, "dx_parts": parts.value}
+
+
+def lce_fused_plan(N: int, H: int, V: int) -> dict:
+    """The fused call's row chunking (include/lce.h): chunk_rows, n_chunks, dx_parts."""
+    rows, nch, parts = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().lce_fused_plan(int(N), int(H), int(V), ctypes.byref(rows), ctypes.byref(nch),
+                                 ctypes.byref(parts)), "lce_fused_plan")
+    return {"chunk_rows": rows.value, "n_chunks": nch.value, "dx_parts": parts.value}
 
 
 def lce_timing_enable(enable: bool = True) -> None:

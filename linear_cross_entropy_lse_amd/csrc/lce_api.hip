@@ -295,38 +295,66 @@ OrderPlan plan_order(int64_t N, int64_t H, int64_t V) {
 struct FusedPlan {
   int64_t Nc, ldu;
   int nchunks, T, S, n_vtiles, nt_h, ksplit, nb_prep, nb_fin;
+  int64_t dxp_rows;   // rows x K parts of the largest chunk's dX partials
   size_t off_state, off_key, off_target, off_deriv, off_gs, off_c1, off_oh, off_rrow, off_keys_a,
       off_keys_b, off_head, off_tail, off_bprep, off_bfin, off_scalars, off_pm, off_ps, off_pz,
       off_pcz, off_pcb, off_labd, off_labo, off_domcol, off_domc, off_de, off_dkey, off_dkeys_a,
       off_dkeys_b, off_dcounts, off_U, off_ref, off_Xs, off_dXp, off_dWacc, total;
 };
 
+// Token tiles per row chunk of the fused call (every chunk but the last has
+// this many).  A chunk has at most 2H rows (its bf16 logits block at most
+// twice the size of W) and, from two tiles of rows on, at most half of the
+// row tiles rounded up (the call never holds every row's logits at once).
+// Among the fewest chunks that meet the bound and up to three more, each
+// count with chunks as even as whole tiles allow, the one with the least
+// estimated time is taken: the logits pass of a chunk takes ceil(n_vt / S)
+// tile products on its slowest workgroup (S = pick_splits of the chunk's
+// tiles), and every chunk after the first reads and rewrites the fp32 dW once
+// more, about V / 16384 tile products (8·V·H bytes at the bandwidth against
+// 2·256²·H flops at one compute unit's MFMA rate, both about 5·10^12 per
+// second).  The chunk GEMM's work does not depend on the chunking.  Even
+// chunks keep a short last chunk from costing a whole dW pass for a few rows.
+int fused_chunk_tiles(int64_t N, int64_t H, int64_t V) {
+  const int64_t T_all = ceil_div(std::max<int64_t>(N, 1), kTile);
+  const int n_vt = (int)ceil_div(V, kTile);
+  const int64_t half = T_all >= 2 ? ceil_div(T_all, 2) : 1;
+  const int64_t lim = std::max<int64_t>(1, std::min<int64_t>(2 * H / kTile, half));
+  const int64_t n_min = ceil_div(T_all, lim);
+  const double dw_pass = (double)V / 16384.0;
+  int64_t best = ceil_div(T_all, n_min);
+  double best_cost = 1e300;
+  for (int64_t n = n_min; n <= n_min + 3 && n <= T_all; ++n) {
+    const int64_t t = ceil_div(T_all, n), last = T_all - (n - 1) * t;
+    if (last <= 0) continue;
+    const double cost = (double)(n - 1) * ceil_div(n_vt, pick_splits((int)t, n_vt)) +
+                        (double)ceil_div(n_vt, pick_splits((int)last, n_vt)) + (double)(n - 1) * dw_pass;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = t;
+    }
+  }
+  return (int)best;
+}
+
 FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   FusedPlan p{};
   const int64_t Np = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
-  // Chunk: the largest power-of-two count of 256-row tiles that is at most
-  // 2H rows (its bf16 logits block at most twice the size of W) and, from
-  // two tiles of rows on, at most half the rows (the call never holds every
-  // row's logits at once).
-  const int64_t lim = std::min<int64_t>(2 * H, Np >= 2 * kTile ? Np / 2 : Np);
-  int64_t tiles = 1;
-  while (tiles * 2 * kTile <= lim) tiles *= 2;
-  p.Nc = std::min<int64_t>(Np, tiles * kTile);
+  p.T = fused_chunk_tiles(N, H, V);
+  p.Nc = (int64_t)p.T * kTile;
   p.nchunks = (int)ceil_div(std::max<int64_t>(N, 1), p.Nc);
-  p.T = (int)(p.Nc / kTile);
   p.n_vtiles = (int)ceil_div(V, kTile);
   p.ldu = (int64_t)p.n_vtiles * kTile;
   p.S = pick_splits(p.T, p.n_vtiles);
   p.nt_h = (int)ceil_div(H, kTile);
-  // Average K steps per workgroup: both contractions of the chunk, each
-  // T·nt_h·(V/64) tile-steps, over kTargetCUs workgroups; one dX part must
-  // not exceed it.
+  // K parts of each chunk's dX tiles (dx_parts of the chunk's own token
+  // tiles: a short last chunk has few dX tiles, each over the whole
+  // vocabulary, and takes more parts), at a part stride of the chunk's rows.
   const int64_t steps = ceil_div(V, kBK);
-  const int64_t avg = std::max<int64_t>(1, 2 * (int64_t)p.T * p.nt_h * steps / kTargetCUs);
-  int64_t ks = std::max<int64_t>(1, ceil_div(steps, avg));
-  ks = std::min<int64_t>(ks, 16);
-  const int64_t D = ceil_div(steps, ks);
-  p.ksplit = (int)ceil_div(steps, D);   // every part holds at least one step
+  const int64_t last_rows = std::max<int64_t>(N, 1) - (int64_t)(p.nchunks - 1) * p.Nc;
+  p.ksplit = dx_parts(steps, p.T, p.nt_h);
+  p.dxp_rows = std::max<int64_t>(p.ksplit * p.Nc,
+                                 dx_parts(steps, (int)ceil_div(last_rows, kTile), p.nt_h) * last_rows);
   p.nb_prep = row_prep_blocks(std::max<int64_t>(N, 1));
   p.nb_fin = lse_finalize_blocks(Np);
   size_t o = 0;
@@ -367,7 +395,7 @@ FusedPlan plan_fused(int64_t N, int64_t H, int64_t V, lce_dtype dW_dtype) {
   p.off_U = o;       o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)p.ldu);
   p.off_ref = o;     o = align_up(o + sizeof(float) * (size_t)p.Nc * 2 * (size_t)p.n_vtiles);
   p.off_Xs = o;      o = align_up(o + sizeof(uint16_t) * (size_t)p.Nc * (size_t)H);
-  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.ksplit * (size_t)p.Nc * (size_t)H);
+  p.off_dXp = o;     o = align_up(o + sizeof(float) * (size_t)p.dxp_rows * (size_t)H);
   p.off_dWacc = o;
   if (dW_dtype == LCE_BF16) o = align_up(o + sizeof(float) * (size_t)V * (size_t)H);
   p.total = std::max<size_t>(o, kAlign);
@@ -896,6 +924,17 @@ lce_status lce_backward_plan(int64_t N, int64_t H, int64_t V, int32_t precise,
   return LCE_OK;
 }
 
+lce_status lce_fused_plan(int64_t N, int64_t H, int64_t V, int64_t* chunk_rows, int32_t* n_chunks,
+                          int32_t* dx_parts) {
+  if (!chunk_rows || !n_chunks || !dx_parts) return LCE_ERR_INVALID_ARG;
+  if (!shape_ok(N, H, V)) return LCE_ERR_SHAPE;
+  const FusedPlan pl = plan_fused(N, H, V, LCE_F32);
+  *chunk_rows = pl.Nc;
+  *n_chunks = pl.nchunks;
+  *dx_parts = pl.ksplit;
+  return LCE_OK;
+}
+
 const char* lce_status_string(lce_status status) {
   switch (status) {
     case LCE_OK: return "ok";
@@ -1296,10 +1335,11 @@ lce_status lce_forward_backward(const void* X_dev, const void* W_dev, const int6
     cp.nt_tok = T; cp.nt_h = pl.nt_h; cp.nt_v = pl.n_vtiles;
     cp.accumulate = 0; cp.dX_acc = dXp; cp.scale = post_scale;
     cp.dW_dst = dW32;
-    cp.ksplit = pl.ksplit; cp.dx_part_stride = pl.Nc * H; cp.dw_accumulate = c > 0;
+    cp.ksplit = dx_parts(ceil_div(V, kBK), T, pl.nt_h); cp.dx_part_stride = nr * H;
+    cp.dw_accumulate = c > 0;
     cp.flags = nullptr;
     LCE_LAUNCH("chunk_gemm", stream, launch_chunk_gemm(cp, stream));
-    LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, pl.ksplit, pl.Nc * H, nr, H, V, state + r0, key + r0, oh + r0, W,
+    LCE_LAUNCH("dx_finalize", stream, launch_dx_finalize(dXp, cp.ksplit, nr * H, nr, H, V, state + r0, key + r0, oh + r0, W,
                                post_scale, fixed ? rrow + r0 : nullptr, dom_col + r0, de + r0,
                                nullptr, static_cast<char*>(dX_dev) + r0 * H * dx_es,
                                dX_dtype == LCE_BF16, stream));

@@ -54,16 +54,34 @@ def backward_chunk_columns(N: int, H: int, V: int) -> int:
     return -(-per // 256) * 256
 
 
-def fused_chunk_rows(N: int, H: int) -> int:
-    """Rows per chunk of the row-chunked fused call: the largest power-of-two
-    count of 256-row tiles with at most 2H rows and, from two tiles of rows
-    on, at most half of the (256-padded) rows."""
-    Np = -(-max(N, 1) // 256) * 256
-    lim = min(2 * H, Np // 2 if Np >= 512 else Np)
-    tiles = 1
-    while tiles * 2 * 256 <= lim:
-        tiles *= 2
-    return min(Np, tiles * 256)
+def fused_chunk_rows(N: int, H: int, V: int) -> int:
+    """Rows per chunk of the row-chunked fused call (every chunk but the last).
+
+    Whole 256-row tiles, at most 2H rows and, from two tiles on, at most half
+    of the tiles rounded up.  Among the fewest chunks that meet this and up to
+    three more, each count with chunks as even as whole tiles allow, the one
+    with the least estimated time: per chunk ceil(n_vt / S) for its logits
+    pass (S = min(256 // tiles, n_vt), at least 1), plus V / 16384 for each
+    chunk after the first (a further pass over the fp32 dW)."""
+    T = -(-max(N, 1) // 256)
+    nvt = -(-V // 256)
+    half = -(-T // 2) if T >= 2 else 1
+    lim = max(1, min(2 * H // 256, half))
+    n_min = -(-T // lim)
+
+    def waves(t):
+        return -(-nvt // max(1, min(256 // t, nvt)))
+
+    best, best_cost = -(-T // n_min), None
+    for n in range(n_min, min(n_min + 3, T) + 1):
+        t = -(-T // n)
+        last = T - (n - 1) * t
+        if last <= 0:
+            continue
+        cost = float(n - 1) * waves(t) + float(waves(last)) + float(n - 1) * (V / 16384.0)
+        if best_cost is None or cost < best_cost:
+            best, best_cost = t, cost
+    return best * 256
 
 
 def sample_rows(w: L.Workload, y: np.ndarray):
@@ -71,7 +89,7 @@ def sample_rows(w: L.Workload, y: np.ndarray):
     vocabulary rows, and the mask of those vocabulary rows no label hits."""
     N, H, V = w.N, w.H, w.V
     rng = np.random.default_rng(w.seed + 303)
-    nc = fused_chunk_rows(N, H)
+    nc = fused_chunk_rows(N, H, V)
     edges = [r for k in range(1, -(-N // nc)) for r in (k * nc - 1, k * nc)]
     dx = np.unique(np.concatenate([L.row_sample(N, N_DX_ROWS, seed=w.seed + 301),
                                    np.array(edges, dtype=np.int64), [0, N - 1]]))

@@ -93,6 +93,47 @@ def test_shape_limits(lib):
     assert bwd(lib, V=big + 1) == _lib.LCE_ERR_SHAPE
 
 
+def test_fused_plan_matches_the_sampling_mirror(lib):
+    """The fused call's row chunking (lce_fused_plan) equals the mirror the
+    full-size tests use to sample both sides of every chunk boundary, and
+    meets its stated bounds: whole tiles, at most 2H rows (one tile at least)
+    and, from two tiles on, at most half the tiles rounded up; chunks as even
+    as whole tiles allow; the last chunk holds at least one row; the dX parts
+    of a full chunk follow dx_parts of its tiles."""
+    import random
+    from tests import fullsize_samples as FS
+
+    def dx_parts(steps, T, nt_h):
+        avg = max(1, 2 * T * nt_h * steps // 256)
+        ks = min(max(1, -(-steps // avg)), 16)
+        return -(-steps // -(-steps // ks))
+
+    rng = random.Random(12)
+    shapes = [(8192, 2304, 256128), (16384, 4096, 32000), (8192, 4096, 128256), (32768, 3584, 152064),
+              (256, 64, 1000), (8448, 2304, 256128), (4352, 2304, 256128), (1, 8, 1), (0, 64, 100)]
+    shapes += [(rng.randint(1, 70000), 8 * rng.randint(1, 1024), rng.randint(1, 300000)) for _ in range(300)]
+    rows, nch, parts = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    for N, H, V in shapes:
+        assert lib.lce_fused_plan(N, H, V, ctypes.byref(rows), ctypes.byref(nch),
+                                  ctypes.byref(parts)) == _lib.LCE_OK
+        nc = FS.fused_chunk_rows(N, H, V)
+        assert rows.value == nc, (N, H, V, rows.value, nc)
+        T, t = -(-max(N, 1) // 256), nc // 256
+        assert nc % 256 == 0 and t >= 1
+        assert t == 1 or nc <= 2 * H
+        assert T == 1 or t <= -(-T // 2)
+        assert nch.value == -(-max(N, 1) // nc) and max(N, 1) - (nch.value - 1) * nc >= 1
+        assert t == -(-T // nch.value), (N, H, V)
+        assert parts.value == dx_parts(-(-V // 64), t, -(-H // 256)), (N, H, V)
+    for N, H, V, n_expect in [(8192, 2304, 256128, 2), (8448, 2304, 256128, 2), (4352, 2304, 256128, 2)]:
+        assert lib.lce_fused_plan(N, H, V, ctypes.byref(rows), ctypes.byref(nch),
+                                  ctypes.byref(parts)) == _lib.LCE_OK
+        assert nch.value == n_expect, (N, nch.value)
+    assert lib.lce_fused_plan(8, 12, 5, ctypes.byref(rows), ctypes.byref(nch),
+                              ctypes.byref(parts)) == _lib.LCE_ERR_SHAPE
+    assert lib.lce_fused_plan(8, 16, 5, None, ctypes.byref(nch), ctypes.byref(parts)) == _lib.LCE_ERR_INVALID_ARG
+
+
 def test_backward_plan_matches_the_sampling_mirror(lib):
     """The chunking the library reports (lce_backward_plan) equals the mirror
     the full-size tests use to place their samples at chunk boundaries
