@@ -147,8 +147,8 @@ N_FUSED = 24
 
 @pytest.mark.parametrize("k", range(N_FUSED))
 def test_random_shape_fused_call(lce, k):
-    """The row-chunked fused call (its own grids: row chunks of a power of two
-    of 256-row tiles, split-K dX, accumulating dW) on the same kind of draws,
+    """The row-chunked fused call (its own grids: even row chunks of whole
+    256-row tiles, split-K dX per chunk, accumulating dW) on the same kind of draws,
     against the oracle's forward_backward_chunked.  The call takes label
     smoothing only without a softcap, so a draw with both drops the smoothing."""
     N, H, V, softcap, opts, labels = draw(1000 + k)
