@@ -65,6 +65,11 @@ CASES = [
     # an exactly taken entry must come out of the in-place rescale as −gs·e/V.
     (300, 64, 2, dict(label_smoothing=0.1)),
     (400, 376, 5, dict(label_smoothing=0.2, reduction="sum")),
+    # Uneven row chunks with their own dX K parts: 1536 + 1536 + 1025 rows,
+    # 6, 6 and 7 parts (the last chunk's part stride is its 1025 rows); and
+    # 1536 + 1064 rows, 6 and 7 parts.
+    (4097, 1024, 6000, dict(softcap=30.0)),
+    (2600, 1024, 4000, dict(z_loss=1e-3, reduction="none")),
 ]
 
 

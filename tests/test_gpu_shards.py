@@ -71,6 +71,10 @@ CASES = [
     (300, 64, 40000, [0, 0.5, 1.0], dict(softcap=30.0, label_smoothing=0.1, z_loss=1e-3,
                                          logit_scale=1.3, reduction="none")),
     (96, 48, 700, [0, 0.1, 0.9, 1.0], dict(label_smoothing=0.2)),
+    # 33 token tiles: each shard's forward runs a launch of 32 token tiles and
+    # one of the last tile, whose partials and per-row logit sums (label
+    # smoothing) sit in a block of their own.
+    (8400, 64, 3000, [0, 0.4, 1.0], dict(label_smoothing=0.1, softcap=30.0)),
 ]
 
 

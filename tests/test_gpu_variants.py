@@ -48,6 +48,9 @@ CASES = [
     (300, 64, 40000, dict(softcap=30.0, label_smoothing=0.05, reduction="none")),
     (700, 48, 20000, dict(softcap=4.0, logit_scale=2.0, reduction="sum")),
     (96, 64, 300, dict(softcap=80.0, label_smoothing=0.3, z_loss=5e-3)),   # general softcap path
+    # 36 token tiles: the forward's last 4 tiles run in a launch of their own,
+    # whose partials and logit sums (label smoothing) form a block of their own.
+    (9100, 64, 2500, dict(label_smoothing=0.1, z_loss=1e-3)),
 ]
 
 
