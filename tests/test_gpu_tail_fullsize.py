@@ -1,0 +1,133 @@
+"""The Gemma-2 2B head (H = 2304, V = 256128, softcap 30) at 8448 tokens, 33
+token tiles: the forward's and the logit gradient's launches for the token
+tiles past the last full group or round, and the fused call's uneven row
+chunks (4352 and 4096 rows), at the real head shape.
+
+The full-size goldens hold 8192-token workloads, where neither exists, and the
+float64 oracle cannot give every row's LSE at this size inside a test, so two
+kinds of check are used:
+  * sampled rows against the oracle at test time (only their own logits are
+    needed): LSE and loss (abs ≤ 2e-3) and dX, whole (rel L2 ≤ 1e-3) and as
+    its dense part, the output minus the oracle's one-hot term against the
+    oracle's softmax term (rel L2 ≤ 1e-2), on 47 token rows: the first and
+    last rows of the last tile, rows around the 8192 boundary and the fused
+    call's chunk boundary, and seeded rows elsewhere;
+  * additivity over rows, which holds at any size: under the summed loss a
+    row's gradient depends on its own logits, LSE and label alone, so the
+    step on all 8448 rows equals the step on rows [0, 8192) (32 token tiles,
+    no tail) together with the step on rows [8192, 8448) (one tile): equal
+    LSE (abs ≤ 1e-6: both sides split the vocabulary the same ways) and dX
+    rows, and dW the sum of the two (rel L2 ≤ 1e-5, fp32 summation order
+    aside; the label-free dW rows, whose value is the dense part alone,
+    ≤ 1e-4).  The same for the fused call, whose sub-batches run as 2 chunks
+    of 4096 rows and 1 of 256; its chunks of 17 and 16 token tiles split the
+    vocabulary 15 and 16 ways, so its LSE merges the partials in another
+    order than the sub-batches' and may differ by a few fp32 ulps (abs ≤ 1e-5
+    at an LSE of about 12).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lce_inputs as L
+from oracle import lce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+N, H, V, SOFTCAP = 8448, 2304, 256128, 30.0
+CUT = 8192
+LSE_ATOL = 2e-3
+GRAD_RTOL = 1e-3
+DENSE_RTOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def lce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_lse_amd as P
+    P.load()
+    return P
+
+
+@pytest.fixture(scope="module")
+def case(lce):
+    print(f"[tail fullsize] inputs N={N} H={H} V={V} softcap={SOFTCAP}", flush=True)
+    w = L.Workload("tail_fullsize", N=N, H=H, V=V, labels="zipf", ignore_frac=0.10,
+                   softcap=SOFTCAP, seed=L.BASE_SEED + 40)
+    X, W, y = L.make_inputs(w)
+    return X, W, y
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def exact_step(lce, X, W, y):
+    out = lce.lce_forward_ex(X, W, y, softcap=SOFTCAP, reduction="sum")
+    dX, dW = lce.lce_backward_ex(X, W, y, out["lse"], 1.0, softcap=SOFTCAP, reduction="sum")
+    return out["lse"], out["loss"], dX, dW
+
+
+def fused_step(lce, X, W, y):
+    out, dX, dW = lce.lce_forward_backward(X, W, y, 1.0, softcap=SOFTCAP, reduction="sum")
+    return out["lse"], out["loss"], dX, dW
+
+
+@pytest.mark.parametrize("path", ["exact", "fused"])
+def test_tail_rows_against_oracle(lce, case, path):
+    X, W, y = case
+    step = exact_step if path == "exact" else fused_step
+    print(f"[tail fullsize] {path}: GPU step", flush=True)
+    lse, loss, dX, _ = step(lce, X.cuda(), W.cuda(), y.cuda())
+    torch.cuda.synchronize()
+    chunk = lce.lce_fused_plan(N, H, V)["chunk_rows"]
+    rows = np.unique(np.concatenate([
+        np.arange(CUT - 4, CUT + 8), np.arange(N - 8, N), [chunk - 2, chunk - 1, chunk, chunk + 1],
+        L.row_sample(N, 24, seed=4040)])).astype(np.int64)
+    print(f"[tail fullsize] {path}: oracle on {len(rows)} rows", flush=True)
+    opts = O.options(softcap=SOFTCAP, reduction="sum")
+    X64, W64, y64 = L.to_f64(X[rows]), L.to_f64(W), y.numpy()
+    f = O.forward_ex(X64, W64, y64[rows], opts)
+    n_valid = int((y64 != L.IGNORE_INDEX).sum())
+    scale = O.row_scale(y64[rows], 1.0, n_valid, opts)
+    dense, onehot = O.dX_rows_parts(X64, W64, y64[rows], f["lse"], scale, opts)
+    g_lse, g_loss = lse.cpu().numpy()[rows], loss.cpu().numpy()[rows]
+    gx = dX[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    e_lse = float(np.abs(g_lse - f["lse"]).max())
+    e_loss = float(np.abs(g_loss - f["loss"]).max())
+    e_dx, e_dense = rel_l2(gx, dense + onehot), rel_l2(gx - onehot, dense)
+    print(f"[tail fullsize] {path}: LSE {e_lse:.2e} loss {e_loss:.2e} dX {e_dx:.2e} "
+          f"dense part {e_dense:.2e}", flush=True)
+    assert e_lse <= LSE_ATOL and e_loss <= LSE_ATOL
+    assert e_dx <= GRAD_RTOL and e_dense <= DENSE_RTOL
+
+
+@pytest.mark.parametrize("path", ["exact", "fused"])
+def test_tail_step_is_additive_over_rows(lce, case, path):
+    X, W, y = case
+    step = exact_step if path == "exact" else fused_step
+    Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
+    print(f"[tail fullsize] {path}: all rows, then [0, {CUT}) and [{CUT}, {N})", flush=True)
+    lse, _, dX, dW = step(lce, Xd, Wd, yd)
+    lse_a, _, dX_a, dW_a = step(lce, Xd[:CUT].contiguous(), Wd, yd[:CUT].contiguous())
+    lse_b, _, dX_b, dW_b = step(lce, Xd[CUT:].contiguous(), Wd, yd[CUT:].contiguous())
+    torch.cuda.synchronize()
+    e_lse = max(float((lse[:CUT] - lse_a).abs().max()), float((lse[CUT:] - lse_b).abs().max()))
+    e_dx = float(torch.linalg.vector_norm((dX - torch.cat([dX_a, dX_b])).double()) /
+                 torch.linalg.vector_norm(dX.double()))
+    dW_sum = dW_a.double() + dW_b.double()
+    e_dw = float(torch.linalg.vector_norm(dW.double() - dW_sum) / torch.linalg.vector_norm(dW_sum))
+    hit = torch.zeros(V, dtype=torch.bool, device="cuda")
+    hit[yd[yd != L.IGNORE_INDEX]] = True
+    free = ~hit
+    e_free = float(torch.linalg.vector_norm(dW[free].double() - dW_sum[free]) /
+                   torch.linalg.vector_norm(dW_sum[free]))
+    print(f"[tail fullsize] {path}: LSE {e_lse:.2e} dX {e_dx:.2e} dW {e_dw:.2e} "
+          f"label-free dW rows {e_free:.2e} ({int(free.sum())} rows)", flush=True)
+    assert e_lse <= (1e-6 if path == "exact" else 1e-5)
+    assert e_dx <= 1e-5 and e_dw <= 1e-5
+    assert e_free <= 1e-4
