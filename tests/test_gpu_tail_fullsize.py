@@ -1,7 +1,8 @@
-"""The Gemma-2 2B head (H = 2304, V = 256128, softcap 30) at 8448 tokens, 33
-token tiles: the forward's and the logit gradient's launches for the token
-tiles past the last full group or round, and the fused call's uneven row
-chunks (4352 and 4096 rows), at the real head shape.
+"""The Gemma-2 2B head (H = 2304, V = 256128, softcap 30) and the Llama-3 8B
+head (H = 4096, V = 128256) at 8448 tokens, 33 token tiles: the forward's and
+the logit gradient's launches for the token tiles past the last full group or
+round, and the fused call's uneven row chunks (4352 and 4096 rows), at real
+head shapes.
 
 The full-size goldens hold 8192-token workloads, where neither exists, and the
 float64 oracle cannot give every row's LSE at this size inside a test, so two
@@ -23,7 +24,13 @@ kinds of check are used:
     of 4096 rows and 1 of 256; its chunks of 17 and 16 token tiles split the
     vocabulary 15 and 16 ways, so its LSE merges the partials in another
     order than the sub-batches' and may differ by a few fp32 ulps (abs ≤ 1e-5
-    at an LSE of about 12).
+    at an LSE of about 12).  Under the softcap the stored block's reference
+    is fixed and the rest stays at the fp32 bars above; without it the
+    reference is the running maximum along each split's sweep, which moves
+    with the splits, so the block's bf16 rounding differs between the two
+    sides: dX and dW within 1e-4, the label-free dW rows within the dense
+    part's bf16 bar, 1e-2 (measured 1.2e-3, about the rms of one bf16
+    rounding, 2^-8/√12).
 """
 import numpy as np
 import pytest
@@ -34,8 +41,10 @@ from oracle import lce_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-N, H, V, SOFTCAP = 8448, 2304, 256128, 30.0
-CUT = 8192
+N, CUT = 8448, 8192
+# head: H, V, softcap (Gemma-2 2B: the fused call's fixed reference; Llama-3
+# 8B: its running reference and in-place rescale)
+HEADS = {"gemma2_2b": (2304, 256128, 30.0), "llama3_8b": (4096, 128256, 0.0)}
 LSE_ATOL = 2e-3
 GRAD_RTOL = 1e-3
 DENSE_RTOL = 1e-2
@@ -50,13 +59,14 @@ def lce():
     return P
 
 
-@pytest.fixture(scope="module")
-def case(lce):
-    print(f"[tail fullsize] inputs N={N} H={H} V={V} softcap={SOFTCAP}", flush=True)
+@pytest.fixture(scope="module", params=sorted(HEADS))
+def case(lce, request):
+    H, V, softcap = HEADS[request.param]
+    print(f"[tail fullsize] {request.param}: inputs N={N} H={H} V={V} softcap={softcap}", flush=True)
     w = L.Workload("tail_fullsize", N=N, H=H, V=V, labels="zipf", ignore_frac=0.10,
-                   softcap=SOFTCAP, seed=L.BASE_SEED + 40)
+                   softcap=softcap, seed=L.BASE_SEED + 40 + H)
     X, W, y = L.make_inputs(w)
-    return X, W, y
+    return request.param, softcap, X, W, y
 
 
 def rel_l2(a, b):
@@ -66,30 +76,31 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
-def exact_step(lce, X, W, y):
-    out = lce.lce_forward_ex(X, W, y, softcap=SOFTCAP, reduction="sum")
-    dX, dW = lce.lce_backward_ex(X, W, y, out["lse"], 1.0, softcap=SOFTCAP, reduction="sum")
+def exact_step(lce, X, W, y, softcap):
+    out = lce.lce_forward_ex(X, W, y, softcap=softcap, reduction="sum")
+    dX, dW = lce.lce_backward_ex(X, W, y, out["lse"], 1.0, softcap=softcap, reduction="sum")
     return out["lse"], out["loss"], dX, dW
 
 
-def fused_step(lce, X, W, y):
-    out, dX, dW = lce.lce_forward_backward(X, W, y, 1.0, softcap=SOFTCAP, reduction="sum")
+def fused_step(lce, X, W, y, softcap):
+    out, dX, dW = lce.lce_forward_backward(X, W, y, 1.0, softcap=softcap, reduction="sum")
     return out["lse"], out["loss"], dX, dW
 
 
 @pytest.mark.parametrize("path", ["exact", "fused"])
 def test_tail_rows_against_oracle(lce, case, path):
-    X, W, y = case
+    head, softcap, X, W, y = case
+    H, V = X.shape[1], W.shape[0]
     step = exact_step if path == "exact" else fused_step
-    print(f"[tail fullsize] {path}: GPU step", flush=True)
-    lse, loss, dX, _ = step(lce, X.cuda(), W.cuda(), y.cuda())
+    print(f"[tail fullsize] {head} {path}: GPU step", flush=True)
+    lse, loss, dX, _ = step(lce, X.cuda(), W.cuda(), y.cuda(), softcap)
     torch.cuda.synchronize()
     chunk = lce.lce_fused_plan(N, H, V)["chunk_rows"]
     rows = np.unique(np.concatenate([
         np.arange(CUT - 4, CUT + 8), np.arange(N - 8, N), [chunk - 2, chunk - 1, chunk, chunk + 1],
         L.row_sample(N, 24, seed=4040)])).astype(np.int64)
-    print(f"[tail fullsize] {path}: oracle on {len(rows)} rows", flush=True)
-    opts = O.options(softcap=SOFTCAP, reduction="sum")
+    print(f"[tail fullsize] {head} {path}: oracle on {len(rows)} rows", flush=True)
+    opts = O.options(softcap=softcap, reduction="sum")
     X64, W64, y64 = L.to_f64(X[rows]), L.to_f64(W), y.numpy()
     f = O.forward_ex(X64, W64, y64[rows], opts)
     n_valid = int((y64 != L.IGNORE_INDEX).sum())
@@ -100,7 +111,7 @@ def test_tail_rows_against_oracle(lce, case, path):
     e_lse = float(np.abs(g_lse - f["lse"]).max())
     e_loss = float(np.abs(g_loss - f["loss"]).max())
     e_dx, e_dense = rel_l2(gx, dense + onehot), rel_l2(gx - onehot, dense)
-    print(f"[tail fullsize] {path}: LSE {e_lse:.2e} loss {e_loss:.2e} dX {e_dx:.2e} "
+    print(f"[tail fullsize] {head} {path}: LSE {e_lse:.2e} loss {e_loss:.2e} dX {e_dx:.2e} "
           f"dense part {e_dense:.2e}", flush=True)
     assert e_lse <= LSE_ATOL and e_loss <= LSE_ATOL
     assert e_dx <= GRAD_RTOL and e_dense <= DENSE_RTOL
@@ -108,13 +119,14 @@ def test_tail_rows_against_oracle(lce, case, path):
 
 @pytest.mark.parametrize("path", ["exact", "fused"])
 def test_tail_step_is_additive_over_rows(lce, case, path):
-    X, W, y = case
+    head, softcap, X, W, y = case
+    V = W.shape[0]
     step = exact_step if path == "exact" else fused_step
     Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
-    print(f"[tail fullsize] {path}: all rows, then [0, {CUT}) and [{CUT}, {N})", flush=True)
-    lse, _, dX, dW = step(lce, Xd, Wd, yd)
-    lse_a, _, dX_a, dW_a = step(lce, Xd[:CUT].contiguous(), Wd, yd[:CUT].contiguous())
-    lse_b, _, dX_b, dW_b = step(lce, Xd[CUT:].contiguous(), Wd, yd[CUT:].contiguous())
+    print(f"[tail fullsize] {head} {path}: all rows, then [0, {CUT}) and [{CUT}, {N})", flush=True)
+    lse, _, dX, dW = step(lce, Xd, Wd, yd, softcap)
+    lse_a, _, dX_a, dW_a = step(lce, Xd[:CUT].contiguous(), Wd, yd[:CUT].contiguous(), softcap)
+    lse_b, _, dX_b, dW_b = step(lce, Xd[CUT:].contiguous(), Wd, yd[CUT:].contiguous(), softcap)
     torch.cuda.synchronize()
     e_lse = max(float((lse[:CUT] - lse_a).abs().max()), float((lse[CUT:] - lse_b).abs().max()))
     e_dx = float(torch.linalg.vector_norm((dX - torch.cat([dX_a, dX_b])).double()) /
@@ -126,8 +138,9 @@ def test_tail_step_is_additive_over_rows(lce, case, path):
     free = ~hit
     e_free = float(torch.linalg.vector_norm(dW[free].double() - dW_sum[free]) /
                    torch.linalg.vector_norm(dW_sum[free]))
-    print(f"[tail fullsize] {path}: LSE {e_lse:.2e} dX {e_dx:.2e} dW {e_dw:.2e} "
+    print(f"[tail fullsize] {head} {path}: LSE {e_lse:.2e} dX {e_dx:.2e} dW {e_dw:.2e} "
           f"label-free dW rows {e_free:.2e} ({int(free.sum())} rows)", flush=True)
+    running_ref = path == "fused" and softcap == 0.0
     assert e_lse <= (1e-6 if path == "exact" else 1e-5)
-    assert e_dx <= 1e-5 and e_dw <= 1e-5
-    assert e_free <= 1e-4
+    assert e_dx <= (1e-4 if running_ref else 1e-5) and e_dw <= (1e-4 if running_ref else 1e-5)
+    assert e_free <= (DENSE_RTOL if running_ref else 1e-4)
