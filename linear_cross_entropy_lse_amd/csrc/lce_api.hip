@@ -286,12 +286,13 @@ OrderPlan plan_order(int64_t N, int64_t H, int64_t V) {
   return p;
 }
 
-// Fused row-chunk variant.  Chunk rows: 256 times a power of two, at most H
-// (the bf16 logits block Nc x V is then no larger than W), at least 256, at
-// most N rounded up; a power-of-two count of token tiles divides the 256
-// workgroups of the grid evenly.  The dX tiles of one chunk contract over the whole vocabulary;
+// Fused row-chunk variant.  Chunk rows: whole 256-row tiles, T of them in
+// every chunk but the last (fused_chunk_tiles sets T and with it the chunk
+// count).  The dX tiles of one chunk contract over the whole vocabulary;
 // their K range is split so that one part costs no more than the average
-// work per workgroup (the dW tiles contract over the chunk's rows only).
+// work per workgroup (the dW tiles contract over the chunk's rows only),
+// each chunk by its own token tiles: ksplit is a full chunk's, dxp_rows
+// covers the last chunk's parts too.
 struct FusedPlan {
   int64_t Nc, ldu;
   int nchunks, T, S, n_vtiles, nt_h, ksplit, nb_prep, nb_fin;

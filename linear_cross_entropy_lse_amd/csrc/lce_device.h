@@ -660,8 +660,9 @@ __device__ __forceinline__ void grid_tile(int g, int T, int tt, int ss, int& ti,
 // (rt·S = kXcds·kCusPerXcd), and within the round the workgroups of XCD x
 // (hardware id % 8) take a (rt / 8) x S block of it.  Workgroups start in id
 // order, so the ones resident together form about one round, and each XCD's
-// block shares its X and W blocks in L2.  In the last round ti may pass the
-// last token tile; the caller skips such a workgroup.
+// block shares its X and W blocks in L2.  In a partly filled last round (the
+// host launches full rounds only) ti would pass the last token tile; the
+// caller skips such a workgroup.
 __device__ __forceinline__ void round_tile(int b, int rt, int& ti, int& split) {
   const int per_round = kXcds * kCusPerXcd;
   const int r = b / per_round, q = b - r * per_round;

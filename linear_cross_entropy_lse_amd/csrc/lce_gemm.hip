@@ -371,7 +371,7 @@ grad_logits_kernel(GradParams p) {
   int ti, split;
   if (p.round_tiles > 0) {
     round_tile(blockIdx.x, p.round_tiles, ti, split);
-    if (ti >= p.T) return;   // past the last token tile (last round only)
+    if (ti >= p.T) return;   // past the last token tile (the host launches full rounds only)
   } else {
     grid_tile(xcd_remap(blockIdx.x, gridDim.x), p.T, p.tt, p.ss, ti, split);
   }
