@@ -55,6 +55,38 @@ def test_workspace_queries(lib):
         assert lib.lce_forward_workspace_bytes(N, H, V) < 64 * N * 8 + (1 << 20)
 
 
+def test_forward_workspace_holds_the_split_partials(lib):
+    """The forward workspace is the row state and target (8 bytes a row), the
+    split partials m, s and the logit sums (12 bytes a row and split) and the
+    per-block sums (24 bytes a block of 256 rows), each region aligned to 256
+    bytes.  Up to 32 token tiles every row has S = min(256 / T, vocabulary
+    tiles) splits; past that the rows of the full groups of 32 tiles have 8
+    and the r tiles after them min(256 / r, vocabulary tiles), so the tail's
+    block adds at most 256·256 partials, 768 KiB, over 8 a row."""
+    import random
+
+    def parts(N, V):
+        T, nvt = max(1, -(-N // 256)), -(-V // 256)
+        S = max(1, min(256 // min(T, 32), nvt))
+        tail = T % 32 if T > 32 else 0
+        if not tail:
+            return S * N, 0
+        main = (T - tail) * 256
+        s_tail = max(1, min(256 // tail, nvt))
+        return S * main + s_tail * (N - main), s_tail * (N - main)
+
+    rng = random.Random(13)
+    shapes = [(8192, 256128), (8193, 256128), (8448, 256128), (16640, 32000), (16383, 5), (1, 1),
+              (32 * 256 + 1, 1000), (63 * 256, 128256), (640000, 2048)]
+    shapes += [(rng.randint(1, 200000), rng.randint(1, 300000)) for _ in range(300)]
+    for N, V in shapes:
+        total, tail = parts(N, V)
+        lo = 8 * N + 12 * total + 24 * -(-N // 256)
+        ws = lib.lce_forward_workspace_bytes(N, 64, V)
+        assert lo <= ws <= lo + 6 * 256, (N, V, ws, lo)
+        assert 12 * tail <= 768 << 10
+
+
 FAKE = 1 << 20  # a 256-byte-aligned non-NULL address: never dereferenced on these paths
 
 
