@@ -107,3 +107,26 @@ def test_vocabulary_permutation(lce, N, H, V, softcap):
           flush=True)
     assert e_lse <= ATOL and e_loss <= ATOL
     assert e_dx <= GRAD_RTOL and e_dw <= GRAD_RTOL
+
+
+def test_noncontiguous_inputs_match_contiguous(lce):
+    """Strided and transposed views (a contiguity class of wrong results the
+    Liger Kernel paper page lists among its test cases) give bitwise the
+    results of contiguous copies: the binding passes the kernels, which
+    address memory directly, contiguous tensors."""
+    N, H, V, softcap = 300, 72, 2000, 30.0
+    X, W, y = inputs(N, H, V, 7300, softcap)
+    Xv = X.t().contiguous().t()                                   # column-major view
+    Wbig = torch.zeros(2 * V, H, dtype=torch.bfloat16, device="cuda")
+    Wbig[::2] = W
+    Wv = Wbig[::2]                                                # row stride 2H
+    ybig = torch.full((2 * N,), -7, dtype=torch.int64, device="cuda")
+    ybig[1::2] = y
+    yv = ybig[1::2]                                               # element stride 2
+    assert not (Xv.is_contiguous() or Wv.is_contiguous() or yv.is_contiguous())
+    print(f"[invariance] non-contiguous views N={N} H={H} V={V}", flush=True)
+    a, dX, dW = step(lce, X, W, y, softcap)
+    b, dXv, dWv = step(lce, Xv, Wv, yv, softcap)
+    for k in ("loss", "lse", "mean", "n_valid"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(dX, dXv) and torch.equal(dW, dWv)
