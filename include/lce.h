@@ -455,9 +455,9 @@ lce_status lce_backward_plan(int64_t N, int64_t H, int64_t V, int32_t precise,
 /*
  * The row chunking of lce_forward_backward for these sizes (host call, pure
  * computation, the plan the call follows): the rows per chunk (a multiple of
- * 256; the last chunk holds the rest, at least one row), the number of
- * chunks, and the K parts the dX tiles of a full chunk are split into (a
- * shorter last chunk may take more).  The workspace holds one bf16 block of
+ * 256; the last chunk holds the rest, at least one row; N = 0 is planned as
+ * one row), the number of chunks, and the K parts the dX tiles of a full
+ * chunk are split into (a shorter last chunk may take more).  The workspace holds one bf16 block of
  * chunk_rows x 256·ceil(V/256) values.  Returns LCE_OK, LCE_ERR_SHAPE (shape
  * out of range) or LCE_ERR_INVALID_ARG (NULL output).
  */
