@@ -46,6 +46,7 @@ def step(lce, X, W, y, dloss, softcap, precise=False):
     (600, 136, 40000, 30.0, False),    # several chunks, K tail, ragged rows and vocabulary
     (256, 64, 1000, 0.0, False),       # the tiny workload's shape
     (300, 64, 2000, 30.0, True),       # the precise gradient (two contractions per chunk)
+    (8300, 64, 3000, 30.0, False),     # 33 token tiles: the forward's and the gradient's tail launches
 ])
 def test_graph_replays_match_eager(lce, N, H, V, softcap, precise):
     seeds = [21, 22, 23]
