@@ -1,4 +1,4 @@
-"""The training step captured in a HIP graph.
+"""The training step, and the row-chunked fused call, captured in a HIP graph.
 
 Every entry point of the step only enqueues kernels on the caller's stream (no
 allocation, copy, memset or synchronisation inside the library), so a
@@ -72,4 +72,40 @@ def test_graph_replays_match_eager(lce, N, H, V, softcap, precise):
             assert torch.equal(a, b)
         # eager work between replays
         step(lce, *sets[(k + 1) % 3], dloss, softcap, precise)
+        torch.cuda.synchronize()
+
+
+def fused_step(lce, X, W, y, dloss, softcap):
+    out, dX, dW = lce.lce_forward_backward(X, W, y, dloss, softcap=softcap)
+    return [out["loss"], out["lse"], out["reduced"], out["n_valid"], dX, dW]
+
+
+@pytest.mark.parametrize("N,H,V,softcap", [
+    (600, 136, 40000, 30.0),     # two row chunks, fixed reference
+    (2600, 1024, 4000, 0.0),     # uneven chunks (1536 + 1064 rows, 6 and 7 dX parts), running reference
+])
+def test_fused_graph_replays_match_eager(lce, N, H, V, softcap):
+    """The row-chunked fused call captured once and replayed, as above."""
+    seeds = [31, 32, 33]
+    sets = [inputs(N, H, V, s, softcap) for s in seeds]
+    dloss = torch.tensor(0.7, dtype=torch.float32, device="cuda")
+    print(f"[graph] fused N={N} H={H} V={V} softcap={softcap}: eager", flush=True)
+    eager = [fused_step(lce, X, W, y, dloss, softcap) for X, W, y in sets]
+    torch.cuda.synchronize()
+    Xb, Wb, yb = (t.clone() for t in sets[0])
+    g = torch.cuda.CUDAGraph()
+    print("[graph] fused capture", flush=True)
+    with torch.cuda.graph(g):
+        outs = fused_step(lce, Xb, Wb, yb, dloss, softcap)
+    for rep, k in enumerate([0, 1, 2, 1, 0]):
+        X, W, y = sets[k]
+        Xb.copy_(X)
+        Wb.copy_(W)
+        yb.copy_(y)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] fused replay {rep} on input set {k}", flush=True)
+        for a, b in zip(eager[k], outs):
+            assert torch.equal(a, b)
+        fused_step(lce, *sets[(k + 1) % 3], dloss, softcap)
         torch.cuda.synchronize()
