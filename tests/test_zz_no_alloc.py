@@ -108,3 +108,43 @@ def test_noalloc_limit_and_empty(lib):
     torch.cuda.synchronize()
     assert st == _lib.LCE_OK
     assert float(mean) == 0.0 and int(nv) == 0
+
+
+def test_noalloc_under_graph_capture(lib):
+    """The use the variant exists for: the call captured into a HIP graph
+    (nothing is allocated inside the capture) and replayed on new inputs
+    copied into the captured buffers, with eager calls between the replays;
+    every replay equals lce_forward on the same inputs bit for bit.  The
+    first call on the device (which looks up the scratch address) runs
+    before the capture."""
+    from linear_cross_entropy_lse_amd import _lib
+    N, H, V, c = 9000, 64, 3000, 30.0
+    sets = [inputs(N, H, V, c, 20 + k) for k in range(3)]
+    refs = [forward_with_workspace(lib, *s, c) for s in sets]
+    torch.cuda.synchronize()
+    Xb, Wb, yb = (t.clone() for t in sets[0])
+    forward_noalloc(lib, Xb, Wb, yb, c)
+    out = {"loss": torch.empty(N, device="cuda"), "lse": torch.empty(N, device="cuda"),
+           "mean": torch.empty(1, device="cuda"),
+           "n_valid": torch.empty(1, dtype=torch.int32, device="cuda"),
+           "bad": torch.empty(1, dtype=torch.int32, device="cuda")}
+    g = torch.cuda.CUDAGraph()
+    print(f"[noalloc] capture N={N} H={H} V={V} softcap={c}", flush=True)
+    with torch.cuda.graph(g):
+        st = lib.lce_forward_noalloc(Xb.data_ptr(), Wb.data_ptr(), yb.data_ptr(), N, H, V, -100,
+                                     ctypes.c_float(c), out["loss"].data_ptr(),
+                                     out["lse"].data_ptr(), out["mean"].data_ptr(),
+                                     out["n_valid"].data_ptr(), out["bad"].data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == _lib.LCE_OK, _lib.status_string(st)
+    for rep, k in enumerate([1, 2, 0, 1]):
+        X, W, y = sets[k]
+        Xb.copy_(X)
+        Wb.copy_(W)
+        yb.copy_(y)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[noalloc] replay {rep} on input set {k}", flush=True)
+        for key in out:
+            assert torch.equal(out[key], refs[k][key]), key
+        forward_noalloc(lib, *sets[(k + 2) % 3], c)   # eager use of the same scratch between replays
