@@ -1,4 +1,5 @@
-"""The training step, and the row-chunked fused call, captured in a HIP graph.
+"""The training step, the row-chunked fused call, and the vocabulary shards
+with the vocabulary order and the sorted backward, captured in a HIP graph.
 
 Every entry point of the step only enqueues kernels on the caller's stream (no
 allocation, copy, memset or synchronisation inside the library), so a
@@ -108,4 +109,42 @@ def test_fused_graph_replays_match_eager(lce, N, H, V, softcap):
         for a, b in zip(eager[k], outs):
             assert torch.equal(a, b)
         fused_step(lce, *sets[(k + 1) % 3], dloss, softcap)
+        torch.cuda.synchronize()
+
+
+def shard_and_sorted_step(lce, X, W, y, dloss, softcap):
+    from tests.test_gpu_shards import run_shards
+    V = W.shape[0]
+    _, out, dX, dW = run_shards(lce, X, W, y, [0, V // 3, V], dict(softcap=softcap), dloss)
+    mean_logit, order = lce.lce_vocab_order(X, W, y)
+    lse = lce.lce_forward(X, W, y, -100, softcap)["lse"]
+    sX, sW = lce.lce_backward_sorted(X, W, y, lse, dloss, order, softcap=softcap)
+    return [out["loss"], out["lse"], out["reduced"], dX, dW, mean_logit, order, sX, sW]
+
+
+def test_shard_and_sorted_graph_replays_match_eager(lce):
+    """Two vocabulary shards (forwards, merge, backwards), the vocabulary
+    order and the backward on it, captured once and replayed, as above."""
+    N, H, V, softcap = 700, 72, 6000, 30.0
+    sets = [inputs(N, H, V, s, softcap) for s in (41, 42, 43)]
+    dloss = torch.tensor(0.7, dtype=torch.float32, device="cuda")
+    print(f"[graph] shards + sorted N={N} H={H} V={V}: eager", flush=True)
+    eager = [shard_and_sorted_step(lce, X, W, y, dloss, softcap) for X, W, y in sets]
+    torch.cuda.synchronize()
+    Xb, Wb, yb = (t.clone() for t in sets[0])
+    g = torch.cuda.CUDAGraph()
+    print("[graph] shards + sorted capture", flush=True)
+    with torch.cuda.graph(g):
+        outs = shard_and_sorted_step(lce, Xb, Wb, yb, dloss, softcap)
+    for rep, k in enumerate([0, 1, 2, 1]):
+        X, W, y = sets[k]
+        Xb.copy_(X)
+        Wb.copy_(W)
+        yb.copy_(y)
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] shards + sorted replay {rep} on input set {k}", flush=True)
+        for a, b in zip(eager[k], outs):
+            assert torch.equal(a, b)
+        shard_and_sorted_step(lce, *sets[(k + 1) % 3], dloss, softcap)
         torch.cuda.synchronize()
