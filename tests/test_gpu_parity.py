@@ -274,12 +274,29 @@ def test_zero_weight_closed_form(lce):
     assert rel_l2(g["dW"], expect) < 1e-3
 
 
-def test_deterministic_bitwise(lce):
-    X, W, y = synth(600, 200, 1500, seed=12, softcap=5.0)
+@pytest.mark.parametrize("N,H,V", [
+    (600, 200, 1500),
+    (8300, 64, 3000),    # 33 token tiles: the forward's and the gradient's tail launches
+])
+def test_deterministic_bitwise(lce, N, H, V):
+    X, W, y = synth(N, H, V, seed=12, softcap=5.0)
     a = run_gpu(lce, X, W, y, 5.0)
     b = run_gpu(lce, X, W, y, 5.0)
     for k in ("loss", "lse", "mean", "dX", "dW"):
         assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+
+
+def test_fused_deterministic_bitwise(lce):
+    """The fused call twice on uneven row chunks (1536 + 1064 rows, their own
+    dX parts): bitwise the same outputs."""
+    X, W, y = synth(2600, 1024, 4000, seed=14, softcap=0.0)
+    Xd, Wd, yd = X.cuda(), W.cuda(), y.cuda()
+    a = lce.lce_forward_backward(Xd, Wd, yd, 1.0)
+    b = lce.lce_forward_backward(Xd, Wd, yd, 1.0)
+    torch.cuda.synchronize()
+    for k in ("loss", "lse", "reduced"):
+        assert torch.equal(a[0][k], b[0][k]), k
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
 
 
 def test_autograd_wrapper(lce):
